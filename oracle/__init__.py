@@ -1,0 +1,119 @@
+"""CPU oracle for exact top-k -> top-p sampling (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the package smoke check and the CPU-baseline leg of the
+benchmark may import this package.  The HIP sampler never calls it and shares
+no code with it.
+
+``oracle/tes_oracle.cpp`` is the definition (plain C++, stable sort, 128-bit
+integers, its own Philox4x32-10); this module builds it with the host
+compiler and exposes it through ctypes.  ``oracle/brute.py`` is an
+independent exact-rational brute force for tiny rows, used to pin it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tes_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle_tes.so")
+_lib = None
+
+INFO_FIELDS = ("k_eff", "P", "m_inf", "M_k", "T", "kept", "M_p", "t", "pos", "kind")
+
+
+def build(force: bool = True, out: str | None = None, src: str | None = None) -> str:
+    """Compile the oracle into a shared library with g++ and return its path."""
+    out = out or _LIB
+    src = src or _SRC
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", tmp, src]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one built oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_uniform_u64.argtypes = [ctypes.c_uint64] * 3
+        lib.oracle_uniform_u64.restype = ctypes.c_uint64
+        lib.oracle_sample_row.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_sample_row.restype = ctypes.c_int
+        lib.oracle_topk_topp_sample.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int]
+        lib.oracle_topk_topp_sample.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    # -- Philox -------------------------------------------------------------
+    def philox(self, ctr, key):
+        c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+        k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+        o = (ctypes.c_uint32 * 4)()
+        self.lib.oracle_philox4x32_10(c, k, o)
+        return [int(x) for x in o]
+
+    def uniform_u64(self, seed: int, row: int, offset: int) -> int:
+        return int(self.lib.oracle_uniform_u64(seed, row, offset))
+
+    # -- sampling -------------------------------------------------------------
+    def sample_row(self, row, top_k: int, top_p: float, u: int, want_renorm: bool = True):
+        row = np.ascontiguousarray(row, dtype=np.float32)
+        V = row.size
+        tok = np.zeros(1, np.int32)
+        ren = np.zeros(V, np.float32) if want_renorm else None
+        info = np.zeros(10, np.int64)
+        rc = self.lib.oracle_sample_row(
+            row.ctypes.data, V, int(top_k), float(top_p), int(u) & (2**64 - 1),
+            tok.ctypes.data, ren.ctypes.data if ren is not None else None, info.ctypes.data)
+        if rc:
+            raise RuntimeError("oracle_sample_row failed: %d" % rc)
+        return int(tok[0]), ren, dict(zip(INFO_FIELDS, (int(x) for x in info)))
+
+    def sample(self, probs, top_k, top_p, seed: int, offset: int, want_renorm: bool = False,
+               want_info: bool = False, n_threads: int | None = None):
+        probs = np.ascontiguousarray(probs, dtype=np.float32)
+        B, V = probs.shape
+        top_k = np.ascontiguousarray(top_k, dtype=np.int32)
+        top_p = np.ascontiguousarray(top_p, dtype=np.float32)
+        assert top_k.shape == (B,) and top_p.shape == (B,)
+        tok = np.zeros(B, np.int32)
+        ren = np.zeros((B, V), np.float32) if want_renorm else None
+        info = np.zeros((B, 10), np.int64) if want_info else None
+        if n_threads is None:
+            n_threads = len(os.sched_getaffinity(0))
+        rc = self.lib.oracle_topk_topp_sample(
+            probs.ctypes.data, B, V, top_k.ctypes.data, top_p.ctypes.data,
+            int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), tok.ctypes.data,
+            ren.ctypes.data if ren is not None else None,
+            info.ctypes.data if info is not None else None, int(n_threads))
+        if rc:
+            raise RuntimeError("oracle_topk_topp_sample failed: %d" % rc)
+        return tok, ren, info
+
+
+def load(path: str | None = None) -> Oracle:
+    """Load the built oracle (building it first if it is missing or stale)."""
+    global _lib
+    if path is not None:
+        return Oracle(path)
+    if _lib is None:
+        build(force=False)
+        _lib = Oracle(_LIB)
+    return _lib

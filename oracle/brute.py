@@ -1,0 +1,116 @@
+"""Brute-force exact-rational reference for tiny rows (TEST INFRASTRUCTURE).
+
+Written from the definitions, not from the C++ oracle, so that the two can
+pin each other:
+
+* the support is the set of entries whose *rank* is below k, where rank(i)
+  counts entries with a larger value, or an equal value and a lower index
+  (the FlashInfer "cake_sampling" page, Semantics: first k of
+  lexsort(-prob, index); ties go to the lower vocabulary index).  This is an
+  O(V^2) count, no sort;
+* values are compared as exact rationals after sanitising (NaN, negative,
+  -0.0 become +0; same page, NaN / Inf);
+* masses are floor(min(x, 1) * 2^32) evaluated with ``fractions.Fraction``;
+* the kept set is the shortest sorted prefix whose inclusive mass reaches
+  (P / 2^24) of the top-k mass -- the nucleus of SonicSampler eq. (10),
+  taken relative to the top-k mass as in the top-k-first composition;
+* the token is the kept entry whose CDF interval [S_excl, S_incl) / M_p
+  contains u / 2^64 (inverse CDF), again with exact rationals.
+
+Usable for V up to a few dozen; intended for V <= 10.
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+from fractions import Fraction
+
+TWO24 = 1 << 24
+TWO32 = 1 << 32
+TWO64 = 1 << 64
+
+
+def _f32(x) -> float:
+    """Round-trip through fp32 so the value is exactly the stored float."""
+    return struct.unpack("<f", struct.pack("<f", float(x)))[0]
+
+
+def _from_bits(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", bits & 0xFFFFFFFF))[0]
+
+
+def sanitized_value(x: float):
+    """+0 for NaN and for anything carrying a sign bit; math.inf stays inf."""
+    if math.isnan(x) or math.copysign(1.0, x) < 0:
+        return Fraction(0)
+    if math.isinf(x):
+        return math.inf
+    return Fraction(x)
+
+
+def _greater(a, b) -> bool:
+    if a is math.inf:
+        return b is not math.inf
+    if b is math.inf:
+        return False
+    return a > b
+
+
+def fixed_p(p: float) -> int:
+    p = _f32(p)
+    if math.isnan(p) or p <= 0:
+        return 1
+    if p >= 1:
+        return TWO24
+    r = round(Fraction(p) * TWO24)  # Python rounds half to even
+    return max(1, int(r))
+
+
+def brute_row(row_bits, k: int, p: float, u: int):
+    """Return (token, kept indices in sorted order, weights as Fractions).
+
+    ``row_bits`` is a sequence of fp32 bit patterns (ints), so NaN payloads,
+    -0.0 and denormals reach this function unchanged.
+    """
+    xs = [_from_bits(int(v)) for v in row_bits]
+    V = len(xs)
+    vals = [sanitized_value(x) for x in xs]
+    k_eff = V if (k <= 0 or k >= V) else k
+
+    rank = []
+    for i in range(V):
+        r = 0
+        for j in range(V):
+            if _greater(vals[j], vals[i]) or (vals[j] == vals[i] and j < i):
+                r += 1
+        rank.append(r)
+    support = sorted((i for i in range(V) if rank[i] < k_eff), key=lambda i: rank[i])
+
+    infs = [i for i in support if vals[i] is math.inf]
+    if infs:
+        m = len(infs)
+        # u / 2^64 falls in [t/m, (t+1)/m)
+        t = next(t for t in range(m) if Fraction(u, TWO64) < Fraction(t + 1, m))
+        return infs[t], infs, [Fraction(1, m)] * m
+
+    def mass(v):
+        return TWO32 if v >= 1 else math.floor(v * TWO32)
+
+    q = [mass(vals[i]) for i in support]
+    M_k = sum(q)
+    if M_k == 0:
+        return min(support), [], []
+
+    target = Fraction(fixed_p(p), TWO24) * M_k
+    n = next(n for n in range(1, len(support) + 1) if sum(q[:n]) >= target)
+    kept = support[:n]
+    M_p = sum(q[:n])
+    x = Fraction(u, TWO64)
+    acc = 0
+    for j in range(n):
+        lo, hi = Fraction(acc, M_p), Fraction(acc + q[j], M_p)
+        acc += q[j]
+        if lo <= x < hi:
+            return kept[j], kept, [Fraction(qj, M_p) for qj in q[:n]]
+    raise AssertionError("u outside [0, 1)")

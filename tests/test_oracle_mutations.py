@@ -1,0 +1,133 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle/tes_oracle.cpp, changes one expression into a
+plausible mistake (a flipped tie rule, a floor turned into rounding, an
+off-by-one in the top-p test, a swapped Philox word, ...), builds the copy
+into a temporary directory and runs the pin battery against it.  The test
+passes only if at least one pin fails for every planted mistake.  Nothing
+here touches the GPU.
+"""
+
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import tests.test_oracle_brute as pb
+import tests.test_oracle_philox as pp
+import tests.test_oracle_properties as pr
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "tes_oracle.cpp")
+
+MUTATIONS = {
+    "tie_to_higher_index": (
+        "return key[a] > key[b]; });",
+        "return key[a] != key[b] ? key[a] > key[b] : a > b; });"),
+    "negatives_not_sanitised": (
+        "if (std::isnan(x) || std::signbit(x)) return 0u;",
+        "if (std::isnan(x)) return 0u;"),
+    "mass_rounds_instead_of_floor": (
+        "return (uint64_t)std::floor(std::ldexp(v, 32));",
+        "return (uint64_t)std::nearbyint(std::ldexp(v, 32));"),
+    "mass_not_saturated": (
+        "if (v >= 1.0) return (uint64_t)1 << 32;",
+        "if (v >= 2.0) return (uint64_t)1 << 33;"),
+    "threshold_floor_not_ceil": (
+        "(((uint64_t)prod & 0xFFFFFFu) != 0 ? 1 : 0)",
+        "0"),
+    "keep_while_not_strict": (
+        "while (kept < k_eff && s_excl < T)",
+        "while (kept < k_eff && s_excl <= T)"),
+    "draw_compare_not_strict": (
+        "while (s_incl <= t)",
+        "while (s_incl < t)"),
+    "uniform_words_swapped": (
+        "return (uint64_t)out[0] | ((uint64_t)out[1] << 32);",
+        "return (uint64_t)out[1] | ((uint64_t)out[0] << 32);"),
+    "philox_weyl_constant": (
+        "kPhiloxWeyl1 = 0xBB67AE85u;",
+        "kPhiloxWeyl1 = 0xBB67AE86u;"),
+    "philox_key_word": (
+        "uint32_t n0 = hi1 ^ c[1] ^ k[0];",
+        "uint32_t n0 = hi1 ^ c[1] ^ k[1];"),
+    "counter_row_offset_swapped": (
+        "uint32_t ctr[4] = {(uint32_t)offset, (uint32_t)(offset >> 32), (uint32_t)row,\n"
+        "                       (uint32_t)(row >> 32)};",
+        "uint32_t ctr[4] = {(uint32_t)row, (uint32_t)(row >> 32), (uint32_t)offset,\n"
+        "                       (uint32_t)(offset >> 32)};"),
+    "p_truncated": (
+        "double r = std::nearbyint(scaled);",
+        "double r = std::floor(scaled);"),
+    "p_not_clamped_low": (
+        "if (!(p > 0.0f)) return 1;",
+        "if (!(p > 0.0f)) return 0;"),
+    "inf_draw_modulo": (
+        "uint64_t t = (uint64_t)(((u128)u * (u128)inf_count) >> 64);",
+        "uint64_t t = u % (uint64_t)inf_count;"),
+    "inf_weight": (
+        "float w = (float)(1.0 / (double)inf_count);",
+        "float w = (float)(1.0 / (double)(inf_count + 1));"),
+    "zero_mass_first_sorted": (
+        "*token = (int32_t)*std::min_element(order.begin(), order.end());",
+        "*token = (int32_t)order[0];"),
+    "renorm_by_topk_mass": (
+        "renorm[order[j]] = (float)((double)q[j] / (double)M_p);",
+        "renorm[order[j]] = (float)((double)q[j] / (double)M_k);"),
+}
+
+
+def _pins(orc, torch_exe, rocrand_exe):
+    """Yield callables; each raises AssertionError when a pin fails."""
+    yield lambda: pb.test_exact_p_boundaries(orc)
+    yield lambda: pb.test_p_rounds_half_to_even(orc)
+    yield lambda: pb.test_heavy_ties(orc)
+    for V in (1, 3, 8):
+        yield lambda V=V: pb.test_plain_and_special_rows(orc, V)
+    yield lambda: pb.test_rows_with_infinities(orc, 4)
+    yield lambda: pr.test_zero_mass_rows_return_smallest_support_index(orc)
+    yield lambda: pr.test_masses_closed_form(orc)
+    yield lambda: pr.test_equal_values_keep_ceil_pn(orc, 100, 0.77)
+    if torch_exe:
+        yield lambda: pp.test_block_function_matches_pytorch(orc, torch_exe)
+        yield lambda: pp.test_row_uniform_mapping(orc, torch_exe)
+    if rocrand_exe:
+        yield lambda: pp.test_block_function_matches_rocrand(orc, rocrand_exe)
+
+
+@pytest.fixture(scope="module")
+def harnesses(tmp_path_factory):
+    t = r = None
+    try:
+        t = pp._build(tmp_path_factory, "USE_TORCH", [pp.TORCH_INC])
+    except BaseException:
+        pass
+    try:
+        r = pp._build(tmp_path_factory, "USE_ROCRAND", [pp.ROCM_INC], ["__HIP_PLATFORM_AMD__"])
+    except BaseException:
+        pass
+    return t, r
+
+
+def test_unmutated_oracle_passes_every_pin(orc, harnesses):
+    for pin in _pins(orc, *harnesses):
+        pin()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, harnesses, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found: " + name
+    mutated = tmp_path / "tes_oracle_mut.cpp"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", str(lib),
+                    str(mutated)], check=True)
+    mut = oracle.load(str(lib))
+    for pin in _pins(mut, *harnesses):
+        try:
+            pin()
+        except AssertionError:
+            return
+    pytest.fail("no pin caught the planted mistake " + name)

@@ -1,0 +1,185 @@
+"""Seeded synthetic workloads for exact top-k -> top-p sampling.
+
+This module only builds inputs: fp32 probability rows and the per-row
+``top_k`` / ``top_p`` parameters.  It holds none of the sampling method's
+arithmetic, so the CPU oracle and the GPU path can both consume it without
+sharing any logic.
+
+Every config follows one recipe, all in float64 until the final cast:
+
+1. ``rng = numpy.random.default_rng(seed)`` (PCG64);
+2. logits ``x = scale * rng.standard_normal((B, V))``;
+3. per row, a few tokens get a boost (the low-entropy "informative" outliers
+   that the Qrita page describes on top of quasi-Gaussian noise, section 3.1);
+4. ``probs = exp(x - max) / sum`` per row, then cast to fp32 round-to-nearest.
+
+The generator call order below is frozen: changing it changes every input.
+The vocabulary sizes are those of real tokenizers named on the pages
+(151,936 and 128,256 in the Qrita evaluation setup, 262,144 = 2**18 in the
+SonicSampler top-k sweep); the data is synthetic because no model logits
+are available.
+"""
+
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Workload", "CONFIGS", "make", "softmax64", "sha256_of"]
+
+
+@dataclass
+class Workload:
+    name: str
+    probs: np.ndarray  # float32 [B, V], C-contiguous
+    top_k: np.ndarray  # int32 [B]
+    top_p: np.ndarray  # float32 [B]
+    seed: int
+    offset: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.probs.shape[0])
+
+    @property
+    def V(self) -> int:
+        return int(self.probs.shape[1])
+
+
+def softmax64(x: np.ndarray) -> np.ndarray:
+    """Row softmax in float64: exp(x - rowmax) / rowsum."""
+    m = x.max(axis=1, keepdims=True)
+    e = np.exp(x - m)
+    e /= e.sum(axis=1, keepdims=True)
+    return e
+
+
+def _boost_rows(rng, x, n_lo, n_hi, b_lo, b_hi):
+    """Per row: n ~ U{n_lo..n_hi} distinct tokens get a boost ~ U[b_lo, b_hi]."""
+    B, V = x.shape
+    for b in range(B):
+        n = int(rng.integers(n_lo, n_hi + 1))
+        idx = rng.choice(V, n, replace=False)
+        x[b, idx] += rng.uniform(b_lo, b_hi, size=n)
+
+
+def _cfg1():
+    # Tiny reference: B=4, V=1000, 3 random tokens boosted by +10, k=50, p=0.9.
+    B, V, seed = 4, 1000, 0
+    rng = np.random.default_rng(seed)
+    x = 2.0 * rng.standard_normal((B, V))
+    for b in range(B):
+        idx = rng.choice(V, 3, replace=False)
+        x[b, idx] += 10.0
+    probs = softmax64(x).astype(np.float32)
+    top_k = np.full(B, 50, np.int32)
+    top_p = np.full(B, 0.9, np.float32)
+    return Workload("tiny_b4_v1000", probs, top_k, top_p, seed, 0)
+
+
+def _cfg2():
+    # B=64, V=32,000, low-entropy rows; k ~ U{1..1024}, p ~ U[0.5, 1.0].
+    B, V, seed = 64, 32000, 1
+    rng = np.random.default_rng(seed)
+    x = 2.0 * rng.standard_normal((B, V))
+    _boost_rows(rng, x, 1, 8, 8.0, 15.0)
+    probs = softmax64(x).astype(np.float32)
+    top_k = rng.integers(1, 1025, size=B).astype(np.int32)
+    top_p = rng.uniform(0.5, 1.0, size=B).astype(np.float32)
+    return Workload("b64_v32000", probs, top_k, top_p, seed, 0)
+
+
+def _cfg3():
+    # Heterogeneous batch B=256, V=151,936: 25% greedy (k=1), 25% top-p only
+    # (k=V, p ~ U[0.8, 0.99]), 50% k ~ U{20..1024} with p ~ U[0.7, 1.0].
+    B, V, seed = 256, 151936, 2
+    rng = np.random.default_rng(seed)
+    x = 2.0 * rng.standard_normal((B, V))
+    _boost_rows(rng, x, 1, 8, 8.0, 15.0)
+    probs = softmax64(x).astype(np.float32)
+    perm = rng.permutation(B)
+    greedy, full, slab = perm[:64], perm[64:128], perm[128:]
+    top_k = np.empty(B, np.int32)
+    top_p = np.empty(B, np.float32)
+    top_k[greedy] = 1
+    top_p[greedy] = 1.0
+    top_k[full] = V
+    top_p[full] = rng.uniform(0.8, 0.99, size=full.size).astype(np.float32)
+    top_k[slab] = rng.integers(20, 1025, size=slab.size)
+    top_p[slab] = rng.uniform(0.7, 1.0, size=slab.size).astype(np.float32)
+    cls = np.empty(B, dtype="<U6")
+    cls[greedy], cls[full], cls[slab] = "greedy", "full", "slab"
+    return Workload("hetero_b256_v151936", probs, top_k, top_p, seed, 0, {"row_class": cls})
+
+
+_NAN_PATTERNS = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0x7FFFFFFF], dtype=np.uint32)
+
+
+def _cfg4():
+    # Ties and edge rows: B=1024, V=128,256, probs quantised to multiples of
+    # 2**-20 then renormalised; 1% all-zero rows, 1% rows with NaN / negative /
+    # -0.0 entries, 1% rows with 2-5 +inf entries.
+    B, V, seed = 1024, 128256, 3
+    rng = np.random.default_rng(seed)
+    x = 2.0 * rng.standard_normal((B, V))
+    _boost_rows(rng, x, 1, 8, 8.0, 15.0)
+    p64 = softmax64(x)
+    del x
+    p64 = np.rint(p64 * 2.0**20) * 2.0**-20
+    p64 /= p64.sum(axis=1, keepdims=True)
+    probs = p64.astype(np.float32)
+    del p64
+    perm = rng.permutation(B)
+    zero_rows, nan_rows, inf_rows = perm[:10], perm[10:20], perm[20:30]
+    probs[zero_rows] = 0.0
+    bits = probs.view(np.uint32)
+    for b in nan_rows:
+        am = int(np.argmax(probs[b]))
+        idx = rng.choice(V, 12, replace=False)
+        bits[b, am] = _NAN_PATTERNS[0]
+        bits[b, idx[:4]] = _NAN_PATTERNS
+        probs[b, idx[4:8]] = -probs[b, idx[4:8]]
+        bits[b, idx[8:12]] = 0x80000000  # -0.0
+    for b in inf_rows:
+        n = int(rng.integers(2, 6))
+        idx = rng.choice(V, n, replace=False)
+        probs[b, idx] = np.inf
+    top_k = rng.integers(1, 1025, size=B).astype(np.int32)
+    top_p = rng.uniform(0.5, 1.0, size=B).astype(np.float32)
+    cls = np.full(B, "plain", dtype="<U5")
+    cls[zero_rows], cls[nan_rows], cls[inf_rows] = "zero", "nan", "inf"
+    return Workload("ties_edges_b1024_v128256", probs, top_k, top_p, seed, 0, {"row_class": cls})
+
+
+def _cfg5():
+    # Speculative-verify shape, top-p only: 64 requests x 8 draft positions =
+    # 512 rows, V=262,144, high-entropy logits 0.5*N(0,1), k=V, p=0.95.
+    B, V, seed = 512, 262144, 4
+    rng = np.random.default_rng(seed)
+    probs = np.empty((B, V), np.float32)
+    step = 64
+    for r0 in range(0, B, step):
+        x = 0.5 * rng.standard_normal((step, V))
+        probs[r0:r0 + step] = softmax64(x).astype(np.float32)
+    top_k = np.full(B, V, np.int32)
+    top_p = np.full(B, 0.95, np.float32)
+    return Workload("specverify_b512_v262144", probs, top_k, top_p, seed, 0)
+
+
+CONFIGS = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+
+
+def make(cfg: int) -> Workload:
+    """Build config ``cfg`` (1..5)."""
+    return CONFIGS[cfg]()
+
+
+def sha256_of(w: Workload) -> str:
+    h = hashlib.sha256()
+    for a in (w.probs, w.top_k, w.top_p):
+        h.update(np.ascontiguousarray(a).tobytes())
+    h.update(f"{w.seed}:{w.offset}".encode())
+    return h.hexdigest()
