@@ -1,0 +1,120 @@
+/*
+ * tes_sampler.h -- C ABI of the MI355X (gfx950) exact top-k -> top-p sampler.
+ *
+ * Operation (FlashInfer "cake_sampling" documentation page, section
+ * "Semantics", and its description of the sparse top-p stage): for every row
+ * b of a [B][V] fp32 probability matrix,
+ *   1. sanitise: NaN, negative and -0.0 entries count as +0 and are never
+ *      sampled; +inf is kept;
+ *   2. support S = the first k_eff entries of lexsort(-prob, index), i.e. a
+ *      stable descending sort with ties going to the lower vocabulary index;
+ *      k_eff = V when top_k[b] <= 0 or top_k[b] >= V, else top_k[b];
+ *   3. if S holds m > 0 entries equal to +inf, exactly those are kept with
+ *      weight 1/m and the draw is uniform among them;
+ *   4. otherwise masses q = floor(min(prob, 1) * 2^32) (exact integers) and
+ *      M_k = sum over S.  If M_k = 0 the token is the smallest vocabulary index
+ *      in S and the renormalised row is all zero;
+ *   5. top-p on exact 64-bit fixed-point prefix sums: P = round-half-even(
+ *      top_p[b] * 2^24) clamped to [1, 2^24] (NaN or <= 0 gives 1, >= 1 gives
+ *      2^24); sorted position j is kept while its exclusive prefix mass is
+ *      below ceil(P * M_k / 2^24).  This is the shortest prefix holding at
+ *      least top_p of the top-k mass (the nucleus of the SonicSampler paper,
+ *      eq. (10), taken relative to the top-k mass);
+ *   6. one inverse-CDF draw per row: u = x0 | x1 << 32 of Philox4x32-10
+ *      (Salmon et al., SC'11) with key (seed lo, seed hi) and counter
+ *      (offset lo, offset hi, b lo, b hi); t = floor(u * M_p / 2^64) with M_p
+ *      the kept mass; token = first kept position whose inclusive prefix mass
+ *      exceeds t;
+ *   7. optional renormalised output: renorm_out[b][i] = fp32(q_i / M_p) for kept
+ *      i (1/m for kept +inf entries), 0 elsewhere.
+ * Every decision is integer arithmetic, so results are bitwise reproducible
+ * across launches, streams and internal paths.
+ *
+ * Status codes: 0 on success, a negative TES_ERR_* value on failure.  Nothing
+ * aborts or throws across this interface.  Probability values are never an
+ * error (NaN, negatives, zero rows and out-of-range top_k / top_p follow the
+ * rules above and every output is finite).
+ */
+#ifndef TES_SAMPLER_H
+#define TES_SAMPLER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TES_OK 0
+#define TES_ERR_INVALID_ARGUMENT (-1) /* bad handle, pointer, size or alignment */
+#define TES_ERR_NO_DEVICE (-2)        /* no HIP device, or device index out of range */
+#define TES_ERR_UNSUPPORTED_DEVICE (-3) /* device is not gfx950 */
+#define TES_ERR_OUT_OF_MEMORY (-4)    /* host or device allocation failed at create */
+#define TES_ERR_LAUNCH (-5)           /* HIP runtime error while enqueueing */
+#define TES_ERR_TOO_LARGE (-6)        /* B or V above the limits given at create */
+
+/* Flags for sampler_create.  They select internal paths for testing; none of
+ * them changes any output. */
+#define TES_FLAG_NONE 0u
+/* Resolve every row with the multi-pass whole-row select instead of the
+ * single-read candidate buffer. */
+#define TES_FLAG_FORCE_ROW_SELECT 1u
+/* Shrink the candidate buffer's retention targets so that compaction and the
+ * multi-pass fallback run on ordinary inputs. */
+#define TES_FLAG_TINY_BUFFER 2u
+/* Record per-row path statistics (see sampler_get_stats). */
+#define TES_FLAG_STATS 4u
+
+typedef struct tes_sampler tes_sampler;
+
+/* Create a sampler bound to HIP device `device`.
+ *   out        receives the handle (host pointer; must not be NULL).
+ *   max_batch  largest B any later call may pass (>= 1).
+ *   max_vocab  largest V any later call may pass (1 .. 2^30).
+ *   flags      TES_FLAG_* bits.
+ * The handle owns its (small) device workspace, allocated here and released
+ * by sampler_destroy.  Returns TES_ERR_NO_DEVICE when no GPU is present,
+ * TES_ERR_UNSUPPORTED_DEVICE when the device is not gfx950. */
+int sampler_create(tes_sampler **out, int device, int max_batch, int max_vocab,
+                   unsigned flags);
+
+/* Sample one token per row; asynchronous on `stream`.
+ *   probs       device, fp32 [B][V] row-major, contiguous, 4-byte aligned
+ *               (16-byte alignment and V % 4 == 0 enable 16-byte loads);
+ *               read only.
+ *   B, V        batch rows (0 .. max_batch; B = 0 is a no-op) and vocabulary
+ *               size (1 .. max_vocab).
+ *   top_k       device, int32 [B]; <= 0 or >= V disables top-k.
+ *   top_p       device, fp32 [B]; clamped as described above.
+ *   seed,offset Philox key and 128-bit-block offset; row b uses counter
+ *               (offset, b).  Advance offset by at least 1 between calls
+ *               that must draw independently.
+ *   out_tokens  device, int32 [B]; receives the sampled vocabulary index.
+ *   renorm_out  device, fp32 [B][V] or NULL; when given, every entry of every
+ *               row is written (dense, vocabulary order).
+ *   stream      hipStream_t (NULL = default stream) on the sampler's device.
+ * All device buffers are owned by the caller and must stay valid until the
+ * enqueued work completes; outputs must not alias probs.  No allocation and
+ * no host synchronisation happen inside the call.  One handle must not be
+ * used from two streams concurrently. */
+int topk_topp_sample(tes_sampler *s, const float *probs, int B, int V, const int32_t *top_k,
+                     const float *top_p, uint64_t seed, uint64_t offset, int32_t *out_tokens,
+                     float *renorm_out, void *stream);
+
+/* Release the handle and its workspace.  NULL is accepted. */
+int sampler_destroy(tes_sampler *s);
+
+/* Static English description of a status code. */
+const char *sampler_status_string(int status);
+
+/* Copy per-row path statistics of the last call (handle created with
+ * TES_FLAG_STATS) to host memory: 4 uint32 per row = {path, passes over the
+ * row, buffer compactions, reserved}.  path: 0 candidate buffer, 1 candidate
+ * buffer with top-p-only rows, 2 whole-row select.  Synchronises the device.
+ * `host_out` holds 4 * B uint32. */
+int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TES_SAMPLER_H */

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP sampler (through the C ABI) against the CPU oracle.
+
+Bar: token ids bit-exact, kept sets (nonzero pattern of renorm_out)
+bit-exact, renorm_out within 1e-6 relative.  Every internal path (candidate
+buffer, top-p-only hit, whole-row select, forced variants) must agree.
+"""
+
+import numpy as np
+import pytest
+
+import top_exact_sampling_amd as tes
+import workloads
+from tests import golden_cases
+from tests.gpu_util import assert_parity, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    tes.lib()  # fail loudly when the HIP library is missing
+    return torch
+
+
+@pytest.fixture(scope="module")
+def sampler(torch_cuda):
+    s = tes.Sampler(0, max_batch=4096, max_vocab=1 << 20, flags=tes.TES_FLAG_STATS)
+    yield s
+    s.close()
+
+
+@pytest.fixture(scope="module")
+def variant_samplers(torch_cuda):
+    out = {
+        "row_select": tes.Sampler(0, 4096, 1 << 20, tes.TES_FLAG_FORCE_ROW_SELECT),
+        "tiny_buffer": tes.Sampler(0, 4096, 1 << 20, tes.TES_FLAG_TINY_BUFFER),
+        "row_select_tiny": tes.Sampler(
+            0, 4096, 1 << 20, tes.TES_FLAG_FORCE_ROW_SELECT | tes.TES_FLAG_TINY_BUFFER),
+    }
+    yield out
+    for s in out.values():
+        s.close()
+
+
+_WL = {}
+
+
+def wl(cfg):
+    if cfg not in _WL:
+        _WL[cfg] = workloads.make(cfg)
+    return _WL[cfg]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity_with_renorm(sampler, orc, cfg):
+    w = wl(cfg)
+    log("[gpu] config %d %s B=%d V=%d renorm" % (cfg, w.name, w.B, w.V))
+    gtok, gren = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=True)
+    assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, gren, w.name)
+    st = sampler.stats(w.B)
+    log("[gpu]   paths %s, passes max %d" % (np.bincount(st[:, 0], minlength=3).tolist(),
+                                            st[:, 1].max()))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity_tokens_only(sampler, orc, cfg):
+    # The launch the benchmark times: renorm_out = NULL.
+    w = wl(cfg)
+    log("[gpu] config %d %s tokens only" % (cfg, w.name))
+    gtok, _ = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=False)
+    assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, None, w.name)
+
+
+@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "row_select_tiny"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_forced_paths_agree(variant_samplers, orc, variant, cfg):
+    w = wl(cfg)
+    rows = np.arange(w.B)
+    if cfg in (3, 4):
+        rng = np.random.default_rng(cfg)
+        rows = np.sort(rng.choice(w.B, 48, replace=False))
+        if cfg == 4:
+            cls = w.meta["row_class"]
+            rows = np.unique(np.concatenate([rows, np.flatnonzero(cls != "plain")]))
+    probs = np.ascontiguousarray(w.probs[rows])
+    log("[gpu] variant %s config %d rows %d" % (variant, cfg, rows.size))
+    gtok, gren = run_gpu(variant_samplers[variant], probs, w.top_k[rows], w.top_p[rows], w.seed,
+                         w.offset, renorm=True)
+    assert_parity(orc, probs, w.top_k[rows], w.top_p[rows], w.seed, w.offset, gtok, gren,
+                  "%s/%s" % (variant, w.name))
+
+
+def test_golden_worked_examples(sampler, orc):
+    # The worked examples fix u directly while the GPU derives u from Philox,
+    # so each example runs with several (seed, offset) and is compared with
+    # the oracle's row function at that u, plus the fixed renorm values.
+    for name, row, k, p, draws, ren_want in golden_cases.load():
+        probs = row[None, :]
+        for seed, off in ((0, 0), (1, 5), (77, 2**40)):
+            u = orc.uniform_u64(seed, 0, off)
+            gtok, gren = run_gpu(sampler, probs, [k], [p], seed, off, renorm=True)
+            otok, _, _ = orc.sample_row(row, k, p, u)
+            assert gtok[0] == otok, name
+            np.testing.assert_allclose(gren[0], np.array(ren_want, np.float32), rtol=1e-6,
+                                       atol=0, err_msg=name)
+
+
+def _adversarial_batch(V, rng):
+    rows, ks, ps, names = [], [], [], []
+
+    def add(x, k, p, name):
+        rows.append(np.asarray(x, np.float32))
+        ks.append(k)
+        ps.append(p)
+        names.append(name)
+
+    flat = np.full(V, 1.0 / V, np.float32)
+    for k in (1, 50, 1024, 2000, V):
+        for p in (0.5, 1.0):
+            add(flat, k, p, "flat k%d p%g" % (k, p))
+    asc = np.linspace(1.0, 2.0, V).astype(np.float64)
+    asc = (asc / asc.sum()).astype(np.float32)
+    for k in (1, 37, 1024, V):
+        add(asc, k, 0.9, "ascending k%d" % k)
+        add(asc[::-1], k, 0.9, "descending k%d" % k)
+    few = np.zeros(V, np.float32)
+    nf = min(V, 10)
+    few[rng.choice(V, nf, replace=False)] = rng.random(nf).astype(np.float32)
+    add(few, 100, 0.95, "k above positives")
+    add(few, V, 1.0, "few positives full")
+    den = np.full(V, np.float32(1e-40), np.float32)
+    add(den, 20, 0.9, "all denormal")
+    add(den, V, 0.9, "all denormal full")
+    add(np.full(V, np.inf, np.float32), 50, 0.9, "all inf k50")
+    add(np.full(V, np.inf, np.float32), V, 0.9, "all inf full")
+    many_inf = rng.random(V).astype(np.float32)
+    many_inf[rng.choice(V, min(V, 1500), replace=False)] = np.inf
+    add(many_inf, V, 0.9, "1500 inf full")
+    add(many_inf, 1024, 0.9, "1500 inf k1024")
+    near = (1.0 + 1e-6 * rng.random(V)).astype(np.float64)
+    add((near / near.sum()).astype(np.float32), V, 0.95, "near uniform full")
+    fat = (rng.random(V) * 1e-6).astype(np.float32)
+    fat[rng.choice(V, min(V, 3000), replace=False)] = np.float32(1e-4)
+    fat[rng.choice(V, min(V, 200), replace=False)] = np.float32(1e-3)
+    for k in (150, 1024, V):
+        add(fat, k, 0.97, "fat bucket k%d" % k)
+    for p in (1e-9, 0.0, float("nan"), 1.0, 5.0):
+        add(asc, V, p, "p=%r" % p)
+        add(asc, 64, p, "p=%r k64" % p)
+    neg = rng.standard_normal(V).astype(np.float32)
+    add(neg, 100, 0.9, "gaussian with negatives")
+    add(neg, V, 0.9, "gaussian with negatives full")
+    return np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32), names
+
+
+@pytest.mark.parametrize("V", [151936, 262144, 5000, 1021, 4])
+def test_adversarial_rows(sampler, variant_samplers, orc, V):
+    rng = np.random.default_rng(V)
+    probs, ks, ps, names = _adversarial_batch(V, rng)
+    for label, s in (("default", sampler), ("row_select", variant_samplers["row_select"]),
+                     ("tiny_buffer", variant_samplers["tiny_buffer"])):
+        log("[gpu] adversarial V=%d rows=%d sampler=%s" % (V, len(names), label))
+        gtok, gren = run_gpu(s, probs, ks, ps, 9, 3, renorm=True)
+        assert_parity(orc, probs, ks, ps, 9, 3, gtok, gren, "adversarial V=%d %s" % (V, label))
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 999, 1000, 1024, 1025, 4097, 8191, 8192, 8193, 40000])
+def test_ragged_vocab_sizes(sampler, orc, V):
+    rng = np.random.default_rng(V + 17)
+    B = 24
+    x = 2.0 * rng.standard_normal((B, V))
+    x[:, : min(V, 3)] += 9.0
+    e = np.exp(x - x.max(1, keepdims=True))
+    probs = (e / e.sum(1, keepdims=True)).astype(np.float32)
+    ks = rng.integers(-2, V + 3, size=B).astype(np.int32)
+    ks[:4] = [1, V, 0, 1024]
+    ps = rng.uniform(0.3, 1.0, size=B).astype(np.float32)
+    log("[gpu] ragged V=%d" % V)
+    gtok, gren = run_gpu(sampler, probs, ks, ps, 3, 11, renorm=True)
+    assert_parity(orc, probs, ks, ps, 3, 11, gtok, gren, "ragged V=%d" % V)
+
+
+def test_unaligned_rows_use_scalar_path(sampler, orc, torch_cuda):
+    torch = torch_cuda
+    w = wl(2)
+    B, V = 16, w.V
+    flat = torch.zeros(B * V + 1, dtype=torch.float32, device="cuda")
+    flat[1:] = torch.from_numpy(w.probs[:B].reshape(-1)).cuda()
+    probs_dev = flat[1:].view(B, V)  # 4-byte aligned, not 16-byte aligned
+    assert probs_dev.data_ptr() % 16 != 0
+    log("[gpu] unaligned rows")
+    gtok, gren = run_gpu(sampler, w.probs[:B], w.top_k[:B], w.top_p[:B], 5, 6, renorm=True,
+                         probs_dev=probs_dev)
+    assert_parity(orc, w.probs[:B], w.top_k[:B], w.top_p[:B], 5, 6, gtok, gren, "unaligned")
+
+
+def test_seeds_and_offsets(sampler, orc):
+    w = wl(2)
+    for seed, off in ((0, 1), (2**64 - 1, 2**64 - 1), (123456789, 2**33 + 5)):
+        log("[gpu] seed %d offset %d" % (seed, off))
+        gtok, _ = run_gpu(sampler, w.probs, w.top_k, w.top_p, seed, off, renorm=False)
+        assert_parity(orc, w.probs, w.top_k, w.top_p, seed, off, gtok, None, "seed/offset")
+
+
+def test_determinism_streams_and_graph_replay(sampler, torch_cuda):
+    torch = torch_cuda
+    w = wl(3)
+    pd = torch.from_numpy(w.probs).cuda()
+    kd = torch.from_numpy(w.top_k).cuda()
+    qd = torch.from_numpy(w.top_p).cuda()
+    ref = sampler.sample(pd, kd, qd, w.seed, w.offset).clone()
+    torch.cuda.synchronize()
+    log("[gpu] determinism: side stream")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        again = sampler.sample(pd, kd, qd, w.seed, w.offset)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref)
+    log("[gpu] determinism: graph capture and replay")
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        sampler.sample(pd, kd, qd, w.seed, w.offset, out_tokens=out)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        sampler.sample(pd, kd, qd, w.seed, w.offset, out_tokens=out)
+    for i in range(4):
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs" % i
+        _ = (pd[:2].sum() + 1).item()  # eager work between replays
+
+
+def test_zero_batch_and_argument_errors(sampler, torch_cuda):
+    torch = torch_cuda
+    h = sampler.handle
+    assert tes.topk_topp_sample(h, 0, 0, 10, 0, 0, 0, 0, 0, None, None) == tes.TES_OK
+    p = torch.zeros(4, 8, device="cuda")
+    k = torch.zeros(4, dtype=torch.int32, device="cuda")
+    q = torch.zeros(4, device="cuda")
+    t = torch.zeros(4, dtype=torch.int32, device="cuda")
+    args = (p.data_ptr(), 4, 8, k.data_ptr(), q.data_ptr(), 0, 0, t.data_ptr(), None, None)
+    assert tes.topk_topp_sample(None, *args) == tes.TES_ERR_INVALID_ARGUMENT
+    bad = list(args)
+    bad[0] = p.data_ptr() + 2
+    assert tes.topk_topp_sample(h, *bad) == tes.TES_ERR_INVALID_ARGUMENT
+    bad = list(args)
+    bad[1] = 10**6
+    assert tes.topk_topp_sample(h, *bad) == tes.TES_ERR_TOO_LARGE
+    assert tes.topk_topp_sample(h, *args) == tes.TES_OK
+    torch.cuda.synchronize()

@@ -1,0 +1,146 @@
+"""Python binding of the MI355X exact top-k -> top-p sampler (C ABI in
+``include/tes_sampler.h``).
+
+The functions below carry the C names and only marshal arguments: every step
+of the sampling path runs in the HIP kernels of ``libtes_sampler.so``.  The
+library must have been built (``top_exact_sampling_amd.build.build()``); if
+it is missing, loading fails with an error instead of falling back to
+anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtes_sampler.so")
+
+TES_OK = 0
+TES_ERR_INVALID_ARGUMENT = -1
+TES_ERR_NO_DEVICE = -2
+TES_ERR_UNSUPPORTED_DEVICE = -3
+TES_ERR_OUT_OF_MEMORY = -4
+TES_ERR_LAUNCH = -5
+TES_ERR_TOO_LARGE = -6
+
+TES_FLAG_NONE = 0
+TES_FLAG_FORCE_ROW_SELECT = 1
+TES_FLAG_TINY_BUFFER = 2
+TES_FLAG_STATS = 4
+
+EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
+            "sampler_get_stats")
+
+_lib = None
+
+
+class TesError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (%d)" % (what, sampler_status_string(status), status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtes_sampler.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libtes_sampler.so is not built; run "
+                              "top_exact_sampling_amd.build.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.sampler_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_uint]
+        L.sampler_create.restype = ctypes.c_int
+        L.topk_topp_sample.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
+                                       ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
+        L.topk_topp_sample.restype = ctypes.c_int
+        L.sampler_destroy.argtypes = [vp]
+        L.sampler_destroy.restype = ctypes.c_int
+        L.sampler_status_string.argtypes = [ctypes.c_int]
+        L.sampler_status_string.restype = ctypes.c_char_p
+        L.sampler_get_stats.argtypes = [vp, vp, ctypes.c_int]
+        L.sampler_get_stats.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# -- C names ----------------------------------------------------------------
+def sampler_status_string(status: int) -> str:
+    return lib().sampler_status_string(int(status)).decode()
+
+
+def sampler_create(device: int, max_batch: int, max_vocab: int, flags: int = 0) -> int:
+    h = ctypes.c_void_p()
+    rc = lib().sampler_create(ctypes.byref(h), int(device), int(max_batch), int(max_vocab),
+                              int(flags))
+    if rc != TES_OK:
+        raise TesError(rc, "sampler_create")
+    return h.value
+
+
+def topk_topp_sample(handle, probs_ptr: int, B: int, V: int, top_k_ptr: int, top_p_ptr: int,
+                     seed: int, offset: int, out_tokens_ptr: int, renorm_ptr, stream) -> int:
+    """Raw call with device pointers (ints); returns the status code."""
+    return lib().topk_topp_sample(handle, probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
+                                  int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                  out_tokens_ptr, renorm_ptr, stream)
+
+
+def sampler_destroy(handle) -> int:
+    return lib().sampler_destroy(handle)
+
+
+def sampler_get_stats(handle, B: int):
+    import numpy as np
+
+    out = np.zeros((B, 4), np.uint32)
+    rc = lib().sampler_get_stats(handle, out.ctypes.data, int(B))
+    if rc != TES_OK:
+        raise TesError(rc, "sampler_get_stats")
+    return out
+
+
+# -- torch convenience (marshalling only) -----------------------------------
+class Sampler:
+    """Owns one sampler handle; ``sample`` passes torch tensors through."""
+
+    def __init__(self, device: int = 0, max_batch: int = 1024, max_vocab: int = 262144,
+                 flags: int = 0):
+        self.device = device
+        self.handle = sampler_create(device, max_batch, max_vocab, flags)
+
+    def close(self):
+        if self.handle:
+            sampler_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sample(self, probs, top_k, top_p, seed: int, offset: int, out_tokens=None,
+               renorm_out=None, stream=None):
+        import torch
+
+        B, V = probs.shape
+        for t, dt in ((probs, torch.float32), (top_k, torch.int32), (top_p, torch.float32)):
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("expected contiguous %s on the GPU" % dt)
+        if out_tokens is None:
+            out_tokens = torch.empty(B, dtype=torch.int32, device=probs.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(probs.device)
+        rc = topk_topp_sample(self.handle, probs.data_ptr(), B, V, top_k.data_ptr(),
+                              top_p.data_ptr(), seed, offset, out_tokens.data_ptr(),
+                              renorm_out.data_ptr() if renorm_out is not None else None,
+                              stream.cuda_stream)
+        if rc != TES_OK:
+            raise TesError(rc, "topk_topp_sample")
+        return out_tokens
+
+    def stats(self, B: int):
+        return sampler_get_stats(self.handle, B)
