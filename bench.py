@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark: exact top-k -> top-p sampling on one MI355X.
+
+One step = one call of topk_topp_sample over the whole heterogeneous batch
+(B=256 rows, V=151,936 fp32 probabilities; 64 greedy rows, 64 top-p-only rows,
+128 rows with k in [20, 1024]), tokens only (renorm_out = NULL), inputs
+already resident in HBM.  Timed steps rotate over several copies of the
+input so that the 256 MiB Infinity Cache cannot serve a repeated read.
+
+Prints one JSON line: rows/s for the whole job, the kernel's achieved HBM
+bandwidth against the 8 TB/s peak (algorithmic bytes = B*V*4 + 12*B per
+launch divided by the kernel's average duration, timed with HIP events on the
+launch stream), and the CPU oracle timed on the host cores as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "rows/s and achieved HBM GB/s (% of peak) at B=256, V=151,936 top-k+top-p"
+KERNEL_SRC = os.path.join(ROOT, "top_exact_sampling_amd", "csrc", "tes_sampler.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tes_sample_kernel_hetero_b256_v151936.json")
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, min_wall=5.0, max_reps=20):
+    import oracle
+
+    orc = oracle.load()
+    cores = min(16, len(os.sched_getaffinity(0)))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.sample(w.probs, w.top_k, w.top_p, w.seed, w.offset + reps, n_threads=cores)
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_wall or reps >= max_reps:
+            break
+    return {
+        "value": round(reps * w.B / wall, 1),
+        "unit": "rows/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d full passes over all %d rows of %s (stable sort per row, %d host threads)"
+                  % (reps, w.B, w.name, cores),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="rotating input copies (> MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle check")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this sampler has no multi-GPU path "
+              "(rows are independent; see the sharding note in the design document). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_exact_sampling_amd as tes
+    import workloads
+
+    w = workloads.make(3)
+    B, V = w.B, w.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sampler = tes.Sampler(0, max_batch=B, max_vocab=V)
+    probs = [torch.from_numpy(w.probs).to(dev) for _ in range(args.copies)]
+    top_k = torch.from_numpy(w.top_k).to(dev)
+    top_p = torch.from_numpy(w.top_p).to(dev)
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset, out_tokens=out,
+                       stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # Timed region: exactly `steps` calls, each bracketed by HIP events on the
+    # launch stream (the events also give the kernel's average duration).
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    kern_ms = float(np.mean(per_launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+
+    alg_bytes = B * V * 4 + 12 * B
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        step(0)
+        torch.cuda.synchronize()
+        gtok = out.cpu().numpy()
+        otok, _, _ = oracle.load().sample(w.probs, w.top_k, w.top_p, w.seed, w.offset)
+        parity = "bit-exact" if np.array_equal(gtok, otok) else \
+            "MISMATCH on %d rows" % int((gtok != otok).sum())
+
+    traffic = traffic_from_profile()
+    line = {
+        "metric": METRIC,
+        "value": round(B / (ms_per_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": B,
+            "V": V,
+            "row_mix": "64 greedy (k=1), 64 top-p only (k=V, p~U[0.8,0.99]), "
+                       "128 k~U{20..1024} with p~U[0.7,1.0]",
+            "input": "fp32 probs, softmax of 2*N(0,1) logits with 1-8 tokens boosted U[8,15]",
+            "renorm_out": None,
+            "input_copies_rotated": args.copies,
+            "kernel_ms_hip_events": round(kern_ms, 5),
+            "parity_vs_oracle": parity,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(w),
+    }
+    sampler.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

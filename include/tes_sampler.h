@@ -107,10 +107,14 @@ int sampler_destroy(tes_sampler *s);
 const char *sampler_status_string(int status);
 
 /* Copy per-row path statistics of the last call (handle created with
- * TES_FLAG_STATS) to host memory: 4 uint32 per row = {path, passes over the
- * row, buffer compactions, reserved}.  path: 0 candidate buffer, 1 candidate
- * buffer with top-p-only rows, 2 whole-row select.  Synchronises the device.
- * `host_out` holds 4 * B uint32. */
+ * TES_FLAG_STATS) to host memory: 8 uint32 per row = {path, passes over the
+ * row, candidate-buffer compactions, row kind, stream time, resolve time,
+ * renorm-write time, entries gathered by the second pass}.  path: 0 candidate
+ * buffer (k <= 1024), 1 top-p-only row decided by the buffered prefix, 2
+ * top-p-only row finished by one gather pass, 3 whole-row select.  kind: 0
+ * normal, 1 +inf row, 2 zero-mass row.  Times are in ticks of the device's
+ * constant wall clock (100 MHz on MI355X).  Synchronises the device.
+ * `host_out` holds 8 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);
 
 #ifdef __cplusplus

@@ -95,7 +95,7 @@ def sampler_destroy(handle) -> int:
 def sampler_get_stats(handle, B: int):
     import numpy as np
 
-    out = np.zeros((B, 4), np.uint32)
+    out = np.zeros((B, 8), np.uint32)
     rc = lib().sampler_get_stats(handle, out.ctypes.data, int(B))
     if rc != TES_OK:
         raise TesError(rc, "sampler_get_stats")
