@@ -58,11 +58,15 @@ extern "C" {
 /* Resolve every row with the multi-pass whole-row select instead of the
  * single-read candidate buffer. */
 #define TES_FLAG_FORCE_ROW_SELECT 1u
-/* Shrink the candidate buffer's retention targets so that compaction and the
- * multi-pass fallback run on ordinary inputs. */
+/* Compact the top-k candidate buffer whenever it holds more than k entries,
+ * and shrink the gather capacities of the other paths, so that compaction
+ * and the multi-pass fallback run on ordinary inputs. */
 #define TES_FLAG_TINY_BUFFER 2u
 /* Record per-row path statistics (see sampler_get_stats). */
 #define TES_FLAG_STATS 4u
+/* Cut top-p-only rows into segments of 4096 floats instead of 32768, so that
+ * the cross-segment exchanges run on small vocabularies too. */
+#define TES_FLAG_SMALL_SEGMENTS 8u
 
 typedef struct tes_sampler tes_sampler;
 
@@ -107,14 +111,34 @@ int sampler_destroy(tes_sampler *s);
 const char *sampler_status_string(int status);
 
 /* Copy per-row path statistics of the last call (handle created with
- * TES_FLAG_STATS) to host memory: 8 uint32 per row = {path, passes over the
- * row, candidate-buffer compactions, row kind, stream time, resolve time,
- * renorm-write time, entries gathered by the second pass}.  path: 0 candidate
- * buffer (k <= 1024), 1 top-p-only row decided by the buffered prefix, 2
- * top-p-only row finished by one gather pass, 3 whole-row select.  kind: 0
- * normal, 1 +inf row, 2 zero-mass row.  Times are in ticks of the device's
- * constant wall clock (100 MHz on MI355X).  Synchronises the device.
- * `host_out` holds 8 * B uint32. */
+ * TES_FLAG_STATS) to host memory: 16 uint32 per row =
+ *   [0] path: 0 top-k row (k <= 1024) resolved from its candidate buffer,
+ *       1 top-p-only row resolved from exchanged histograms and gathered bins,
+ *       2 top-p-only row that fell back to whole-row passes,
+ *       3 row resolved by whole-row passes (1024 < k < V, or forced),
+ *       4 greedy row (k = 1);
+ *   [1] kind: 0 normal, 1 +inf row, 2 zero-mass row;
+ *   [2] segments the row was cut into;
+ *   [3] candidate-buffer compactions (path 0) or passes over the row (path 3);
+ *   [4] entries gathered for the final selects (paths 0, 1, 2);
+ *   [5] device wall clock when the row was resolved (low 32 bits);
+ *   [6] 0xFFFFFFFF minus the earliest wall clock at which a segment of the
+ *       row started;
+ *   [7] why a top-p-only row left its fast path (bits): 1 first exchange
+ *       timed out, 2 the draw spans more coarse bins than are exchanged (their
+ *       count in bits 8..15), 4 second exchange timed out, 8 inconsistent fine
+ *       bins, 16 a segment gathered too many entries, 32 too many in total;
+ *   [8..13] wall-clock ticks spent in successive phases, summed over the
+ *       row's segments: greedy [8] whole item; top-k [8] streaming with its
+ *       compactions, [9] final sort and selects, [10] the compactions alone,
+ *       [11] the sampled first part, [12] the threshold estimate, [13] the
+ *       rest of the row; top-p-only
+ *       [8] loads and histogram, [9] first exchange, [10] its analysis and
+ *       the second publication, [11] second exchange, [12] gather and
+ *       arrival, [13] final selects;
+ *   [14..15] reserved (0).
+ * The wall clock is the device's constant 100 MHz counter.  Synchronises the
+ * device.  `host_out` holds 16 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ def torch_cuda():
 
 @pytest.fixture(scope="module")
 def sampler(torch_cuda):
-    s = tes.Sampler(0, max_batch=4096, max_vocab=1 << 20, flags=tes.TES_FLAG_STATS)
+    s = tes.Sampler(0, max_batch=4096, max_vocab=1 << 18, flags=tes.TES_FLAG_STATS)
     yield s
     s.close()
 
@@ -36,10 +36,13 @@ def sampler(torch_cuda):
 @pytest.fixture(scope="module")
 def variant_samplers(torch_cuda):
     out = {
-        "row_select": tes.Sampler(0, 4096, 1 << 20, tes.TES_FLAG_FORCE_ROW_SELECT),
-        "tiny_buffer": tes.Sampler(0, 4096, 1 << 20, tes.TES_FLAG_TINY_BUFFER),
+        "row_select": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_FORCE_ROW_SELECT),
+        "tiny_buffer": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_TINY_BUFFER),
         "row_select_tiny": tes.Sampler(
-            0, 4096, 1 << 20, tes.TES_FLAG_FORCE_ROW_SELECT | tes.TES_FLAG_TINY_BUFFER),
+            0, 4096, 1 << 18, tes.TES_FLAG_FORCE_ROW_SELECT | tes.TES_FLAG_TINY_BUFFER),
+        "small_segments": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS),
+        "small_tiny": tes.Sampler(
+            0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS | tes.TES_FLAG_TINY_BUFFER),
     }
     yield out
     for s in out.values():
@@ -62,8 +65,9 @@ def test_config_parity_with_renorm(sampler, orc, cfg):
     gtok, gren = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=True)
     assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, gren, w.name)
     st = sampler.stats(w.B)
-    log("[gpu]   paths %s, passes max %d" % (np.bincount(st[:, 0], minlength=3).tolist(),
-                                            st[:, 1].max()))
+    log("[gpu]   paths %s, kinds %s, gathered max %d" % (
+        np.bincount(st[:, 0], minlength=5).tolist(), np.bincount(st[:, 1], minlength=3).tolist(),
+        st[:, 4].max()))
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -75,7 +79,8 @@ def test_config_parity_tokens_only(sampler, orc, cfg):
     assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, None, w.name)
 
 
-@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "row_select_tiny"])
+@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "row_select_tiny",
+                                     "small_segments", "small_tiny"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_forced_paths_agree(variant_samplers, orc, variant, cfg):
     w = wl(cfg)
@@ -162,7 +167,9 @@ def test_adversarial_rows(sampler, variant_samplers, orc, V):
     rng = np.random.default_rng(V)
     probs, ks, ps, names = _adversarial_batch(V, rng)
     for label, s in (("default", sampler), ("row_select", variant_samplers["row_select"]),
-                     ("tiny_buffer", variant_samplers["tiny_buffer"])):
+                     ("tiny_buffer", variant_samplers["tiny_buffer"]),
+                     ("small_segments", variant_samplers["small_segments"]),
+                     ("small_tiny", variant_samplers["small_tiny"])):
         log("[gpu] adversarial V=%d rows=%d sampler=%s" % (V, len(names), label))
         gtok, gren = run_gpu(s, probs, ks, ps, 9, 3, renorm=True)
         assert_parity(orc, probs, ks, ps, 9, 3, gtok, gren, "adversarial V=%d %s" % (V, label))

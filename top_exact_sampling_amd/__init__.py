@@ -28,6 +28,9 @@ TES_FLAG_NONE = 0
 TES_FLAG_FORCE_ROW_SELECT = 1
 TES_FLAG_TINY_BUFFER = 2
 TES_FLAG_STATS = 4
+TES_FLAG_SMALL_SEGMENTS = 8
+
+STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
             "sampler_get_stats")
@@ -95,7 +98,7 @@ def sampler_destroy(handle) -> int:
 def sampler_get_stats(handle, B: int):
     import numpy as np
 
-    out = np.zeros((B, 8), np.uint32)
+    out = np.zeros((B, STAT_WORDS), np.uint32)
     rc = lib().sampler_get_stats(handle, out.ctypes.data, int(B))
     if rc != TES_OK:
         raise TesError(rc, "sampler_get_stats")

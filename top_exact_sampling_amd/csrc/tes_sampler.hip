@@ -10,33 +10,44 @@
 // integer arithmetic on exact masses, so every internal path gives bitwise
 // identical results.
 //
-// Design (one workgroup of 1024 threads per row):
-//   * Every entry becomes a 64-bit composite (key << 32) | ~index, key = the
+// Design.
+//   * Every entry is a 64-bit composite (key << 32) | ~index, key = the
 //     sanitised fp32 bits.  Composites are unique and order entries exactly as
 //     the stable descending sort does.
-//   * Candidate buffer.  The row is streamed once with 16-byte loads, eight
-//     loads in flight per thread.  An entry whose composite is >= a running
-//     threshold theta is appended to an LDS buffer (wave ballot + one LDS
-//     atomic per wave).  After each group of eight rounds one barrier checks
-//     the fill; a radix select over the buffer's 11-bit composite digits
-//     (LDS histograms) then compacts it to at least the best L entries and
-//     raises theta.  Nothing below theta can re-enter the best L, so one read
-//     leaves every entry >= theta in LDS.  This takes the place of the
-//     2048-bucket radix select and candidate list of the cake_sampling page,
-//     as a running filter instead of a sampled bound.
-//   * k <= 1024: weighted radix selects over the buffer (exact u64 mass
-//     histograms per digit) give the k-th composite, the top-p boundary and
-//     the drawn entry; the support is never sorted.
-//   * k >= V (top-p only): the same stream keeps the best >= 1024 entries and
-//     also builds an exact mass histogram over 1/128-octave key bins (every
-//     key with a nonzero mass falls in one of 4097 bins).  If the buffered
-//     prefix already holds the top-p mass the row is finished in LDS (a
-//     truncation hit, the exact analogue of the Gaussian sigma-truncation of
-//     the Qrita paper, section 3.1).  Otherwise the histogram names the bin of
-//     the boundary and the bins the draw can fall in, one more pass gathers
-//     just those bins, and the selects finish in LDS.
-//   * 1024 < k < V rows, and rows that defeat the above (more +inf entries
-//     than buffered, over-full bins), use a multi-pass whole-row radix select.
+//   * A persistent grid (three 512-thread workgroups per CU) takes work items
+//     in a fixed round-robin order; no queue counter is shared.  Top-p-only
+//     rows (k >= V) come first: each is cut into register-resident segments of
+//     at most 5120 16-byte vectors, and the segments of one row are placed in
+//     the same round of the grid so that they run at the same time.  Every
+//     other row is one item for one workgroup that streams the row once with
+//     eight 16-byte loads per thread in flight.  Giving each streamed row the
+//     same number of loads in flight shares HBM evenly between rows, and the
+//     bound on bytes in flight keeps the latency of the exchanges low.
+//   * Greedy rows (k = 1): streaming argmax of the composites.
+//   * Top-k rows (k <= 1024): the streamed entries at or above a running
+//     threshold go to an LDS candidate buffer; whenever it holds more than
+//     2048 entries a one-digit radix cut (or, if that cut keeps too many, an
+//     exact select of the k-th best) raises the threshold, which never passes
+//     the row's k-th best.  The buffer ends holding the row's best k, which
+//     mass-weighted radix selects finish.  This stands in for the
+//     2048-bucket radix select and candidate list of the cake_sampling page.
+//   * Top-p-only rows: each segment builds an exact mass histogram over
+//     1/128-octave key bins in LDS.  Two small exchanges follow through a
+//     per-row workspace (device-coherent stores, then a relaxed arrival
+//     counter; readers acquire; every wait is bounded): the summed 1/8-octave
+//     histogram names the coarse bin of the top-p boundary and the coarse bins
+//     the draw can fall in, and the fine bins of just those coarse bins then
+//     name the fine boundary bin and the fine draw bins.  Every segment
+//     gathers the entries of those few fine bins from its registers and the
+//     last segment to arrive finishes in LDS.  The row is read once.  This is
+//     the exact-integer analogue of the pivot and sigma-truncation searches of
+//     the Qrita paper (sections 3.1-3.2): the boundary is found by mass,
+//     never by sorting the nucleus.
+//   * Rows with 1024 < k < V, and any row whose fast path cannot decide
+//     (over-full gather, too many draw bins, an exchange that times out), are
+//     resolved by one workgroup with exact multi-pass radix selects over the
+//     whole row.
+//   * renorm_out is written by a second kernel from the per-row decision.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,62 +59,209 @@
 
 typedef uint64_t u64;
 typedef uint32_t u32;
+typedef uint16_t u16;
 
 namespace {
 
-constexpr int kBlock = 1024;            // threads per workgroup (16 waves)
+constexpr int kBlock = 512;            // threads per workgroup (8 waves)
 constexpr int kWaves = kBlock / 64;
-constexpr int kCap = 8192;              // candidate buffer entries (64 KiB of LDS)
-constexpr int kBins = 2048;             // 11-bit radix digits
-constexpr u32 kSlabMaxK = 1024;         // largest k served by the candidate buffer
-constexpr u32 kFullKeep = 1024;         // best entries always kept for top-p-only rows
+constexpr int kWavesPerSimd = 4;       // two workgroups per CU
+constexpr int kSlotsFull = 16;         // vectors per thread of a register-resident segment
+constexpr u32 kSegVecFull = kBlock * kSlotsFull;
+constexpr u32 kSegVecSmall = kBlock * 2;     // segment size under TES_FLAG_SMALL_SEGMENTS
+constexpr u32 kStreamDepth = 8;        // 16-byte loads per thread in flight when streaming
+constexpr u32 kChunk = 1024;           // rows per launch
+constexpr u32 kSlabMaxK = 1024;        // largest k served by the streaming top-k path
+constexpr size_t kWsBudget = 256u << 20;  // workspace bytes per sampler (rows per launch follow)
+constexpr int kBins = 2048;            // 11-bit radix digits
 constexpr u32 kInfKey = 0x7F800000u;
-constexpr u32 kOneKey = 0x3F800000u;    // 1.0f: masses saturate at 2^32 from here
-constexpr u32 kMinMassKey = 95u << 23;  // 2^-32: the smallest value with a nonzero mass
-constexpr int kFineShift = 16;          // fine bins: exponent + 7 mantissa bits
+constexpr u32 kOneKey = 0x3F800000u;   // 1.0f: masses saturate at 2^32 from here
+constexpr u32 kMinMassKey = 95u << 23; // 2^-32: the smallest value with a nonzero mass
+constexpr int kFineShift = 16;         // fine bins: exponent + 7 mantissa bits
 constexpr u32 kFineBase = kMinMassKey >> kFineShift;
 constexpr int kFineBins = (int)((kOneKey >> kFineShift) - kFineBase) + 1;  // 4097
-constexpr int kGroup = 8;               // rounds per group = loads in flight per thread
-constexpr u32 kSoftFill = kCap / 2;     // compact when a group leaves more than this
+constexpr int kCoarseBins = (kFineBins - 1) / 16 + 1;                       // 257
+constexpr int kDMax = 48;              // coarse bins whose fine bins are exchanged
+constexpr u32 kGSeg = 512;             // gathered entries per top-p-only segment
+constexpr u32 kSpinLimit = 1u << 16;   // polls before an exchange gives up
+constexpr u32 kMaxSegWs = 64;          // exchange slots per row in the workspace
 constexpr u64 kNoUpper = ~0ull;
 
+static_assert(kFineBins == 4097, "fine bin layout");
+static_assert(kCoarseBins == 257, "coarse bin layout");
+
 enum RowKind : u32 { kNormal = 0, kInfRow = 1, kZeroRow = 2 };
-enum RowPath : u32 { kPathBuffer = 0, kPathHit = 1, kPathGather = 2, kPathRowSelect = 3 };
+enum RowClass : u32 { kClsFull = 0, kClsWhole = 1, kClsSlab = 2, kClsGreedy = 3 };
+enum RowPath : u32 {
+    kPathSlab = 0, kPathFull = 1, kPathFullFallback = 2, kPathWhole = 3, kPathGreedy = 4,
+    kPathSlabFallback = 5
+};
+enum RowFlag : u32 { kFlagFail = 1u };
+constexpr int kStatWords = 16;  // per-row debug statistics (TES_FLAG_STATS)
+
+// ---------------------------------------------------------------------------
+// Workspace layout (device memory owned by the sampler handle)
+// ---------------------------------------------------------------------------
+struct RowState {  // zero between calls
+    u32 arrive_a;  // top-p-only: first exchange
+    u32 arrive_b;  // top-p-only: second exchange
+    u32 ticket;    // last-arriver ticket
+    u32 flags;     // kFlagFail
+    u32 pad[12];
+};
+static_assert(sizeof(RowState) == 64, "row state size");
+
+struct Decision {  // what renorm_out needs
+    u32 kind;
+    u32 m;
+    u32 token;
+    u32 path;
+    u64 c_keep;  // kept entries have composite >= c_keep
+    u64 M_p;     // kept mass (normal rows)
+};
+
+struct PubC {  // first exchange of a top-p-only segment (and its gather count)
+    u64 M;
+    u64 ninf;
+    u64 ng;      // entries gathered for the final selects (written last)
+    u64 coarse[kCoarseBins];
+};
+struct PubF {  // second exchange: fine bins of the listed coarse bins
+    u64 fine[kDMax][16];
+};
+
+struct Params {
+    const float* probs;  // first row of this launch
+    const int32_t* top_k;
+    const float* top_p;
+    int32_t* out_tokens;
+    u32* stats;          // per row, 8 words, or null
+    unsigned char* ws;
+    u64 seed;
+    u64 offset;
+    u32 V;
+    u32 nvec;       // vectors per row
+    u32 rows;       // rows in this launch
+    u32 row_base;   // global index of the first row (Philox counter, stats)
+    u32 seg_vec_full;  // vectors per register-resident segment of a top-p-only row
+    u32 s_ws;       // segment slots per row in the workspace
+    u32 rowbytes;   // bytes of the per-row exchange area
+    u32 chunk;      // rows the workspace holds
+    u32 flags;
+};
+
+__device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
+    return reinterpret_cast<RowState*>(p.ws) + r;
+}
+__device__ __forceinline__ Decision* ws_decision(const Params& p, u32 r) {
+    return reinterpret_cast<Decision*>(p.ws + (size_t)p.chunk * sizeof(RowState)) + r;
+}
+__device__ __forceinline__ unsigned char* ws_row(const Params& p, u32 r) {
+    return p.ws + (size_t)p.chunk * (sizeof(RowState) + sizeof(Decision)) + (size_t)r * p.rowbytes;
+}
+__device__ __forceinline__ PubC* pub_c(const Params& p, u32 r, u32 seg) {
+    return reinterpret_cast<PubC*>(ws_row(p, r)) + seg;
+}
+__device__ __forceinline__ PubF* pub_f(const Params& p, u32 r, u32 seg) {
+    return reinterpret_cast<PubF*>(ws_row(p, r) + (size_t)p.s_ws * sizeof(PubC)) + seg;
+}
+__device__ __forceinline__ u64* gather_area(const Params& p, u32 r, u32 seg) {
+    return reinterpret_cast<u64*>(ws_row(p, r) + (size_t)p.s_ws * (sizeof(PubC) + sizeof(PubF))) +
+           (size_t)seg * kGSeg;
+}
+// Pointers to device memory reach the kernel through LDS (see params_from),
+// which hides their address space; every access to rows and workspace goes
+// through these casts so that it is a global-memory instruction.  (A generic
+// "flat" access also counts against the LDS counter, so any LDS wait would
+// drain the loads in flight.)
+#define TES_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ TES_GLOBAL T* gp(T* a) {
+    return (TES_GLOBAL T*)a;
+}
+template <typename T>
+__device__ __forceinline__ T ld_g(const T* a) {
+    return *(const TES_GLOBAL T*)a;
+}
+
+// Device-coherent accessors for exchanged words.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* a, T v) {
+    __hip_atomic_store(gp(a), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(T* a) {
+    return __hip_atomic_load(gp(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T add_dev(T* a, T v) {
+    return __hip_atomic_fetch_add(gp(a), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void or_dev(T* a, T v) {
+    __hip_atomic_fetch_or(gp(a), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Shared memory
+// ---------------------------------------------------------------------------
+// LDS regions are shared by phases that never overlap in time:
+//   selects     sbuf = entries [0, 16 KiB) (kSelCap), shcnt [16, 24 KiB), shmass [24, 40 KiB)
+//   sorting     [0, 32 KiB) as u64[4096] (two halves of up to 2048 entries)
+//   top-k rows  candidate buffer [0, 32 KiB) (kSlabCap), packed 16-bit digit counts [32, 36 KiB)
+//   top-p rows  fine mass histogram [0, 32.8 KiB)
+constexpr u32 kSelCap = 2048;   // entries a select or a sort handles
+constexpr u32 kSlabCap = 4096;  // top-k candidate buffer
+constexpr int kRegionBytes = 40 * 1024;
 
 struct Smem {
-    u64 buf[kCap];
-    u64 hfine[kFineBins];
-    u64 hmass[kBins];
-    u32 hcnt[kBins];
+    Params p;                  // this launch's parameters (copied from the kernel arguments)
+    alignas(16) unsigned char region[kRegionBytes];
+    u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
+    u64 cabove[kCoarseBins];   // mass of the coarse bins above each bin
+    u64 finem[kDMax * 16];     // summed fine masses of the listed coarse bins
+    int flist[kDMax];          // listed coarse bins
+    u16 rows[kChunk];          // rows of this launch in class order
     u64 wpart[kWaves];
     u64 bc[4];
-    u64 theta;
-    u32 gctr[3];
-    u32 rctr;
-    u32 ccount;
+    u32 ctr[4];
+    u32 misc[8];
+    alignas(16) u16 wcnt[2][kWaves];  // per-wave append counts of a streaming step (double-buffered)
+    u32 npass;                 // passes over the row of the current item (statistics)
 };
+static_assert(kFineBins * 8 <= kRegionBytes, "fine histogram fits the region");
+
+__device__ __forceinline__ u64* sbuf(Smem& s) { return reinterpret_cast<u64*>(s.region); }
+__device__ __forceinline__ const u64* sbuf(const Smem& s) {
+    return reinterpret_cast<const u64*>(s.region);
+}
+__device__ __forceinline__ u32* shcnt(Smem& s) { return reinterpret_cast<u32*>(s.region + 16384); }
+__device__ __forceinline__ u64* shmass(Smem& s) { return reinterpret_cast<u64*>(s.region + 24576); }
+__device__ __forceinline__ u64* shfine(Smem& s) { return reinterpret_cast<u64*>(s.region); }
+__device__ __forceinline__ u32* shdig(Smem& s) { return reinterpret_cast<u32*>(s.region + 32768); }
 
 struct Sel {
     u64 c;      // selected composite
     u64 above;  // weight of the considered entries strictly above it
 };
 
-struct Outcome {
+struct Digit {
+    u32 d;
+    u32 cnt;
+    u64 above;
+};
+
+struct Outcome {  // a resolved row
     u32 token;
     u32 kind;
-    u64 c_keep;  // kept entries are those with composite >= c_keep
+    u64 c_keep;  // kept entries have composite >= c_keep
     u64 M_p;     // kept mass (normal rows)
-    u32 m;       // number of kept +inf entries (inf rows)
-    u32 path;
-    u32 passes;
-    u32 compactions;
-    u32 gathered;
+    u32 m;       // kept +inf entries (+inf rows)
 };
 
 // ---------------------------------------------------------------------------
 // Scalar helpers
 // ---------------------------------------------------------------------------
-
 // +0 for NaN and for anything with the sign bit set; otherwise the raw bits.
 __device__ __forceinline__ u32 sanitize(u32 bits) { return bits <= kInfKey ? bits : 0u; }
 
@@ -112,6 +270,7 @@ __device__ __forceinline__ u64 composite(u32 key, u32 idx) {
 }
 
 __device__ __forceinline__ u32 comp_index(u64 c) { return ~(u32)c; }
+__device__ __forceinline__ u32 comp_key(u64 c) { return (u32)(c >> 32); }
 
 // floor(min(x, 1) * 2^32) for the non-negative float whose bits are `key`.
 // x * 2^32 is exact in fp32 and the conversion truncates, i.e. floors.
@@ -172,10 +331,40 @@ __device__ u64 philox_uniform(u64 seed, u64 row, u64 offset) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave / block primitives (wave64)
+// Wave / block primitives (wave64, 8 waves)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32 lane_id() { return threadIdx.x & 63u; }
 __device__ __forceinline__ u32 wave_id() { return threadIdx.x >> 6; }
+
+// Values every lane holds identically (read from LDS or derived from such);
+// moving them to scalar registers keeps vector registers for row data.
+__device__ __forceinline__ u32 uni(u32 v) { return (u32)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ u64 uni(u64 v) {
+    return ((u64)uni((u32)(v >> 32)) << 32) | (u64)uni((u32)v);
+}
+
+// The launch parameters, read from LDS into scalar registers.
+__device__ __forceinline__ Params params_from(const Smem& s) {
+    Params p;
+    p.probs = reinterpret_cast<const float*>(uni((u64)s.p.probs));
+    p.top_k = reinterpret_cast<const int32_t*>(uni((u64)s.p.top_k));
+    p.top_p = reinterpret_cast<const float*>(uni((u64)s.p.top_p));
+    p.out_tokens = reinterpret_cast<int32_t*>(uni((u64)s.p.out_tokens));
+    p.stats = reinterpret_cast<u32*>(uni((u64)s.p.stats));
+    p.ws = reinterpret_cast<unsigned char*>(uni((u64)s.p.ws));
+    p.seed = uni(s.p.seed);
+    p.offset = uni(s.p.offset);
+    p.V = uni(s.p.V);
+    p.nvec = uni(s.p.nvec);
+    p.rows = uni(s.p.rows);
+    p.row_base = uni(s.p.row_base);
+    p.seg_vec_full = uni(s.p.seg_vec_full);
+    p.s_ws = uni(s.p.s_ws);
+    p.rowbytes = uni(s.p.rowbytes);
+    p.chunk = uni(s.p.chunk);
+    p.flags = uni(s.p.flags);
+    return p;
+}
 
 __device__ __forceinline__ u32 mbcnt64(u64 m) {
     return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
@@ -186,12 +375,19 @@ __device__ __forceinline__ u64 wave_sum(u64 v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
-
 __device__ __forceinline__ u64 wave_min(u64 v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         u64 w = __shfl_xor(v, o, 64);
         v = w < v ? w : v;
+    }
+    return v;
+}
+__device__ __forceinline__ u64 wave_max(u64 v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        u64 w = __shfl_xor(v, o, 64);
+        v = w > v ? w : v;
     }
     return v;
 }
@@ -204,9 +400,8 @@ __device__ u64 block_sum(Smem& s, u64 v) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) t += s.wpart[w];
     __syncthreads();
-    return t;
+    return uni(t);
 }
-
 __device__ u64 block_min(Smem& s, u64 v) {
     v = wave_min(v);
     if (lane_id() == 0) s.wpart[wave_id()] = v;
@@ -215,10 +410,20 @@ __device__ u64 block_min(Smem& s, u64 v) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) t = s.wpart[w] < t ? s.wpart[w] : t;
     __syncthreads();
-    return t;
+    return uni(t);
+}
+__device__ u64 block_max(Smem& s, u64 v) {
+    v = wave_max(v);
+    if (lane_id() == 0) s.wpart[wave_id()] = v;
+    __syncthreads();
+    u64 t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t = s.wpart[w] > t ? s.wpart[w] : t;
+    __syncthreads();
+    return uni(t);
 }
 
-__device__ u64 block_excl_scan(Smem& s, u64 v) {
+__device__ __forceinline__ u64 block_excl_scan(Smem& s, u64 v) {
     u64 x = v;
     const u32 lane = lane_id();
 #pragma unroll
@@ -235,34 +440,111 @@ __device__ u64 block_excl_scan(Smem& s, u64 v) {
     return pre + x - v;
 }
 
-// Append `c` at s.buf[base + slot] for every lane with pred set; slots come
-// from one LDS atomic per wave on *ctr.  Slots at or beyond `cap` are counted
-// but not written.  Must be reached by whole waves.
-__device__ __forceinline__ void wave_append(Smem& s, bool pred, u64 c, u32* ctr, u32 base,
-                                            u32 cap = kCap) {
-    u64 m = __ballot(pred);
+// Append `c` at arr[base + slot] for every lane with pred set; slots come from
+// one LDS atomic per wave on *ctr.  Slots at or beyond `cap` are counted but
+// not written.  Must be reached by whole waves.
+__device__ __forceinline__ void wave_append(u64* arr, bool pred, u64 c, u32* ctr, u32 base,
+                                            u32 cap) {
+    const u64 m = __ballot(pred);
     if (m == 0) return;
     const int leader = __ffsll((unsigned long long)m) - 1;
     u32 pos0 = 0;
     if ((int)lane_id() == leader) pos0 = atomicAdd(ctr, (u32)__popcll(m));
     pos0 = __shfl(pos0, leader, 64);
     const u32 pos = base + pos0 + mbcnt64(m);
-    if (pred && pos < cap) s.buf[pos] = c;
+    if (pred && pos < cap) arr[pos] = c;
+}
+
+// Appends, for every lane, its entries c[e] whose bit e is set in `mask`
+// (e < N) at arr[base + ...]: slots in lane order from one LDS atomic per wave
+// for the wave's total, each lane's offset from a prefix sum over the bits of
+// its count.  Slots at or beyond `cap` are counted but not written.  Must be
+// reached by whole waves.
+template <int N>
+__device__ __forceinline__ void wave_append_n(u64* arr, u32 mask, const u64 (&c)[N], u32* ctr,
+                                              u32 base, u32 cap) {
+    const u32 cnt = (u32)__popc(mask);
+    const u64 any = __ballot(cnt != 0);
+    if (any == 0) return;
+    u32 pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= N; ++b) {
+        const u64 bb = __ballot((cnt >> b) & 1u);
+        pre += mbcnt64(bb) << b;
+        tot += (u32)__popcll(bb) << b;
+    }
+    const int leader = __ffsll((unsigned long long)any) - 1;
+    u32 pos0 = 0;
+    if ((int)lane_id() == leader) pos0 = atomicAdd(ctr, tot);
+    pos0 = (u32)__builtin_amdgcn_readlane((int)pos0, leader);
+    u32 pos = base + pos0 + pre;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        if ((mask >> e) & 1u) {
+            if (pos < cap) arr[pos] = c[e];
+            ++pos;
+        }
+    }
+}
+
+// Every exchanged word is written with a device-coherent store (st_dev); a
+// publication is complete once each wave's stores have completed, which is
+// what vm_wait() waits for.  The arrival counters are then bumped with
+// relaxed device-scope atomics, and a reader invalidates its caches (acquire)
+// after it has seen the count it waits for.
+__device__ __forceinline__ void vm_wait() {
+    // s_waitcnt vmcnt(0), expcnt and lgkmcnt left unconstrained (gfx9 layout).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Publish this workgroup's exchanged data, count it in at *ctr and wait until
+// `n` workgroups have arrived (bounded).  Returns false on a timeout.
+__device__ bool arrive_wait(Smem& s, u32* ctr, u32 n) {
+    vm_wait();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        add_dev(ctr, 1u);
+        u32 ok = 1, it = 0;
+        while (ld_dev(ctr) < n) {
+            if (++it > kSpinLimit) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s.misc[7] = ok;
+    }
+    __syncthreads();
+    const bool ok = uni(s.misc[7]) != 0;
+    __syncthreads();
+    return ok;
+}
+
+// Count in at the row's ticket; true in the workgroup that arrives last, which
+// has then acquired everything the others published.
+__device__ bool arrive_last(Smem& s, u32* ticket, u32 n) {
+    vm_wait();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const u32 t = add_dev(ticket, 1u);
+        s.misc[6] = (t == n - 1) ? 1u : 0u;
+        if (t == n - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    const bool last = uni(s.misc[6]) != 0;
+    __syncthreads();
+    return last;
 }
 
 // ---------------------------------------------------------------------------
-// Histogram search
+// Histogram search and radix selects
 // ---------------------------------------------------------------------------
-struct Digit {
-    u32 d;
-    u32 cnt;
-    u64 above;
-};
-
 // Bins [0, nb) taken in descending order: the bin where the cumulative weight
-// first reaches W (1 <= W <= total weight); `above` = weight of higher bins.
-template <typename H>
-__device__ Digit find_desc(Smem& s, int nb, u64 W, H weight) {
+// first reaches W (1 <= W <= total weight); `above` = weight of higher bins,
+// `cnt` = count(bin).
+template <typename WF, typename CF>
+__device__ Digit find_desc(Smem& s, int nb, u64 W, WF weight, CF count) {
     const int per = (nb + kBlock - 1) / kBlock;
     const int top = nb - 1 - (int)threadIdx.x * per;
     u64 local = 0;
@@ -271,6 +553,7 @@ __device__ Digit find_desc(Smem& s, int nb, u64 W, H weight) {
     if (threadIdx.x == 0) {
         s.bc[0] = 0;
         s.bc[1] = 0;
+        s.bc[3] = 0;
     }
     u64 acc = block_excl_scan(s, local);
     for (int j = 0; j < per; ++j) {
@@ -280,15 +563,16 @@ __device__ Digit find_desc(Smem& s, int nb, u64 W, H weight) {
             if (acc < W && W <= acc + w) {
                 s.bc[0] = (u64)b;
                 s.bc[1] = acc;
+                s.bc[3] = count(b);
             }
             acc += w;
         }
     }
     __syncthreads();
     Digit g;
-    g.d = (u32)s.bc[0];
-    g.above = s.bc[1];
-    g.cnt = 0;
+    g.d = uni((u32)s.bc[0]);
+    g.above = uni(s.bc[1]);
+    g.cnt = uni((u32)s.bc[3]);
     __syncthreads();
     return g;
 }
@@ -296,47 +580,50 @@ __device__ Digit find_desc(Smem& s, int nb, u64 W, H weight) {
 __device__ __forceinline__ int level_shift(int l) { return l < 5 ? 52 - 11 * l : 0; }
 __device__ __forceinline__ int level_width(int l) { return l < 5 ? 11 : 8; }
 __device__ __forceinline__ u64 level_high_mask(int l) {
-    int top = level_shift(l) + level_width(l);
+    const int top = level_shift(l) + level_width(l);
     return top >= 64 ? 0ull : (~0ull << top);
 }
 
-// Weighted radix select over the entries c of s.buf[base, base + n) with
+// Weighted radix select over the entries c given by get(i, c) for i < n with
 // lo <= c < hi: the composite at which the descending cumulative weight (one
-// per entry, or its mass) first reaches W (1 <= W <= total).
-__device__ Sel select_buffer(Smem& s, u32 base, u32 n, u64 W, bool mass, u64 lo, u64 hi) {
+// per entry, or its mass) first reaches W (1 <= W <= total).  hc (and, for
+// mass weights, hm) are LDS digit tables of kBins entries.
+template <typename Get>
+__device__ Sel radix_select(Smem& s, u32 n, Get get, u64 W, bool mass, u64 lo, u64 hi, u32* hc,
+                            u64* hmw) {
     u64 prefix = 0, above = 0;
     for (int l = 0; l < 6; ++l) {
         const int sh = level_shift(l), wd = level_width(l);
         const u64 hm = level_high_mask(l);
         const u32 dmask = (1u << wd) - 1;
         for (int b = threadIdx.x; b < (1 << wd); b += kBlock) {
-            s.hcnt[b] = 0;
-            s.hmass[b] = 0;
+            hc[b] = 0;
+            if (mass) hmw[b] = 0;
         }
         __syncthreads();
         for (u32 i = threadIdx.x; i < n; i += kBlock) {
-            const u64 c = s.buf[base + i];
-            if (c >= lo && c < hi && (c & hm) == prefix) {
+            u64 c;
+            if (get(i, c) && c >= lo && c < hi && (c & hm) == prefix) {
                 const u32 d = (u32)(c >> sh) & dmask;
-                atomicAdd(&s.hcnt[d], 1u);
-                if (mass) atomicAdd((unsigned long long*)&s.hmass[d],
-                                    (unsigned long long)key_mass((u32)(c >> 32)));
+                atomicAdd(&hc[d], 1u);
+                if (mass) atomicAdd((unsigned long long*)&hmw[d],
+                                    (unsigned long long)key_mass(comp_key(c)));
             }
         }
         __syncthreads();
-        Digit g = mass ? find_desc(s, 1 << wd, W - above, [&](int b) { return s.hmass[b]; })
-                       : find_desc(s, 1 << wd, W - above, [&](int b) { return (u64)s.hcnt[b]; });
-        g.cnt = s.hcnt[g.d];
+        auto cf = [&](int b) { return (u64)hc[b]; };
+        const Digit g = mass ? find_desc(s, 1 << wd, W - above, [&](int b) { return hmw[b]; }, cf)
+                             : find_desc(s, 1 << wd, W - above, cf, cf);
         above += g.above;
         prefix |= (u64)g.d << sh;
         if (g.cnt == 1 || l == 5) {
             const u64 m2 = ~0ull << sh;
             for (u32 i = threadIdx.x; i < n; i += kBlock) {
-                const u64 c = s.buf[base + i];
-                if (c >= lo && c < hi && (c & m2) == prefix) s.bc[2] = c;
+                u64 c;
+                if (get(i, c) && c >= lo && c < hi && (c & m2) == prefix) s.bc[2] = c;
             }
             __syncthreads();
-            Sel r{s.bc[2], above};
+            const Sel r{uni(s.bc[2]), above};
             __syncthreads();
             return r;
         }
@@ -344,300 +631,339 @@ __device__ Sel select_buffer(Smem& s, u32 base, u32 n, u64 W, bool mass, u64 lo,
     return Sel{0, 0};  // not reached
 }
 
-// Keep at least the best L of s.buf[0..n) (n > L), choosing a radix
-// threshold that leaves at most keep_max >= L entries; raises s.theta.
-__device__ __noinline__ u32 compact_buffer(Smem& s, u32 n, u32 L, u32 keep_max) {
-    u64 prefix = 0;
-    u32 above = 0;
-    for (int l = 0; l < 6; ++l) {
-        const int sh = level_shift(l), wd = level_width(l);
-        const u64 hm = level_high_mask(l);
-        const u32 dmask = (1u << wd) - 1;
-        for (int b = threadIdx.x; b < (1 << wd); b += kBlock) s.hcnt[b] = 0;
-        __syncthreads();
-        for (u32 i = threadIdx.x; i < n; i += kBlock) {
-            const u64 c = s.buf[i];
-            if ((c & hm) == prefix) atomicAdd(&s.hcnt[(u32)(c >> sh) & dmask], 1u);
-        }
-        __syncthreads();
-        Digit g = find_desc(s, 1 << wd, (u64)(L - above), [&](int b) { return (u64)s.hcnt[b]; });
-        g.cnt = s.hcnt[g.d];
-        above += (u32)g.above;
-        prefix |= (u64)g.d << sh;
-        if (above + g.cnt <= keep_max) break;
-    }
-    constexpr int kPer = kCap / kBlock;
+// Select over sbuf(s)[0, n), n <= kSelCap (the digit tables sit above it).
+// One out-of-line copy: selects run once per row, with little else live.
+__device__ __noinline__ Sel select_buf(Smem& s, u32 n, u64 W, bool mass, u64 lo = 0,
+                                       u64 hi = kNoUpper) {
+    return radix_select(s, n, [&](u32 i, u64& c) { c = sbuf(s)[i]; return true; }, W, mass, lo, hi,
+                        shcnt(s), shmass(s));
+}
+
+// Count select over the top-k candidate buffer sbuf(s)[0, n), n <= kSlabCap
+// (its digit table sits above the buffer).
+__device__ __forceinline__ u64 select_slab(Smem& s, u32 n, u64 W) {
+    return radix_select(s, n, [&](u32 i, u64& c) { c = sbuf(s)[i]; return true; }, W, false, 0,
+                        kNoUpper, shdig(s), nullptr)
+        .c;
+}
+
+// Keep the entries of sbuf(s)[0, n) (n <= kSlabCap) at or above `keep`, in
+// place; returns how many there are.
+__device__ __forceinline__ u32 keep_above(Smem& s, u32 n, u64 keep) {
+    constexpr int kPer = kSlabCap / kBlock;
     u64 mine[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const u32 i = threadIdx.x + j * kBlock;
-        mine[j] = i < n ? s.buf[i] : 0ull;
+        mine[j] = i < n ? sbuf(s)[i] : 0ull;
     }
-    if (threadIdx.x == 0) s.ccount = 0;
-    __syncthreads();
+    u32 mask = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const u32 i = threadIdx.x + j * kBlock;
-        wave_append(s, i < n && mine[j] >= prefix, mine[j], &s.ccount, 0);
-    }
+    for (int j = 0; j < kPer; ++j)
+        mask |= (threadIdx.x + j * kBlock < n && mine[j] >= keep) ? 1u << j : 0u;
+    if (threadIdx.x == 0) s.ctr[3] = 0;
     __syncthreads();
-    const u32 kept = s.ccount;
-    if (threadIdx.x == 0 && prefix > s.theta) s.theta = prefix;
+    wave_append_n<kPer>(sbuf(s), mask, mine, &s.ctr[3], 0, kSlabCap);
+    __syncthreads();
+    const u32 kept = uni(s.ctr[3]);
     __syncthreads();
     return kept;
 }
 
 // ---------------------------------------------------------------------------
-// Streaming pass
+// Row data access
 // ---------------------------------------------------------------------------
 template <int VEC>
 struct VecT;
+typedef float f4 __attribute__((ext_vector_type(4)));
 template <>
 struct VecT<4> {
-    typedef float4 T;
-    __device__ static float get(const float4& v, int e) {
-        return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-    }
+    typedef f4 T;
+    __device__ static float get(const T& v, int e) { return v[e]; }
 };
 template <>
 struct VecT<1> {
     typedef float T;
-    __device__ static float get(const float& v, int) { return v; }
+    __device__ static float get(const T& v, int) { return v; }
 };
 
-// Re-run the candidate filter over rounds [ra, rb) one round at a time,
-// compacting before any round that could overflow the buffer.  Used for the
-// first group of a row (theta still 0) and for a group whose appends did not
-// fit; the mass histogram is not touched here.
-struct Fill {
-    u32 fill;
-    u32 compactions;
-};
+// Row data is read once: non-temporal loads keep it from displacing the
+// exchanged words and the kernel's own code in L2.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+    return __builtin_nontemporal_load((const TES_GLOBAL T*)p);
+}
 
-template <int VEC>
-__device__ __noinline__ Fill replay_rounds(Smem& s, const typename VecT<VEC>::T* __restrict__ rv,
-                                           u32 nvec, u32 ra, u32 rb, u32 L, u32 keep_max,
-                                           u32 fill) {
-    u32 compactions = 0;
-    typedef typename VecT<VEC>::T VT;
-    constexpr u32 kRound = kBlock * VEC;
-    for (u32 rr = ra; rr < rb; ++rr) {
-        if (fill > kCap - kRound) {
-            fill = compact_buffer(s, fill, L, keep_max);
-            ++compactions;
-        }
-        const u64 theta = s.theta;
-        if (threadIdx.x == 0) s.rctr = 0;
-        __syncthreads();
-        const u32 iv = rr * kBlock + threadIdx.x;
-        const bool valid = iv < nvec;
-        const VT x = valid ? rv[iv] : VT{};
+// Collects the composites of this workgroup's register-resident entries whose
+// key satisfies pred: the first `cap` (<= kSelCap) go to sbuf(s) through
+// per-wave appends and are then copied to out[0, cap) with device-coherent
+// stores.  Returns how many there are, which may exceed cap.
+template <int VEC, int NS, typename Pred>
+__device__ __forceinline__ u32 gather_regs(Smem& s, const typename VecT<VEC>::T (&x)[NS], u32 v0,
+                                           u32 v1, Pred pred, u64* out, u32 cap) {
+    if (threadIdx.x == 0) s.ctr[3] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < NS; ++d) {
+        const u32 i = v0 + d * kBlock + threadIdx.x;
+        u64 c[VEC];
+        u32 mask = 0;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const u64 c = composite(sanitize(__float_as_uint(VecT<VEC>::get(x, e))), iv * VEC + e);
-            wave_append(s, valid && c >= theta, c, &s.rctr, fill);
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
+            c[e] = composite(key, i * VEC + e);
+            mask |= (i < v1 && pred(key)) ? 1u << e : 0u;
         }
-        __syncthreads();
-        fill += s.rctr;
-        __syncthreads();
+        wave_append_n<VEC>(sbuf(s), mask, c, &s.ctr[3], 0, cap);
     }
-    return Fill{fill, compactions};
+    __syncthreads();
+    const u32 total = uni(s.ctr[3]);
+    const u32 m = total < cap ? total : cap;
+    for (u32 j = threadIdx.x; j < m; j += kBlock) st_dev(&out[j], sbuf(s)[j]);
+    __syncthreads();
+    return total;
 }
 
-// One read of the row.  Leaves in s.buf[0, fill) every entry whose composite
-// is >= s.theta (plus possibly some below it), at least the row's best
-// min(L, V) entries; with FULL also the exact fine mass histogram s.hfine.
-template <int VEC, bool FULL>
-__device__ Fill stream_row(Smem& s, const float* __restrict__ row, u32 V, u32 L, u32 keep_max) {
-    u32 compactions = 0;
-    typedef typename VecT<VEC>::T VT;
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
-    const u32 nvec = V / VEC;
-    const u32 nr = (nvec + kBlock - 1) / kBlock;
-    const u32 last = nvec - 1;
-    const u32 tid = threadIdx.x;
-    u32 fill = 0;
-    u64 theta = 0;
+// Bitonic sort, descending, of sbuf(s)[0, kBlock * E) (E = 1, 2 or 4).  Thread t
+// holds positions [t * E, t * E + E) in registers: pairs within a thread are
+// exchanged directly, pairs within a wave through lane shuffles, and pairs
+// across waves through LDS, alternating between the two halves of the region
+// so that each such stage needs one barrier.
+template <int E, int S>
+__device__ __forceinline__ void cas_local(u64 (&v)[E], u32 base, u32 size) {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if ((j & S) == 0) {
+            const bool desc = ((base + j) & size) == 0;
+            const u64 a = v[j], b = v[j + S];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[j] = sw ? b : a;
+            v[j + S] = sw ? a : b;
+        }
+    }
+}
 
-    // pf[d] holds round g * kGroup + d.  The loads of group g + 1 are issued
-    // slot by slot while group g is processed; iteration g = -1 only issues
-    // the first group, so every load sits at one program point and the
-    // registers of a slot never move.
-    constexpr u32 kRound = kBlock * VEC;
-    VT pf[kGroup];
-    const int ngroups = (int)((nr + kGroup - 1) / kGroup);
-    for (int g = -1; g < ngroups; ++g) {
-        const u32 r0 = (u32)g * kGroup;
-        u32* ctr = &s.gctr[(u32)(g + 3) % 3];
-        // Group 0 starts from theta = 0: it appends round by round, compacting
-        // whenever a round could overflow.  Later groups append freely and
-        // check the fill once, at the group barrier.
-        const bool careful = g == 0;
+template <int E>
+__device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
+    constexpr u32 N = kBlock * E;
+    static_assert(2 * N <= kSlabCap, "sort needs two LDS halves");
+    const u32 base = threadIdx.x * E;
 #pragma unroll
-        for (int d = 0; d < kGroup; ++d) {
-            if (g >= 0) {
-                const u32 iv = (r0 + d) * kBlock + tid;
-                const bool valid = iv < nvec;
-                u64 c[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(pf[d], e)));
-                    if (FULL && valid && key >= kMinMassKey)
-                        atomicAdd((unsigned long long*)&s.hfine[fine_bin(key)],
-                                  (unsigned long long)key_mass(key));
-                    c[e] = composite(key, iv * VEC + e);
-                }
-                if (careful) {
-                    if (fill > kCap - kRound) {
-                        fill = compact_buffer(s, fill, L, keep_max);
-                        ++compactions;
-                    }
-                    theta = s.theta;
-                    if (tid == 0) s.rctr = 0;
-                    __syncthreads();
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        wave_append(s, valid && c[e] >= theta, c[e], &s.rctr, fill);
-                    __syncthreads();
-                    fill += s.rctr;
-                    __syncthreads();
+    for (int j = 0; j < E; ++j) v[j] = sbuf(s)[base + j];
+    u32 half = 0;
+    for (u32 size = 2; size <= N; size <<= 1) {
+        for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride < (u32)E) {
+                if (stride == 1) {
+                    if constexpr (E >= 2) cas_local<E, 1>(v, base, size);
                 } else {
-                    bool pass[VEC];
-                    bool any = false;
+                    if constexpr (E >= 4) cas_local<E, 2>(v, base, size);
+                }
+            } else if (stride < 64u * E) {
+                const int lo = (int)(stride / E);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        pass[e] = valid && c[e] >= theta;
-                        any |= pass[e];
-                    }
-                    if (__ballot(any)) {
+                for (int j = 0; j < E; ++j) {
+                    const u32 i = base + j;
+                    const u64 o = __shfl_xor(v[j], lo, 64);
+                    const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
+                    v[j] = keep_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
+                }
+            } else {
+                u64* bx = sbuf(s) + half;
+                half ^= N;
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) wave_append(s, pass[e], c[e], ctr, fill);
-                    }
+                for (int j = 0; j < E; ++j) bx[base + j] = v[j];
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    const u32 i = base + j;
+                    const u64 o = bx[i ^ stride];
+                    const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
+                    v[j] = keep_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
                 }
             }
-            pf[d] = rv[min((u32)(g + 1) * kGroup * kBlock + d * kBlock + tid, last)];
         }
-        if (g < 0) continue;
-        if (!careful) {
-            __syncthreads();
-            const u32 napp = *ctr;
-            if (fill + napp > (u32)kCap) {
-                // Some appends did not fit: redo this group round by round.
-                const Fill f = replay_rounds<VEC>(s, rv, nvec, r0, min(r0 + kGroup, nr), L,
-                                                  keep_max, fill);
-                fill = f.fill;
-                compactions += f.compactions;
-            } else {
-                fill += napp;
-            }
-        }
-        // The counter of group g + 2 was last used by group g - 1, whose count
-        // every thread read before this group's barrier.
-        if (tid == 0) s.gctr[(u32)(g + 2) % 3] = 0;
-        if (fill > kSoftFill) {
-            fill = compact_buffer(s, fill, L, keep_max);
-            ++compactions;
-        }
-        theta = s.theta;
     }
-    return Fill{fill, compactions};
+    __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// Whole-row passes
-// ---------------------------------------------------------------------------
-// Calls f(key, idx, valid) for every element, VEC per thread per round; every
-// thread makes the same number of calls, so f may use wave collectives.  Loads
-// run kGroup rounds ahead.
+// Finish a row from its support sorted descending: positions [0, kk) of the
+// register arrays of sort_desc.
+template <int E>
+__device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u32 kk, u64 P, u64 u) {
+    const u32 base = threadIdx.x * E;
+    u64 q[E];
+    u64 ninf_l = 0, msum = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const bool in = base + j < kk;
+        const u32 key = comp_key(v[j]);
+        q[j] = in ? key_mass(key) : 0;
+        ninf_l += (in && key == kInfKey) ? 1u : 0u;
+        msum += q[j];
+    }
+    const u64 ninf = block_sum(s, ninf_l);
+    Outcome o{};
+    if (threadIdx.x == 0) s.bc[0] = s.bc[1] = s.bc[2] = s.bc[3] = 0;
+    if (ninf > 0) {
+        // +inf entries sort first, in index order: keep them all, draw the t-th.
+        const u64 t = __umul64hi(u, ninf);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if (base + j == t) s.bc[0] = v[j];
+            if (base + j == ninf - 1) s.bc[1] = v[j];
+        }
+        __syncthreads();
+        o.kind = kInfRow;
+        o.m = (u32)ninf;
+        o.token = comp_index(uni(s.bc[0]));
+        o.c_keep = uni(s.bc[1]);
+        __syncthreads();
+        return o;
+    }
+    const u64 Mk = block_sum(s, msum);
+    if (Mk == 0) {
+        // No entry of the support has a mass: the smallest index in it.
+        u64 mi = ~0ull;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if (base + j < kk) mi = (u64)comp_index(v[j]) < mi ? (u64)comp_index(v[j]) : mi;
+        o.kind = kZeroRow;
+        o.token = (u32)block_min(s, mi);
+        return o;
+    }
+    const u64 T = topp_threshold(P, Mk);
+    const u64 ex = block_excl_scan(s, msum);
+    u64 acc = ex;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (acc < T && T <= acc + q[j]) {  // the last kept position
+            s.bc[0] = acc + q[j];
+            s.bc[1] = v[j];
+        }
+        acc += q[j];
+    }
+    __syncthreads();
+    const u64 M_p = uni(s.bc[0]);
+    o.c_keep = uni(s.bc[1]);
+    const u64 t = __umul64hi(u, M_p);
+    acc = ex;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (acc <= t && t < acc + q[j]) s.bc[2] = v[j];
+        acc += q[j];
+    }
+    __syncthreads();
+    o.kind = kNormal;
+    o.M_p = M_p;
+    o.token = comp_index(uni(s.bc[2]));
+    __syncthreads();
+    return o;
+}
+
+// Calls f(key, idx, valid) for every element of a row, VEC per thread per
+// round; every thread makes the same number of calls, so f may use wave
+// collectives.  Eight rounds of loads are kept in flight.
 template <int VEC, typename F>
-__device__ void for_each_entry(const float* __restrict__ row, u32 V, F f) {
+__device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
     typedef typename VecT<VEC>::T VT;
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
-    const u32 nvec = V / VEC;
+    constexpr u32 kG = kStreamDepth;
     const u32 nr = (nvec + kBlock - 1) / kBlock;
     const u32 last = nvec - 1;
-    VT pf[kGroup];
+    VT pf[kG];
 #pragma unroll
-    for (int d = 0; d < kGroup; ++d) pf[d] = rv[min(d * kBlock + threadIdx.x, last)];
-    for (u32 r0 = 0; r0 < nr; r0 += kGroup) {
+    for (u32 d = 0; d < kG; ++d) {
+        pf[d] = ld_stream(&rv[min(d * kBlock + threadIdx.x, last)]);
+        __builtin_amdgcn_sched_barrier(0);  // issue in consumption order
+    }
+    for (u32 r0 = 0; r0 < nr; r0 += kG) {
 #pragma unroll
-        for (int d = 0; d < kGroup; ++d) {
+        for (u32 d = 0; d < kG; ++d) {
             const u32 iv = (r0 + d) * kBlock + threadIdx.x;
             const bool valid = iv < nvec;
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 f(sanitize(__float_as_uint(VecT<VEC>::get(pf[d], e))), iv * VEC + e, valid);
-            pf[d] = rv[min((r0 + d + kGroup) * kBlock + threadIdx.x, last)];
+            pf[d] = ld_stream(&rv[min((r0 + d + kG) * kBlock + threadIdx.x, last)]);
+            // Keep the refill here: hoisted above the other steps it would
+            // turn the pipeline into load-all-then-wait.
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-row resolution (1024 < k < V, forced, and fallbacks)
+// ---------------------------------------------------------------------------
 // Weighted radix select over the entries of the row with composite >= lo:
-// histogram one 11-bit digit per pass; once the selected bucket holds at most
-// gather_cap entries, gather it into LDS and finish there.
+// histogram one digit per pass; once the selected bucket holds at most
+// gather_cap (<= kSelCap) entries, gather it into LDS and finish there.
 template <int VEC>
-__device__ Sel select_row(Smem& s, const float* row, u32 V, u64 W, bool mass, u64 lo,
-                          u32 gather_cap, u32& passes) {
+__device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass, u64 lo,
+                          u32 gather_cap) {
     u64 prefix = 0, above = 0;
     for (int l = 0; l < 6; ++l) {
         const int sh = level_shift(l), wd = level_width(l);
         const u64 hm = level_high_mask(l);
         const u32 dmask = (1u << wd) - 1;
         for (int b = threadIdx.x; b < kBins; b += kBlock) {
-            s.hcnt[b] = 0;
-            s.hmass[b] = 0;
+            shcnt(s)[b] = 0;
+            shmass(s)[b] = 0;
         }
         __syncthreads();
-        for_each_entry<VEC>(row, V, [&](u32 key, u32 idx, bool valid) {
+        for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
             const u64 c = composite(key, idx);
             if (valid && c >= lo && (c & hm) == prefix) {
                 const u32 d = (u32)(c >> sh) & dmask;
-                atomicAdd(&s.hcnt[d], 1u);
-                if (mass) atomicAdd((unsigned long long*)&s.hmass[d],
+                atomicAdd(&shcnt(s)[d], 1u);
+                if (mass) atomicAdd((unsigned long long*)&shmass(s)[d],
                                     (unsigned long long)key_mass(key));
             }
         });
-        ++passes;
+        if (threadIdx.x == 0) ++s.npass;
         __syncthreads();
-        Digit g = mass ? find_desc(s, 1 << wd, W - above, [&](int b) { return s.hmass[b]; })
-                       : find_desc(s, 1 << wd, W - above, [&](int b) { return (u64)s.hcnt[b]; });
-        g.cnt = s.hcnt[g.d];
+        auto cf = [&](int b) { return (u64)shcnt(s)[b]; };
+        const Digit g = mass ? find_desc(s, 1 << wd, W - above, [&](int b) { return shmass(s)[b]; }, cf)
+                             : find_desc(s, 1 << wd, W - above, cf, cf);
         above += g.above;
         prefix |= (u64)g.d << sh;
         const u64 m2 = ~0ull << sh;
         if (g.cnt <= gather_cap || l == 5) {
-            if (threadIdx.x == 0) s.ccount = 0;
+            if (threadIdx.x == 0) s.ctr[3] = 0;
             __syncthreads();
-            for_each_entry<VEC>(row, V, [&](u32 key, u32 idx, bool valid) {
+            for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
                 const u64 c = composite(key, idx);
-                wave_append(s, valid && c >= lo && (c & m2) == prefix, c, &s.ccount, 0);
+                wave_append(sbuf(s), valid && c >= lo && (c & m2) == prefix, c, &s.ctr[3], 0,
+                            kSelCap);
             });
-            ++passes;
+            if (threadIdx.x == 0) ++s.npass;
             __syncthreads();
-            const u32 n = s.ccount;
+            const u32 n = uni(s.ctr[3]);
             __syncthreads();
-            Sel r = select_buffer(s, 0, n, W - above, mass, 0, kNoUpper);
+            const Sel r = select_buf(s, n < kSelCap ? n : kSelCap, W - above, mass);
             return Sel{r.c, above + r.above};
         }
     }
     return Sel{0, 0};  // not reached
 }
 
-// Exact resolution of a row from whole-row passes only.
 template <int VEC>
-__device__ void resolve_row(Smem& s, const float* row, u32 V, u32 k_eff, u64 P, u64 u,
-                            u32 gather_cap, Outcome& o) {
+__device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec, u32 V, u32 k_eff, u64 P,
+                               u64 u, u32 gather_cap) {
+    Outcome o{};
     u64 lo = 0;
-    if (k_eff < V) lo = select_row<VEC>(s, row, V, k_eff, false, 0, gather_cap, o.passes).c;
+    if (k_eff < V) lo = select_row<VEC>(s, row, nvec, k_eff, false, 0, gather_cap).c;
     u64 mk = 0, ninf = 0, minidx = ~0ull;
-    for_each_entry<VEC>(row, V, [&](u32 key, u32 idx, bool valid) {
+    for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
         if (valid && composite(key, idx) >= lo) {
             mk += key_mass(key);
             ninf += key == kInfKey;
             minidx = idx < minidx ? idx : minidx;
         }
     });
-    ++o.passes;
+    if (threadIdx.x == 0) ++s.npass;
     const u64 M_k = block_sum(s, mk);
     const u64 m = block_sum(s, ninf);
     minidx = block_min(s, minidx);
@@ -645,245 +971,687 @@ __device__ void resolve_row(Smem& s, const float* row, u32 V, u32 k_eff, u64 P, 
         const u64 t = __umul64hi(u, m);
         o.kind = kInfRow;
         o.m = (u32)m;
-        o.token = comp_index(select_row<VEC>(s, row, V, t + 1, false, 0, gather_cap, o.passes).c);
-        o.c_keep = select_row<VEC>(s, row, V, m, false, 0, gather_cap, o.passes).c;
-        return;
+        o.token = comp_index(select_row<VEC>(s, row, nvec, t + 1, false, 0, gather_cap).c);
+        o.c_keep = select_row<VEC>(s, row, nvec, m, false, 0, gather_cap).c;
+        return o;
     }
     if (M_k == 0) {
         o.kind = kZeroRow;
         o.token = (u32)minidx;
-        return;
+        return o;
     }
     const u64 T = topp_threshold(P, M_k);
-    const Sel bt = select_row<VEC>(s, row, V, T, true, lo, gather_cap, o.passes);
-    const u64 M_p = bt.above + key_mass((u32)(bt.c >> 32));
+    const Sel bt = select_row<VEC>(s, row, nvec, T, true, lo, gather_cap);
+    const u64 M_p = bt.above + key_mass(comp_key(bt.c));
     const u64 t = __umul64hi(u, M_p);
-    const Sel dr = select_row<VEC>(s, row, V, t + 1, true, lo, gather_cap, o.passes);
+    const Sel dr = select_row<VEC>(s, row, nvec, t + 1, true, lo, gather_cap);
     o.kind = kNormal;
     o.c_keep = bt.c;
     o.M_p = M_p;
     o.token = comp_index(dr.c);
+    return o;
 }
 
-// Counts, masses and the smallest index over buffered entries c >= lo.
-struct BufStats {
-    u64 n, ninf, mass, minidx;
-};
-
-__device__ BufStats buffer_stats(Smem& s, u32 fill, u64 lo) {
-    u64 n = 0, ninf = 0, q = 0, mi = ~0ull;
-    for (u32 i = threadIdx.x; i < fill; i += kBlock) {
-        const u64 c = s.buf[i];
-        if (c >= lo) {
-            const u32 key = (u32)(c >> 32);
-            ++n;
-            ninf += key == kInfKey;
-            q += key_mass(key);
-            const u64 id = comp_index(c);
-            mi = id < mi ? id : mi;
+// ---------------------------------------------------------------------------
+// Row completion
+// ---------------------------------------------------------------------------
+__device__ void finish_row(Smem& s, const Params& p, u32 r, const Outcome& o, u32 path,
+                           u32 gathered) {
+    if (threadIdx.x == 0) {
+        *gp(&p.out_tokens[r]) = (int32_t)o.token;
+        Decision* d = ws_decision(p, r);
+        *gp(&d->kind) = o.kind;
+        *gp(&d->m) = o.m;
+        *gp(&d->token) = o.token;
+        *gp(&d->path) = path;
+        *gp(&d->c_keep) = o.c_keep;
+        *gp(&d->M_p) = o.M_p;
+        if (p.stats) {
+            u32* st = p.stats + kStatWords * (size_t)(p.row_base + r);
+            *gp(&st[0]) = path;
+            *gp(&st[1]) = o.kind;
+            *gp(&st[4]) = gathered;
+            *gp(&st[5]) = (u32)wall_clock64();
         }
     }
-    BufStats r;
-    r.n = block_sum(s, n);
-    r.ninf = block_sum(s, ninf);
-    r.mass = block_sum(s, q);
-    r.minidx = block_min(s, mi);
-    return r;
 }
 
-// Resolve from the buffered prefix {c >= lo} (a prefix of the row's sorted
-// order).  `support_complete`: the prefix is the whole support (k <= 1024
-// rows) and M_k is its mass; otherwise M_k is given (top-p-only rows) and
-// the function returns false when the prefix cannot decide.
-__device__ bool resolve_prefix(Smem& s, u32 fill, u64 lo, const BufStats& st,
-                               bool support_complete, u64 M_k, u64 P, u64 u, Outcome& o) {
-    if (st.ninf > 0) {
-        if (!support_complete && st.ninf == st.n) return false;  // more +inf may lie below
-        const u64 m = st.ninf;
+__device__ void stat_start(const Params& p, u32 r, u32 segments) {
+    if (p.stats && threadIdx.x == 0) {
+        u32* st = p.stats + kStatWords * (size_t)(p.row_base + r);
+        *gp(&st[2]) = segments;
+        __hip_atomic_fetch_max(gp(&st[6]), 0xFFFFFFFFu - (u32)wall_clock64(), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ void stat_add(const Params& p, u32 r, int word, u32 v) {
+    if (p.stats && threadIdx.x == 0 && v)
+        add_dev(&p.stats[kStatWords * (size_t)(p.row_base + r) + word], v);
+}
+
+// Records why a top-p-only row left its fast path (stats word 7).
+__device__ __forceinline__ void stat_why(const Params& p, u32 r, u32 bits) {
+    if (p.stats && threadIdx.x == 0)
+        __hip_atomic_fetch_or(gp(&p.stats[kStatWords * (size_t)(p.row_base + r) + 7]), bits,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Debug phase timer: adds the ticks since `t` to stats word `word` and
+// returns the current tick (only with TES_FLAG_STATS).
+__device__ __forceinline__ u64 stat_phase(const Params& p, u32 r, int word, u64 t) {
+    if (!p.stats) return 0;
+    const u64 now = wall_clock64();
+    stat_add(p, r, word, (u32)(now - t));
+    return now;
+}
+
+// ---------------------------------------------------------------------------
+// Greedy rows (k = 1)
+// ---------------------------------------------------------------------------
+template <int VEC>
+__device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
+    const Params p = params_from(s);
+    stat_start(p, r, 1);
+    const u64 tp = p.stats ? wall_clock64() : 0;
+    u64 best = 0;
+    for_each_entry<VEC>(p.probs + (size_t)r * p.V, p.nvec, [&](u32 key, u32 idx, bool valid) {
+        const u64 c = valid ? composite(key, idx) : 0ull;
+        best = c > best ? c : best;
+    });
+    best = block_max(s, best);
+    stat_phase(p, r, 8, tp);
+    Outcome o{};
+    const u32 key = comp_key(best);
+    o.token = comp_index(best);
+    o.c_keep = best;
+    o.m = 1;
+    o.M_p = key_mass(key);
+    o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
+    finish_row(s, p, r, o, kPathGreedy, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k rows (2 <= k <= 1024)
+// ---------------------------------------------------------------------------
+template <int VEC>
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u64 u);
+
+// Streams the row once and keeps, in the LDS buffer, every entry whose key is
+// at or above a threshold key tkey, chosen so that about 1.5 k (and at least
+// k) entries of the row pass.  The test is one subtraction and one compare on
+// the raw bits: for tkey > 0, sanitize(b) >= tkey exactly when tkey <= b <=
+// the bits of +inf; tkey = 0 keeps everything.
+//   The first kStreamDepth steps (2048 entries each, the first loads in
+//   flight) are a sample: their keys are counted in 1/128-octave bins before
+//   anything else happens, and tkey becomes the lower edge of the bin that
+//   holds the sample's j-th best, j = ceil(1.5 k n / V) + 12 for n sampled
+//   entries (j = k when the sample is the whole row).
+//   Then the row is streamed from its start with no barriers: each lane with
+//   passing entries takes slots with one LDS atomic; slots beyond the buffer
+//   are counted but not written.
+// The buffer then holds exactly the entries at or above tkey.  When their
+// number is between k and the capacity, it holds the row's best k; otherwise
+// the row is resolved by whole-row passes.
+template <int VEC>
+__device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
+    const Params p = params_from(s);
+    typedef typename VecT<VEC>::T VT;
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V);
+    const u32 nvec = p.nvec;
+    // Issued before the stream so that its latency is hidden.
+    const float top_p = ld_g(&p.top_p[r]);
+    stat_start(p, r, 1);
+    const u64 tp = p.stats ? wall_clock64() : 0;
+    const u32 nsteps = (nvec + kBlock - 1) / kBlock;
+    const u32 last = nvec - 1;
+    u32* hist = reinterpret_cast<u32*>(s.region);  // sample counts per fine bin
+    for (int b = threadIdx.x; b < kFineBins; b += kBlock) hist[b] = 0;
+    if (threadIdx.x == 0) s.ctr[0] = 0;
+    __syncthreads();
+    VT pf[kStreamDepth];
+#pragma unroll
+    for (u32 d = 0; d < kStreamDepth; ++d) {
+        pf[d] = ld_stream(&rv[min(d * kBlock + threadIdx.x, last)]);
+        __builtin_amdgcn_sched_barrier(0);  // issue in consumption order
+    }
+    // The sample.
+    u32 nmass = 0;
+#pragma unroll
+    for (u32 d = 0; d < kStreamDepth; ++d) {
+        const bool valid = d * kBlock + threadIdx.x < nvec;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(pf[d], e)));
+            if (valid && key >= kMinMassKey) {
+                atomicAdd(&hist[fine_bin(key)], 1u);
+                ++nmass;
+            }
+        }
+    }
+    const u32 nsamp = min(kStreamDepth * kBlock, nvec) * VEC;
+    const u32 j = nsteps <= kStreamDepth
+                      ? k
+                      : (u32)(((u64)3 * k * nsamp + 2ull * p.V - 1) / (2ull * p.V)) + 12;
+    const u32 tot = (u32)block_sum(s, nmass);  // also orders the histogram
+    u32 tkey = 0;
+    if (j <= tot) {
+        auto cw = [&](int b) { return (u64)hist[b]; };
+        const Digit g = find_desc(s, kFineBins, j, cw, cw);
+        tkey = (u32)(g.d + kFineBase) << kFineShift;
+    }
+    __syncthreads();  // the histogram is dead; the buffer takes its place
+    const u32 span = kInfKey - tkey;
+    u64 tq = stat_phase(p, r, 11, tp);
+    // Appends this lane's passing entries of one vector (slots from one LDS
+    // atomic per lane).
+    auto append = [&](const VT& x, u32 iv) {
+        u32 mask = 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+            mask |= (iv < nvec && (tkey == 0 || b - tkey <= span)) ? 1u << e : 0u;
+        }
+        if (mask) {
+            u32 pos = atomicAdd(&s.ctr[0], (u32)__popc(mask));
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if ((mask >> e) & 1u) {
+                    if (pos < kSlabCap)
+                        sbuf(s)[pos] = composite(sanitize(__float_as_uint(VecT<VEC>::get(x, e))),
+                                                 iv * VEC + e);
+                    ++pos;
+                }
+            }
+        }
+    };
+    // Every step issues exactly one refill load (clamped into the row), so the
+    // compiler can count the loads in flight and wait for one at a time; steps
+    // past the end of the row append nothing.
+    for (u32 r0 = 0; r0 < nsteps; r0 += kStreamDepth) {
+#pragma unroll
+        for (u32 d = 0; d < kStreamDepth; ++d) {
+            append(pf[d], (r0 + d) * kBlock + threadIdx.x);
+            pf[d] = ld_stream(&rv[min((r0 + d + kStreamDepth) * kBlock + threadIdx.x, last)]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    u32 fill = uni(s.ctr[0]);
+    __syncthreads();
+    tq = stat_phase(p, r, 13, tq);
+    stat_phase(p, r, 8, tp);
+    const u64 P = fixed_p(top_p);
+    const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    if (fill >= k && fill <= kSlabCap) {
+        slab_finish<VEC>(s, r, fill, k, P, u);
+    } else {
+        const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
+                                           kSelCap);
+        finish_row(s, p, r, o, kPathSlabFallback, fill);
+    }
+}
+
+// The buffer sbuf(s)[0, n), k <= n <= kSlabCap, holds the row's best k.  Cut
+// it to exactly those when it holds more than a sort takes (always under
+// TES_FLAG_TINY_BUFFER), sort descending (padded with zeros, which sort last)
+// and finish on the first k positions.
+template <int VEC>
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u64 u) {
+    const Params p = params_from(s);
+    const u64 tp = p.stats ? wall_clock64() : 0;
+    const u32 gathered = n;
+    if (n > kSelCap || ((p.flags & TES_FLAG_TINY_BUFFER) && n > k)) {
+        n = keep_above(s, n, select_slab(s, n, k));
+        stat_add(p, r, 3, 1);
+    }
+    const u32 pad = n <= kBlock ? kBlock : n <= 2 * kBlock ? 2 * kBlock : 4 * kBlock;
+    for (u32 i = n + threadIdx.x; i < pad; i += kBlock) sbuf(s)[i] = 0;
+    __syncthreads();
+    Outcome o;
+    if (pad == kBlock) {
+        u64 v[1];
+        sort_desc<1>(s, v);
+        o = resolve_sorted<1>(s, v, k, P, u);
+    } else if (pad == 2 * kBlock) {
+        u64 v[2];
+        sort_desc<2>(s, v);
+        o = resolve_sorted<2>(s, v, k, P, u);
+    } else {
+        u64 v[4];
+        sort_desc<4>(s, v);
+        o = resolve_sorted<4>(s, v, k, P, u);
+    }
+    stat_phase(p, r, 9, tp);
+    finish_row(s, p, r, o, kPathSlab, gathered);
+}
+
+// ---------------------------------------------------------------------------
+// Top-p-only rows (k >= V)
+// ---------------------------------------------------------------------------
+// Coarse bin holding descending mass position P (1 <= P <= total), from the
+// summed coarse histogram and its descending exclusive prefix.
+__device__ __forceinline__ int coarse_of_pos(const Smem& s, u64 P) {
+    int lo = 0, hi = kCoarseBins - 1;  // largest bin whose cumulative mass reaches P
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s.cabove[mid] + s.coarse[mid] >= P) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Fine bin holding descending mass position P, looked up in the exchanged
+// fine bins of the listed coarse bins; -1 if its coarse bin is not listed.
+// `above` receives the mass of all higher fine bins.
+__device__ __forceinline__ int fine_of_pos(const Smem& s, int nlist, u64 P, u64& above) {
+    const int cb = coarse_of_pos(s, P);
+    int j = -1;
+    for (int q = 0; q < nlist; ++q)
+        if (s.flist[q] == cb) j = q;
+    if (j < 0) return -1;
+    u64 acc = s.cabove[cb];
+    for (int f = 15; f >= 0; --f) {
+        const u64 w = s.finem[j * 16 + f];
+        if (acc < P && P <= acc + w) {
+            above = acc;
+            return cb * 16 + f;
+        }
+        acc += w;
+    }
+    return -1;
+}
+
+template <int VEC>
+__device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
+                                         u64 above_f, int fbT, int nlist, bool failed);
+
+template <int VEC>
+__device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, u32 nseg) {
+    const Params p = params_from(s);
+    typedef typename VecT<VEC>::T VT;
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V);
+    const u32 sv = (p.nvec + nseg - 1) / nseg;
+    const u32 v0 = seg * sv, v1 = min(v0 + sv, p.nvec);
+    const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
+    const u32 gcap = tiny ? 16u : kGSeg;
+    const int dmax = tiny ? 1 : kDMax;
+    RowState* rs = ws_state(p, r);
+    const float top_p = ld_g(&p.top_p[r]);  // issued early: its latency hides behind the loads
+    stat_start(p, r, nseg);
+    u64 tp = p.stats ? wall_clock64() : 0;
+
+    VT x[kSlotsFull];
+#pragma unroll
+    for (int d = 0; d < kSlotsFull; ++d) {
+        const u32 i = v0 + d * kBlock + threadIdx.x;
+        if (i < v1) x[d] = ld_stream(&rv[i]);
+    }
+    for (int i = threadIdx.x; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
+    __syncthreads();
+    u64 M = 0, ninf = 0;
+#pragma unroll
+    for (int d = 0; d < kSlotsFull; ++d) {
+        const u32 i = v0 + d * kBlock + threadIdx.x;
+        if (i < v1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
+                if (key >= kMinMassKey) {
+                    const u64 q = key_mass(key);
+                    atomicAdd((unsigned long long*)&shfine(s)[fine_bin(key)], (unsigned long long)q);
+                    M += q;
+                    ninf += key == kInfKey;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    M = block_sum(s, M);
+    ninf = block_sum(s, ninf);
+    tp = stat_phase(p, r, 8, tp);
+
+    // First exchange: this segment's mass, +inf count and coarse histogram.
+    PubC* pc = pub_c(p, r, seg);
+    for (int b = threadIdx.x; b < kCoarseBins; b += kBlock) {
+        u64 v = 0;
+        const int f0 = b * 16, f1 = min(f0 + 16, kFineBins);
+        for (int f = f0; f < f1; ++f) v += shfine(s)[f];
+        st_dev(&pc->coarse[b], v);
+    }
+    if (threadIdx.x == 0) {
+        st_dev(&pc->M, M);
+        st_dev(&pc->ninf, ninf);
+    }
+    const bool ok = arrive_wait(s, &rs->arrive_a, nseg);
+    tp = stat_phase(p, r, 9, tp);
+
+    // Every segment sums the exchange and takes the same decisions.  The
+    // counter was acquired, so the published words are read with ordinary
+    // loads that can be in flight together.
+    u64 Mt = 0, nit = 0;
+    for (u32 q = 0; q < nseg; ++q) {
+        Mt += ld_g(&pub_c(p, r, q)->M);
+        nit += ld_g(&pub_c(p, r, q)->ninf);
+    }
+    Mt = uni(Mt);
+    nit = uni(nit);
+    for (int b = threadIdx.x; b < kCoarseBins; b += kBlock) {
+        u64 v = 0;
+        for (u32 q = 0; q < nseg; ++q) v += ld_g(&pub_c(p, r, q)->coarse[b]);
+        s.coarse[b] = v;
+    }
+    __syncthreads();
+    {
+        // cabove[b] = mass of the coarse bins above b (descending exclusive scan).
+        const int b = kCoarseBins - 1 - (int)threadIdx.x;
+        const u64 w = b >= 0 ? s.coarse[b] : 0;
+        const u64 ex = block_excl_scan(s, w);
+        if (b >= 0) s.cabove[b] = ex;
+        __syncthreads();
+    }
+    const u64 P = fixed_p(top_p);
+    const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    const u32 kind = nit > 0 ? kInfRow : (Mt == 0 ? kZeroRow : kNormal);
+    const u64 T = kind == kNormal ? topp_threshold(P, Mt) : 0;
+    int nlist = 0;
+    bool decidable = ok;
+    if (ok && kind == kNormal) {
+        const int cbT = coarse_of_pos(s, T);
+        const u64 U = s.cabove[cbT] + s.coarse[cbT];
+        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
+        const int chi = coarse_of_pos(s, t_lo + 1), clo = coarse_of_pos(s, t_hi + 1);
+        // Listed coarse bins: the boundary bin, then the draw range.
+        const int cnt = 1 + (chi - clo + 1) - ((cbT >= clo && cbT <= chi) ? 1 : 0);
+        if (cnt > dmax) {
+            decidable = false;
+            stat_why(p, r, 2u | (u32)min(cnt, 255) << 8);
+        } else {
+            if (threadIdx.x == 0) {
+                int q = 0;
+                s.flist[q++] = cbT;
+                for (int b = chi; b >= clo; --b)
+                    if (b != cbT) s.flist[q++] = b;
+            }
+            nlist = cnt;
+            __syncthreads();
+            // Second exchange: this segment's fine bins of the listed coarse bins.
+            PubF* pf = pub_f(p, r, seg);
+            for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
+                const int fb = s.flist[i / 16] * 16 + (i % 16);
+                st_dev(&pf->fine[i / 16][i % 16], fb < kFineBins ? shfine(s)[fb] : (u64)0);
+            }
+        }
+    }
+    if (!ok) stat_why(p, r, 1u);
+    if (!decidable && threadIdx.x == 0)
+        or_dev(&rs->flags, (u32)kFlagFail);
+    tp = stat_phase(p, r, 10, tp);
+    const bool ok2 = arrive_wait(s, &rs->arrive_b, nseg);
+    if (!ok2) stat_why(p, r, 4u);
+    if (threadIdx.x == 0) {
+        if (!ok2)
+            or_dev(&rs->flags, (u32)kFlagFail);
+        s.misc[4] = (!ok2 || (ld_dev(&rs->flags) & kFlagFail)) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool failed = uni(s.misc[4]) != 0;
+    __syncthreads();
+    tp = stat_phase(p, r, 11, tp);
+
+    // Gather, from registers, the entries the last segment needs.
+    int fbT = 0;
+    u64 above_f = 0;
+    u32 ng = 0;
+    u64* garea = gather_area(p, r, seg);
+    if (!failed && kind == kNormal) {
+        for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
+            u64 v = 0;
+            for (u32 q = 0; q < nseg; ++q) v += ld_g(&pub_f(p, r, q)->fine[i / 16][i % 16]);
+            s.finem[i] = v;
+        }
+        __syncthreads();
+        u64 a1 = 0, a2 = 0;
+        fbT = fine_of_pos(s, nlist, T, above_f);
+        const u64 U = fbT >= 0 ? above_f + s.finem[fbT - s.flist[0] * 16] : 0;
+        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
+        const int fdhi = fine_of_pos(s, nlist, t_lo + 1, a1);
+        const int fdlo = fine_of_pos(s, nlist, t_hi + 1, a2);
+        if (fbT < 0 || fdhi < 0 || fdlo < 0) {
+            // Cannot happen for consistent exchanges; decide by the slow path.
+            stat_why(p, r, 8u);
+            if (threadIdx.x == 0)
+                or_dev(&rs->flags, (u32)kFlagFail);
+        } else {
+            // Fine bins are key ranges: the boundary bin and the draw range.
+            const u32 kT0 = (u32)(fbT + kFineBase) << kFineShift;
+            const u32 kT1 = fbT == kFineBins - 1 ? 0xFFFFFFFFu : (u32)(fbT + 1 + kFineBase) << kFineShift;
+            const u32 kD0 = (u32)(fdlo + kFineBase) << kFineShift;
+            const u32 kD1 = fdhi == kFineBins - 1 ? 0xFFFFFFFFu : (u32)(fdhi + 1 + kFineBase) << kFineShift;
+            ng = gather_regs<VEC, kSlotsFull>(
+                s, x, v0, v1,
+                [&](u32 key) { return (key >= kT0 && key < kT1) || (key >= kD0 && key < kD1); },
+                garea, gcap);
+        }
+    } else if (!failed && kind == kInfRow) {
+        ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
+                                          garea, gcap);
+    }
+    if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
+    const bool last = arrive_last(s, &rs->ticket, nseg);
+    stat_phase(p, r, 12, tp);
+    if (last) full_finish<VEC>(s, r, nseg, kind, nit, T, above_f, fbT, nlist, failed);
+}
+
+// Last segment of a top-p-only row: load every segment's gathered entries
+// and finish (out of line, once per row).
+template <int VEC>
+__device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
+                                         u64 above_f, int fbT, int nlist, bool failed) {
+    const Params p = params_from(s);
+    RowState* rs = ws_state(p, r);
+    u64 tp = p.stats ? wall_clock64() : 0;
+    const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
+    const u32 gcap = tiny ? 16u : kGSeg;
+    const u64 P = fixed_p(ld_g(&p.top_p[r]));
+    const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    u64 over = 0;
+    for (u32 q = threadIdx.x; q < nseg; q += kBlock) over += ld_g(&pub_c(p, r, q)->ng) > gcap;
+    over = block_sum(s, over);
+    if (threadIdx.x == 0) s.misc[3] = ld_dev(&rs->flags);
+    __syncthreads();
+    const bool fail = (uni(s.misc[3]) & kFlagFail) || over != 0 || failed;
+    if (over) stat_why(p, r, 16u);
+    __syncthreads();
+    u32 nall = 0;
+    if (!fail && kind != kZeroRow) {
+        if (threadIdx.x == 0) s.ctr[3] = 0;
+        __syncthreads();
+        for (u32 q = 0; q < nseg; ++q) {
+            const u32 nq = (u32)ld_g(&pub_c(p, r, q)->ng);
+            const u64* gq = gather_area(p, r, q);
+            for (u32 i0 = 0; i0 < nq; i0 += kBlock) {
+                const u32 i = i0 + threadIdx.x;
+                const u64 c = i < nq ? ld_g(&gq[i]) : 0;
+                wave_append(sbuf(s), i < nq, c, &s.ctr[3], 0, kSelCap);
+            }
+        }
+        __syncthreads();
+        nall = uni(s.ctr[3]);
+        __syncthreads();
+    }
+    Outcome o{};
+    u32 path = kPathFull;
+    if (!fail && nall > kSelCap) stat_why(p, r, 32u);
+    if (fail || nall > kSelCap) {
+        o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, p.V, P, u, kSelCap);
+        path = kPathFullFallback;
+    } else if (kind == kZeroRow) {
+        o.kind = kZeroRow;
+        o.token = 0;  // the support is the whole row: its smallest index
+    } else if (kind == kInfRow) {
+        const u64 m = nit;
         const u64 t = __umul64hi(u, m);
         o.kind = kInfRow;
         o.m = (u32)m;
-        o.token = comp_index(select_buffer(s, 0, fill, t + 1, false, lo, kNoUpper).c);
-        o.c_keep = select_buffer(s, 0, fill, m, false, lo, kNoUpper).c;
-        return true;
+        o.token = comp_index(select_buf(s, nall, t + 1, false).c);
+        u64 mn = ~0ull;
+        for (u32 i = threadIdx.x; i < nall; i += kBlock) mn = sbuf(s)[i] < mn ? sbuf(s)[i] : mn;
+        o.c_keep = block_min(s, mn);
+    } else {
+        const Sel sb = select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
+        const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
+        const u64 t = __umul64hi(u, M_p);
+        u64 above_d = 0;
+        const int fd = fine_of_pos(s, nlist, t + 1, above_d);
+        const Sel sd = select_buf(s, nall, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
+        o.kind = kNormal;
+        o.c_keep = sb.c;
+        o.M_p = M_p;
+        o.token = comp_index(sd.c);
     }
-    if (M_k == 0) {
-        o.kind = kZeroRow;
-        o.token = support_complete ? (u32)st.minidx : 0u;  // a top-p-only support starts at 0
-        return true;
+    if (threadIdx.x == 0) {
+        st_dev(&rs->arrive_a, 0u);
+        st_dev(&rs->arrive_b, 0u);
+        st_dev(&rs->ticket, 0u);
+        st_dev(&rs->flags, 0u);
     }
-    const u64 T = topp_threshold(P, M_k);
-    if (st.mass < T) return false;
-    const Sel bt = select_buffer(s, 0, fill, T, true, lo, kNoUpper);
-    const u64 M_p = bt.above + key_mass((u32)(bt.c >> 32));
-    const u64 t = __umul64hi(u, M_p);
-    const Sel dr = select_buffer(s, 0, fill, t + 1, true, lo, kNoUpper);
-    o.kind = kNormal;
-    o.c_keep = bt.c;
-    o.M_p = M_p;
-    o.token = comp_index(dr.c);
-    return true;
+    stat_phase(p, r, 13, tp);
+    finish_row(s, p, r, o, path, nall);
 }
 
-// Top-p-only row whose nucleus is larger than the buffered prefix: the fine
-// histogram names the boundary bin and the bins the draw can fall in; one
-// pass gathers those bins into s.buf[fill, kCap) and the selects finish
-// there.  Returns false if the gathered entries do not fit.
+// ---------------------------------------------------------------------------
+// Whole-row items
+// ---------------------------------------------------------------------------
 template <int VEC>
-__device__ bool resolve_gather(Smem& s, const float* row, u32 V, u32 fill, u64 M, u64 P, u64 u,
-                               Outcome& o) {
-    const u64 T = topp_threshold(P, M);
-    auto hw = [&](int b) { return s.hfine[b]; };
-    const Digit bT = find_desc(s, kFineBins, T, hw);
-    const u64 hT = s.hfine[bT.d];
-    // M_p lies in [T, above(bT) + mass(bT)], so t lies in [t_lo, t_hi].
-    const u64 t_lo = __umul64hi(u, T);
-    const u64 t_hi = __umul64hi(u, bT.above + hT);
-    const Digit bDhi = find_desc(s, kFineBins, t_lo + 1, hw);  // bin holding position t_lo
-    const Digit bDlo = find_desc(s, kFineBins, t_hi + 1, hw);  // bin holding position t_hi
-    const u32 bt = bT.d, dlo = bDlo.d, dhi = bDhi.d;
-    if (threadIdx.x == 0) s.ccount = 0;
+__device__ __attribute__((always_inline)) void do_whole(Smem& s, u32 r, u32 k_eff) {
+    const Params p = params_from(s);
+    stat_start(p, r, 1);
+    const u64 P = fixed_p(ld_g(&p.top_p[r]));
+    const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
+    if (threadIdx.x == 0) s.npass = 0;
+    const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k_eff, P, u,
+                                       tiny ? 64u : kSelCap);
+    stat_add(p, r, 3, uni(s.npass));
+    finish_row(s, p, r, o, kPathWhole, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32 row_k_eff(const Params& p, u32 r) {
+    const int32_t k = ld_g(&p.top_k[r]);
+    return (k <= 0 || (u32)k >= p.V) ? p.V : (u32)k;
+}
+
+__device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full) {
+    if (p.flags & TES_FLAG_FORCE_ROW_SELECT) return kClsWhole;
+    if (k_eff == 1) return kClsGreedy;
+    if (k_eff <= kSlabMaxK) return kClsSlab;
+    if (k_eff == p.V && s_full <= p.s_ws) return kClsFull;
+    return kClsWhole;
+}
+
+// One work item per workgroup, in block order.  Items [0, nf * S) are the
+// segments of the nf top-p-only rows, S consecutive items per row: blocks are
+// dispatched in order, so the segments of a row start together and wait for
+// each other only briefly (the waits are bounded all the same).  The other
+// rows follow, one item each: whole-row rows, top-k rows, then greedy rows.
+// Blocks beyond the last item return at once.  No item loop: values live
+// across one would raise the register pressure of every path.
+template <int VEC>
+__global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params p) {
+    __shared__ Smem s;
+    if (threadIdx.x == 0) {
+        s.p = p;
+        s.npass = 0;
+    }
+    const u32 s_full = (p.nvec + p.seg_vec_full - 1) / p.seg_vec_full;
+
+    // Rows in class order (stable within a class): each thread takes two rows.
+    const u32 r0 = threadIdx.x * 2;
+    u32 cls[2];
+    u64 local = 0;  // four 16-bit class counts
+    for (int j = 0; j < 2; ++j) {
+        const u32 r = r0 + j;
+        cls[j] = r < p.rows ? row_class(p, row_k_eff(p, r), s_full) : 4u;
+        if (cls[j] < 4) local += 1ull << (16 * cls[j]);
+    }
+    const u64 ex = block_excl_scan(s, local);
+    if (threadIdx.x == kBlock - 1) {
+        const u64 tot = ex + local;
+        s.misc[0] = (u32)(tot & 0xFFFF);
+        s.misc[1] = (u32)((tot >> 16) & 0xFFFF);
+        s.misc[2] = (u32)((tot >> 32) & 0xFFFF);
+        s.misc[3] = (u32)((tot >> 48) & 0xFFFF);
+    }
     __syncthreads();
-    const u32 cap = kCap - fill;
-    for_each_entry<VEC>(row, V, [&](u32 key, u32 idx, bool valid) {
-        bool take = false;
-        if (valid && key >= kMinMassKey) {
-            const u32 b = fine_bin(key);
-            take = b == bt || (b >= dlo && b <= dhi);
+    u32 base[4];
+    u32 acc = 0;
+    for (int c = 0; c < 4; ++c) {
+        base[c] = acc;
+        acc += s.misc[c];
+    }
+    u32 seen[4] = {0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {
+        const u32 c = cls[j];
+        if (c < 4) {
+            s.rows[base[c] + (u32)((ex >> (16 * c)) & 0xFFFF) + seen[c]] = (u16)(r0 + j);
+            ++seen[c];
         }
-        wave_append(s, take, composite(key, idx), &s.ccount, fill, kCap);
-    });
-    ++o.passes;
+    }
     __syncthreads();
-    const u32 ng = s.ccount;
+    const u32 nf = uni(s.misc[kClsFull]);
+    const u32 n_whole = uni(s.misc[kClsWhole]);
+    const u32 n_slab = uni(s.misc[kClsSlab]);
+    const u32 full_end = nf * s_full;
+    const u32 item = blockIdx.x;
     __syncthreads();
-    o.gathered = ng;
-    if (ng > cap) return false;
-    const Sel sb = select_buffer(s, fill, ng, T - bT.above, true, fine_lo(bt), fine_hi(bt));
-    const u64 M_p = bT.above + sb.above + key_mass((u32)(sb.c >> 32));
-    const u64 t = __umul64hi(u, M_p);
-    const Digit bD = find_desc(s, kFineBins, t + 1, hw);
-    const Sel sd = select_buffer(s, fill, ng, t + 1 - bD.above, true, fine_lo(bD.d),
-                                 fine_hi(bD.d));
-    o.kind = kNormal;
-    o.c_keep = sb.c;
-    o.M_p = M_p;
-    o.token = comp_index(sd.c);
-    return true;
+    if (item < full_end) {
+        const u32 j = item / s_full;
+        do_full<VEC>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
+    } else if (item < full_end + (p.rows - nf)) {
+        const u32 i = item - full_end;
+        const u32 r = uni((u32)s.rows[nf + i]);
+        if (i < n_whole)
+            do_whole<VEC>(s, r, row_k_eff(p, r));
+        else if (i < n_whole + n_slab)
+            do_slab<VEC>(s, r, row_k_eff(p, r));
+        else
+            do_greedy<VEC>(s, r);
+    }
 }
 
+// renorm_out[r][i] = q_i / M_p for kept entries (1/m for kept +inf), else 0.
 template <int VEC>
-__device__ void write_renorm(const float* __restrict__ row, float* __restrict__ out, u32 V,
-                             const Outcome& o) {
+__global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict__ probs, u32 V,
+                                                         u32 nvec, const Decision* __restrict__ dec,
+                                                         float* __restrict__ out) {
     typedef typename VecT<VEC>::T VT;
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
-    VT* __restrict__ ov = reinterpret_cast<VT*>(out);
-    const u32 nvec = V / VEC;
-    const double inv = o.kind == kNormal ? 1.0 / (double)o.M_p : 0.0;
-    const float w_inf = o.kind == kInfRow ? (float)(1.0 / (double)o.m) : 0.0f;
-    for (u32 iv = threadIdx.x; iv < nvec; iv += kBlock) {
+    const u32 r = blockIdx.y;
+    const Decision d = dec[r];
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
+    VT* __restrict__ ov = reinterpret_cast<VT*>(out + (size_t)r * V);
+    const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
+    const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
+    for (u32 iv = blockIdx.x * 256 + threadIdx.x; iv < nvec; iv += gridDim.x * 256) {
         const VT x = rv[iv];
-        float r[VEC];
+        float o[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x, e)));
-            const bool kept = o.kind != kZeroRow && composite(key, iv * VEC + e) >= o.c_keep;
-            r[e] = !kept ? 0.0f
-                         : (o.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
+            const bool kept = d.kind != kZeroRow && composite(key, iv * VEC + e) >= d.c_keep;
+            o[e] = !kept ? 0.0f
+                         : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
         }
         if constexpr (VEC == 4) {
-            ov[iv] = make_float4(r[0], r[1], r[2], r[3]);
+            ov[iv] = f4{o[0], o[1], o[2], o[3]};
         } else {
-            ov[iv] = r[0];
+            ov[iv] = o[0];
         }
     }
 }
 
-constexpr int kStatWords = 8;
-
-template <int VEC>
-__global__ __launch_bounds__(kBlock) void tes_sample_kernel(
-    const float* __restrict__ probs, u32 V, const int32_t* __restrict__ top_k,
-    const float* __restrict__ top_p, u64 seed, u64 offset, int32_t* __restrict__ out_tokens,
-    float* __restrict__ renorm, unsigned flags, u32* __restrict__ stats) {
-    __shared__ Smem s;
-    const u64 t0 = wall_clock64();
-    const u32 b = blockIdx.x;
-    const float* row = probs + (size_t)b * V;
-    const int32_t kin = top_k[b];
-    const u32 k_eff = (kin <= 0 || (u32)kin >= V) ? V : (u32)kin;
-    const u64 P = fixed_p(top_p[b]);
-    const u64 u = philox_uniform(seed, b, offset);
-    const bool force_row = flags & TES_FLAG_FORCE_ROW_SELECT;
-    const bool tiny = flags & TES_FLAG_TINY_BUFFER;
-    const u32 gather_cap = tiny ? 64u : (u32)kCap;
-
-    if (threadIdx.x == 0) {
-        s.gctr[0] = s.gctr[1] = s.gctr[2] = 0;
-        s.theta = 0;
-    }
-    Outcome o{};
-    bool done = false;
-    u64 t1 = t0;
-    if (!force_row && k_eff <= kSlabMaxK) {
-        __syncthreads();
-        const u32 keep_max = tiny ? k_eff : (k_eff > 2048u ? k_eff : 2048u);
-        const Fill f = stream_row<VEC, false>(s, row, V, k_eff, keep_max);
-        const u32 fill = f.fill;
-        o.compactions = f.compactions;
-        t1 = wall_clock64();
-        o.passes = 1;
-        o.path = kPathBuffer;
-        // The support is the best k_eff buffered entries.
-        const u64 c_k = select_buffer(s, 0, fill, k_eff, false, 0, kNoUpper).c;
-        const BufStats st = buffer_stats(s, fill, c_k);
-        done = resolve_prefix(s, fill, c_k, st, true, st.mass, P, u, o);
-    } else if (!force_row && k_eff == V) {
-        for (int i = threadIdx.x; i < kFineBins; i += kBlock) s.hfine[i] = 0;
-        __syncthreads();
-        const u32 L = tiny ? 64u : kFullKeep;
-        const u32 keep_max = tiny ? L : 2048u;
-        const Fill f = stream_row<VEC, true>(s, row, V, L, keep_max);
-        const u32 fill = f.fill;
-        o.compactions = f.compactions;
-        t1 = wall_clock64();
-        o.passes = 1;
-        u64 hm = 0;
-        for (int i = threadIdx.x; i < kFineBins; i += kBlock) hm += s.hfine[i];
-        const u64 M = block_sum(s, hm);
-        const u64 lo = s.theta;
-        const BufStats st = buffer_stats(s, fill, lo);
-        o.path = kPathHit;
-        done = resolve_prefix(s, fill, lo, st, false, M, P, u, o);
-        if (!done && st.ninf == 0 && M > 0) {
-            o.path = kPathGather;
-            done = resolve_gather<VEC>(s, row, V, tiny ? kCap - 64u : fill, M, P, u, o);
-        }
-    } else {
-        __syncthreads();
-    }
-    if (!done) {
-        o.path = kPathRowSelect;
-        resolve_row<VEC>(s, row, V, k_eff, P, u, gather_cap, o);
-    }
-    const u64 t2 = wall_clock64();
-    if (threadIdx.x == 0) out_tokens[b] = (int32_t)o.token;
-    if (renorm) write_renorm<VEC>(row, renorm + (size_t)b * V, V, o);
-    if (stats) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            u32* st = stats + (size_t)kStatWords * b;
-            st[0] = o.path;
-            st[1] = o.passes + (renorm ? 1u : 0u);
-            st[2] = o.compactions;
-            st[3] = o.kind;
-            st[4] = (u32)(t1 - t0);
-            st[5] = (u32)(t2 - t1);
-            st[6] = (u32)(wall_clock64() - t2);
-            st[7] = o.gathered;
-        }
-    }
-}
 
 }  // namespace
 
@@ -895,6 +1663,12 @@ struct tes_sampler {
     int max_batch;
     int max_vocab;
     unsigned flags;
+    unsigned char* ws;
+    size_t ws_bytes;
+    u32 s_ws;
+    u32 rowbytes;
+    u32 chunk;
+    u32 seg_full;
     u32* d_stats;
 };
 
@@ -916,6 +1690,8 @@ struct DeviceGuard {
     }
 };
 
+u32 ceil_div(u32 a, u32 b) { return (a + b - 1) / b; }
+
 }  // namespace
 
 extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int max_vocab,
@@ -924,7 +1700,8 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     *out = nullptr;
     if (max_batch < 1 || max_vocab < 1 || max_vocab > (1 << 30) || device < 0)
         return TES_ERR_INVALID_ARGUMENT;
-    if (flags & ~(TES_FLAG_FORCE_ROW_SELECT | TES_FLAG_TINY_BUFFER | TES_FLAG_STATS))
+    if (flags & ~(TES_FLAG_FORCE_ROW_SELECT | TES_FLAG_TINY_BUFFER | TES_FLAG_STATS |
+                  TES_FLAG_SMALL_SEGMENTS))
         return TES_ERR_INVALID_ARGUMENT;
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
@@ -935,11 +1712,43 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return TES_ERR_NO_DEVICE;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return TES_ERR_UNSUPPORTED_DEVICE;
-    tes_sampler* s = new (std::nothrow) tes_sampler{device, max_batch, max_vocab, flags, nullptr};
+    tes_sampler* s = new (std::nothrow) tes_sampler{};
     if (!s) return TES_ERR_OUT_OF_MEMORY;
+    s->device = device;
+    s->max_batch = max_batch;
+    s->max_vocab = max_vocab;
+    s->flags = flags;
+    s->seg_full = (flags & TES_FLAG_SMALL_SEGMENTS) ? kSegVecSmall : kSegVecFull;
+    // Exchange slots per row: enough for 16-byte rows of max_vocab; top-p-only
+    // rows that need more segments (large scalar-path rows) use whole-row passes.
+    s->s_ws = ceil_div(ceil_div((u32)max_vocab, 4), s->seg_full);
+    if (s->s_ws < 1) s->s_ws = 1;
+    if (s->s_ws > kMaxSegWs) s->s_ws = kMaxSegWs;
+    size_t rb = (size_t)s->s_ws * (sizeof(PubC) + sizeof(PubF) + (size_t)kGSeg * sizeof(u64));
+    rb = (rb + 255) & ~(size_t)255;
+    s->rowbytes = (u32)rb;
+    s->chunk = (u32)max_batch < kChunk ? (u32)max_batch : kChunk;
+    const size_t per_row = sizeof(RowState) + sizeof(Decision) + rb;
+    const size_t budget_rows = kWsBudget / per_row;
+    if (budget_rows < s->chunk) s->chunk = budget_rows < 1 ? 1u : (u32)budget_rows;
+    s->ws_bytes = (size_t)s->chunk * (sizeof(RowState) + sizeof(Decision)) + (size_t)s->chunk * rb;
+    DeviceGuard g(device);
+    if (!g.ok) {
+        delete s;
+        return TES_ERR_NO_DEVICE;
+    }
+    if (hipMalloc(&s->ws, s->ws_bytes) != hipSuccess) {
+        delete s;
+        return TES_ERR_OUT_OF_MEMORY;
+    }
+    if (hipMemset(s->ws, 0, s->ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(s->ws);
+        delete s;
+        return TES_ERR_OUT_OF_MEMORY;
+    }
     if (flags & TES_FLAG_STATS) {
-        DeviceGuard g(device);
-        if (!g.ok || hipMalloc(&s->d_stats, sizeof(u32) * kStatWords * (size_t)max_batch) != hipSuccess) {
+        if (hipMalloc(&s->d_stats, sizeof(u32) * kStatWords * (size_t)max_batch) != hipSuccess) {
+            (void)hipFree(s->ws);
             delete s;
             return TES_ERR_OUT_OF_MEMORY;
         }
@@ -964,22 +1773,63 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
     DeviceGuard g(s->device);
     if (!g.ok) return TES_ERR_LAUNCH;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    u32* stats = (s->flags & TES_FLAG_STATS) ? s->d_stats : nullptr;
-    if (vec4)
-        hipLaunchKernelGGL(tes_sample_kernel<4>, dim3(B), dim3(kBlock), 0, st, probs, (u32)V,
-                           top_k, top_p, seed, offset, out_tokens, renorm_out, s->flags, stats);
-    else
-        hipLaunchKernelGGL(tes_sample_kernel<1>, dim3(B), dim3(kBlock), 0, st, probs, (u32)V,
-                           top_k, top_p, seed, offset, out_tokens, renorm_out, s->flags, stats);
-    if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+    const u32 nvec = vec4 ? (u32)V / 4 : (u32)V;
+    const u32 s_full = ceil_div(nvec, s->seg_full);
+    for (int c0 = 0; c0 < B; c0 += (int)s->chunk) {
+        const u32 rows = (u32)(B - c0) < s->chunk ? (u32)(B - c0) : s->chunk;
+        Params p;
+        p.probs = probs + (size_t)c0 * V;
+        p.top_k = top_k + c0;
+        p.top_p = top_p + c0;
+        p.out_tokens = out_tokens + c0;
+        p.stats = (s->flags & TES_FLAG_STATS) ? s->d_stats : nullptr;
+        p.ws = s->ws;
+        p.seed = seed;
+        p.offset = offset;
+        p.V = (u32)V;
+        p.nvec = nvec;
+        p.rows = rows;
+        p.row_base = (u32)c0;
+        p.seg_vec_full = s->seg_full;
+        p.s_ws = s->s_ws;
+        p.rowbytes = s->rowbytes;
+        p.chunk = s->chunk;
+        p.flags = s->flags;
+        if (p.stats &&
+            hipMemsetAsync(p.stats + (size_t)kStatWords * c0, 0, sizeof(u32) * kStatWords * rows,
+                           st) != hipSuccess)
+            return TES_ERR_LAUNCH;
+        // Enough blocks for every row to be top-p-only; the kernel knows the
+        // actual mix, and blocks beyond the last item return at once.
+        const u32 grid = rows * (s_full <= s->s_ws ? s_full : 1u);
+        if (vec4)
+            hipLaunchKernelGGL(tes_main_kernel<4>, dim3(grid), dim3(kBlock), 0, st, p);
+        else
+            hipLaunchKernelGGL(tes_main_kernel<1>, dim3(grid), dim3(kBlock), 0, st, p);
+        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        if (renorm_out) {
+            const Decision* dec =
+                reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
+            const u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
+            float* ro = renorm_out + (size_t)c0 * V;
+            if (vec4)
+                hipLaunchKernelGGL(tes_renorm_kernel<4>, dim3(gx, rows), dim3(256), 0, st,
+                                   p.probs, (u32)V, nvec, dec, ro);
+            else
+                hipLaunchKernelGGL(tes_renorm_kernel<1>, dim3(gx, rows), dim3(256), 0, st,
+                                   p.probs, (u32)V, nvec, dec, ro);
+            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        }
+    }
     return TES_OK;
 }
 
 extern "C" int sampler_destroy(tes_sampler* s) {
     if (!s) return TES_OK;
-    if (s->d_stats) {
+    {
         DeviceGuard g(s->device);
-        (void)hipFree(s->d_stats);
+        if (s->ws) (void)hipFree(s->ws);
+        if (s->d_stats) (void)hipFree(s->d_stats);
     }
     delete s;
     return TES_OK;
@@ -1004,8 +1854,8 @@ extern "C" int sampler_get_stats(tes_sampler* s, uint32_t* host_out, int B) {
     DeviceGuard g(s->device);
     if (!g.ok) return TES_ERR_LAUNCH;
     if (hipDeviceSynchronize() != hipSuccess) return TES_ERR_LAUNCH;
-    if (hipMemcpy(host_out, s->d_stats, sizeof(u32) * kStatWords * (size_t)B, hipMemcpyDeviceToHost) !=
-        hipSuccess)
+    if (hipMemcpy(host_out, s->d_stats, sizeof(u32) * kStatWords * (size_t)B,
+                  hipMemcpyDeviceToHost) != hipSuccess)
         return TES_ERR_LAUNCH;
     return TES_OK;
 }
