@@ -9,8 +9,9 @@ input so that the 256 MiB Infinity Cache cannot serve a repeated read.
 
 Prints one JSON line: rows/s for the whole job, the kernel's achieved HBM
 bandwidth against the 8 TB/s peak (algorithmic bytes = B*V*4 + 12*B per
-launch divided by the kernel's average duration, timed with HIP events on the
-launch stream), and the CPU oracle timed on the host cores as a baseline.
+launch divided by the kernel's average duration: one pair of HIP events on the
+launch stream brackets the timed region, which holds exactly one kernel launch
+per step), and the CPU oracle timed on the host cores as a baseline.
 """
 
 from __future__ import annotations
@@ -28,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "rows/s and achieved HBM GB/s (% of peak) at B=256, V=151,936 top-k+top-p"
 KERNEL_SRC = os.path.join(ROOT, "top_exact_sampling_amd", "csrc", "tes_sampler.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tes_sample_kernel_hetero_b256_v151936.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tes_main_kernel_hetero_b256_v151936_traffic.txt")
 
 
 def source_hash() -> str:
@@ -37,19 +38,26 @@ def source_hash() -> str:
 
 
 def traffic_from_profile():
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    when the kernel source changed since the counters were taken."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    t = {}
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            for ln in f:
+                if ":" in ln and not ln.startswith((" ", "#")):
+                    k, v = ln.split(":", 1)
+                    t[k.strip()] = v.strip()
+    except OSError:
         return None
     if t.get("kernel_source_sha256_16") != source_hash():
         return None
-    return t.get("traffic_bytes_per_launch")
+    try:
+        return int(t["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(w, min_wall=5.0, max_reps=20):
+def cpu_baseline(w, min_wall=10.0, max_reps=40):
     import oracle
 
     orc = oracle.load()
@@ -122,20 +130,20 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # Timed region: exactly `steps` calls, each bracketed by HIP events on the
-    # launch stream (the events also give the kernel's average duration).
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: exactly `steps` calls, back to back on the launch stream,
+    # bracketed by one pair of HIP events on that stream (each call is one
+    # kernel launch, so the events give its average duration).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
-    kern_ms = float(np.mean(per_launch_ms))
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     alg_bytes = B * V * 4 + 12 * B
