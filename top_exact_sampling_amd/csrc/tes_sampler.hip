@@ -218,6 +218,8 @@ struct Smem {
     Params p;                  // this launch's parameters (copied from the kernel arguments)
     alignas(16) unsigned char region[kRegionBytes];
     u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
+    u64 csum[2];               // summed mass and +inf count of a top-p-only row
+    u32 gn[kMaxSegWs];         // entries each segment of a top-p-only row gathered
     u64 cabove[kCoarseBins];   // mass of the coarse bins above each bin
     u64 finem[kDMax * 16];     // summed fine masses of the listed coarse bins
     int flist[kDMax];          // listed coarse bins
@@ -370,6 +372,33 @@ __device__ __forceinline__ u32 mbcnt64(u64 m) {
     return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
 }
 
+// The value lane (l ^ m) holds, for m = 1, 2, 4, 8, 16 or 32, without going
+// through LDS: DPP quad permutes and (half-)row mirrors compose to the xors
+// within 16 lanes (xor 4 = quad reverse then half-row mirror, xor 8 =
+// half-row mirror then row mirror), ds_swizzle in bit mode gives xor 16 and
+// permlane32_swap exchanges the two halves of the wave.
+__device__ __forceinline__ u32 lane_xor(u32 v, u32 m) {
+    const int x = (int)v;
+    switch (m) {
+        case 1: return (u32)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+        case 2: return (u32)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+        case 4:
+            return (u32)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false),
+                                                 0x141, 0xF, 0xF, false);
+        case 8:
+            return (u32)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
+                                                 0x140, 0xF, 0xF, false);
+        case 16: return (u32)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+        default: {
+            const auto pr = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            return threadIdx.x & 32u ? pr[0] : pr[1];
+        }
+    }
+}
+__device__ __forceinline__ u64 lane_xor64(u64 v, u32 m) {
+    return ((u64)lane_xor((u32)(v >> 32), m) << 32) | (u64)lane_xor((u32)v, m);
+}
+
 __device__ __forceinline__ u64 wave_sum(u64 v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -483,6 +512,28 @@ __device__ __forceinline__ void wave_append_n(u64* arr, u32 mask, const u64 (&c)
         if ((mask >> e) & 1u) {
             if (pos < cap) arr[pos] = c[e];
             ++pos;
+        }
+    }
+}
+
+// Adds word i of every segment's record to acc(i, value) for i < n; record q
+// holds u64 words at rec0 + q * stride.  Each thread issues four independent
+// loads before using them, so one round trip to L2 serves 2048 words whatever
+// the number of segments.
+template <typename Acc>
+__device__ __forceinline__ void sum_words(const u64* rec0, u32 stride, u32 nseg, u32 n, Acc acc) {
+    const u32 total = nseg * n;
+    for (u32 t0 = 0; t0 < total; t0 += 4 * kBlock) {
+        u64 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32 t = t0 + j * kBlock + threadIdx.x;
+            v[j] = t < total ? ld_g(rec0 + (size_t)(t / n) * stride + (t % n)) : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32 t = t0 + j * kBlock + threadIdx.x;
+            if (t < total) acc(t % n, v[j]);
         }
     }
 }
@@ -751,7 +802,12 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
 #pragma unroll
     for (int j = 0; j < E; ++j) v[j] = sbuf(s)[base + j];
     u32 half = 0;
+    // Fully unrolled: every stage's kind (in-thread, lane shuffle, LDS) and
+    // partner offsets are compile-time constants, and the shuffles of one
+    // stage are issued together.
+#pragma unroll
     for (u32 size = 2; size <= N; size <<= 1) {
+#pragma unroll
         for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
             if (stride < (u32)E) {
                 if (stride == 1) {
@@ -760,11 +816,11 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
                     if constexpr (E >= 4) cas_local<E, 2>(v, base, size);
                 }
             } else if (stride < 64u * E) {
-                const int lo = (int)(stride / E);
+                const u32 lo = stride / E;
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
                     const u32 i = base + j;
-                    const u64 o = __shfl_xor(v[j], lo, 64);
+                    const u64 o = lane_xor64(v[j], lo);
                     const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
                     v[j] = keep_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
                 }
@@ -1208,18 +1264,22 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u6
     const u32 pad = n <= kBlock ? kBlock : n <= 2 * kBlock ? 2 * kBlock : 4 * kBlock;
     for (u32 i = n + threadIdx.x; i < pad; i += kBlock) sbuf(s)[i] = 0;
     __syncthreads();
+    u64 ts = stat_phase(p, r, 14, tp);
     Outcome o;
     if (pad == kBlock) {
         u64 v[1];
         sort_desc<1>(s, v);
+        ts = stat_phase(p, r, 15, ts);
         o = resolve_sorted<1>(s, v, k, P, u);
     } else if (pad == 2 * kBlock) {
         u64 v[2];
         sort_desc<2>(s, v);
+        ts = stat_phase(p, r, 15, ts);
         o = resolve_sorted<2>(s, v, k, P, u);
     } else {
         u64 v[4];
         sort_desc<4>(s, v);
+        ts = stat_phase(p, r, 15, ts);
         o = resolve_sorted<4>(s, v, k, P, u);
     }
     stat_phase(p, r, 9, tp);
@@ -1305,6 +1365,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             }
         }
     }
+    // Accumulators of the exchanges (ordered by the barriers below).
+    for (int i = threadIdx.x; i < kCoarseBins; i += kBlock) s.coarse[i] = 0;
+    for (int i = threadIdx.x; i < kDMax * 16; i += kBlock) s.finem[i] = 0;
+    if (threadIdx.x < 2) s.csum[threadIdx.x] = 0;
     __syncthreads();
     M = block_sum(s, M);
     ninf = block_sum(s, ninf);
@@ -1328,19 +1392,16 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // Every segment sums the exchange and takes the same decisions.  The
     // counter was acquired, so the published words are read with ordinary
     // loads that can be in flight together.
-    u64 Mt = 0, nit = 0;
-    for (u32 q = 0; q < nseg; ++q) {
-        Mt += ld_g(&pub_c(p, r, q)->M);
-        nit += ld_g(&pub_c(p, r, q)->ninf);
-    }
-    Mt = uni(Mt);
-    nit = uni(nit);
-    for (int b = threadIdx.x; b < kCoarseBins; b += kBlock) {
-        u64 v = 0;
-        for (u32 q = 0; q < nseg; ++q) v += ld_g(&pub_c(p, r, q)->coarse[b]);
-        s.coarse[b] = v;
-    }
+    static_assert(sizeof(PubC) == 8 * (3 + kCoarseBins), "PubC is M, ninf, ng, coarse[]");
+    sum_words(reinterpret_cast<const u64*>(pub_c(p, r, 0)), sizeof(PubC) / 8, nseg, 3 + kCoarseBins,
+              [&](u32 i, u64 v) {
+                  if (i < 2) atomicAdd((unsigned long long*)&s.csum[i], (unsigned long long)v);
+                  else if (i >= 3)
+                      atomicAdd((unsigned long long*)&s.coarse[i - 3], (unsigned long long)v);
+              });
     __syncthreads();
+    const u64 Mt = uni(s.csum[0]);
+    const u64 nit = uni(s.csum[1]);
     {
         // cabove[b] = mass of the coarse bins above b (descending exclusive scan).
         const int b = kCoarseBins - 1 - (int)threadIdx.x;
@@ -1404,11 +1465,11 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     u32 ng = 0;
     u64* garea = gather_area(p, r, seg);
     if (!failed && kind == kNormal) {
-        for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
-            u64 v = 0;
-            for (u32 q = 0; q < nseg; ++q) v += ld_g(&pub_f(p, r, q)->fine[i / 16][i % 16]);
-            s.finem[i] = v;
-        }
+        static_assert(sizeof(PubF) == 8 * 16 * kDMax, "PubF is fine[kDMax][16]");
+        sum_words(reinterpret_cast<const u64*>(pub_f(p, r, 0)), sizeof(PubF) / 8, nseg,
+                  (u32)nlist * 16, [&](u32 i, u64 v) {
+                      atomicAdd((unsigned long long*)&s.finem[i], (unsigned long long)v);
+                  });
         __syncthreads();
         u64 a1 = 0, a2 = 0;
         fbT = fine_of_pos(s, nlist, T, above_f);
@@ -1455,8 +1516,12 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     const u64 P = fixed_p(ld_g(&p.top_p[r]));
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     u64 over = 0;
-    for (u32 q = threadIdx.x; q < nseg; q += kBlock) over += ld_g(&pub_c(p, r, q)->ng) > gcap;
-    over = block_sum(s, over);
+    for (u32 q = threadIdx.x; q < nseg; q += kBlock) {
+        const u64 n = ld_g(&pub_c(p, r, q)->ng);
+        s.gn[q] = (u32)(n < gcap ? n : gcap);
+        over += n > gcap;
+    }
+    over = block_sum(s, over);  // also orders s.gn
     if (threadIdx.x == 0) s.misc[3] = ld_dev(&rs->flags);
     __syncthreads();
     const bool fail = (uni(s.misc[3]) & kFlagFail) || over != 0 || failed;
@@ -1466,14 +1531,22 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     if (!fail && kind != kZeroRow) {
         if (threadIdx.x == 0) s.ctr[3] = 0;
         __syncthreads();
-        for (u32 q = 0; q < nseg; ++q) {
-            const u32 nq = (u32)ld_g(&pub_c(p, r, q)->ng);
-            const u64* gq = gather_area(p, r, q);
-            for (u32 i0 = 0; i0 < nq; i0 += kBlock) {
-                const u32 i = i0 + threadIdx.x;
-                const u64 c = i < nq ? ld_g(&gq[i]) : 0;
-                wave_append(sbuf(s), i < nq, c, &s.ctr[3], 0, kSelCap);
+        // Every segment's gather area at once, four loads per thread in flight.
+        const u64* g0 = gather_area(p, r, 0);
+        const u32 total = nseg * gcap;
+        for (u32 t0 = 0; t0 < total; t0 += 4 * kBlock) {
+            u64 c[4];
+            bool in[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32 t = t0 + j * kBlock + threadIdx.x;
+                const bool tin = t < total;
+                const u32 q = tin ? t / gcap : 0u, i = tin ? t - q * gcap : 0u;
+                in[j] = tin && i < s.gn[q];
+                c[j] = in[j] ? ld_g(&g0[(size_t)q * kGSeg + i]) : 0;
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wave_append(sbuf(s), in[j], c[j], &s.ctr[3], 0, kSelCap);
         }
         __syncthreads();
         nall = uni(s.ctr[3]);
