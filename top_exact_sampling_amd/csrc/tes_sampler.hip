@@ -1143,11 +1143,13 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u6
 //   anything else happens, and tkey becomes the lower edge of the bin that
 //   holds the sample's j-th best, j = ceil(1.5 k n / V) + 12 for n sampled
 //   entries (j = k when the sample is the whole row).
-//   Then the row is streamed from its start with no barriers: each lane with
-//   passing entries takes slots with one LDS atomic; slots beyond the buffer
-//   are counted but not written.
-// The buffer then holds exactly the entries at or above tkey.  When their
-// number is between k and the capacity, it holds the row's best k; otherwise
+//   Then the row is streamed from its start with no barriers and no atomics:
+//   each wave appends to its own region of kSlabCap / 8 entries, at its
+//   running count (a scalar) plus the lane's rank among the wave's passing
+//   lanes (mbcnt of the element's ballot).  Entries beyond a region are
+//   counted but not written.  Afterwards the regions are packed together.
+// The buffer then holds exactly the entries at or above tkey.  When no region
+// overflowed and there are at least k, it holds the row's best k; otherwise
 // the row is resolved by whole-row passes.
 template <int VEC>
 __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
@@ -1163,7 +1165,6 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
     const u32 last = nvec - 1;
     u32* hist = reinterpret_cast<u32*>(s.region);  // sample counts per fine bin
     for (int b = threadIdx.x; b < kFineBins; b += kBlock) hist[b] = 0;
-    if (threadIdx.x == 0) s.ctr[0] = 0;
     __syncthreads();
     VT pf[kStreamDepth];
 #pragma unroll
@@ -1199,25 +1200,22 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
     __syncthreads();  // the histogram is dead; the buffer takes its place
     const u32 span = kInfKey - tkey;
     u64 tq = stat_phase(p, r, 11, tp);
-    // Appends this lane's passing entries of one vector (slots from one LDS
-    // atomic per lane).
+    constexpr u32 kRegion = kSlabCap / kWaves;
+    const u32 wave = uni(wave_id());
+    u64* const reg = sbuf(s) + wave * kRegion;
+    u32 wfill = 0;  // entries this wave has appended (wave-uniform)
+    // Appends this lane's passing entries of one vector.
     auto append = [&](const VT& x, u32 iv) {
-        u32 mask = 0;
+        const bool valid = iv < nvec;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-            mask |= (iv < nvec && (tkey == 0 || b - tkey <= span)) ? 1u << e : 0u;
-        }
-        if (mask) {
-            u32 pos = atomicAdd(&s.ctr[0], (u32)__popc(mask));
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                if ((mask >> e) & 1u) {
-                    if (pos < kSlabCap)
-                        sbuf(s)[pos] = composite(sanitize(__float_as_uint(VecT<VEC>::get(x, e))),
-                                                 iv * VEC + e);
-                    ++pos;
-                }
+            const bool pass = valid && (tkey == 0 || b - tkey <= span);
+            const u64 m = __ballot(pass);
+            if (m) {
+                const u32 pos = wfill + mbcnt64(m);
+                if (pass && pos < kRegion) reg[pos] = composite(sanitize(b), iv * VEC + e);
+                wfill += (u32)__popcll(m);
             }
         }
     };
@@ -1232,14 +1230,40 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // Pack the regions: wave w's entries move to the offset of the waves below.
+    if (lane_id() == 0) s.gn[wave] = wfill;
     __syncthreads();
-    u32 fill = uni(s.ctr[0]);
+    u32 fill = 0, before = 0;
+    bool over = false;
+#pragma unroll
+    for (u32 w = 0; w < (u32)kWaves; ++w) {
+        const u32 cw = uni(s.gn[w]);
+        over |= cw > kRegion;
+        fill += cw;
+        before += w < wave ? cw : 0u;
+    }
+    constexpr int kPerLane = kRegion / 64;
+    u64 mine[kPerLane];
+    const u32 nmine = wfill < kRegion ? wfill : kRegion;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const u32 i = lane_id() + 64u * j;
+        mine[j] = i < nmine ? reg[i] : 0ull;
+    }
+    __syncthreads();
+    if (!over) {
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const u32 i = lane_id() + 64u * j;
+            if (i < nmine) sbuf(s)[before + i] = mine[j];
+        }
+    }
     __syncthreads();
     tq = stat_phase(p, r, 13, tq);
     stat_phase(p, r, 8, tp);
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
-    if (fill >= k && fill <= kSlabCap) {
+    if (!over && fill >= k) {
         slab_finish<VEC>(s, r, fill, k, P, u);
     } else {
         const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
