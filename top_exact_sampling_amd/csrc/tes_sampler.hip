@@ -219,6 +219,8 @@ struct Smem {
     alignas(16) unsigned char region[kRegionBytes];
     u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
     u64 csum[2];               // summed mass and +inf count of a top-p-only row
+    u64 loc_above[4];          // results of coarse_locate / fine_locate
+    int loc_bin[4];
     u32 gn[kMaxSegWs];         // entries each segment of a top-p-only row gathered
     u64 cabove[kCoarseBins];   // mass of the coarse bins above each bin
     u64 finem[kDMax * 16];     // summed fine masses of the listed coarse bins
@@ -746,31 +748,52 @@ __device__ __forceinline__ T ld_stream(const T* p) {
 }
 
 // Collects the composites of this workgroup's register-resident entries whose
-// key satisfies pred: the first `cap` (<= kSelCap) go to sbuf(s) through
-// per-wave appends and are then copied to out[0, cap) with device-coherent
-// stores.  Returns how many there are, which may exceed cap.
+// key satisfies pred and writes the first `cap` (<= kSelCap) of them to
+// out[0, cap) with device-coherent stores.  Each wave first appends to its
+// own LDS region of kSelCap / 8 entries (scalar running count plus the lane's
+// rank in the element's ballot, no atomics); the regions are then packed.
+// Returns how many there are, which may exceed cap (or be reported as cap + 1
+// when a wave's region overflowed).
 template <int VEC, int NS, typename Pred>
 __device__ __forceinline__ u32 gather_regs(Smem& s, const typename VecT<VEC>::T (&x)[NS], u32 v0,
                                            u32 v1, Pred pred, u64* out, u32 cap) {
-    if (threadIdx.x == 0) s.ctr[3] = 0;
-    __syncthreads();
+    constexpr u32 kReg = kSelCap / kWaves;
+    const u32 wave = uni(wave_id());
+    u64* const reg = sbuf(s) + wave * kReg;
+    u32 wfill = 0;
 #pragma unroll
     for (int d = 0; d < NS; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
-        u64 c[VEC];
-        u32 mask = 0;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
-            c[e] = composite(key, i * VEC + e);
-            mask |= (i < v1 && pred(key)) ? 1u << e : 0u;
+            const bool take = i < v1 && pred(key);
+            const u64 m = __ballot(take);
+            if (m) {
+                const u32 pos = wfill + mbcnt64(m);
+                if (take && pos < kReg) reg[pos] = composite(key, i * VEC + e);
+                wfill += (u32)__popcll(m);
+            }
         }
-        wave_append_n<VEC>(sbuf(s), mask, c, &s.ctr[3], 0, cap);
     }
+    if (lane_id() == 0) s.gn[wave] = wfill;
     __syncthreads();
-    const u32 total = uni(s.ctr[3]);
-    const u32 m = total < cap ? total : cap;
-    for (u32 j = threadIdx.x; j < m; j += kBlock) st_dev(&out[j], sbuf(s)[j]);
+    u32 total = 0, before = 0;
+    bool over = false;
+#pragma unroll
+    for (u32 w = 0; w < (u32)kWaves; ++w) {
+        const u32 cw = uni(s.gn[w]);
+        over |= cw > kReg;
+        total += cw;
+        before += w < wave ? cw : 0u;
+    }
+    if (over) total = total > cap ? total : cap + 1;  // reported as too many
+    // This wave's entries go to out[before, before + n) while below cap.
+    const u32 n = wfill < kReg ? wfill : kReg;
+    if (!over) {
+        for (u32 j = lane_id(); j < n; j += 64)
+            if (before + j < cap) st_dev(&out[before + j], reg[j]);
+    }
     __syncthreads();
     return total;
 }
@@ -1313,36 +1336,60 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u6
 // ---------------------------------------------------------------------------
 // Top-p-only rows (k >= V)
 // ---------------------------------------------------------------------------
-// Coarse bin holding descending mass position P (1 <= P <= total), from the
-// summed coarse histogram and its descending exclusive prefix.
-__device__ __forceinline__ int coarse_of_pos(const Smem& s, u64 P) {
-    int lo = 0, hi = kCoarseBins - 1;  // largest bin whose cumulative mass reaches P
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s.cabove[mid] + s.coarse[mid] >= P) lo = mid; else hi = mid - 1;
+// Coarse bins holding descending mass positions P[n] (1 <= P[n] <= total)
+// of the summed coarse histogram and its descending exclusive prefix: bin b
+// holds P when cabove[b] < P <= cabove[b] + coarse[b], which is true of
+// exactly one bin.  One thread per bin; the results are workgroup-uniform.
+template <int N>
+__device__ __forceinline__ void coarse_locate(Smem& s, const u64 (&P)[N], int (&bin)[N]) {
+    if (threadIdx.x < (u32)N) s.loc_bin[threadIdx.x] = 0;
+    __syncthreads();
+    const int b = (int)threadIdx.x;
+    if (b < kCoarseBins) {
+        const u64 lo = s.cabove[b], hi = lo + s.coarse[b];
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            if (lo < P[n] && P[n] <= hi) s.loc_bin[n] = b;
     }
-    return lo;
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < N; ++n) bin[n] = (int)uni((u32)s.loc_bin[n]);
+    __syncthreads();
 }
 
-// Fine bin holding descending mass position P, looked up in the exchanged
-// fine bins of the listed coarse bins; -1 if its coarse bin is not listed.
-// `above` receives the mass of all higher fine bins.
-__device__ __forceinline__ int fine_of_pos(const Smem& s, int nlist, u64 P, u64& above) {
-    const int cb = coarse_of_pos(s, P);
-    int j = -1;
-    for (int q = 0; q < nlist; ++q)
-        if (s.flist[q] == cb) j = q;
-    if (j < 0) return -1;
-    u64 acc = s.cabove[cb];
-    for (int f = 15; f >= 0; --f) {
-        const u64 w = s.finem[j * 16 + f];
-        if (acc < P && P <= acc + w) {
-            above = acc;
-            return cb * 16 + f;
-        }
-        acc += w;
+// Fine bins holding descending mass positions P[n], looked up among the
+// exchanged fine bins of the listed coarse bins (bin -1 when the position's
+// coarse bin is not listed); above[n] receives the mass of all higher fine
+// bins.  One thread per listed fine bin.
+template <int N>
+__device__ __forceinline__ void fine_locate(Smem& s, int nlist, const u64 (&P)[N], int (&bin)[N],
+                                            u64 (&above)[N]) {
+    if (threadIdx.x < (u32)N) {
+        s.loc_bin[threadIdx.x] = -1;
+        s.loc_above[threadIdx.x] = 0;
     }
-    return -1;
+    __syncthreads();
+    for (int i = (int)threadIdx.x; i < nlist * 16; i += kBlock) {
+        const int j = i >> 4, f = i & 15;
+        const int cb = s.flist[j];
+        u64 a = s.cabove[cb];
+        for (int g = 15; g > f; --g) a += s.finem[j * 16 + g];
+        const u64 w = s.finem[i];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            if (a < P[n] && P[n] <= a + w) {
+                s.loc_bin[n] = cb * 16 + f;
+                s.loc_above[n] = a;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        bin[n] = (int)uni((u32)s.loc_bin[n]);
+        above[n] = uni(s.loc_above[n]);
+    }
+    __syncthreads();
 }
 
 template <int VEC>
@@ -1364,15 +1411,20 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     stat_start(p, r, nseg);
     u64 tp = p.stats ? wall_clock64() : 0;
 
+    // The histogram is cleared first so that each vector is counted as soon
+    // as its load returns (loads are issued, and waited for, in order).
+    for (int i = threadIdx.x; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
+    __syncthreads();
     VT x[kSlotsFull];
 #pragma unroll
     for (int d = 0; d < kSlotsFull; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
-        if (i < v1) x[d] = ld_stream(&rv[i]);
+        x[d] = ld_stream(&rv[i < v1 ? i : v1 - 1]);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    for (int i = threadIdx.x; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
-    __syncthreads();
-    u64 M = 0, ninf = 0;
+    // The segment's mass is the sum of the histogram, taken afterwards; +inf
+    // entries are counted only by waves that hold one.
+    u64 ninf = 0;
 #pragma unroll
     for (int d = 0; d < kSlotsFull; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
@@ -1380,12 +1432,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
-                if (key >= kMinMassKey) {
-                    const u64 q = key_mass(key);
-                    atomicAdd((unsigned long long*)&shfine(s)[fine_bin(key)], (unsigned long long)q);
-                    M += q;
-                    ninf += key == kInfKey;
-                }
+                if (key >= kMinMassKey)
+                    atomicAdd((unsigned long long*)&shfine(s)[fine_bin(key)],
+                              (unsigned long long)key_mass(key));
+                if (__ballot(key == kInfKey)) ninf += key == kInfKey;
             }
         }
     }
@@ -1394,6 +1444,8 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     for (int i = threadIdx.x; i < kDMax * 16; i += kBlock) s.finem[i] = 0;
     if (threadIdx.x < 2) s.csum[threadIdx.x] = 0;
     __syncthreads();
+    u64 M = 0;
+    for (int i = threadIdx.x; i < kFineBins; i += kBlock) M += shfine(s)[i];
     M = block_sum(s, M);
     ninf = block_sum(s, ninf);
     tp = stat_phase(p, r, 8, tp);
@@ -1441,10 +1493,14 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     int nlist = 0;
     bool decidable = ok;
     if (ok && kind == kNormal) {
-        const int cbT = coarse_of_pos(s, T);
-        const u64 U = s.cabove[cbT] + s.coarse[cbT];
+        int c1[1];
+        coarse_locate(s, {T}, c1);
+        const int cbT = c1[0];
+        const u64 U = uni(s.cabove[cbT]) + uni(s.coarse[cbT]);
         const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
-        const int chi = coarse_of_pos(s, t_lo + 1), clo = coarse_of_pos(s, t_hi + 1);
+        int c2[2];
+        coarse_locate(s, {t_lo + 1, t_hi + 1}, c2);
+        const int chi = c2[0], clo = c2[1];
         // Listed coarse bins: the boundary bin, then the draw range.
         const int cnt = 1 + (chi - clo + 1) - ((cbT >= clo && cbT <= chi) ? 1 : 0);
         if (cnt > dmax) {
@@ -1495,12 +1551,19 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
                       atomicAdd((unsigned long long*)&s.finem[i], (unsigned long long)v);
                   });
         __syncthreads();
-        u64 a1 = 0, a2 = 0;
-        fbT = fine_of_pos(s, nlist, T, above_f);
-        const u64 U = fbT >= 0 ? above_f + s.finem[fbT - s.flist[0] * 16] : 0;
+        const u64 tg = stat_phase(p, r, 14, tp);
+        int f1[1];
+        u64 a1[1];
+        fine_locate(s, nlist, {T}, f1, a1);
+        fbT = f1[0];
+        above_f = a1[0];
+        const u64 U = fbT >= 0 ? above_f + uni(s.finem[fbT - s.flist[0] * 16]) : 0;
         const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
-        const int fdhi = fine_of_pos(s, nlist, t_lo + 1, a1);
-        const int fdlo = fine_of_pos(s, nlist, t_hi + 1, a2);
+        int f2[2];
+        u64 a2[2];
+        fine_locate(s, nlist, {t_lo + 1, t_hi + 1}, f2, a2);
+        const int fdhi = f2[0], fdlo = f2[1];
+        stat_phase(p, r, 15, tg);
         if (fbT < 0 || fdhi < 0 || fdlo < 0) {
             // Cannot happen for consistent exchanges; decide by the slow path.
             stat_why(p, r, 8u);
@@ -1598,8 +1661,11 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         const Sel sb = select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
         const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
         const u64 t = __umul64hi(u, M_p);
-        u64 above_d = 0;
-        const int fd = fine_of_pos(s, nlist, t + 1, above_d);
+        int fdv[1];
+        u64 adv[1];
+        fine_locate(s, nlist, {t + 1}, fdv, adv);
+        const int fd = fdv[0];
+        const u64 above_d = adv[0];
         const Sel sd = select_buf(s, nall, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
         o.kind = kNormal;
         o.c_keep = sb.c;
