@@ -208,11 +208,12 @@ __device__ __forceinline__ void or_dev(T* a, T v) {
 // LDS regions are shared by phases that never overlap in time:
 //   selects     sbuf = entries [0, 16 KiB) (kSelCap), shcnt [16, 24 KiB), shmass [24, 40 KiB)
 //   sorting     [0, 32 KiB) as u64[4096] (two halves of up to 2048 entries)
-//   top-k rows  candidate buffer [0, 32 KiB) (kSlabCap), packed 16-bit digit counts [32, 36 KiB)
+//   top-k rows  candidate buffer [0, 32 KiB) (kSlabCap), digit counts [32, 40 KiB)
 //   top-p rows  fine mass histogram [0, 32.8 KiB)
+//   bin tables  shtab [32, 48 KiB): 2048 packed (count, mass) words of the binned selects
 constexpr u32 kSelCap = 2048;   // entries a select or a sort handles
 constexpr u32 kSlabCap = 4096;  // top-k candidate buffer
-constexpr int kRegionBytes = 40 * 1024;
+constexpr int kRegionBytes = 48 * 1024;
 
 struct Smem {
     Params p;                  // this launch's parameters (copied from the kernel arguments)
@@ -243,6 +244,7 @@ __device__ __forceinline__ u32* shcnt(Smem& s) { return reinterpret_cast<u32*>(s
 __device__ __forceinline__ u64* shmass(Smem& s) { return reinterpret_cast<u64*>(s.region + 24576); }
 __device__ __forceinline__ u64* shfine(Smem& s) { return reinterpret_cast<u64*>(s.region); }
 __device__ __forceinline__ u32* shdig(Smem& s) { return reinterpret_cast<u32*>(s.region + 32768); }
+__device__ __forceinline__ u64* shtab(Smem& s) { return reinterpret_cast<u64*>(s.region + 32768); }
 
 struct Sel {
     u64 c;      // selected composite
@@ -403,24 +405,51 @@ __device__ __forceinline__ u64 lane_xor64(u64 v, u32 m) {
 
 __device__ __forceinline__ u64 wave_sum(u64 v) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    for (u32 o = 32; o >= 1; o >>= 1) v += lane_xor64(v, o);
     return v;
 }
 __device__ __forceinline__ u64 wave_min(u64 v) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        u64 w = __shfl_xor(v, o, 64);
+    for (u32 o = 32; o >= 1; o >>= 1) {
+        const u64 w = lane_xor64(v, o);
         v = w < v ? w : v;
     }
     return v;
 }
 __device__ __forceinline__ u64 wave_max(u64 v) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        u64 w = __shfl_xor(v, o, 64);
+    for (u32 o = 32; o >= 1; o >>= 1) {
+        const u64 w = lane_xor64(v, o);
         v = w > v ? w : v;
     }
     return v;
+}
+
+__device__ __forceinline__ u64 read_lane(u64 v, u32 lane) {
+    return ((u64)(u32)__builtin_amdgcn_readlane((int)(u32)(v >> 32), (int)lane) << 32) |
+           (u64)(u32)__builtin_amdgcn_readlane((int)(u32)v, (int)lane);
+}
+
+// The value of the lane CTRL (a DPP row shift) names, 0 where that lane lies
+// outside the row of 16.
+template <int CTRL>
+__device__ __forceinline__ u64 dpp_shift64(u64 v) {
+    const u32 lo = (u32)__builtin_amdgcn_update_dpp(0, (int)(u32)v, CTRL, 0xF, 0xF, true);
+    const u32 hi = (u32)__builtin_amdgcn_update_dpp(0, (int)(u32)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((u64)hi << 32) | lo;
+}
+
+// Inclusive prefix sum across the wave (all lanes active): shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then the totals of the rows below.
+__device__ __forceinline__ u64 wave_incl_scan(u64 x) {
+    x += dpp_shift64<0x111>(x);  // row_shr:1
+    x += dpp_shift64<0x112>(x);  // row_shr:2
+    x += dpp_shift64<0x114>(x);  // row_shr:4
+    x += dpp_shift64<0x118>(x);  // row_shr:8
+    const u64 r0 = read_lane(x, 15), r1 = read_lane(x, 31), r2 = read_lane(x, 47);
+    const u32 lane = lane_id();
+    const u64 off = lane < 16u ? 0ull : lane < 32u ? r0 : lane < 48u ? r0 + r1 : r0 + r1 + r2;
+    return x + off;
 }
 
 __device__ u64 block_sum(Smem& s, u64 v) {
@@ -455,13 +484,8 @@ __device__ u64 block_max(Smem& s, u64 v) {
 }
 
 __device__ __forceinline__ u64 block_excl_scan(Smem& s, u64 v) {
-    u64 x = v;
+    const u64 x = wave_incl_scan(v);
     const u32 lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        u64 y = __shfl_up(x, o, 64);
-        if (lane >= (u32)o) x += y;
-    }
     if (lane == 63) s.wpart[wave_id()] = x;
     __syncthreads();
     u64 pre = 0;
@@ -748,7 +772,9 @@ __device__ __forceinline__ T ld_stream(const T* p) {
 }
 
 // Collects the composites of this workgroup's register-resident entries whose
-// key satisfies pred and writes the first `cap` (<= kSelCap) of them to
+// raw bits satisfy pred (which must accept only bits <= those of +inf, i.e.
+// keys that sanitising leaves unchanged) and writes the first `cap`
+// (<= kSelCap) of them to
 // out[0, cap) with device-coherent stores.  Each wave first appends to its
 // own LDS region of kSelCap / 8 entries (scalar running count plus the lane's
 // rank in the element's ballot, no atomics); the regions are then packed.
@@ -766,7 +792,7 @@ __device__ __forceinline__ u32 gather_regs(Smem& s, const typename VecT<VEC>::T 
         const u32 i = v0 + d * kBlock + threadIdx.x;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
+            const u32 key = __float_as_uint(VecT<VEC>::get(x[d], e));
             const bool take = i < v1 && pred(key);
             const u64 m = __ballot(take);
             if (m) {
@@ -939,6 +965,251 @@ __device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u3
     o.token = comp_index(uni(s.bc[2]));
     __syncthreads();
     return o;
+}
+
+// ---------------------------------------------------------------------------
+// Binned selects over a small LDS entry set
+// ---------------------------------------------------------------------------
+// The entries are counted into 2048 bins that ascend with the composite, a
+// descending exclusive scan of the table gives every bin's count and mass
+// above it, and the entries are scattered bin by bin.  A position in the
+// descending order (by count) or a cumulative mass then names its bin from
+// the table alone, and only that bin, at most 64 entries, is sorted, by one
+// wave with lane exchanges.  This replaces full sorts and multi-level radix
+// selects, whose cost is dominated by workgroup barriers and by the four
+// cycles every wave64 ALU instruction occupies a SIMD.
+constexpr int kTabBins = 2048;
+constexpr int kTabCountShift = 45;  // a bin holds < 2^19 entries of mass <= 2^32 each
+constexpr u64 kTabMassMask = (1ull << kTabCountShift) - 1;
+
+// Lanes [0, n) hold entries and lanes above hold zeros (n wave-uniform);
+// returns them sorted descending across the wave, by a bitonic network over
+// the smallest power of two >= n lanes.
+__device__ __forceinline__ u64 wave_sort_desc(u64 v, u32 n) {
+    const u32 lane = lane_id();
+#pragma unroll
+    for (u32 size = 2; size <= 64; size <<= 1) {
+        if ((size >> 1) >= n) break;
+#pragma unroll
+        for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
+            const u64 o = lane_xor64(v, stride);
+            const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+            v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+        }
+    }
+    return v;
+}
+
+// Bins the entries c[j] with dig[j] >= 0 (J per thread) and scatters them to
+// out[] in descending bin order.  Afterwards shtab(s)[b] holds the packed
+// count << 45 | mass of the entries in bins above b, the entries of bin b sit,
+// in no particular order, at out[count_above(b), count_above(b) + count(b)),
+// and the packed total is returned.
+template <int J>
+__device__ __forceinline__ u64 bin_scatter(Smem& s, const u64 (&c)[J], const int (&dig)[J],
+                                           u64* out) {
+    u64* tab = shtab(s);
+    for (int b = threadIdx.x; b < kTabBins; b += kBlock) tab[b] = 0;
+    __syncthreads();
+    u32 slot[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        slot[j] = 0;
+        if (dig[j] >= 0) {
+            const u64 inc = (1ull << kTabCountShift) | key_mass(comp_key(c[j]));
+            slot[j] = (u32)(atomicAdd((unsigned long long*)&tab[dig[j]], (unsigned long long)inc) >>
+                            kTabCountShift);
+        }
+    }
+    __syncthreads();
+    // Thread t owns bins 2047 - 4t down to 2044 - 4t.
+    static_assert(kTabBins == 4 * kBlock, "four bins per thread");
+    const int b0 = kTabBins - 1 - 4 * (int)threadIdx.x;
+    u64 w[4], loc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = tab[b0 - i];
+        loc += w[i];
+    }
+    u64 ex = block_excl_scan(s, loc);  // its barriers order the reads above before the writes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tab[b0 - i] = ex;
+        ex += w[i];
+    }
+    if (threadIdx.x == kBlock - 1) s.bc[0] = ex;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (dig[j] >= 0) out[(u32)(tab[dig[j]] >> kTabCountShift) + slot[j]] = c[j];
+    __syncthreads();
+    return uni(s.bc[0]);
+}
+
+// Wave-level view of a scattered table: locating bins by cumulative mass and
+// sorting one bin.  Every member is wave-uniform except the per-lane v / inc.
+struct BinView {
+    const u64* tab;
+    const u64* srt;
+    u64 total;
+    int cur = -1;   // bin currently held sorted in v
+    u32 st = 0;     // its first position
+    u64 v = 0;      // its entries, descending, one per lane (zero past the end)
+    u64 inc = 0;    // their inclusive prefix masses within the bin
+
+    __device__ u32 cnt_above(int b) const { return (u32)(tab[b] >> kTabCountShift); }
+    __device__ u64 mass_above(int b) const { return tab[b] & kTabMassMask; }
+    __device__ u32 end_of(int b) const {
+        return b > 0 ? cnt_above(b - 1) : (u32)(total >> kTabCountShift);
+    }
+    // The bin b with mass_above(b) < W <= mass_above(b) + mass(b), for
+    // 1 <= W <= total mass: the last position (descending bins) whose mass
+    // above is below W, found 32 bins at a time.
+    __device__ int find_mass(u64 W) const {
+        const u32 lane = lane_id();
+        const u64 a = mass_above(kTabBins - 1 - 32 * (int)lane);
+        const u64 m1 = __ballot(a < W);
+        const int l1 = 63 - __builtin_clzll(m1);
+        const int q = 32 * l1 + (int)(lane & 31u);
+        const u64 a2 = mass_above(kTabBins - 1 - q);
+        const u64 m2 = __ballot(lane < 32u && a2 < W);
+        return kTabBins - 1 - (32 * l1 + (63 - __builtin_clzll(m2)));
+    }
+    // Loads and sorts bin b; false when it holds more than 64 entries.
+    __device__ bool load(int b) {
+        if (b == cur) return true;
+        st = cnt_above(b);
+        const u32 n = end_of(b) - st;
+        if (n > 64u) return false;
+        const u32 lane = lane_id();
+        const u64 x = lane < n ? srt[st + lane] : 0ull;
+        v = wave_sort_desc(x, n);
+        inc = wave_incl_scan(key_mass(comp_key(v)));
+        cur = b;
+        return true;
+    }
+};
+
+// Top-k finish from the candidate buffer sbuf(s)[0, n), k <= n <= kSlabCap,
+// which holds every entry of the row with key >= tkey (tkey > 0, a multiple of
+// 2^16).  Bins are 1/128-octave key ranges counted from tkey (bin 2047 takes
+// every key 16 octaves or more above it).  The support's k-th entry, the top-p
+// boundary and the drawn entry are each located in the table and resolved by
+// sorting their bin.  Returns false, with the buffer holding the same entries
+// in another order, when a bin it needs holds more than 64 entries or the
+// support holds +inf entries or has no mass; the caller then sorts.
+__device__ __noinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+                                         Outcome& o) {
+    constexpr int J = kSlabCap / kBlock;
+    const u32 tbin = tkey >> kFineShift;
+    u64 c[J];
+    int dig[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const u32 i = threadIdx.x + (u32)j * kBlock;
+        c[j] = i < n ? sbuf(s)[i] : 0ull;
+        const u32 d = (comp_key(c[j]) >> kFineShift) - tbin;
+        dig[j] = i < n ? (int)(d < (u32)kTabBins ? d : (u32)kTabBins - 1) : -1;
+    }
+    __syncthreads();  // the scatter overwrites the buffer
+    const u64 total = bin_scatter<J>(s, c, dig, sbuf(s));
+    if (wave_id() == 0) {
+        BinView bv{shtab(s), sbuf(s), total};
+        // +inf entries, the largest keys, can only sit in the top bin.
+        const u32 ntop = bv.end_of(kTabBins - 1);
+        const u32 lane = lane_id();
+        const bool has_inf = ntop > 64u || __ballot(lane < ntop && comp_key(sbuf(s)[lane]) == kInfKey);
+        const u32 kkey = comp_key(sbuf(s)[k - 1]);
+        const u32 kd = (kkey >> kFineShift) - tbin;
+        const int bk = (int)(kd < (u32)kTabBins ? kd : (u32)kTabBins - 1);
+        bool ok = !has_inf && bv.load(bk);
+        u64 Mk = 0;
+        if (ok) Mk = bv.mass_above(bk) + read_lane(bv.inc, k - 1 - bv.st);
+        ok = ok && Mk > 0;
+        u64 cT = 0, Mp = 0, cd = 0;
+        if (ok) {
+            const u64 T = topp_threshold(P, Mk);
+            const int bT = bv.find_mass(T);
+            ok = bv.load(bT);
+            const u64 base = ok ? bv.mass_above(bT) : 0;
+            const u64 mT = ok ? __ballot(base + bv.inc >= T) : 0;
+            ok = mT != 0;  // always set for a consistent table
+            if (ok) {
+                const u32 L = (u32)__builtin_ctzll(mT);
+                cT = read_lane(bv.v, L);
+                Mp = base + read_lane(bv.inc, L);
+                const u64 t = __umul64hi(u, Mp);
+                const int bd = bv.find_mass(t + 1);
+                ok = bv.load(bd);
+                const u64 base2 = ok ? bv.mass_above(bd) : 0;
+                const u64 md = ok ? __ballot(base2 + bv.inc > t) : 0;
+                ok = md != 0;
+                if (ok) cd = read_lane(bv.v, (u32)__builtin_ctzll(md));
+            }
+        }
+        if (lane_id() == 0) {
+            s.misc[5] = ok ? 1u : 0u;
+            s.bc[1] = cT;
+            s.bc[2] = Mp;
+            s.bc[3] = cd;
+        }
+    }
+    __syncthreads();
+    const bool ok = uni(s.misc[5]) != 0;
+    o = Outcome{};
+    o.kind = kNormal;
+    o.c_keep = uni(s.bc[1]);
+    o.M_p = uni(s.bc[2]);
+    o.token = comp_index(uni(s.bc[3]));
+    __syncthreads();
+    return ok;
+}
+
+// Mass select inside fine bin f (< kFineBins - 1) over sbuf(s)[0, n), n <=
+// kSelCap: the entry at which the bin's descending cumulative mass first
+// reaches W (1 <= W <= the bin's mass), with the bin's mass above it.  Bins
+// are 32 consecutive keys (key bits 15..5); when the bin holding W has more
+// than 64 entries the radix select decides.
+__device__ __noinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
+    constexpr int J = kSelCap / kBlock;
+    const u32 fkey = (u32)(f + (int)kFineBase);
+    u64 c[J];
+    int dig[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const u32 i = threadIdx.x + (u32)j * kBlock;
+        c[j] = i < n ? sbuf(s)[i] : 0ull;
+        const u32 key = comp_key(c[j]);
+        dig[j] = (i < n && (key >> kFineShift) == fkey) ? (int)((key >> 5) & (kTabBins - 1)) : -1;
+    }
+    u64* srt = sbuf(s) + kSelCap;
+    const u64 total = bin_scatter<J>(s, c, dig, srt);
+    if (wave_id() == 0) {
+        BinView bv{shtab(s), srt, total};
+        const int b = bv.find_mass(W);
+        bool ok = bv.load(b);
+        const u64 base = ok ? bv.mass_above(b) : 0;
+        const u64 m = ok ? __ballot(base + bv.inc >= W) : 0;
+        ok = m != 0;  // always set for a consistent table
+        if (ok && lane_id() == 0) s.misc[5] = 1u;
+        if (ok) {
+            const u32 L = (u32)__builtin_ctzll(m);
+            const u64 cw = read_lane(bv.v, L);
+            const u64 above = base + read_lane(bv.inc, L) - key_mass(comp_key(cw));
+            if (lane_id() == 0) {
+                s.bc[1] = cw;
+                s.bc[2] = above;
+            }
+        } else if (lane_id() == 0) {
+            s.misc[5] = 0u;
+        }
+    }
+    __syncthreads();
+    const bool ok = uni(s.misc[5]) != 0;
+    const Sel r{uni(s.bc[1]), uni(s.bc[2])};
+    __syncthreads();
+    if (ok) return r;
+    return select_buf(s, n, W, true, fine_lo(f), fine_hi(f));
 }
 
 // Calls f(key, idx, valid) for every element of a row, VEC per thread per
@@ -1154,7 +1425,7 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
 // Top-k rows (2 <= k <= 1024)
 // ---------------------------------------------------------------------------
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u64 u);
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u);
 
 // Streams the row once and keeps, in the LDS buffer, every entry whose key is
 // at or above a threshold key tkey, chosen so that about 1.5 k (and at least
@@ -1287,7 +1558,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     if (!over && fill >= k) {
-        slab_finish<VEC>(s, r, fill, k, P, u);
+        slab_finish<VEC>(s, r, fill, k, tkey, P, u);
     } else {
         const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
                                            kSelCap);
@@ -1295,15 +1566,25 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
     }
 }
 
-// The buffer sbuf(s)[0, n), k <= n <= kSlabCap, holds the row's best k.  Cut
-// it to exactly those when it holds more than a sort takes (always under
-// TES_FLAG_TINY_BUFFER), sort descending (padded with zeros, which sort last)
-// and finish on the first k positions.
+// The buffer sbuf(s)[0, n), k <= n <= kSlabCap, holds the row's best k (and
+// every entry with key >= tkey).  The binned finish decides most rows; the
+// others (and every row under TES_FLAG_TINY_BUFFER) cut the buffer to exactly
+// the best k when it holds more than a sort takes, sort it descending (padded
+// with zeros, which sort last) and finish on the first k positions.
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u64 P, u64 u) {
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
+    if (!(p.flags & TES_FLAG_TINY_BUFFER) && tkey > 0) {
+        Outcome ob;
+        if (binned_topk(s, n, k, tkey, P, u, ob)) {
+            stat_phase(p, r, 9, tp);
+            finish_row(s, p, r, ob, kPathSlab, gathered);
+            return;
+        }
+        stat_why(p, r, 64u);
+    }
     if (n > kSelCap || ((p.flags & TES_FLAG_TINY_BUFFER) && n > k)) {
         n = keep_above(s, n, select_slab(s, n, k));
         stat_add(p, r, 3, 1);
@@ -1551,7 +1832,6 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
                       atomicAdd((unsigned long long*)&s.finem[i], (unsigned long long)v);
                   });
         __syncthreads();
-        const u64 tg = stat_phase(p, r, 14, tp);
         int f1[1];
         u64 a1[1];
         fine_locate(s, nlist, {T}, f1, a1);
@@ -1563,7 +1843,6 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         u64 a2[2];
         fine_locate(s, nlist, {t_lo + 1, t_hi + 1}, f2, a2);
         const int fdhi = f2[0], fdlo = f2[1];
-        stat_phase(p, r, 15, tg);
         if (fbT < 0 || fdhi < 0 || fdlo < 0) {
             // Cannot happen for consistent exchanges; decide by the slow path.
             stat_why(p, r, 8u);
@@ -1571,21 +1850,26 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
                 or_dev(&rs->flags, (u32)kFlagFail);
         } else {
             // Fine bins are key ranges: the boundary bin and the draw range.
+            // (The top fine bin ends at +inf inclusive: NaN and negative bits
+            // lie above it and are never taken.)
             const u32 kT0 = (u32)(fbT + kFineBase) << kFineShift;
-            const u32 kT1 = fbT == kFineBins - 1 ? 0xFFFFFFFFu : (u32)(fbT + 1 + kFineBase) << kFineShift;
+            const u32 kT1 = fbT == kFineBins - 1 ? kInfKey + 1 : (u32)(fbT + 1 + kFineBase) << kFineShift;
             const u32 kD0 = (u32)(fdlo + kFineBase) << kFineShift;
-            const u32 kD1 = fdhi == kFineBins - 1 ? 0xFFFFFFFFu : (u32)(fdhi + 1 + kFineBase) << kFineShift;
+            const u32 kD1 = fdhi == kFineBins - 1 ? kInfKey + 1 : (u32)(fdhi + 1 + kFineBase) << kFineShift;
+            const u32 wT = kT1 - kT0, wD = kD1 - kD0;
+            const u64 tg = p.stats ? wall_clock64() : 0;
             ng = gather_regs<VEC, kSlotsFull>(
-                s, x, v0, v1,
-                [&](u32 key) { return (key >= kT0 && key < kT1) || (key >= kD0 && key < kD1); },
-                garea, gcap);
+                s, x, v0, v1, [&](u32 b) { return (b - kT0 < wT) | (b - kD0 < wD); }, garea, gcap);
+            stat_phase(p, r, 14, tg);
         }
     } else if (!failed && kind == kInfRow) {
         ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
                                           garea, gcap);
     }
+    const u64 ta = p.stats ? wall_clock64() : 0;
     if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
     const bool last = arrive_last(s, &rs->ticket, nseg);
+    stat_phase(p, r, 15, ta);
     stat_phase(p, r, 12, tp);
     if (last) full_finish<VEC>(s, r, nseg, kind, nit, T, above_f, fbT, nlist, failed);
 }
@@ -1602,38 +1886,44 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     const u32 gcap = tiny ? 16u : kGSeg;
     const u64 P = fixed_p(ld_g(&p.top_p[r]));
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
-    u64 over = 0;
-    for (u32 q = threadIdx.x; q < nseg; q += kBlock) {
-        const u64 n = ld_g(&pub_c(p, r, q)->ng);
-        s.gn[q] = (u32)(n < gcap ? n : gcap);
-        over += n > gcap;
+    // One round of loads: the gather counts, the row's flags and, for up to
+    // eight segments, every gather area whatever its count turns out to be.
+    static_assert(kGSeg == 512, "gather areas of 2^9 entries");
+    const u32 gsh = tiny ? 4u : 9u;  // gcap = 2^gsh
+    const u32 gmask = (1u << gsh) - 1;
+    const u64* g0 = gather_area(p, r, 0);
+    const u32 total = nseg << gsh;
+    const u64 ngv = threadIdx.x < nseg ? ld_g(&pub_c(p, r, threadIdx.x)->ng) : 0;
+    const u32 fl = threadIdx.x == 0 ? ld_dev(&rs->flags) : 0u;
+    constexpr int kL = 8;
+    u64 c[kL];
+#pragma unroll
+    for (int j = 0; j < kL; ++j) {
+        const u32 t = j * kBlock + threadIdx.x;
+        c[j] = t < total ? ld_g(&g0[(size_t)(t >> gsh) * kGSeg + (t & gmask)]) : 0;
     }
-    over = block_sum(s, over);  // also orders s.gn
-    if (threadIdx.x == 0) s.misc[3] = ld_dev(&rs->flags);
-    __syncthreads();
+    if (threadIdx.x < nseg) s.gn[threadIdx.x] = (u32)(ngv < gcap ? ngv : gcap);
+    if (threadIdx.x == 0) {
+        s.misc[3] = fl;
+        s.ctr[3] = 0;
+    }
+    // (Its barriers publish s.gn, s.misc[3] and s.ctr[3].)
+    const u64 over = block_sum(s, (threadIdx.x < nseg && ngv > gcap) ? 1u : 0u);
     const bool fail = (uni(s.misc[3]) & kFlagFail) || over != 0 || failed;
     if (over) stat_why(p, r, 16u);
-    __syncthreads();
     u32 nall = 0;
     if (!fail && kind != kZeroRow) {
-        if (threadIdx.x == 0) s.ctr[3] = 0;
-        __syncthreads();
-        // Every segment's gather area at once, four loads per thread in flight.
-        const u64* g0 = gather_area(p, r, 0);
-        const u32 total = nseg * gcap;
-        for (u32 t0 = 0; t0 < total; t0 += 4 * kBlock) {
-            u64 c[4];
-            bool in[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32 t = t0 + j * kBlock + threadIdx.x;
-                const bool tin = t < total;
-                const u32 q = tin ? t / gcap : 0u, i = tin ? t - q * gcap : 0u;
-                in[j] = tin && i < s.gn[q];
-                c[j] = in[j] ? ld_g(&g0[(size_t)q * kGSeg + i]) : 0;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wave_append(sbuf(s), in[j], c[j], &s.ctr[3], 0, kSelCap);
+        for (int j = 0; j < kL; ++j) {
+            const u32 t = j * kBlock + threadIdx.x;
+            const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
+            wave_append(sbuf(s), in, c[j], &s.ctr[3], 0, kSelCap);
+        }
+        for (u32 t0 = kL * kBlock; t0 < total; t0 += kBlock) {  // more than eight segments
+            const u32 t = t0 + threadIdx.x;
+            const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
+            const u64 cc = in ? ld_g(&g0[(size_t)(t >> gsh) * kGSeg + (t & gmask)]) : 0;
+            wave_append(sbuf(s), in, cc, &s.ctr[3], 0, kSelCap);
         }
         __syncthreads();
         nall = uni(s.ctr[3]);
@@ -1658,7 +1948,9 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         for (u32 i = threadIdx.x; i < nall; i += kBlock) mn = sbuf(s)[i] < mn ? sbuf(s)[i] : mn;
         o.c_keep = block_min(s, mn);
     } else {
-        const Sel sb = select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
+        const bool binned = !tiny && fbT < kFineBins - 1;
+        const Sel sb = binned ? fine_select(s, nall, fbT, T - above_f)
+                              : select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
         const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
         const u64 t = __umul64hi(u, M_p);
         int fdv[1];
@@ -1666,7 +1958,9 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         fine_locate(s, nlist, {t + 1}, fdv, adv);
         const int fd = fdv[0];
         const u64 above_d = adv[0];
-        const Sel sd = select_buf(s, nall, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
+        const Sel sd = (!tiny && fd < kFineBins - 1)
+                           ? fine_select(s, nall, fd, t + 1 - above_d)
+                           : select_buf(s, nall, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
         o.kind = kNormal;
         o.c_keep = sb.c;
         o.M_p = M_p;
