@@ -69,7 +69,8 @@ constexpr int kWavesPerSimd = 4;       // two workgroups per CU
 constexpr int kSlotsFull = 16;         // vectors per thread of a register-resident segment
 constexpr u32 kSegVecFull = kBlock * kSlotsFull;
 constexpr u32 kSegVecSmall = kBlock * 2;     // segment size under TES_FLAG_SMALL_SEGMENTS
-constexpr u32 kStreamDepth = 8;        // 16-byte loads per thread in flight when streaming
+constexpr u32 kStreamDepth = 16;       // 16-byte loads per thread in flight when streaming
+constexpr u32 kPassDepth = 8;          // the same for the passes of whole-row selects
 constexpr u32 kChunk = 1024;           // rows per launch
 constexpr u32 kSlabMaxK = 1024;        // largest k served by the streaming top-k path
 constexpr size_t kWsBudget = 256u << 20;  // workspace bytes per sampler (rows per launch follow)
@@ -86,6 +87,7 @@ constexpr u32 kGSeg = 512;             // gathered entries per top-p-only segmen
 constexpr u32 kSpinLimit = 1u << 16;   // polls before an exchange gives up
 constexpr u32 kMaxSegWs = 64;          // exchange slots per row in the workspace
 constexpr u64 kNoUpper = ~0ull;
+constexpr int kIntMin = -2147483647 - 1;
 
 static_assert(kFineBins == 4097, "fine bin layout");
 static_assert(kCoarseBins == 257, "coarse bin layout");
@@ -234,7 +236,7 @@ struct Smem {
     alignas(16) u16 wcnt[2][kWaves];  // per-wave append counts of a streaming step (double-buffered)
     u32 npass;                 // passes over the row of the current item (statistics)
 };
-static_assert(kFineBins * 8 <= kRegionBytes, "fine histogram fits the region");
+static_assert((kFineBins + 1) * 8 <= kRegionBytes, "fine histogram fits the region");
 
 __device__ __forceinline__ u64* sbuf(Smem& s) { return reinterpret_cast<u64*>(s.region); }
 __device__ __forceinline__ const u64* sbuf(const Smem& s) {
@@ -242,7 +244,9 @@ __device__ __forceinline__ const u64* sbuf(const Smem& s) {
 }
 __device__ __forceinline__ u32* shcnt(Smem& s) { return reinterpret_cast<u32*>(s.region + 16384); }
 __device__ __forceinline__ u64* shmass(Smem& s) { return reinterpret_cast<u64*>(s.region + 24576); }
-__device__ __forceinline__ u64* shfine(Smem& s) { return reinterpret_cast<u64*>(s.region); }
+// Fine mass histogram of a top-p-only segment: bins [0, kFineBins) plus a
+// discard slot at index -1.
+__device__ __forceinline__ u64* shfine(Smem& s) { return reinterpret_cast<u64*>(s.region + 8); }
 __device__ __forceinline__ u32* shdig(Smem& s) { return reinterpret_cast<u32*>(s.region + 32768); }
 __device__ __forceinline__ u64* shtab(Smem& s) { return reinterpret_cast<u64*>(s.region + 32768); }
 
@@ -1212,14 +1216,14 @@ __device__ __noinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     return select_buf(s, n, W, true, fine_lo(f), fine_hi(f));
 }
 
-// Calls f(key, idx, valid) for every element of a row, VEC per thread per
-// round; every thread makes the same number of calls, so f may use wave
-// collectives.  Eight rounds of loads are kept in flight.
-template <int VEC, typename F>
-__device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
+// Calls f(x, iv, valid) for every vector x (index iv) of a row, one per thread
+// per round; every thread makes the same number of calls (valid is false past
+// the end of the row), so f may use wave collectives.  kG rounds of loads are
+// kept in flight.
+template <int VEC, u32 kG, typename F>
+__device__ __forceinline__ void for_each_vec(const float* __restrict__ row, u32 nvec, F f) {
     typedef typename VecT<VEC>::T VT;
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
-    constexpr u32 kG = kStreamDepth;
     const u32 nr = (nvec + kBlock - 1) / kBlock;
     const u32 last = nvec - 1;
     VT pf[kG];
@@ -1232,16 +1236,24 @@ __device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
 #pragma unroll
         for (u32 d = 0; d < kG; ++d) {
             const u32 iv = (r0 + d) * kBlock + threadIdx.x;
-            const bool valid = iv < nvec;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                f(sanitize(__float_as_uint(VecT<VEC>::get(pf[d], e))), iv * VEC + e, valid);
+            f(pf[d], iv, iv < nvec);
             pf[d] = ld_stream(&rv[min((r0 + d + kG) * kBlock + threadIdx.x, last)]);
             // Keep the refill here: hoisted above the other steps it would
             // turn the pipeline into load-all-then-wait.
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+}
+
+// Calls f(key, idx, valid) for every element of a row (sanitised key).
+template <int VEC, u32 kG = kPassDepth, typename F>
+__device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
+    typedef typename VecT<VEC>::T VT;
+    for_each_vec<VEC, kG>(row, nvec, [&](const VT& x, u32 iv, bool valid) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            f(sanitize(__float_as_uint(VecT<VEC>::get(x, e))), iv * VEC + e, valid);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1402,19 +1414,52 @@ __device__ __forceinline__ u64 stat_phase(const Params& p, u32 r, int word, u64 
 template <int VEC>
 __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
     const Params p = params_from(s);
+    typedef typename VecT<VEC>::T VT;
     stat_start(p, r, 1);
     const u64 tp = p.stats ? wall_clock64() : 0;
-    u64 best = 0;
-    for_each_entry<VEC>(p.probs + (size_t)r * p.V, p.nvec, [&](u32 key, u32 idx, bool valid) {
-        const u64 c = valid ? composite(key, idx) : 0ull;
-        best = c > best ? c : best;
+    const float* row = p.probs + (size_t)r * p.V;
+    // The largest bits as signed integers: non-negative floats order as their
+    // bits, negative ones (which count as zero) lie below all of them and NaN
+    // bits above +inf.  Each lane keeps the first of its vectors holding its
+    // largest value; the row's smallest index holding the maximum comes from
+    // reloading those vectors afterwards.
+    int best = kIntMin;
+    u32 bvec = 0;
+    for_each_vec<VEC, kStreamDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
+        int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
+#pragma unroll
+        for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
+        const bool up = valid && mx > best;
+        best = up ? mx : best;
+        bvec = up ? iv : bvec;
     });
-    best = block_max(s, best);
+    const int K = (int)((u32)block_max(s, (u64)((u32)best ^ 0x80000000u)) ^ 0x80000000u);
+    u64 cbest;
+    if (K > (int)kInfKey) {
+        // NaN bits are the largest: take the exact maximum of the composites.
+        u64 b = 0;
+        for_each_entry<VEC>(row, p.nvec, [&](u32 key, u32 idx, bool valid) {
+            const u64 c = valid ? composite(key, idx) : 0ull;
+            b = c > b ? c : b;
+        });
+        cbest = block_max(s, b);
+    } else if (K <= 0) {
+        cbest = composite(0u, 0u);  // every entry counts as zero: the smallest index
+    } else {
+        u64 idx = ~0ull;
+        if (best == K) {
+            const VT x = ld_g(&reinterpret_cast<const VT*>(row)[bvec]);
+#pragma unroll
+            for (int e = VEC - 1; e >= 0; --e)
+                if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K) idx = (u64)bvec * VEC + e;
+        }
+        cbest = composite((u32)K, (u32)block_min(s, idx));
+    }
     stat_phase(p, r, 8, tp);
     Outcome o{};
-    const u32 key = comp_key(best);
-    o.token = comp_index(best);
-    o.c_keep = best;
+    const u32 key = comp_key(cbest);
+    o.token = comp_index(cbest);
+    o.c_keep = cbest;
     o.m = 1;
     o.M_p = key_mass(key);
     o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
@@ -1492,23 +1537,41 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
         tkey = (u32)(g.d + kFineBase) << kFineShift;
     }
     __syncthreads();  // the histogram is dead; the buffer takes its place
+    if (tkey == 0) {
+        // Fewer than j sampled entries have a mass (a row of mostly zeros, or
+        // a short row with fewer than k): whole-row passes decide.
+        const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k,
+                                           fixed_p(top_p), philox_uniform(p.seed, p.row_base + r, p.offset),
+                                           kSelCap);
+        finish_row(s, p, r, o, kPathSlabFallback, 0);
+        return;
+    }
     const u32 span = kInfKey - tkey;
     u64 tq = stat_phase(p, r, 11, tp);
     constexpr u32 kRegion = kSlabCap / kWaves;
     const u32 wave = uni(wave_id());
     u64* const reg = sbuf(s) + wave * kRegion;
     u32 wfill = 0;  // entries this wave has appended (wave-uniform)
-    // Appends this lane's passing entries of one vector.
+    // Appends this lane's passing entries of one vector.  Passing bits are
+    // non-negative as signed integers, so a vector whose largest signed bits
+    // are below tkey has none; a wave with no such vector skips the rest.
     auto append = [&](const VT& x, u32 iv) {
         const bool valid = iv < nvec;
+        int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
+#pragma unroll
+        for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
+        const u64 vm = __builtin_amdgcn_ballot_w64(valid);
+        if ((__builtin_amdgcn_ballot_w64(mx >= (int)tkey) & vm) == 0) return;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-            const bool pass = valid && (tkey == 0 || b - tkey <= span);
-            const u64 m = __ballot(pass);
+            // Passing bits are keys: no sanitising.
+            const u64 m = __builtin_amdgcn_ballot_w64(b - tkey <= span) & vm;
             if (m) {
-                const u32 pos = wfill + mbcnt64(m);
-                if (pass && pos < kRegion) reg[pos] = composite(sanitize(b), iv * VEC + e);
+                // Past the region's last slot, entries land on that slot and
+                // the count reports the overflow.
+                if ((b - tkey <= span) & valid)
+                    reg[min(wfill + mbcnt64(m), kRegion - 1)] = composite(b, iv * VEC + e);
                 wfill += (u32)__popcll(m);
             }
         }
@@ -1532,7 +1595,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
 #pragma unroll
     for (u32 w = 0; w < (u32)kWaves; ++w) {
         const u32 cw = uni(s.gn[w]);
-        over |= cw > kRegion;
+        over |= cw > kRegion - 1;
         fill += cw;
         before += w < wave ? cw : 0u;
     }
@@ -1694,7 +1757,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
 
     // The histogram is cleared first so that each vector is counted as soon
     // as its load returns (loads are issued, and waited for, in order).
-    for (int i = threadIdx.x; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
+    for (int i = (int)threadIdx.x - 1; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
     __syncthreads();
     VT x[kSlotsFull];
 #pragma unroll
@@ -1703,20 +1766,33 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         x[d] = ld_stream(&rv[i < v1 ? i : v1 - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // Branch-free binning of the raw bits: the bin index (key >> 16) - base
+    // clamped to [-1, kFineBins - 1] sends keys below 2^-32 to the discard
+    // slot and keys >= 1.0, +inf, NaN and negative bits to the top bin; the
+    // mass floor(x * 2^32) clamped to [0, 2^32 - 256] is zero for NaN and
+    // negatives, exact below 1.0, and 2^32 - 256 from 1.0 up, so the top bin
+    // ends holding (2^32 - 256) times its count, whose mass is count * 2^32.
     // The segment's mass is the sum of the histogram, taken afterwards; +inf
-    // entries are counted only by waves that hold one.
+    // entries (and NaN bits) show up as signed maxima >= +inf and are counted
+    // only by waves that hold one.
+    constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256, the largest float below 2^32
     u64 ninf = 0;
 #pragma unroll
     for (int d = 0; d < kSlotsFull; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
         if (i < v1) {
+            int mx = kIntMin;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x[d], e)));
-                if (key >= kMinMassKey)
-                    atomicAdd((unsigned long long*)&shfine(s)[fine_bin(key)],
-                              (unsigned long long)key_mass(key));
-                if (__ballot(key == kInfKey)) ninf += key == kInfKey;
+                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
+                mx = max(mx, (int)b);
+                const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, -1), kFineBins - 1);
+                const float q = fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
+                atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)(u32)q);
+            }
+            if (__ballot(mx >= (int)kInfKey)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x[d], e)) == kInfKey;
             }
         }
     }
@@ -1724,6 +1800,11 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     for (int i = threadIdx.x; i < kCoarseBins; i += kBlock) s.coarse[i] = 0;
     for (int i = threadIdx.x; i < kDMax * 16; i += kBlock) s.finem[i] = 0;
     if (threadIdx.x < 2) s.csum[threadIdx.x] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        u64& top = shfine(s)[kFineBins - 1];
+        top = (top / (u64)kTopMass) << 32;
+    }
     __syncthreads();
     u64 M = 0;
     for (int i = threadIdx.x; i < kFineBins; i += kBlock) M += shfine(s)[i];
