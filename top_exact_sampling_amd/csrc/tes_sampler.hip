@@ -150,6 +150,8 @@ struct Params {
     u32 rowbytes;   // bytes of the per-row exchange area
     u32 chunk;      // rows the workspace holds
     u32 flags;
+    u32 split;      // workgroups a top-k or greedy row may be split between (1 or 2)
+    u32 slots;      // workgroups resident at once on the device
 };
 
 __device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
@@ -170,6 +172,23 @@ __device__ __forceinline__ PubF* pub_f(const Params& p, u32 r, u32 seg) {
 __device__ __forceinline__ u64* gather_area(const Params& p, u32 r, u32 seg) {
     return reinterpret_cast<u64*>(ws_row(p, r) + (size_t)p.s_ws * (sizeof(PubC) + sizeof(PubF))) +
            (size_t)seg * kGSeg;
+}
+// A top-k or greedy row streamed by two workgroups: each publishes its half's
+// result in the row's exchange area, and the last to arrive finishes.
+struct HalfPub {
+    u64 best;  // greedy: the half's largest composite
+    u32 fill;  // top-k: candidates the half kept (more than kHalfCap: too many)
+    u32 tkey;  // top-k: the half's threshold key
+    u32 over;  // top-k: the half cannot be used
+    u32 pad[3];
+};
+constexpr u32 kHalfCap = 2048;  // published candidates per half
+constexpr size_t kHalfBytes = 2 * sizeof(HalfPub) + 2 * (size_t)kHalfCap * sizeof(u64);
+__device__ __forceinline__ HalfPub* half_pub(const Params& p, u32 r, u32 h) {
+    return reinterpret_cast<HalfPub*>(ws_row(p, r)) + h;
+}
+__device__ __forceinline__ u64* half_cands(const Params& p, u32 r, u32 h) {
+    return reinterpret_cast<u64*>(ws_row(p, r) + 2 * sizeof(HalfPub)) + (size_t)h * kHalfCap;
 }
 // Pointers to device memory reach the kernel through LDS (see params_from),
 // which hides their address space; every access to rows and workspace goes
@@ -373,6 +392,8 @@ __device__ __forceinline__ Params params_from(const Smem& s) {
     p.rowbytes = uni(s.p.rowbytes);
     p.chunk = uni(s.p.chunk);
     p.flags = uni(s.p.flags);
+    p.split = uni(s.p.split);
+    p.slots = uni(s.p.slots);
     return p;
 }
 
@@ -1171,45 +1192,128 @@ __device__ __noinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P,
 
 // Mass select inside fine bin f (< kFineBins - 1) over sbuf(s)[0, n), n <=
 // kSelCap: the entry at which the bin's descending cumulative mass first
-// reaches W (1 <= W <= the bin's mass), with the bin's mass above it.  Bins
-// are 32 consecutive keys (key bits 15..5); when the bin holding W has more
-// than 64 entries the radix select decides.
+// reaches W (1 <= W <= the bin's mass), with the bin's mass above it.  The
+// bin's entries are first compacted into a list.  Up to 64 of them are sorted
+// by one wave; up to 256 are split by one wave into 64 sub-bins of 1024 keys
+// (an LDS table of packed count and mass, scanned across the lanes) and only
+// the sub-bin holding W is sorted.  Larger bins go through the workgroup's
+// 2048-bin table (32 keys per bin), and the radix select decides when even
+// that bin holds more than 64 entries.
 __device__ __noinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
-    constexpr int J = kSelCap / kBlock;
     const u32 fkey = (u32)(f + (int)kFineBase);
-    u64 c[J];
-    int dig[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const u32 i = threadIdx.x + (u32)j * kBlock;
-        c[j] = i < n ? sbuf(s)[i] : 0ull;
-        const u32 key = comp_key(c[j]);
-        dig[j] = (i < n && (key >> kFineShift) == fkey) ? (int)((key >> 5) & (kTabBins - 1)) : -1;
-    }
-    u64* srt = sbuf(s) + kSelCap;
-    const u64 total = bin_scatter<J>(s, c, dig, srt);
-    if (wave_id() == 0) {
-        BinView bv{shtab(s), srt, total};
-        const int b = bv.find_mass(W);
-        bool ok = bv.load(b);
-        const u64 base = ok ? bv.mass_above(b) : 0;
-        const u64 m = ok ? __ballot(base + bv.inc >= W) : 0;
-        ok = m != 0;  // always set for a consistent table
-        if (ok && lane_id() == 0) s.misc[5] = 1u;
-        if (ok) {
-            const u32 L = (u32)__builtin_ctzll(m);
-            const u64 cw = read_lane(bv.v, L);
-            const u64 above = base + read_lane(bv.inc, L) - key_mass(comp_key(cw));
-            if (lane_id() == 0) {
-                s.bc[1] = cw;
-                s.bc[2] = above;
-            }
-        } else if (lane_id() == 0) {
-            s.misc[5] = 0u;
-        }
+    u64* list = sbuf(s) + kSelCap;
+    if (threadIdx.x == 0) s.ctr[2] = 0;
+    __syncthreads();
+    for (u32 i0 = 0; i0 < n; i0 += kBlock) {
+        const u32 i = i0 + threadIdx.x;
+        const u64 c = i < n ? sbuf(s)[i] : 0ull;
+        wave_append(list, i < n && (comp_key(c) >> kFineShift) == fkey, c, &s.ctr[2], 0, kSelCap);
     }
     __syncthreads();
-    const bool ok = uni(s.misc[5]) != 0;
+    const u32 nf = uni(s.ctr[2]);
+    bool ok = false;
+    if (nf <= 256u) {
+        if (wave_id() == 0) {
+            const u32 lane = lane_id();
+            bool wok = true;
+            u64 v = 0, inc = 0, base = 0;
+            if (nf <= 64u) {
+                const u64 x = lane < nf ? list[lane] : 0ull;
+                v = wave_sort_desc(x, nf);
+                inc = wave_incl_scan(key_mass(comp_key(v)));
+            } else {
+                // 64 sub-bins by key bits 15..10; lane l owns sub-bin 63 - l
+                // (descending), entries j * 64 + l are the lane's.
+                u64* tab = shtab(s);
+                tab[lane] = 0;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                u64 c[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32 i = (u32)j * 64u + lane;
+                    c[j] = i < nf ? list[i] : 0ull;
+                    if (i < nf)
+                        atomicAdd((unsigned long long*)&tab[63 - ((comp_key(c[j]) >> 10) & 63u)],
+                                  (unsigned long long)key_mass(comp_key(c[j])));
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                const u64 m = tab[lane];
+                const u64 mi = wave_incl_scan(m);
+                const u64 me = mi - m;  // mass of the sub-bins above lane's
+                const u64 sel = __builtin_amdgcn_ballot_w64(me < W && W <= mi);
+                wok = sel != 0;
+                const u32 L = wok ? (u32)__builtin_ctzll(sel) : 0u;
+                const u32 sb = 63u - L;
+                base = read_lane(me, L);
+                // Collect the sub-bin's entries into lanes (at most 64).
+                u32 cnt = 0;
+                u64 x = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32 i = (u32)j * 64u + lane;
+                    const bool in = i < nf && ((comp_key(c[j]) >> 10) & 63u) == sb;
+                    const u64 bm = __builtin_amdgcn_ballot_w64(in);
+                    if (in) {
+                        const u32 pos = cnt + mbcnt64(bm);
+                        if (pos < 64u) tab[64 + pos] = c[j];
+                    }
+                    cnt += (u32)__popcll(bm);
+                }
+                wok = wok && cnt <= 64u;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                x = (wok && lane < cnt) ? tab[64 + lane] : 0ull;
+                v = wave_sort_desc(x, cnt);
+                inc = wave_incl_scan(key_mass(comp_key(v)));
+            }
+            const u64 m = wok ? __builtin_amdgcn_ballot_w64(base + inc >= W) : 0;
+            wok = wok && m != 0;
+            if (lane == 0) s.misc[5] = wok ? 1u : 0u;
+            if (wok) {
+                const u32 L = (u32)__builtin_ctzll(m);
+                const u64 cw = read_lane(v, L);
+                const u64 above = base + read_lane(inc, L) - key_mass(comp_key(cw));
+                if (lane == 0) {
+                    s.bc[1] = cw;
+                    s.bc[2] = above;
+                }
+            }
+        }
+        __syncthreads();
+        ok = uni(s.misc[5]) != 0;
+    } else {
+        // The workgroup's table over the list: 2048 bins of 32 keys.
+        constexpr int J = kSelCap / kBlock;
+        u64 c[J];
+        int dig[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const u32 i = threadIdx.x + (u32)j * kBlock;
+            c[j] = i < nf ? list[i] : 0ull;
+            dig[j] = i < nf ? (int)((comp_key(c[j]) >> 5) & (kTabBins - 1)) : -1;
+        }
+        __syncthreads();  // the scatter rewrites the list
+        const u64 total = bin_scatter<J>(s, c, dig, list);
+        if (wave_id() == 0) {
+            BinView bv{shtab(s), list, total};
+            const int b = bv.find_mass(W);
+            bool wok = bv.load(b);
+            const u64 base = wok ? bv.mass_above(b) : 0;
+            const u64 m = wok ? __ballot(base + bv.inc >= W) : 0;
+            wok = m != 0;
+            if (lane_id() == 0) s.misc[5] = wok ? 1u : 0u;
+            if (wok) {
+                const u32 L = (u32)__builtin_ctzll(m);
+                const u64 cw = read_lane(bv.v, L);
+                const u64 above = base + read_lane(bv.inc, L) - key_mass(comp_key(cw));
+                if (lane_id() == 0) {
+                    s.bc[1] = cw;
+                    s.bc[2] = above;
+                }
+            }
+        }
+        __syncthreads();
+        ok = uni(s.misc[5]) != 0;
+    }
     const Sel r{uni(s.bc[1]), uni(s.bc[2])};
     __syncthreads();
     if (ok) return r;
@@ -1412,20 +1516,24 @@ __device__ __forceinline__ u64 stat_phase(const Params& p, u32 r, int word, u64 
 // Greedy rows (k = 1)
 // ---------------------------------------------------------------------------
 template <int VEC>
-__device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
+__device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, u32 S) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
-    stat_start(p, r, 1);
+    stat_start(p, r, S);
     const u64 tp = p.stats ? wall_clock64() : 0;
-    const float* row = p.probs + (size_t)r * p.V;
+    // This workgroup's part: the row, or half of it when split.
+    const u32 hv = (p.nvec + S - 1) / S;
+    const u32 v0 = h * hv;
+    const u32 nv = min(v0 + hv, p.nvec) - v0;
+    const float* part = p.probs + (size_t)r * p.V + (size_t)v0 * VEC;
     // The largest bits as signed integers: non-negative floats order as their
     // bits, negative ones (which count as zero) lie below all of them and NaN
     // bits above +inf.  Each lane keeps the first of its vectors holding its
-    // largest value; the row's smallest index holding the maximum comes from
+    // largest value; the part's smallest index holding the maximum comes from
     // reloading those vectors afterwards.
     int best = kIntMin;
     u32 bvec = 0;
-    for_each_vec<VEC, kStreamDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
+    for_each_vec<VEC, kStreamDepth>(part, nv, [&](const VT& x, u32 iv, bool valid) {
         int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
 #pragma unroll
         for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
@@ -1438,22 +1546,31 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
     if (K > (int)kInfKey) {
         // NaN bits are the largest: take the exact maximum of the composites.
         u64 b = 0;
-        for_each_entry<VEC>(row, p.nvec, [&](u32 key, u32 idx, bool valid) {
-            const u64 c = valid ? composite(key, idx) : 0ull;
+        for_each_entry<VEC>(part, nv, [&](u32 key, u32 idx, bool valid) {
+            const u64 c = valid ? composite(key, v0 * VEC + idx) : 0ull;
             b = c > b ? c : b;
         });
         cbest = block_max(s, b);
     } else if (K <= 0) {
-        cbest = composite(0u, 0u);  // every entry counts as zero: the smallest index
+        cbest = composite(0u, v0 * VEC);  // every entry counts as zero: the smallest index
     } else {
         u64 idx = ~0ull;
         if (best == K) {
-            const VT x = ld_g(&reinterpret_cast<const VT*>(row)[bvec]);
+            const VT x = ld_g(&reinterpret_cast<const VT*>(part)[bvec]);
 #pragma unroll
             for (int e = VEC - 1; e >= 0; --e)
-                if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K) idx = (u64)bvec * VEC + e;
+                if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K)
+                    idx = (u64)(v0 + bvec) * VEC + e;
         }
         cbest = composite((u32)K, (u32)block_min(s, idx));
+    }
+    if (S > 1) {
+        RowState* rs = ws_state(p, r);
+        if (threadIdx.x == 0) st_dev(&half_pub(p, r, h)->best, cbest);
+        if (!arrive_last(s, &rs->ticket, S)) return;
+        const u64 ob = ld_g(&half_pub(p, r, 1 - h)->best);
+        cbest = ob > cbest ? ob : cbest;
+        if (threadIdx.x == 0) st_dev(&rs->ticket, 0u);
     }
     stat_phase(p, r, 8, tp);
     Outcome o{};
@@ -1472,33 +1589,41 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r) {
 template <int VEC>
 __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u);
 
-// Streams the row once and keeps, in the LDS buffer, every entry whose key is
-// at or above a threshold key tkey, chosen so that about 1.5 k (and at least
-// k) entries of the row pass.  The test is one subtraction and one compare on
-// the raw bits: for tkey > 0, sanitize(b) >= tkey exactly when tkey <= b <=
-// the bits of +inf; tkey = 0 keeps everything.
+// Streams its part of the row (the whole row, or half of it when the row is
+// split between two workgroups) once and keeps, in the LDS buffer, every entry
+// whose key is at or above a threshold key tkey > 0, chosen so that about
+// 1.5 k (and at least k) entries of the row pass.  The test is one subtraction
+// and one compare on the raw bits: sanitize(b) >= tkey exactly when tkey <= b
+// <= the bits of +inf.
 //   The first kStreamDepth steps (2048 entries each, the first loads in
 //   flight) are a sample: their keys are counted in 1/128-octave bins before
 //   anything else happens, and tkey becomes the lower edge of the bin that
 //   holds the sample's j-th best, j = ceil(1.5 k n / V) + 12 for n sampled
 //   entries (j = k when the sample is the whole row).
-//   Then the row is streamed from its start with no barriers and no atomics:
+//   Then the part is streamed from its start with no barriers and no atomics:
 //   each wave appends to its own region of kSlabCap / 8 entries, at its
 //   running count (a scalar) plus the lane's rank among the wave's passing
 //   lanes (mbcnt of the element's ballot).  Entries beyond a region are
 //   counted but not written.  Afterwards the regions are packed together.
-// The buffer then holds exactly the entries at or above tkey.  When no region
-// overflowed and there are at least k, it holds the row's best k; otherwise
-// the row is resolved by whole-row passes.
+// The buffer then holds exactly the part's entries at or above tkey.  A whole
+// row that kept at least k without overflowing holds the row's best k.  The
+// two halves of a split row publish their buffers and thresholds; the last to
+// arrive joins them, and with T = the larger threshold, every entry of the row
+// at or above T is in the union, so the union holds the row's best k when at
+// least k of its entries are at or above T.  Rows that fail these tests (or
+// whose sample holds fewer than j entries with a mass) are resolved by
+// whole-row passes.
 template <int VEC>
-__device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
+__device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u32 h, u32 S) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V);
-    const u32 nvec = p.nvec;
+    const u32 hv = (p.nvec + S - 1) / S;
+    const u32 v0 = h * hv;
+    const u32 nvec = min(v0 + hv, p.nvec) - v0;  // vectors of this part
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V) + v0;
     // Issued before the stream so that its latency is hidden.
     const float top_p = ld_g(&p.top_p[r]);
-    stat_start(p, r, 1);
+    stat_start(p, r, S);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 nsteps = (nvec + kBlock - 1) / kBlock;
     const u32 last = nvec - 1;
@@ -1526,7 +1651,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
         }
     }
     const u32 nsamp = min(kStreamDepth * kBlock, nvec) * VEC;
-    const u32 j = nsteps <= kStreamDepth
+    const u32 j = (S == 1 && nsteps <= kStreamDepth)
                       ? k
                       : (u32)(((u64)3 * k * nsamp + 2ull * p.V - 1) / (2ull * p.V)) + 12;
     const u32 tot = (u32)block_sum(s, nmass);  // also orders the histogram
@@ -1537,7 +1662,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
         tkey = (u32)(g.d + kFineBase) << kFineShift;
     }
     __syncthreads();  // the histogram is dead; the buffer takes its place
-    if (tkey == 0) {
+    const bool no_tkey = tkey == 0;
+    if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the half reports itself unusable
+    if (no_tkey && S == 1) {
         // Fewer than j sampled entries have a mass (a row of mostly zeros, or
         // a short row with fewer than k): whole-row passes decide.
         const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k,
@@ -1571,7 +1698,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
                 // Past the region's last slot, entries land on that slot and
                 // the count reports the overflow.
                 if ((b - tkey <= span) & valid)
-                    reg[min(wfill + mbcnt64(m), kRegion - 1)] = composite(b, iv * VEC + e);
+                    reg[min(wfill + mbcnt64(m), kRegion - 1)] = composite(b, (v0 + iv) * VEC + e);
                 wfill += (u32)__popcll(m);
             }
         }
@@ -1620,8 +1747,42 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k) {
     stat_phase(p, r, 8, tp);
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    u32 tmin = tkey;
+    if (S > 1) {
+        // Publish this half, then the last half to arrive joins the other's
+        // candidates to its own.
+        RowState* rs = ws_state(p, r);
+        HalfPub* mine = half_pub(p, r, h);
+        over = over || no_tkey || fill > kHalfCap;
+        if (!over) {
+            u64* dst = half_cands(p, r, h);
+            for (u32 i = threadIdx.x; i < fill; i += kBlock) st_dev(&dst[i], sbuf(s)[i]);
+        }
+        if (threadIdx.x == 0) {
+            st_dev(&mine->fill, fill);
+            st_dev(&mine->tkey, tkey);
+            st_dev(&mine->over, over ? 1u : 0u);
+        }
+        if (!arrive_last(s, &rs->ticket, S)) return;
+        const HalfPub* other = half_pub(p, r, 1 - h);
+        const u32 ofill = ld_g(&other->fill), otkey = ld_g(&other->tkey);
+        over = over || ld_g(&other->over) != 0 || fill + ofill > kSlabCap;
+        if (!over) {
+            const u64* src = half_cands(p, r, 1 - h);
+            for (u32 i = threadIdx.x; i < ofill; i += kBlock) sbuf(s)[fill + i] = ld_g(&src[i]);
+            fill += ofill;
+        }
+        const u32 tmax = max(tkey, otkey);
+        tmin = min(tkey, otkey);
+        if (threadIdx.x == 0) st_dev(&rs->ticket, 0u);
+        __syncthreads();
+        u32 above = 0;
+        if (!over)
+            for (u32 i = threadIdx.x; i < fill; i += kBlock) above += comp_key(sbuf(s)[i]) >= tmax;
+        over = over || (u32)block_sum(s, above) < k;  // also orders the joined buffer
+    }
     if (!over && fill >= k) {
-        slab_finish<VEC>(s, r, fill, k, tkey, P, u);
+        slab_finish<VEC>(s, r, fill, k, tmin, P, u);
     } else {
         const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
                                            kSelCap);
@@ -1938,19 +2099,15 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             const u32 kD0 = (u32)(fdlo + kFineBase) << kFineShift;
             const u32 kD1 = fdhi == kFineBins - 1 ? kInfKey + 1 : (u32)(fdhi + 1 + kFineBase) << kFineShift;
             const u32 wT = kT1 - kT0, wD = kD1 - kD0;
-            const u64 tg = p.stats ? wall_clock64() : 0;
             ng = gather_regs<VEC, kSlotsFull>(
                 s, x, v0, v1, [&](u32 b) { return (b - kT0 < wT) | (b - kD0 < wD); }, garea, gcap);
-            stat_phase(p, r, 14, tg);
         }
     } else if (!failed && kind == kInfRow) {
         ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
                                           garea, gcap);
     }
-    const u64 ta = p.stats ? wall_clock64() : 0;
     if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
     const bool last = arrive_last(s, &rs->ticket, nseg);
-    stat_phase(p, r, 15, ta);
     stat_phase(p, r, 12, tp);
     if (last) full_finish<VEC>(s, r, nseg, kind, nit, T, above_f, fbT, nlist, failed);
 }
@@ -2010,6 +2167,7 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         nall = uni(s.ctr[3]);
         __syncthreads();
     }
+    u64 tf = stat_phase(p, r, 14, tp);
     Outcome o{};
     u32 path = kPathFull;
     if (!fail && nall > kSelCap) stat_why(p, r, 32u);
@@ -2032,6 +2190,7 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         const bool binned = !tiny && fbT < kFineBins - 1;
         const Sel sb = binned ? fine_select(s, nall, fbT, T - above_f)
                               : select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
+        tf = stat_phase(p, r, 15, tf);
         const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
         const u64 t = __umul64hi(u, M_p);
         int fdv[1];
@@ -2142,21 +2301,30 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     const u32 nf = uni(s.misc[kClsFull]);
     const u32 n_whole = uni(s.misc[kClsWhole]);
     const u32 n_slab = uni(s.misc[kClsSlab]);
+    const u32 n_greedy = uni(s.misc[kClsGreedy]);
+    // Rows are split only when every item is resident at once: a split adds
+    // workgroups, and ones that wait for a slot only delay the rows they serve.
+    const u32 S = (p.split > 1 && nf * s_full + n_whole + p.split * (n_slab + n_greedy) <= p.slots)
+                      ? p.split : 1u;
     const u32 full_end = nf * s_full;
+    const u32 whole_end = full_end + n_whole;
+    const u32 slab_end = whole_end + n_slab * S;
     const u32 item = blockIdx.x;
     __syncthreads();
     if (item < full_end) {
         const u32 j = item / s_full;
         do_full<VEC>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
-    } else if (item < full_end + (p.rows - nf)) {
-        const u32 i = item - full_end;
-        const u32 r = uni((u32)s.rows[nf + i]);
-        if (i < n_whole)
-            do_whole<VEC>(s, r, row_k_eff(p, r));
-        else if (i < n_whole + n_slab)
-            do_slab<VEC>(s, r, row_k_eff(p, r));
-        else
-            do_greedy<VEC>(s, r);
+    } else if (item < whole_end) {
+        const u32 r = uni((u32)s.rows[nf + (item - full_end)]);
+        do_whole<VEC>(s, r, row_k_eff(p, r));
+    } else if (item < slab_end) {
+        const u32 i = (item - whole_end) / S;
+        const u32 r = uni((u32)s.rows[nf + n_whole + i]);
+        do_slab<VEC>(s, r, row_k_eff(p, r), item - whole_end - i * S, S);
+    } else if (item < slab_end + n_greedy * S) {
+        const u32 i = (item - slab_end) / S;
+        const u32 r = uni((u32)s.rows[nf + n_whole + n_slab + i]);
+        do_greedy<VEC>(s, r, item - slab_end - i * S, S);
     }
 }
 
@@ -2207,6 +2375,7 @@ struct tes_sampler {
     u32 rowbytes;
     u32 chunk;
     u32 seg_full;
+    u32 slots;
     u32* d_stats;
 };
 
@@ -2257,6 +2426,8 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     s->max_vocab = max_vocab;
     s->flags = flags;
     s->seg_full = (flags & TES_FLAG_SMALL_SEGMENTS) ? kSegVecSmall : kSegVecFull;
+    // Two 512-thread workgroups fit on a compute unit (register bound).
+    s->slots = 2u * (u32)(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1);
     // Exchange slots per row: enough for 16-byte rows of max_vocab; top-p-only
     // rows that need more segments (large scalar-path rows) use whole-row passes.
     s->s_ws = ceil_div(ceil_div((u32)max_vocab, 4), s->seg_full);
@@ -2333,13 +2504,18 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
         p.flags = s->flags;
+        // Top-k and greedy rows long enough for two full samples are split
+        // between two workgroups when the exchange area holds both halves.
+        p.split = (s->rowbytes >= kHalfBytes && nvec >= 2 * kStreamDepth * kBlock) ? 2u : 1u;
+        p.slots = s->slots;
         if (p.stats &&
             hipMemsetAsync(p.stats + (size_t)kStatWords * c0, 0, sizeof(u32) * kStatWords * rows,
                            st) != hipSuccess)
             return TES_ERR_LAUNCH;
         // Enough blocks for every row to be top-p-only; the kernel knows the
         // actual mix, and blocks beyond the last item return at once.
-        const u32 grid = rows * (s_full <= s->s_ws ? s_full : 1u);
+        const u32 per_row = s_full <= s->s_ws ? s_full : 1u;
+        const u32 grid = rows * (per_row > p.split ? per_row : p.split);
         if (vec4)
             hipLaunchKernelGGL(tes_main_kernel<4>, dim3(grid), dim3(kBlock), 0, st, p);
         else
