@@ -124,19 +124,19 @@ const char *sampler_status_string(int status);
  *   [5] device wall clock when the row was resolved (low 32 bits);
  *   [6] 0xFFFFFFFF minus the earliest wall clock at which a segment of the
  *       row started;
- *   [7] why a top-p-only row left its fast path (bits): 1 first exchange
- *       timed out, 2 the draw spans more coarse bins than are exchanged (their
- *       count in bits 8..15), 4 second exchange timed out, 8 inconsistent fine
- *       bins, 16 a segment gathered too many entries, 32 too many in total;
- *   [8..13] wall-clock ticks spent in successive phases, summed over the
- *       row's segments: greedy [8] whole item; top-k [8] streaming with its
- *       compactions, [9] final sort and selects, [10] the compactions alone,
- *       [11] the sampled first part, [12] the threshold estimate, [13] the
- *       rest of the row; top-p-only
- *       [8] loads and histogram, [9] first exchange, [10] its analysis and
- *       the second publication, [11] second exchange, [12] gather and
- *       arrival, [13] final selects;
- *   [14..15] reserved (0).
+ *   [7] why a row left its fast path (bits): 1 first exchange timed out,
+ *       2 the draw spans more coarse bins than are exchanged (their count in
+ *       bits 8..15), 4 second exchange timed out, 8 inconsistent fine bins,
+ *       16 a segment gathered too many entries, 32 too many in total (these
+ *       for top-p-only rows), 64 a top-k row's binned finish needed a sort;
+ *   [8..15] wall-clock ticks spent in successive phases, summed over the
+ *       row's workgroups: greedy [8] whole item; top-k [8] streaming,
+ *       [9] the finish, [11] the sampled first part, [13] the rest of the
+ *       stream, [14] and [15] the padding and the sort when the finish
+ *       sorts; top-p-only [8] loads and histogram, [9] first exchange,
+ *       [10] its analysis and the second publication, [11] second exchange,
+ *       [12] gather and arrival, [13] the last segment's finish, [14] its
+ *       loads, [15] its boundary select; other words 0.
  * The wall clock is the device's constant 100 MHz counter.  Synchronises the
  * device.  `host_out` holds 16 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);

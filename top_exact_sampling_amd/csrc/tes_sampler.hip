@@ -14,23 +14,24 @@
 //   * Every entry is a 64-bit composite (key << 32) | ~index, key = the
 //     sanitised fp32 bits.  Composites are unique and order entries exactly as
 //     the stable descending sort does.
-//   * A persistent grid (three 512-thread workgroups per CU) takes work items
-//     in a fixed round-robin order; no queue counter is shared.  Top-p-only
-//     rows (k >= V) come first: each is cut into register-resident segments of
-//     at most 5120 16-byte vectors, and the segments of one row are placed in
-//     the same round of the grid so that they run at the same time.  Every
-//     other row is one item for one workgroup that streams the row once with
-//     eight 16-byte loads per thread in flight.  Giving each streamed row the
-//     same number of loads in flight shares HBM evenly between rows, and the
-//     bound on bytes in flight keeps the latency of the exchanges low.
-//   * Greedy rows (k = 1): streaming argmax of the composites.
-//   * Top-k rows (k <= 1024): the streamed entries at or above a running
-//     threshold go to an LDS candidate buffer; whenever it holds more than
-//     2048 entries a one-digit radix cut (or, if that cut keeps too many, an
-//     exact select of the k-th best) raises the threshold, which never passes
-//     the row's k-th best.  The buffer ends holding the row's best k, which
-//     mass-weighted radix selects finish.  This stands in for the
-//     2048-bucket radix select and candidate list of the cake_sampling page.
+//   * One work item per 512-thread workgroup (two per CU), in block order:
+//     the segments of the top-p-only rows (k >= V) first, cut into
+//     register-resident segments of at most 8192 16-byte vectors and placed
+//     consecutively so that a row's segments run at the same time; then
+//     whole-row rows, top-k rows and greedy rows, one item each (top-k rows,
+//     and greedy rows if there is still room, become two items when every
+//     item fits the resident workgroups).  Streamed rows keep sixteen 16-byte
+//     loads per thread in flight.
+//   * Greedy rows (k = 1): a running maximum of the raw bits as signed
+//     integers per vector, then a reload of the vectors holding the maximum
+//     for its smallest index.
+//   * Top-k rows (k <= 1024): a threshold key from a sampled histogram of the
+//     first loads, then every entry at or above it goes to an LDS candidate
+//     buffer (per-wave regions, ballot ranks, no atomics).  A binned finish
+//     (one table of per-bin counts and masses, single-wave sorts of the few
+//     bins the k-th entry, the top-p boundary and the draw fall in) resolves
+//     the row.  This stands in for the radix select and candidate list of the
+//     cake_sampling page.
 //   * Top-p-only rows: each segment builds an exact mass histogram over
 //     1/128-octave key bins in LDS.  Two small exchanges follow through a
 //     per-row workspace (device-coherent stores, then a relaxed arrival
@@ -39,10 +40,10 @@
 //     the draw can fall in, and the fine bins of just those coarse bins then
 //     name the fine boundary bin and the fine draw bins.  Every segment
 //     gathers the entries of those few fine bins from its registers and the
-//     last segment to arrive finishes in LDS.  The row is read once.  This is
-//     the exact-integer analogue of the pivot and sigma-truncation searches of
-//     the Qrita paper (sections 3.1-3.2): the boundary is found by mass,
-//     never by sorting the nucleus.
+//     last segment to arrive finishes with binned selects.  The row is read
+//     once.  This is the exact-integer analogue of the pivot and
+//     sigma-truncation searches of the Qrita paper (sections 3.1-3.2): the
+//     boundary is found by mass, never by sorting the nucleus.
 //   * Rows with 1024 < k < V, and any row whose fast path cannot decide
 //     (over-full gather, too many draw bins, an exchange that times out), are
 //     resolved by one workgroup with exact multi-pass radix selects over the
@@ -571,21 +572,22 @@ __device__ __forceinline__ void wave_append_n(u64* arr, u32 mask, const u64 (&c)
 // holds u64 words at rec0 + q * stride.  Each thread issues four independent
 // loads before using them, so one round trip to L2 serves 2048 words whatever
 // the number of segments.
+// Sums word i of the nseg published records (record q at rec0 + q * stride)
+// for every i < n and hands each sum to acc(i, sum) exactly once.  Each thread
+// takes whole words and keeps up to four records' loads in flight.
 template <typename Acc>
 __device__ __forceinline__ void sum_words(const u64* rec0, u32 stride, u32 nseg, u32 n, Acc acc) {
-    const u32 total = nseg * n;
-    for (u32 t0 = 0; t0 < total; t0 += 4 * kBlock) {
-        u64 v[4];
+    for (u32 i = threadIdx.x; i < n; i += kBlock) {
+        u64 sum = 0;
+        for (u32 q0 = 0; q0 < nseg; q0 += 4) {
+            u64 v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32 t = t0 + j * kBlock + threadIdx.x;
-            v[j] = t < total ? ld_g(rec0 + (size_t)(t / n) * stride + (t % n)) : 0;
-        }
+            for (int j = 0; j < 4; ++j)
+                v[j] = q0 + j < nseg ? ld_g(rec0 + (size_t)(q0 + j) * stride + i) : 0ull;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32 t = t0 + j * kBlock + threadIdx.x;
-            if (t < total) acc(t % n, v[j]);
+            for (int j = 0; j < 4; ++j) sum += v[j];
         }
+        acc(i, sum);
     }
 }
 
@@ -1994,9 +1996,8 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     static_assert(sizeof(PubC) == 8 * (3 + kCoarseBins), "PubC is M, ninf, ng, coarse[]");
     sum_words(reinterpret_cast<const u64*>(pub_c(p, r, 0)), sizeof(PubC) / 8, nseg, 3 + kCoarseBins,
               [&](u32 i, u64 v) {
-                  if (i < 2) atomicAdd((unsigned long long*)&s.csum[i], (unsigned long long)v);
-                  else if (i >= 3)
-                      atomicAdd((unsigned long long*)&s.coarse[i - 3], (unsigned long long)v);
+                  if (i < 2) s.csum[i] = v;
+                  else if (i >= 3) s.coarse[i - 3] = v;
               });
     __syncthreads();
     const u64 Mt = uni(s.csum[0]);
@@ -2070,9 +2071,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if (!failed && kind == kNormal) {
         static_assert(sizeof(PubF) == 8 * 16 * kDMax, "PubF is fine[kDMax][16]");
         sum_words(reinterpret_cast<const u64*>(pub_f(p, r, 0)), sizeof(PubF) / 8, nseg,
-                  (u32)nlist * 16, [&](u32 i, u64 v) {
-                      atomicAdd((unsigned long long*)&s.finem[i], (unsigned long long)v);
-                  });
+                  (u32)nlist * 16, [&](u32 i, u64 v) { s.finem[i] = v; });
         __syncthreads();
         int f1[1];
         u64 a1[1];
