@@ -72,6 +72,7 @@ constexpr u32 kSegVecFull = kBlock * kSlotsFull;
 constexpr u32 kSegVecSmall = kBlock * 2;     // segment size under TES_FLAG_SMALL_SEGMENTS
 constexpr u32 kStreamDepth = 16;       // 16-byte loads per thread in flight when streaming
 constexpr u32 kPassDepth = 8;          // the same for the passes of whole-row selects
+constexpr u32 kSampleDepth = 4;        // leading steps of a top-k stream that set its threshold
 constexpr u32 kChunk = 1024;           // rows per launch
 constexpr u32 kSlabMaxK = 1024;        // largest k served by the streaming top-k path
 constexpr size_t kWsBudget = 256u << 20;  // workspace bytes per sampler (rows per launch follow)
@@ -1597,7 +1598,7 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey,
 // 1.5 k (and at least k) entries of the row pass.  The test is one subtraction
 // and one compare on the raw bits: sanitize(b) >= tkey exactly when tkey <= b
 // <= the bits of +inf.
-//   The first kStreamDepth steps (2048 entries each, the first loads in
+//   The first kSampleDepth steps (2048 entries each, the first loads in
 //   flight) are a sample: their keys are counted in 1/128-octave bins before
 //   anything else happens, and tkey becomes the lower edge of the bin that
 //   holds the sample's j-th best, j = ceil(1.5 k n / V) + 12 for n sampled
@@ -1641,7 +1642,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     // The sample.
     u32 nmass = 0;
 #pragma unroll
-    for (u32 d = 0; d < kStreamDepth; ++d) {
+    for (u32 d = 0; d < kSampleDepth; ++d) {
         const bool valid = d * kBlock + threadIdx.x < nvec;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -1652,8 +1653,8 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
             }
         }
     }
-    const u32 nsamp = min(kStreamDepth * kBlock, nvec) * VEC;
-    const u32 j = (S == 1 && nsteps <= kStreamDepth)
+    const u32 nsamp = min(kSampleDepth * kBlock, nvec) * VEC;
+    const u32 j = (S == 1 && nsteps <= kSampleDepth)
                       ? k
                       : (u32)(((u64)3 * k * nsamp + 2ull * p.V - 1) / (2ull * p.V)) + 12;
     const u32 tot = (u32)block_sum(s, nmass);  // also orders the histogram
@@ -2301,13 +2302,17 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     const u32 n_whole = uni(s.misc[kClsWhole]);
     const u32 n_slab = uni(s.misc[kClsSlab]);
     const u32 n_greedy = uni(s.misc[kClsGreedy]);
-    // Rows are split only when every item is resident at once: a split adds
-    // workgroups, and ones that wait for a slot only delay the rows they serve.
-    const u32 S = (p.split > 1 && nf * s_full + n_whole + p.split * (n_slab + n_greedy) <= p.slots)
-                      ? p.split : 1u;
+    // Top-k rows are split in two only when every item, halves included, is
+    // resident at once (halves that wait for a slot only delay their rows);
+    // greedy rows too when there is still room.  Second halves come last in
+    // block order.
+    const u32 base_items = nf * s_full + n_whole + n_slab + n_greedy;
+    const u32 S = (p.split > 1 && base_items + (p.split - 1) * n_slab <= p.slots) ? p.split : 1u;
+    const u32 Sg = (S > 1 && base_items + (p.split - 1) * (n_slab + n_greedy) <= p.slots) ? p.split : 1u;
     const u32 full_end = nf * s_full;
     const u32 whole_end = full_end + n_whole;
-    const u32 slab_end = whole_end + n_slab * S;
+    const u32 first_end = whole_end + n_slab;
+    const u32 greedy_end = first_end + n_greedy * Sg;
     const u32 item = blockIdx.x;
     __syncthreads();
     if (item < full_end) {
@@ -2316,14 +2321,17 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     } else if (item < whole_end) {
         const u32 r = uni((u32)s.rows[nf + (item - full_end)]);
         do_whole<VEC>(s, r, row_k_eff(p, r));
-    } else if (item < slab_end) {
-        const u32 i = (item - whole_end) / S;
-        const u32 r = uni((u32)s.rows[nf + n_whole + i]);
-        do_slab<VEC>(s, r, row_k_eff(p, r), item - whole_end - i * S, S);
-    } else if (item < slab_end + n_greedy * S) {
-        const u32 i = (item - slab_end) / S;
+    } else if (item < first_end) {
+        const u32 r = uni((u32)s.rows[nf + n_whole + (item - whole_end)]);
+        do_slab<VEC>(s, r, row_k_eff(p, r), 0, S);
+    } else if (item < greedy_end) {
+        const u32 i = (item - first_end) / Sg;
         const u32 r = uni((u32)s.rows[nf + n_whole + n_slab + i]);
-        do_greedy<VEC>(s, r, item - slab_end - i * S, S);
+        do_greedy<VEC>(s, r, item - first_end - i * Sg, Sg);
+    } else if (item < greedy_end + n_slab * (S - 1)) {
+        const u32 i = (item - greedy_end) % n_slab, h = 1 + (item - greedy_end) / n_slab;
+        const u32 r = uni((u32)s.rows[nf + n_whole + i]);
+        do_slab<VEC>(s, r, row_k_eff(p, r), h, S);
     }
 }
 
