@@ -602,13 +602,17 @@ __device__ __forceinline__ void vm_wait() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Publish this workgroup's exchanged data, count it in at *ctr and wait until
-// `n` workgroups have arrived (bounded).  Returns false on a timeout.
-__device__ bool arrive_wait(Smem& s, u32* ctr, u32 n) {
+// Publish this workgroup's exchanged data and count it in at *ctr.
+__device__ void arrive_only(Smem& s, u32* ctr) {
     vm_wait();
     __syncthreads();
+    if (threadIdx.x == 0) add_dev(ctr, 1u);
+}
+
+// Wait until `n` workgroups have counted in at *ctr (bounded); returns false
+// on a timeout.
+__device__ bool wait_arrivals(Smem& s, u32* ctr, u32 n) {
     if (threadIdx.x == 0) {
-        add_dev(ctr, 1u);
         u32 ok = 1, it = 0;
         while (ld_dev(ctr) < n) {
             if (++it > kSpinLimit) {
@@ -624,6 +628,12 @@ __device__ bool arrive_wait(Smem& s, u32* ctr, u32 n) {
     const bool ok = uni(s.misc[7]) != 0;
     __syncthreads();
     return ok;
+}
+
+// arrive_only, then wait_arrivals.
+__device__ bool arrive_wait(Smem& s, u32* ctr, u32 n) {
+    arrive_only(s, ctr);
+    return wait_arrivals(s, ctr, n);
 }
 
 // Count in at the row's ticket; true in the workgroup that arrives last, which
@@ -797,6 +807,41 @@ struct VecT<1> {
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) {
     return __builtin_nontemporal_load((const TES_GLOBAL T*)p);
+}
+
+// Keeps, in place, the composites of each wave's LDS region (wave w's first
+// `n` entries at sbuf(s) + w * reg; n is the calling wave's count) whose key
+// satisfies pred, and writes the kept entries of all waves, packed, to
+// out[0, cap) with device-coherent stores.  Returns how many there are (which
+// may exceed cap).
+template <typename Pred>
+__device__ __forceinline__ u32 filter_regions(Smem& s, u32 reg, u32 n, Pred pred, u64* out,
+                                              u32 cap) {
+    const u32 wave = uni(wave_id());
+    const u32 lane = lane_id();
+    u64* const rg = sbuf(s) + wave * reg;
+    u32 kept = 0;
+    for (u32 j0 = 0; j0 < n; j0 += 64) {
+        const bool in = j0 + lane < n;
+        const u64 c = in ? rg[j0 + lane] : 0ull;
+        const bool keep = in && pred(comp_key(c));
+        const u64 m = __builtin_amdgcn_ballot_w64(keep);
+        if (keep) rg[kept + mbcnt64(m)] = c;  // never past the entries already read
+        kept += (u32)__popcll(m);
+    }
+    if (lane == 0) s.gn[wave] = kept;
+    __syncthreads();
+    u32 total = 0, before = 0;
+#pragma unroll
+    for (u32 w = 0; w < (u32)kWaves; ++w) {
+        const u32 cw = uni(s.gn[w]);
+        total += cw;
+        before += w < wave ? cw : 0u;
+    }
+    for (u32 j = lane; j < kept; j += 64)
+        if (before + j < cap) st_dev(&out[before + j], rg[j]);
+    __syncthreads();
+    return total;
 }
 
 // Collects the composites of this workgroup's register-resident entries whose
@@ -2052,7 +2097,43 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if (!decidable && threadIdx.x == 0)
         or_dev(&rs->flags, (u32)kFlagFail);
     tp = stat_phase(p, r, 10, tp);
-    const bool ok2 = arrive_wait(s, &rs->arrive_b, nseg);
+    arrive_only(s, &rs->arrive_b);
+    // While the other segments' fine masses arrive, collect this segment's
+    // entries of the listed coarse bins (a superset of the fine bins the
+    // gather will want) into per-wave LDS regions; the fine publication above
+    // was the region's last reader.
+    constexpr u32 kSpecReg = kSlabCap / kWaves;  // entries per wave region
+    const u32 wave = uni(wave_id());
+    u32 sfill = 0;
+    const bool spec = nlist > 0 && !tiny;
+    if (spec) {
+        const int cb = s.flist[0];
+        const int chi = s.flist[nlist > 1 ? 1 : 0], clo = s.flist[nlist - 1];
+        auto ckey0 = [&](int c) { return (u32)(c * 16 + (int)kFineBase) << kFineShift; };
+        auto ckey1 = [&](int c) {
+            return c == kCoarseBins - 1 ? kInfKey + 1 : (u32)((c + 1) * 16 + (int)kFineBase) << kFineShift;
+        };
+        const u32 kB0 = ckey0(cb), wB = ckey1(cb) - kB0;
+        const u32 kR0 = ckey0(min(clo, chi)), wR = ckey1(max(clo, chi)) - kR0;
+        u64* sreg = sbuf(s) + wave * kSpecReg;
+#pragma unroll
+        for (int d = 0; d < kSlotsFull; ++d) {
+            const u32 i = v0 + d * kBlock + threadIdx.x;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
+                const bool take = (i < v1) & ((b - kB0 < wB) | (b - kR0 < wR));
+                const u64 m = __builtin_amdgcn_ballot_w64(take);
+                if (m) {
+                    if ((i < v1) & ((b - kB0 < wB) | (b - kR0 < wR)))
+                        sreg[min(sfill + mbcnt64(m), kSpecReg - 1)] = composite(b, i * VEC + e);
+                    sfill += (u32)__popcll(m);
+                }
+            }
+        }
+        if (lane_id() == 0) s.gn[32 + wave] = sfill;  // read after the barriers below
+    }
+    const bool ok2 = wait_arrivals(s, &rs->arrive_b, nseg);
     if (!ok2) stat_why(p, r, 4u);
     if (threadIdx.x == 0) {
         if (!ok2)
@@ -2099,8 +2180,16 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             const u32 kD0 = (u32)(fdlo + kFineBase) << kFineShift;
             const u32 kD1 = fdhi == kFineBins - 1 ? kInfKey + 1 : (u32)(fdhi + 1 + kFineBase) << kFineShift;
             const u32 wT = kT1 - kT0, wD = kD1 - kD0;
-            ng = gather_regs<VEC, kSlotsFull>(
-                s, x, v0, v1, [&](u32 b) { return (b - kT0 < wT) | (b - kD0 < wD); }, garea, gcap);
+            auto pred = [&](u32 b) { return (b - kT0 < wT) | (b - kD0 < wD); };
+            bool spec_ok = spec;
+            if (spec) {
+#pragma unroll
+                for (u32 w = 0; w < (u32)kWaves; ++w) spec_ok &= uni(s.gn[32 + w]) <= kSpecReg - 1;
+            }
+            if (spec_ok)
+                ng = filter_regions(s, kSpecReg, sfill, pred, garea, gcap);
+            else
+                ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, pred, garea, gcap);
         }
     } else if (!failed && kind == kInfRow) {
         ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
