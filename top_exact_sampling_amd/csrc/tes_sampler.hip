@@ -1945,6 +1945,119 @@ __device__ __forceinline__ void fine_locate(Smem& s, int nlist, const u64 (&P)[N
     __syncthreads();
 }
 
+// Inclusive prefix sums within each row of 16 lanes (all lanes active).
+__device__ __forceinline__ u64 row16_incl_scan(u64 x) {
+    x += dpp_shift64<0x111>(x);
+    x += dpp_shift64<0x112>(x);
+    x += dpp_shift64<0x114>(x);
+    x += dpp_shift64<0x118>(x);
+    return x;
+}
+
+// The lane whose (lo, lo + w] holds W, for one candidate per lane: its index,
+// or 0 when no lane holds it (inconsistent inputs).
+__device__ __forceinline__ u32 lane_holding(u64 lo, u64 w, u64 W, bool valid) {
+    const u64 m = __builtin_amdgcn_ballot_w64(valid && lo < W && W <= lo + w);
+    return m ? (u32)__builtin_ctzll(m) : 0u;
+}
+
+// One wave, after the first exchange: writes s.cabove (descending exclusive
+// prefix of the summed coarse masses) and finds the coarse bins holding the
+// boundary position T and the draw positions t_lo + 1 and t_hi + 1, where t_hi
+// uses the largest mass the boundary's coarse bin allows.  Results go to
+// s.loc_bin: the boundary bin, the draw range's top and bottom bins.  Lane l
+// owns bins 256 - 4l - i (i < 4), and lane 63 also bin 0.
+__device__ __forceinline__ void coarse_plan_wave(Smem& s, u64 T, u64 u) {
+    const u32 lane = lane_id();
+    u64 m[5], cab[5];
+    int bb[5];
+    u64 loc = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        bb[i] = (i < 4 || lane == 63) ? kCoarseBins - 1 - 4 * (int)lane - i : -1;
+        m[i] = bb[i] >= 0 ? s.coarse[bb[i]] : 0ull;
+        loc += m[i];
+    }
+    u64 a = wave_incl_scan(loc) - loc;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        cab[i] = a;
+        if (bb[i] >= 0) s.cabove[bb[i]] = a;
+        a += m[i];
+    }
+    // Each lane reports its bin holding W (or -1); the wave takes the one lane.
+    auto locate = [&](u64 W, u64& cab_out, u64& m_out) {
+        int hit = -1;
+        u64 hc = 0, hm = 0;
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            if (bb[i] >= 0 && cab[i] < W && W <= cab[i] + m[i]) {
+                hit = bb[i];
+                hc = cab[i];
+                hm = m[i];
+            }
+        const u64 bm = __builtin_amdgcn_ballot_w64(hit >= 0);
+        const u32 L = bm ? (u32)__builtin_ctzll(bm) : 0u;
+        cab_out = read_lane(hc, L);
+        m_out = read_lane(hm, L);
+        return bm ? (int)__builtin_amdgcn_readlane(hit, (int)L) : 0;
+    };
+    u64 cT, mT, c1, m1;
+    const int cbT = locate(T, cT, mT);
+    const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, cT + mT);
+    const int chi = locate(t_lo + 1, c1, m1);
+    const int clo = locate(t_hi + 1, c1, m1);
+    if (lane == 0) {
+        s.loc_bin[0] = cbT;
+        s.loc_bin[1] = chi;
+        s.loc_bin[2] = clo;
+    }
+}
+
+// One wave, after the second exchange: the fine bin holding T (in the first
+// listed coarse bin) with the mass above it, then the fine bins holding the
+// draw positions t_lo + 1 and t_hi + 1 (t_hi from the boundary fine bin's
+// largest mass).  Each row of 16 lanes scans the fine masses of one listed
+// coarse bin, highest fine bin first.  Results: s.loc_bin[0..2] = fbT, fine
+// bin of t_lo + 1, of t_hi + 1 (-1 if not found), s.loc_above[0] = mass above
+// fbT.
+__device__ __forceinline__ void fine_plan_wave(Smem& s, int nlist, u64 T, u64 u) {
+    const u32 lane = lane_id();
+    const int f = 15 - (int)(lane & 15u);  // fine bin within the coarse bin
+    const u32 row = lane >> 4;
+    // Pass 1: row 0 scans the boundary's coarse bin (list entry 0).
+    const int cb0 = s.flist[0];
+    const u64 w0 = row == 0 ? s.finem[f] : 0ull;
+    const u64 a0 = s.cabove[cb0] + row16_incl_scan(w0) - w0;
+    const u64 bm0 = __builtin_amdgcn_ballot_w64(row == 0 && a0 < T && T <= a0 + w0);
+    const u32 L0 = bm0 ? (u32)__builtin_ctzll(bm0) : 0u;
+    const int fbT = bm0 ? cb0 * 16 + (15 - (int)L0) : -1;
+    const u64 above_f = read_lane(a0, L0);
+    const u64 U = above_f + read_lane(w0, L0);
+    const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
+    // The list entries whose coarse bins hold the two draw positions.
+    const u64 W1 = t_lo + 1, W2 = t_hi + 1;
+    const bool lj = (int)lane < nlist;
+    const int cbl = lj ? s.flist[lane] : 0;
+    const u64 cl = lj ? s.cabove[cbl] : 0ull, ml = lj ? s.coarse[cbl] : 0ull;
+    const u64 b1 = __builtin_amdgcn_ballot_w64(lj && cl < W1 && W1 <= cl + ml);
+    const u64 b2 = __builtin_amdgcn_ballot_w64(lj && cl < W2 && W2 <= cl + ml);
+    const int j1 = b1 ? (int)__builtin_ctzll(b1) : -1, j2 = b2 ? (int)__builtin_ctzll(b2) : -1;
+    // Pass 2: row 1 scans list entry j1 for W1, row 2 entry j2 for W2.
+    const int jr = row == 1 ? j1 : (row == 2 ? j2 : -1);
+    const u64 Wr = row == 1 ? W1 : W2;
+    const u64 wr = jr >= 0 ? s.finem[jr * 16 + f] : 0ull;
+    const u64 ar = (jr >= 0 ? s.cabove[s.flist[jr]] : 0ull) + row16_incl_scan(wr) - wr;
+    const u64 bm = __builtin_amdgcn_ballot_w64(jr >= 0 && ar < Wr && Wr <= ar + wr);
+    const u64 bm1 = bm & 0x00000000FFFF0000ull, bm2 = bm & 0x0000FFFF00000000ull;
+    if (lane == 0) {
+        s.loc_bin[0] = fbT;
+        s.loc_above[0] = above_f;
+        s.loc_bin[1] = bm1 ? s.flist[j1] * 16 + (15 - ((int)__builtin_ctzll(bm1) - 16)) : -1;
+        s.loc_bin[2] = bm2 ? s.flist[j2] * 16 + (15 - ((int)__builtin_ctzll(bm2) - 32)) : -1;
+    }
+}
+
 template <int VEC>
 __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
                                          u64 above_f, int fbT, int nlist, bool failed);
@@ -2048,14 +2161,6 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     __syncthreads();
     const u64 Mt = uni(s.csum[0]);
     const u64 nit = uni(s.csum[1]);
-    {
-        // cabove[b] = mass of the coarse bins above b (descending exclusive scan).
-        const int b = kCoarseBins - 1 - (int)threadIdx.x;
-        const u64 w = b >= 0 ? s.coarse[b] : 0;
-        const u64 ex = block_excl_scan(s, w);
-        if (b >= 0) s.cabove[b] = ex;
-        __syncthreads();
-    }
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     const u32 kind = nit > 0 ? kInfRow : (Mt == 0 ? kZeroRow : kNormal);
@@ -2063,14 +2168,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     int nlist = 0;
     bool decidable = ok;
     if (ok && kind == kNormal) {
-        int c1[1];
-        coarse_locate(s, {T}, c1);
-        const int cbT = c1[0];
-        const u64 U = uni(s.cabove[cbT]) + uni(s.coarse[cbT]);
-        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
-        int c2[2];
-        coarse_locate(s, {t_lo + 1, t_hi + 1}, c2);
-        const int chi = c2[0], clo = c2[1];
+        if (wave_id() == 0) coarse_plan_wave(s, T, u);
+        __syncthreads();
+        const int cbT = (int)uni((u32)s.loc_bin[0]);
+        const int chi = (int)uni((u32)s.loc_bin[1]), clo = (int)uni((u32)s.loc_bin[2]);
         // Listed coarse bins: the boundary bin, then the draw range.
         const int cnt = 1 + (chi - clo + 1) - ((cbT >= clo && cbT <= chi) ? 1 : 0);
         if (cnt > dmax) {
@@ -2155,17 +2256,11 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         sum_words(reinterpret_cast<const u64*>(pub_f(p, r, 0)), sizeof(PubF) / 8, nseg,
                   (u32)nlist * 16, [&](u32 i, u64 v) { s.finem[i] = v; });
         __syncthreads();
-        int f1[1];
-        u64 a1[1];
-        fine_locate(s, nlist, {T}, f1, a1);
-        fbT = f1[0];
-        above_f = a1[0];
-        const u64 U = fbT >= 0 ? above_f + uni(s.finem[fbT - s.flist[0] * 16]) : 0;
-        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, U);
-        int f2[2];
-        u64 a2[2];
-        fine_locate(s, nlist, {t_lo + 1, t_hi + 1}, f2, a2);
-        const int fdhi = f2[0], fdlo = f2[1];
+        if (wave_id() == 0) fine_plan_wave(s, nlist, T, u);
+        __syncthreads();
+        fbT = (int)uni((u32)s.loc_bin[0]);
+        above_f = uni(s.loc_above[0]);
+        const int fdhi = (int)uni((u32)s.loc_bin[1]), fdlo = (int)uni((u32)s.loc_bin[2]);
         if (fbT < 0 || fdhi < 0 || fdlo < 0) {
             // Cannot happen for consistent exchanges; decide by the slow path.
             stat_why(p, r, 8u);
