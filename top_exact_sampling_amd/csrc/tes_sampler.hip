@@ -1080,10 +1080,12 @@ __device__ __forceinline__ u64 wave_sort_desc(u64 v, u32 n) {
 // and the packed total is returned.
 template <int J>
 __device__ __forceinline__ u64 bin_scatter(Smem& s, const u64 (&c)[J], const int (&dig)[J],
-                                           u64* out) {
+                                           u64* out, bool cleared = false) {
     u64* tab = shtab(s);
-    for (int b = threadIdx.x; b < kTabBins; b += kBlock) tab[b] = 0;
-    __syncthreads();
+    if (!cleared) {  // (a caller that cleared the table earlier has a barrier since)
+        for (int b = threadIdx.x; b < kTabBins; b += kBlock) tab[b] = 0;
+        __syncthreads();
+    }
     u32 slot[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -1172,20 +1174,26 @@ struct BinView {
 // in another order, when a bin it needs holds more than 64 entries or the
 // support holds +inf entries or has no mass; the caller then sorts.
 __device__ __noinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         Outcome& o) {
+                                         Outcome& o, u32 wfill) {
     constexpr int J = kSlabCap / kBlock;
+    static_assert(J * 64 == kSlabCap / kWaves, "a wave region is J entries per lane");
     const u32 tbin = tkey >> kFineShift;
+    const bool regions = wfill != ~0u;
     u64 c[J];
     int dig[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const u32 i = threadIdx.x + (u32)j * kBlock;
-        c[j] = i < n ? sbuf(s)[i] : 0ull;
+        // Packed buffer: thread t takes t + 512 j.  Unpacked wave regions (the
+        // stream's, table already cleared): lane l takes l + 64 j of its wave's.
+        const u32 i = regions ? wave_id() * (kSlabCap / kWaves) + lane_id() + 64u * j
+                              : threadIdx.x + (u32)j * kBlock;
+        const bool in = regions ? lane_id() + 64u * j < wfill : i < n;
+        c[j] = in ? sbuf(s)[i] : 0ull;
         const u32 d = (comp_key(c[j]) >> kFineShift) - tbin;
-        dig[j] = i < n ? (int)(d < (u32)kTabBins ? d : (u32)kTabBins - 1) : -1;
+        dig[j] = in ? (int)(d < (u32)kTabBins ? d : (u32)kTabBins - 1) : -1;
     }
     __syncthreads();  // the scatter overwrites the buffer
-    const u64 total = bin_scatter<J>(s, c, dig, sbuf(s));
+    const u64 total = bin_scatter<J>(s, c, dig, sbuf(s), regions);
     if (wave_id() == 0) {
         BinView bv{shtab(s), sbuf(s), total};
         // +inf entries, the largest keys, can only sit in the top bin.
@@ -1635,7 +1643,8 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // Top-k rows (2 <= k <= 1024)
 // ---------------------------------------------------------------------------
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u);
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+                                         u32 wfill);
 
 // Streams its part of the row (the whole row, or half of it when the row is
 // split between two workgroups) once and keeps, in the LDS buffer, every entry
@@ -1677,6 +1686,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     const u32 last = nvec - 1;
     u32* hist = reinterpret_cast<u32*>(s.region);  // sample counts per fine bin
     for (int b = threadIdx.x; b < kFineBins; b += kBlock) hist[b] = 0;
+    // The binned finish's table (disjoint from the sample counts and the
+    // candidate buffer) is cleared here, under the barriers that follow.
+    for (int b = threadIdx.x; b < kTabBins; b += kBlock) shtab(s)[b] = 0;
     __syncthreads();
     VT pf[kStreamDepth];
 #pragma unroll
@@ -1774,23 +1786,29 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         fill += cw;
         before += w < wave ? cw : 0u;
     }
-    constexpr int kPerLane = kRegion / 64;
-    u64 mine[kPerLane];
-    const u32 nmine = wfill < kRegion ? wfill : kRegion;
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-        const u32 i = lane_id() + 64u * j;
-        mine[j] = i < nmine ? reg[i] : 0ull;
-    }
-    __syncthreads();
-    if (!over) {
+    // A whole row headed for the binned finish leaves its entries in the
+    // regions (that finish reads them there); otherwise the regions are
+    // packed together.
+    const bool direct = S == 1 && !over && fill >= k && !(p.flags & TES_FLAG_TINY_BUFFER);
+    if (!direct) {
+        constexpr int kPerLane = kRegion / 64;
+        u64 mine[kPerLane];
+        const u32 nmine = wfill < kRegion ? wfill : kRegion;
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
             const u32 i = lane_id() + 64u * j;
-            if (i < nmine) sbuf(s)[before + i] = mine[j];
+            mine[j] = i < nmine ? reg[i] : 0ull;
         }
+        __syncthreads();
+        if (!over) {
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) {
+                const u32 i = lane_id() + 64u * j;
+                if (i < nmine) sbuf(s)[before + i] = mine[j];
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     tq = stat_phase(p, r, 13, tq);
     stat_phase(p, r, 8, tp);
     const u64 P = fixed_p(top_p);
@@ -1830,7 +1848,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         over = over || (u32)block_sum(s, above) < k;  // also orders the joined buffer
     }
     if (!over && fill >= k) {
-        slab_finish<VEC>(s, r, fill, k, tmin, P, u);
+        slab_finish<VEC>(s, r, fill, k, tmin, P, u, direct ? wfill : ~0u);
     } else {
         const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
                                            kSelCap);
@@ -1844,13 +1862,16 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // the best k when it holds more than a sort takes, sort it descending (padded
 // with zeros, which sort last) and finish on the first k positions.
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u) {
+__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+                                         u32 wfill) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
+    // wfill != ~0u: the entries are still in the stream's wave regions (this
+    // wave's count), and the binned finish packs them.
     if (!(p.flags & TES_FLAG_TINY_BUFFER) && tkey > 0) {
         Outcome ob;
-        if (binned_topk(s, n, k, tkey, P, u, ob)) {
+        if (binned_topk(s, n, k, tkey, P, u, ob, wfill)) {
             stat_phase(p, r, 9, tp);
             finish_row(s, p, r, ob, kPathSlab, gathered);
             return;
