@@ -54,6 +54,7 @@
 #include <stdint.h>
 
 #include <cstring>
+#include <type_traits>
 #include <new>
 
 #include "tes_sampler.h"
@@ -1696,6 +1697,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         pf[d] = ld_stream(&rv[min(d * kBlock + threadIdx.x, last)]);
         __builtin_amdgcn_sched_barrier(0);  // issue in consumption order
     }
+    // The partial last step's vector (if any), loaded early.
+    const VT tailv = ld_stream(&rv[min((nvec / kBlock) * kBlock + threadIdx.x, last)]);
+    __builtin_amdgcn_sched_barrier(0);
     // The sample.
     u32 nmass = 0;
 #pragma unroll
@@ -1742,38 +1746,44 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     // Appends this lane's passing entries of one vector.  Passing bits are
     // non-negative as signed integers, so a vector whose largest signed bits
     // are below tkey has none; a wave with no such vector skips the rest.
-    auto append = [&](const VT& x, u32 iv) {
-        const bool valid = iv < nvec;
+    // (MASKED: lanes past the end of the part hold a copy of its last vector
+    // and must append nothing.)
+    auto append = [&](auto masked, const VT& x, u32 iv) {
+        constexpr bool kMasked = decltype(masked)::value;
+        const bool valid = !kMasked || iv < nvec;
         int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
 #pragma unroll
         for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
-        const u64 vm = __builtin_amdgcn_ballot_w64(valid);
-        if ((__builtin_amdgcn_ballot_w64(mx >= (int)tkey) & vm) == 0) return;
+        if (__builtin_amdgcn_ballot_w64(valid & (mx >= (int)tkey)) == 0) return;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
             // Passing bits are keys: no sanitising.
-            const u64 m = __builtin_amdgcn_ballot_w64(b - tkey <= span) & vm;
+            const u64 m = __builtin_amdgcn_ballot_w64(valid & (b - tkey <= span));
             if (m) {
                 // Past the region's last slot, entries land on that slot and
                 // the count reports the overflow.
-                if ((b - tkey <= span) & valid)
+                if (valid & (b - tkey <= span))
                     reg[min(wfill + mbcnt64(m), kRegion - 1)] = composite(b, (v0 + iv) * VEC + e);
                 wfill += (u32)__popcll(m);
             }
         }
     };
-    // Every step issues exactly one refill load (clamped into the row), so the
-    // compiler can count the loads in flight and wait for one at a time; steps
-    // past the end of the row append nothing.
-    for (u32 r0 = 0; r0 < nsteps; r0 += kStreamDepth) {
+    // Steps [0, nfull) have every lane inside the part; a partial last step
+    // (its vector loaded up front) is appended after the loop.  Every step
+    // issues exactly one refill load (clamped into the part), so the compiler
+    // can count the loads in flight and wait for one at a time; steps from
+    // nfull on append nothing in the loop.
+    const u32 nfull = nvec / kBlock;
+    for (u32 r0 = 0; r0 < nfull; r0 += kStreamDepth) {
 #pragma unroll
         for (u32 d = 0; d < kStreamDepth; ++d) {
-            append(pf[d], (r0 + d) * kBlock + threadIdx.x);
+            if (r0 + d < nfull) append(std::false_type{}, pf[d], (r0 + d) * kBlock + threadIdx.x);
             pf[d] = ld_stream(&rv[min((r0 + d + kStreamDepth) * kBlock + threadIdx.x, last)]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (nfull * kBlock < nvec) append(std::true_type{}, tailv, nfull * kBlock + threadIdx.x);
     // Pack the regions: wave w's entries move to the offset of the waves below.
     if (lane_id() == 0) s.gn[wave] = wfill;
     __syncthreads();
