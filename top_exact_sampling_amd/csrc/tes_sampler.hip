@@ -244,7 +244,7 @@ struct Smem {
     alignas(16) unsigned char region[kRegionBytes];
     u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
     u64 csum[2];               // summed mass and +inf count of a top-p-only row
-    u64 loc_above[4];          // results of coarse_locate / fine_locate
+    u64 loc_above[4];          // results of the bin lookups (coarse and fine plans, fine_locate)
     int loc_bin[4];
     u32 gn[kMaxSegWs];         // entries each segment of a top-p-only row gathered
     u64 cabove[kCoarseBins];   // mass of the coarse bins above each bin
@@ -1920,27 +1920,6 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey,
 // ---------------------------------------------------------------------------
 // Top-p-only rows (k >= V)
 // ---------------------------------------------------------------------------
-// Coarse bins holding descending mass positions P[n] (1 <= P[n] <= total)
-// of the summed coarse histogram and its descending exclusive prefix: bin b
-// holds P when cabove[b] < P <= cabove[b] + coarse[b], which is true of
-// exactly one bin.  One thread per bin; the results are workgroup-uniform.
-template <int N>
-__device__ __forceinline__ void coarse_locate(Smem& s, const u64 (&P)[N], int (&bin)[N]) {
-    if (threadIdx.x < (u32)N) s.loc_bin[threadIdx.x] = 0;
-    __syncthreads();
-    const int b = (int)threadIdx.x;
-    if (b < kCoarseBins) {
-        const u64 lo = s.cabove[b], hi = lo + s.coarse[b];
-#pragma unroll
-        for (int n = 0; n < N; ++n)
-            if (lo < P[n] && P[n] <= hi) s.loc_bin[n] = b;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < N; ++n) bin[n] = (int)uni((u32)s.loc_bin[n]);
-    __syncthreads();
-}
-
 // Fine bins holding descending mass positions P[n], looked up among the
 // exchanged fine bins of the listed coarse bins (bin -1 when the position's
 // coarse bin is not listed); above[n] receives the mass of all higher fine
@@ -1983,13 +1962,6 @@ __device__ __forceinline__ u64 row16_incl_scan(u64 x) {
     x += dpp_shift64<0x114>(x);
     x += dpp_shift64<0x118>(x);
     return x;
-}
-
-// The lane whose (lo, lo + w] holds W, for one candidate per lane: its index,
-// or 0 when no lane holds it (inconsistent inputs).
-__device__ __forceinline__ u32 lane_holding(u64 lo, u64 w, u64 W, bool valid) {
-    const u64 m = __builtin_amdgcn_ballot_w64(valid && lo < W && W <= lo + w);
-    return m ? (u32)__builtin_ctzll(m) : 0u;
 }
 
 // One wave, after the first exchange: writes s.cabove (descending exclusive
