@@ -263,3 +263,65 @@ def test_zero_batch_and_argument_errors(sampler, torch_cuda):
     assert tes.topk_topp_sample(h, *bad) == tes.TES_ERR_TOO_LARGE
     assert tes.topk_topp_sample(h, *args) == tes.TES_OK
     torch.cuda.synchronize()
+
+
+def _split_batch(V, rng):
+    """Rows whose decisive entries straddle the point where a row split
+    between two workgroups is cut (half the row's 16-byte vectors)."""
+    cut = ((V // 4 + 1) // 2) * 4
+    rows, ks, ps, names = [], [], [], []
+
+    def add(x, k, p, name):
+        rows.append(np.asarray(x, np.float32))
+        ks.append(k)
+        ps.append(p)
+        names.append(name)
+
+    base = (rng.random(V) * 1e-7).astype(np.float32)
+    tie = base.copy()
+    tie[cut - 300: cut] = np.float32(1e-3)
+    tie[cut: cut + 300] = np.float32(1e-3)
+    tie[V - 200:] = np.float32(1e-3)
+    for k in (1, 2, 299, 300, 301, 600, 700, 1024):
+        add(tie, k, 1.0, "ties across the cut k%d" % k)
+        add(tie, k, 0.3, "ties across the cut k%d p0.3" % k)
+    two = base.copy()
+    two[cut - 1] = np.float32(0.25)
+    two[cut] = np.float32(0.25)
+    add(two, 1, 1.0, "greedy tie at the cut")
+    add(two, 2, 0.9, "k2 tie at the cut")
+    second = base.copy()
+    second[cut + 5: cut + 905] = (0.5 + rng.random(900)).astype(np.float32) * 1e-3
+    for k in (1, 10, 512, 1024):
+        add(second, k, 0.8, "mass in the second half k%d" % k)
+    first = second[::-1].copy()
+    for k in (1, 10, 512, 1024):
+        add(first, k, 0.8, "mass in the first half k%d" % k)
+    inf2 = base.copy()
+    inf2[[3, cut + 7, V - 1]] = np.inf
+    for k in (1, 2, 3, 50):
+        add(inf2, k, 0.5, "inf in both halves k%d" % k)
+    nan2 = base.copy()
+    nan2[cut + 11] = np.nan
+    nan2[cut - 11] = np.float32(0.1)
+    add(nan2, 1, 1.0, "greedy with NaN in the second half")
+    add(nan2, 64, 0.9, "k64 with NaN in the second half")
+    zero = np.zeros(V, np.float32)
+    zero[cut + 1] = -1.0
+    add(zero, 1, 1.0, "greedy on a zero row")
+    add(zero, 8, 1.0, "k8 on a zero row")
+    return np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32), names
+
+
+@pytest.mark.parametrize("V", [151936, 65540])
+def test_split_rows(sampler, orc, V):
+    # A small batch leaves room for every top-k and greedy row to be split
+    # between two workgroups; the stats word [2] says how many ran the row.
+    rng = np.random.default_rng(V + 5)
+    probs, ks, ps, names = _split_batch(V, rng)
+    log("[gpu] split rows V=%d rows=%d" % (V, len(names)))
+    gtok, gren = run_gpu(sampler, probs, ks, ps, 21, 4, renorm=True)
+    st = sampler.stats(len(names))
+    assert np.all(st[:, 2] == 2), "rows not split: %s" % [
+        names[i] for i in np.flatnonzero(st[:, 2] != 2)]
+    assert_parity(orc, probs, ks, ps, 21, 4, gtok, gren, "split rows V=%d" % V)
