@@ -116,10 +116,15 @@ const char *sampler_status_string(int status);
  *       1 top-p-only row resolved from exchanged histograms and gathered bins,
  *       2 top-p-only row that fell back to whole-row passes,
  *       3 row resolved by whole-row passes (1024 < k < V, or forced),
- *       4 greedy row (k = 1);
+ *       4 greedy row (k = 1),
+ *       5 top-k row decided by one compacting pass over the whole row
+ *         (its sampled threshold could not decide it: too few sampled
+ *         entries with a mass, or a run of equal values that overflowed
+ *         the candidate buffer);
  *   [1] kind: 0 normal, 1 +inf row, 2 zero-mass row;
  *   [2] segments the row was cut into;
- *   [3] candidate-buffer compactions (path 0) or passes over the row (path 3);
+ *   [3] candidate-buffer compactions (paths 0 and 5) or passes over the row
+ *       (path 3);
  *   [4] entries gathered for the final selects (paths 0, 1, 2);
  *   [5] device wall clock when the row was resolved (low 32 bits);
  *   [6] 0xFFFFFFFF minus the earliest wall clock at which a segment of the

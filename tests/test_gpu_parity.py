@@ -325,3 +325,83 @@ def test_split_rows(sampler, orc, V):
     assert np.all(st[:, 2] == 2), "rows not split: %s" % [
         names[i] for i in np.flatnonzero(st[:, 2] != 2)]
     assert_parity(orc, probs, ks, ps, 21, 4, gtok, gren, "split rows V=%d" % V)
+
+
+def _restream_batch(V, rng):
+    """Top-k rows whose sampled threshold cannot decide them: too few sampled
+    entries with a mass, or a run of equal values at the threshold longer than
+    the candidate buffer."""
+    rows, ks, ps, names = [], [], [], []
+
+    def add(x, k, p, name):
+        rows.append(np.asarray(x, np.float32))
+        ks.append(k)
+        ps.append(p)
+        names.append(name)
+
+    n_pos = min(V // 2, 4500)
+    tail = np.zeros(V, np.float32)
+    tail[V - n_pos:] = (rng.random(n_pos) + 0.5).astype(np.float32) / n_pos
+    for k in (2, 700, 1024):
+        add(tail, k, 0.9, "positives only in the tail k%d" % k)
+    few_tail = np.zeros(V, np.float32)
+    few_tail[V - 300:] = np.float32(1.0 / 300)
+    few_tail[V - 300: V - 150] = np.float32(0.5 / 300)
+    for k in (299, 300, 301, 500, 1024):
+        add(few_tail, k, 0.95, "300 tail positives k%d" % k)
+    inf_tail = few_tail.copy()
+    inf_tail[[V - 7, V - 3]] = np.inf
+    add(inf_tail, 500, 0.9, "two inf among tail positives k500")
+    tiny_tail = np.zeros(V, np.float32)
+    tiny_tail[V - 50:] = np.float32(1e-12)  # positive keys without a mass
+    tiny_tail[[5, 9]] = -1.0
+    for k in (20, 50, 51, 200):
+        add(tiny_tail, k, 0.9, "massless tail k%d" % k)
+    for k in (2, 500, 1024):
+        add(np.zeros(V, np.float32), k, 0.9, "zero row k%d" % k)
+    negz = np.zeros(V, np.float32)
+    negz[: min(V, 1000)] = -0.0
+    negz[min(V, 1000): min(V, 1003)] = np.nan
+    add(negz, 64, 0.9, "-0.0 and NaN prefix k64")
+    tie = np.full(V, np.float32(1e-9), np.float32)
+    nt = min(V // 2, 6000)
+    tie[rng.choice(V, nt, replace=False)] = np.float32(1e-4)
+    tie[rng.choice(V, 40, replace=False)] = np.float32(2e-3)
+    for k in (41, 500, 1024):
+        for p in (0.5, 1.0):
+            add(tie, k, p, "6000-long tie at the threshold k%d p%g" % (k, p))
+    q = np.floor(rng.random(V) ** 8 * 64) / 2**20  # few distinct values, many zeros
+    q = (q / q.sum()).astype(np.float32)
+    for k in (1, 10, 700, 1024):
+        add(q, k, 0.8, "quantised k%d" % k)
+    return np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32), names
+
+
+@pytest.mark.parametrize("V", [151936, 128256, 20000])
+def test_restream_rows(sampler, orc, V):
+    rng = np.random.default_rng(V + 29)
+    probs, ks, ps, names = _restream_batch(V, rng)
+    log("[gpu] restream rows V=%d rows=%d" % (V, len(names)))
+    gtok, gren = run_gpu(sampler, probs, ks, ps, 13, 2, renorm=True)
+    st = sampler.stats(len(names))
+    log("[gpu]   paths %s" % np.bincount(st[:, 0], minlength=6).tolist())
+    assert_parity(orc, probs, ks, ps, 13, 2, gtok, gren, "restream rows V=%d" % V)
+    assert (st[:, 0] == 5).sum() >= 8, "the compacting pass did not run"
+
+
+def test_wide_topp_bins_stay_on_the_fast_path(sampler, orc):
+    # High-entropy rows at the speculative-verify shape gather more boundary
+    # and draw entries than one buffer holds; the finish takes them one fine
+    # bin at a time instead of re-reading the row.
+    w = wl(5)
+    rows = np.arange(0, w.B, 8)
+    probs = np.ascontiguousarray(w.probs[rows])
+    log("[gpu] wide top-p bins rows=%d" % rows.size)
+    gtok, gren = run_gpu(sampler, probs, w.top_k[rows], w.top_p[rows], w.seed, w.offset,
+                         renorm=True)
+    st = sampler.stats(rows.size)
+    log("[gpu]   paths %s gathered max %d" % (np.bincount(st[:, 0], minlength=6).tolist(),
+                                             st[:, 4].max()))
+    assert_parity(orc, probs, w.top_k[rows], w.top_p[rows], w.seed, w.offset, gtok, gren,
+                  "wide top-p bins")
+    assert np.all(st[:, 0] == 1), "rows left the fast path: %s" % np.flatnonzero(st[:, 0] != 1)

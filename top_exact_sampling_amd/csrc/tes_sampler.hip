@@ -653,6 +653,37 @@ __device__ bool arrive_last(Smem& s, u32* ticket, u32 n) {
     return last;
 }
 
+// Adds one to hc[d] (and, for mass tables, q to hm[d]) for every lane with
+// pred set.  When at least 8 active lanes share the first active lane's digit
+// (ties, runs of zeros), those lanes are summed across the wave and added by
+// one lane: LDS atomics to one address from many lanes are serialised, which
+// made rows of equal values orders of magnitude slower than others.  Must be
+// reached by whole waves.
+__device__ __forceinline__ void hist_add(u32* hc, u64* hm, bool mass, bool pred, u32 d, u64 q) {
+    const u64 act = __ballot(pred);
+    if (act == 0) return;
+    const int lead = __builtin_ctzll(act);
+    const u32 d0 = (u32)__builtin_amdgcn_readlane((int)d, lead);
+    const u64 sm = __ballot(pred && d == d0);
+    if (__popcll(sm) < 8) {
+        if (pred) {
+            atomicAdd(&hc[d], 1u);
+            if (mass) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)q);
+        }
+        return;
+    }
+    const bool same = pred && d == d0;
+    if (pred && !same) {
+        atomicAdd(&hc[d], 1u);
+        if (mass) atomicAdd((unsigned long long*)&hm[d], (unsigned long long)q);
+    }
+    const u64 qs = mass ? wave_sum(same ? q : 0ull) : 0ull;
+    if ((int)lane_id() == lead) {
+        atomicAdd(&hc[d0], (u32)__popcll(sm));
+        if (mass && qs) atomicAdd((unsigned long long*)&hm[d0], (unsigned long long)qs);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Histogram search and radix selects
 // ---------------------------------------------------------------------------
@@ -717,14 +748,11 @@ __device__ Sel radix_select(Smem& s, u32 n, Get get, u64 W, bool mass, u64 lo, u
             if (mass) hmw[b] = 0;
         }
         __syncthreads();
-        for (u32 i = threadIdx.x; i < n; i += kBlock) {
-            u64 c;
-            if (get(i, c) && c >= lo && c < hi && (c & hm) == prefix) {
-                const u32 d = (u32)(c >> sh) & dmask;
-                atomicAdd(&hc[d], 1u);
-                if (mass) atomicAdd((unsigned long long*)&hmw[d],
-                                    (unsigned long long)key_mass(comp_key(c)));
-            }
+        for (u32 i0 = 0; i0 < n; i0 += kBlock) {
+            const u32 i = i0 + threadIdx.x;
+            u64 c = 0;
+            const bool in = i < n && get(i, c) && c >= lo && c < hi && (c & hm) == prefix;
+            hist_add(hc, hmw, mass, in, (u32)(c >> sh) & dmask, mass ? key_mass(comp_key(c)) : 0ull);
         }
         __syncthreads();
         auto cf = [&](int b) { return (u64)hc[b]; };
@@ -1167,9 +1195,9 @@ struct BinView {
 };
 
 // Top-k finish from the candidate buffer sbuf(s)[0, n), k <= n <= kSlabCap,
-// which holds every entry of the row with key >= tkey (tkey > 0, a multiple of
-// 2^16).  Bins are 1/128-octave key ranges counted from tkey (bin 2047 takes
-// every key 16 octaves or more above it).  The support's k-th entry, the top-p
+// which holds every entry of the row with key >= tkey (0 < tkey <= 1.0, a
+// multiple of 2^16).  Bins are 1/128-octave key ranges counted from tkey (bin
+// 2047 takes every key 16 octaves or more above it, +inf included).  The support's k-th entry, the top-p
 // boundary and the drawn entry are each located in the table and resolved by
 // sorting their bin.  Returns false, with the buffer holding the same entries
 // in another order, when a bin it needs holds more than 64 entries or the
@@ -1438,12 +1466,8 @@ __device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass,
         __syncthreads();
         for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
             const u64 c = composite(key, idx);
-            if (valid && c >= lo && (c & hm) == prefix) {
-                const u32 d = (u32)(c >> sh) & dmask;
-                atomicAdd(&shcnt(s)[d], 1u);
-                if (mass) atomicAdd((unsigned long long*)&shmass(s)[d],
-                                    (unsigned long long)key_mass(key));
-            }
+            hist_add(shcnt(s), shmass(s), mass, valid && c >= lo && (c & hm) == prefix,
+                     (u32)(c >> sh) & dmask, mass ? key_mass(key) : 0ull);
         });
         if (threadIdx.x == 0) ++s.npass;
         __syncthreads();
@@ -1645,7 +1669,106 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // ---------------------------------------------------------------------------
 template <int VEC>
 __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         u32 wfill);
+                                         u32 wfill, u32 path = kPathSlab);
+
+// The smallest index of the row whose key is zero (NaN, negative, -0.0 or
+// +0.0), read in steps of one vector per thread until a step holds one; ~0u
+// when there is none.
+template <int VEC>
+__device__ u32 first_zero_index(Smem& s, const float* __restrict__ row, u32 nvec) {
+    typedef typename VecT<VEC>::T VT;
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
+    for (u32 v0 = 0; v0 < nvec; v0 += kBlock) {
+        const u32 iv = v0 + threadIdx.x;
+        u64 best = ~0ull;
+        if (iv < nvec) {
+            const VT x = ld_g(&rv[iv]);
+#pragma unroll
+            for (int e = VEC - 1; e >= 0; --e)
+                if (sanitize(__float_as_uint(VecT<VEC>::get(x, e))) == 0u) best = (u64)iv * VEC + e;
+        }
+        best = block_min(s, best);
+        if (best != ~0ull) return (u32)best;
+    }
+    return ~0u;
+}
+
+// Exact single pass over the whole row for a top-k row (k <= kSlabMaxK) that
+// its sampled threshold could not decide: a sample with too few entries with a
+// mass, a candidate buffer that overflowed (long runs of equal values at the
+// threshold) or a split row whose halves did not join.  Every entry with key
+// >= theta0 (theta0 >= 1) is appended to the LDS buffer; whenever the buffer
+// could not take one more step, it is cut to the best k so far (a radix select)
+// and the threshold rises to one above the k-th key: the row is read in index
+// order, so a later entry with that key has a larger index and ranks below all
+// k.  The buffer then holds the row's best k among keys >= theta0, or, when
+// fewer exist (theta0 = 1), every entry with a positive key.  A support that
+// also reaches zero keys takes the lowest-indexed zeros after them: they carry
+// no mass, so they are never kept or drawn, and only a support without mass
+// looks at them (its token is the smallest index in the support).
+template <int VEC>
+__device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u64 P, u64 u) {
+    const Params p = params_from(s);
+    typedef typename VecT<VEC>::T VT;
+    const float* row = p.probs + (size_t)r * p.V;
+    constexpr u32 kHigh = kSlabCap - kBlock * VEC;  // room for one more step
+    static_assert(kHigh >= kSlabMaxK, "a cut always has k entries to keep");
+    u32 theta = theta0;  // workgroup-uniform
+    bool closed = false;  // the k-th best so far is +inf: nothing later can enter
+    u32 cuts = 0;
+    if (threadIdx.x == 0) s.ctr[3] = 0;
+    __syncthreads();
+    for_each_vec<VEC, kPassDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
+        const u32 span = kInfKey - theta;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+            wave_append(sbuf(s), valid && !closed && b - theta <= span, composite(b, iv * VEC + e),
+                        &s.ctr[3], 0, kSlabCap);
+        }
+        __syncthreads();
+        const u32 n = uni(s.ctr[3]);
+        if (n > kHigh) {
+            __syncthreads();  // every thread has read the count
+            const u64 ck = select_slab(s, n, k);
+            const u32 kept = keep_above(s, n, ck);
+            const u32 kk = comp_key(ck);
+            closed = kk == kInfKey;
+            theta = closed ? kInfKey : kk + 1;
+            ++cuts;
+            if (threadIdx.x == 0) s.ctr[3] = kept;
+            __syncthreads();
+        }
+    });
+    __syncthreads();
+    const u32 n = uni(s.ctr[3]);
+    __syncthreads();
+    stat_add(p, r, 3, cuts);
+    u64 mn = ~0ull, mass = 0, midx = ~0ull;
+    for (u32 i = threadIdx.x; i < n; i += kBlock) {
+        const u64 c = sbuf(s)[i];
+        mn = c < mn ? c : mn;
+        mass += key_mass(comp_key(c));
+        midx = comp_index(c) < midx ? comp_index(c) : midx;
+    }
+    mn = block_min(s, mn);
+    mass = block_sum(s, mass);
+    // The binned finish's base: at most 1.0, so that +inf entries land in its
+    // top bin, where it looks for them.
+    const u32 tkey = n ? min(comp_key(mn), kOneKey) & ~0xFFFFu : 0u;
+    if (n >= k || (n > 0 && mass > 0)) {
+        // n < k: the zeros that complete the support change nothing.
+        slab_finish<VEC>(s, r, n, n >= k ? k : n, tkey, P, u, ~0u, kPathSlabFallback);
+        return;
+    }
+    // No mass in the support: its smallest index (n < k, so zeros complete it).
+    midx = block_min(s, midx);
+    const u32 z = first_zero_index<VEC>(s, row, p.nvec);
+    Outcome o{};
+    o.kind = kZeroRow;
+    o.token = (u32)(midx < (u64)z ? midx : (u64)z);
+    finish_row(s, p, r, o, kPathSlabFallback, n);
+}
 
 // Streams its part of the row (the whole row, or half of it when the row is
 // split between two workgroups) once and keeps, in the LDS buffer, every entry
@@ -1730,11 +1853,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the half reports itself unusable
     if (no_tkey && S == 1) {
         // Fewer than j sampled entries have a mass (a row of mostly zeros, or
-        // a short row with fewer than k): whole-row passes decide.
-        const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k,
-                                           fixed_p(top_p), philox_uniform(p.seed, p.row_base + r, p.offset),
-                                           kSelCap);
-        finish_row(s, p, r, o, kPathSlabFallback, 0);
+        // a short row with fewer than k): one exact pass over every positive key.
+        slab_restream<VEC>(s, r, k, 1u, fixed_p(top_p),
+                           philox_uniform(p.seed, p.row_base + r, p.offset));
         return;
     }
     const u32 span = kInfKey - tkey;
@@ -1860,9 +1981,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     if (!over && fill >= k) {
         slab_finish<VEC>(s, r, fill, k, tmin, P, u, direct ? wfill : ~0u);
     } else {
-        const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k, P, u,
-                                           kSelCap);
-        finish_row(s, p, r, o, kPathSlabFallback, fill);
+        // A whole row that counted at least k entries at or above its
+        // threshold has its best k there; anything else starts from 1.
+        slab_restream<VEC>(s, r, k, (S == 1 && !no_tkey && fill >= k) ? tkey : 1u, P, u);
     }
 }
 
@@ -1873,7 +1994,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // with zeros, which sort last) and finish on the first k positions.
 template <int VEC>
 __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         u32 wfill) {
+                                         u32 wfill, u32 path) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
@@ -1883,7 +2004,7 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey,
         Outcome ob;
         if (binned_topk(s, n, k, tkey, P, u, ob, wfill)) {
             stat_phase(p, r, 9, tp);
-            finish_row(s, p, r, ob, kPathSlab, gathered);
+            finish_row(s, p, r, ob, path, gathered);
             return;
         }
         stat_why(p, r, 64u);
@@ -1914,7 +2035,7 @@ __device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey,
         o = resolve_sorted<4>(s, v, k, P, u);
     }
     stat_phase(p, r, 9, tp);
-    finish_row(s, p, r, o, kPathSlab, gathered);
+    finish_row(s, p, r, o, path, gathered);
 }
 
 // ---------------------------------------------------------------------------
@@ -2336,31 +2457,74 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     const u64 over = block_sum(s, (threadIdx.x < nseg && ngv > gcap) ? 1u : 0u);
     const bool fail = (uni(s.misc[3]) & kFlagFail) || over != 0 || failed;
     if (over) stat_why(p, r, 16u);
-    u32 nall = 0;
-    if (!fail && kind != kZeroRow) {
+    // Appends the gathered entries with composites in [lo, hi) to the buffer
+    // and returns their number (more than kSelCap: some were not written).
+    auto collect = [&](u64 lo, u64 hi) {
+        if (threadIdx.x == 0) s.ctr[3] = 0;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < kL; ++j) {
             const u32 t = j * kBlock + threadIdx.x;
-            const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
+            const bool in = t < total && (t & gmask) < s.gn[t >> gsh] && c[j] >= lo && c[j] < hi;
             wave_append(sbuf(s), in, c[j], &s.ctr[3], 0, kSelCap);
         }
         for (u32 t0 = kL * kBlock; t0 < total; t0 += kBlock) {  // more than eight segments
             const u32 t = t0 + threadIdx.x;
             const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
             const u64 cc = in ? ld_g(&g0[(size_t)(t >> gsh) * kGSeg + (t & gmask)]) : 0;
-            wave_append(sbuf(s), in, cc, &s.ctr[3], 0, kSelCap);
+            wave_append(sbuf(s), in && cc >= lo && cc < hi, cc, &s.ctr[3], 0, kSelCap);
         }
         __syncthreads();
-        nall = uni(s.ctr[3]);
+        const u32 n = uni(s.ctr[3]);
         __syncthreads();
-    }
+        return n;
+    };
+    u32 nall = 0;
+    if (!fail && kind != kZeroRow) nall = collect(0, kNoUpper);
+    // More than a buffer's worth gathered (wide boundary and draw ranges):
+    // the boundary and the draw are then selected from one fine bin's
+    // entries at a time.
+    const bool staged = !fail && kind == kNormal && nall > kSelCap;
     u64 tf = stat_phase(p, r, 14, tp);
     Outcome o{};
     u32 path = kPathFull;
-    if (!fail && nall > kSelCap) stat_why(p, r, 32u);
-    if (fail || nall > kSelCap) {
+    bool fb = fail || (nall > kSelCap && !staged);
+    if (!fb && kind == kNormal) {
+        u32 n1 = nall;
+        if (staged) n1 = collect(fine_lo(fbT), fine_hi(fbT));
+        fb = n1 > kSelCap;
+        if (!fb) {
+            const bool binned = !tiny && fbT < kFineBins - 1;
+            const Sel sb = binned ? fine_select(s, n1, fbT, T - above_f)
+                                  : select_buf(s, n1, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
+            tf = stat_phase(p, r, 15, tf);
+            const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
+            const u64 t = __umul64hi(u, M_p);
+            int fdv[1];
+            u64 adv[1];
+            fine_locate(s, nlist, {t + 1}, fdv, adv);
+            const int fd = fdv[0];
+            const u64 above_d = adv[0];
+            u32 n2 = n1;
+            if (staged && fd != fbT) n2 = fd >= 0 ? collect(fine_lo(fd), fine_hi(fd)) : kSelCap + 1;
+            fb = n2 > kSelCap;
+            if (!fb) {
+                const Sel sd = (!tiny && fd < kFineBins - 1)
+                                   ? fine_select(s, n2, fd, t + 1 - above_d)
+                                   : select_buf(s, n2, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
+                o.kind = kNormal;
+                o.c_keep = sb.c;
+                o.M_p = M_p;
+                o.token = comp_index(sd.c);
+            }
+        }
+    }
+    if (!fail && fb) stat_why(p, r, 32u);
+    if (fb) {
         o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, p.V, P, u, kSelCap);
         path = kPathFullFallback;
+    } else if (kind == kNormal) {
+        // decided above
     } else if (kind == kZeroRow) {
         o.kind = kZeroRow;
         o.token = 0;  // the support is the whole row: its smallest index
@@ -2373,25 +2537,6 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         u64 mn = ~0ull;
         for (u32 i = threadIdx.x; i < nall; i += kBlock) mn = sbuf(s)[i] < mn ? sbuf(s)[i] : mn;
         o.c_keep = block_min(s, mn);
-    } else {
-        const bool binned = !tiny && fbT < kFineBins - 1;
-        const Sel sb = binned ? fine_select(s, nall, fbT, T - above_f)
-                              : select_buf(s, nall, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
-        tf = stat_phase(p, r, 15, tf);
-        const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
-        const u64 t = __umul64hi(u, M_p);
-        int fdv[1];
-        u64 adv[1];
-        fine_locate(s, nlist, {t + 1}, fdv, adv);
-        const int fd = fdv[0];
-        const u64 above_d = adv[0];
-        const Sel sd = (!tiny && fd < kFineBins - 1)
-                           ? fine_select(s, nall, fd, t + 1 - above_d)
-                           : select_buf(s, nall, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
-        o.kind = kNormal;
-        o.c_keep = sb.c;
-        o.M_p = M_p;
-        o.token = comp_index(sd.c);
     }
     if (threadIdx.x == 0) {
         st_dev(&rs->arrive_a, 0u);
