@@ -76,6 +76,7 @@ constexpr u32 kPassDepth = 8;          // the same for the passes of whole-row s
 constexpr u32 kSampleDepth = 4;        // leading steps of a top-k stream that set its threshold
 constexpr u32 kChunk = 1024;           // rows per launch
 constexpr u32 kSlabMaxK = 1024;        // largest k served by the streaming top-k path
+static_assert(kSlabMaxK < 65536, "top-k row k is kept as u16");
 constexpr size_t kWsBudget = 256u << 20;  // workspace bytes per sampler (rows per launch follow)
 constexpr int kBins = 2048;            // 11-bit radix digits
 constexpr u32 kInfKey = 0x7F800000u;
@@ -251,6 +252,7 @@ struct Smem {
     u64 finem[kDMax * 16];     // summed fine masses of the listed coarse bins
     int flist[kDMax];          // listed coarse bins
     u16 rows[kChunk];          // rows of this launch in class order
+    u16 slab_k[kChunk];        // k of each top-k row (read with the classes)
     u64 wpart[kWaves];
     u64 bc[4];
     u32 ctr[4];
@@ -2457,18 +2459,23 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     const u64 over = block_sum(s, (threadIdx.x < nseg && ngv > gcap) ? 1u : 0u);
     const bool fail = (uni(s.misc[3]) & kFlagFail) || over != 0 || failed;
     if (over) stat_why(p, r, 16u);
-    // Appends the gathered entries with composites in [lo, hi) to the buffer
-    // and returns their number (more than kSelCap: some were not written).
-    auto collect = [&](u64 lo, u64 hi) {
+    // Appends the gathered entries (with composites in [lo, hi) when reloading
+    // them from the gather areas) to the buffer and returns their number (more
+    // than kSelCap: some were not written).  The first call takes the values
+    // loaded above; they are dead afterwards, so nothing holds them across the
+    // selects.
+    auto collect = [&](bool reload, u64 lo, u64 hi) {
         if (threadIdx.x == 0) s.ctr[3] = 0;
         __syncthreads();
+        if (!reload) {
 #pragma unroll
-        for (int j = 0; j < kL; ++j) {
-            const u32 t = j * kBlock + threadIdx.x;
-            const bool in = t < total && (t & gmask) < s.gn[t >> gsh] && c[j] >= lo && c[j] < hi;
-            wave_append(sbuf(s), in, c[j], &s.ctr[3], 0, kSelCap);
+            for (int j = 0; j < kL; ++j) {
+                const u32 t = j * kBlock + threadIdx.x;
+                const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
+                wave_append(sbuf(s), in, c[j], &s.ctr[3], 0, kSelCap);
+            }
         }
-        for (u32 t0 = kL * kBlock; t0 < total; t0 += kBlock) {  // more than eight segments
+        for (u32 t0 = reload ? 0u : kL * kBlock; t0 < total; t0 += kBlock) {
             const u32 t = t0 + threadIdx.x;
             const bool in = t < total && (t & gmask) < s.gn[t >> gsh];
             const u64 cc = in ? ld_g(&g0[(size_t)(t >> gsh) * kGSeg + (t & gmask)]) : 0;
@@ -2480,7 +2487,7 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
         return n;
     };
     u32 nall = 0;
-    if (!fail && kind != kZeroRow) nall = collect(0, kNoUpper);
+    if (!fail && kind != kZeroRow) nall = collect(false, 0, kNoUpper);
     // More than a buffer's worth gathered (wide boundary and draw ranges):
     // the boundary and the draw are then selected from one fine bin's
     // entries at a time.
@@ -2491,7 +2498,7 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
     bool fb = fail || (nall > kSelCap && !staged);
     if (!fb && kind == kNormal) {
         u32 n1 = nall;
-        if (staged) n1 = collect(fine_lo(fbT), fine_hi(fbT));
+        if (staged) n1 = collect(true, fine_lo(fbT), fine_hi(fbT));
         fb = n1 > kSelCap;
         if (!fb) {
             const bool binned = !tiny && fbT < kFineBins - 1;
@@ -2506,7 +2513,7 @@ __device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64
             const int fd = fdv[0];
             const u64 above_d = adv[0];
             u32 n2 = n1;
-            if (staged && fd != fbT) n2 = fd >= 0 ? collect(fine_lo(fd), fine_hi(fd)) : kSelCap + 1;
+            if (staged && fd != fbT) n2 = fd >= 0 ? collect(true, fine_lo(fd), fine_hi(fd)) : kSelCap + 1;
             fb = n2 > kSelCap;
             if (!fb) {
                 const Sel sd = (!tiny && fd < kFineBins - 1)
@@ -2603,7 +2610,9 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     u64 local = 0;  // four 16-bit class counts
     for (int j = 0; j < 2; ++j) {
         const u32 r = r0 + j;
-        cls[j] = r < p.rows ? row_class(p, row_k_eff(p, r), s_full) : 4u;
+        const u32 ke = r < p.rows ? row_k_eff(p, r) : 0u;
+        cls[j] = r < p.rows ? row_class(p, ke, s_full) : 4u;
+        if (cls[j] == kClsSlab) s.slab_k[r] = (u16)ke;
         if (cls[j] < 4) local += 1ull << (16 * cls[j]);
     }
     const u64 ex = block_excl_scan(s, local);
@@ -2655,7 +2664,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
         do_whole<VEC>(s, r, row_k_eff(p, r));
     } else if (item < first_end) {
         const u32 r = uni((u32)s.rows[nf + n_whole + (item - whole_end)]);
-        do_slab<VEC>(s, r, row_k_eff(p, r), 0, S);
+        do_slab<VEC>(s, r, s.slab_k[r], 0, S);
     } else if (item < greedy_end) {
         const u32 i = (item - first_end) / Sg;
         const u32 r = uni((u32)s.rows[nf + n_whole + n_slab + i]);
@@ -2663,7 +2672,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     } else if (item < greedy_end + n_slab * (S - 1)) {
         const u32 i = (item - greedy_end) % n_slab, h = 1 + (item - greedy_end) / n_slab;
         const u32 r = uni((u32)s.rows[nf + n_whole + i]);
-        do_slab<VEC>(s, r, row_k_eff(p, r), h, S);
+        do_slab<VEC>(s, r, s.slab_k[r], h, S);
     }
 }
 
