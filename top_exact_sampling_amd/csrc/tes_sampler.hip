@@ -177,22 +177,27 @@ __device__ __forceinline__ u64* gather_area(const Params& p, u32 r, u32 seg) {
     return reinterpret_cast<u64*>(ws_row(p, r) + (size_t)p.s_ws * (sizeof(PubC) + sizeof(PubF))) +
            (size_t)seg * kGSeg;
 }
-// A top-k or greedy row streamed by two workgroups: each publishes its half's
-// result in the row's exchange area, and the last to arrive finishes.
+// A top-k or greedy row streamed by S <= kMaxSplit workgroups, one part each:
+// each publishes its part's result in the row's exchange area, and the last
+// to arrive finishes.
 struct HalfPub {
-    u64 best;  // greedy: the half's largest composite
-    u32 fill;  // top-k: candidates the half kept (more than kHalfCap: too many)
-    u32 tkey;  // top-k: the half's threshold key
-    u32 over;  // top-k: the half cannot be used
+    u64 best;  // greedy: the part's largest composite
+    u32 fill;  // top-k: candidates the part kept (more than kHalfCap: too many)
+    u32 tkey;  // top-k: the part's threshold key
+    u32 over;  // top-k: the part cannot be used
     u32 pad[3];
 };
-constexpr u32 kHalfCap = 2048;  // published candidates per half
-constexpr size_t kHalfBytes = 2 * sizeof(HalfPub) + 2 * (size_t)kHalfCap * sizeof(u64);
+constexpr u32 kMaxSplit = 8;     // parts a row may be split into
+constexpr u32 kMinPartVec = kStreamDepth * kBlock;  // smallest part: one full burst of loads
+constexpr u32 kHalfCap = 2048;   // published candidates per part
+constexpr size_t kPartBytes = sizeof(HalfPub) + (size_t)kHalfCap * sizeof(u64);
+constexpr size_t kSplitBytes = kMaxSplit * kPartBytes;
 __device__ __forceinline__ HalfPub* half_pub(const Params& p, u32 r, u32 h) {
     return reinterpret_cast<HalfPub*>(ws_row(p, r)) + h;
 }
 __device__ __forceinline__ u64* half_cands(const Params& p, u32 r, u32 h) {
-    return reinterpret_cast<u64*>(ws_row(p, r) + 2 * sizeof(HalfPub)) + (size_t)h * kHalfCap;
+    return reinterpret_cast<u64*>(ws_row(p, r) + kMaxSplit * sizeof(HalfPub)) +
+           (size_t)h * kHalfCap;
 }
 // Pointers to device memory reach the kernel through LDS (see params_from),
 // which hides their address space; every access to rows and workspace goes
@@ -1651,8 +1656,8 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
         RowState* rs = ws_state(p, r);
         if (threadIdx.x == 0) st_dev(&half_pub(p, r, h)->best, cbest);
         if (!arrive_last(s, &rs->ticket, S)) return;
-        const u64 ob = ld_g(&half_pub(p, r, 1 - h)->best);
-        cbest = ob > cbest ? ob : cbest;
+        const u64 ob = threadIdx.x < S ? ld_g(&half_pub(p, r, threadIdx.x)->best) : 0ull;
+        cbest = block_max(s, ob > cbest ? ob : cbest);
         if (threadIdx.x == 0) st_dev(&rs->ticket, 0u);
     }
     stat_phase(p, r, 8, tp);
@@ -1840,9 +1845,12 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         }
     }
     const u32 nsamp = min(kSampleDepth * kBlock, nvec) * VEC;
+    // (1.5 k of the row's share for one or two parts, 2 k beyond: the largest
+    // of many parts' thresholds must still leave k entries above it.)
+    const u64 kmul = S > 2 ? 4 : 3;
     const u32 j = (S == 1 && nsteps <= kSampleDepth)
                       ? k
-                      : (u32)(((u64)3 * k * nsamp + 2ull * p.V - 1) / (2ull * p.V)) + 12;
+                      : (u32)((kmul * k * nsamp + 2ull * p.V - 1) / (2ull * p.V)) + 12;
     const u32 tot = (u32)block_sum(s, nmass);  // also orders the histogram
     u32 tkey = 0;
     if (j <= tot) {
@@ -1946,10 +1954,10 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     stat_phase(p, r, 8, tp);
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
-    u32 tmin = tkey;
+    u32 tbase = tkey;
     if (S > 1) {
-        // Publish this half, then the last half to arrive joins the other's
-        // candidates to its own.
+        // Publish this part, then the last part to arrive joins every part's
+        // candidates at or above the largest threshold T.
         RowState* rs = ws_state(p, r);
         HalfPub* mine = half_pub(p, r, h);
         over = over || no_tkey || fill > kHalfCap;
@@ -1963,25 +1971,59 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
             st_dev(&mine->over, over ? 1u : 0u);
         }
         if (!arrive_last(s, &rs->ticket, S)) return;
-        const HalfPub* other = half_pub(p, r, 1 - h);
-        const u32 ofill = ld_g(&other->fill), otkey = ld_g(&other->tkey);
-        over = over || ld_g(&other->over) != 0 || fill + ofill > kSlabCap;
-        if (!over) {
-            const u64* src = half_cands(p, r, 1 - h);
-            for (u32 i = threadIdx.x; i < ofill; i += kBlock) sbuf(s)[fill + i] = ld_g(&src[i]);
-            fill += ofill;
+        if (threadIdx.x < S) {
+            const HalfPub* hp = half_pub(p, r, threadIdx.x);
+            s.gn[threadIdx.x] = ld_g(&hp->fill);
+            s.gn[kMaxSplit + threadIdx.x] = ld_g(&hp->tkey);
+            s.gn[2 * kMaxSplit + threadIdx.x] = ld_g(&hp->over);
         }
-        const u32 tmax = max(tkey, otkey);
-        tmin = min(tkey, otkey);
-        if (threadIdx.x == 0) st_dev(&rs->ticket, 0u);
+        if (threadIdx.x == 0) {
+            st_dev(&rs->ticket, 0u);
+            s.ctr[3] = 0;
+        }
         __syncthreads();
-        u32 above = 0;
-        if (!over)
-            for (u32 i = threadIdx.x; i < fill; i += kBlock) above += comp_key(sbuf(s)[i]) >= tmax;
-        over = over || (u32)block_sum(s, above) < k;  // also orders the joined buffer
+        u32 tmax = 0;
+        over = false;
+        for (u32 q = 0; q < S; ++q) {
+            tmax = max(tmax, uni(s.gn[kMaxSplit + q]));
+            over = over || uni(s.gn[2 * kMaxSplit + q]) != 0;
+        }
+        // Every entry of the row at or above T is in some part's candidates.
+        // The parts' lists are read as one index space, eight loads per
+        // thread in flight per round (one round for up to 4096 candidates).
+        if (!over) {
+            u32 pre[kMaxSplit + 1];
+            pre[0] = 0;
+            for (u32 q = 0; q < kMaxSplit; ++q) pre[q + 1] = pre[q] + (q < S ? uni(s.gn[q]) : 0u);
+            const u32 total = pre[kMaxSplit];
+            constexpr int kL = 8;
+            for (u32 t0 = 0; t0 < total; t0 += kL * kBlock) {
+                u64 c[kL];
+                bool in[kL];
+#pragma unroll
+                for (int j = 0; j < kL; ++j) {
+                    const u32 t = t0 + (u32)j * kBlock + threadIdx.x;
+                    u32 q = 0;
+#pragma unroll
+                    for (u32 b = 1; b < kMaxSplit; ++b) q += t >= pre[b] ? 1u : 0u;
+                    in[j] = t < total;
+                    c[j] = in[j] ? ld_g(&half_cands(p, r, q)[t - pre[q]]) : 0ull;
+                }
+#pragma unroll
+                for (int j = 0; j < kL; ++j)
+                    wave_append(sbuf(s), in[j] && comp_key(c[j]) >= tmax, c[j], &s.ctr[3], 0,
+                                kSlabCap);
+            }
+        }
+        __syncthreads();
+        fill = uni(s.ctr[3]);
+        __syncthreads();
+        // At least k of them: the row's best k are among them.
+        over = over || fill > kSlabCap || fill < k;
+        tbase = tmax;
     }
     if (!over && fill >= k) {
-        slab_finish<VEC>(s, r, fill, k, tmin, P, u, direct ? wfill : ~0u);
+        slab_finish<VEC>(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
     } else {
         // A whole row that counted at least k entries at or above its
         // threshold has its best k there; anything else starts from 1.
@@ -2643,13 +2685,19 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     const u32 n_whole = uni(s.misc[kClsWhole]);
     const u32 n_slab = uni(s.misc[kClsSlab]);
     const u32 n_greedy = uni(s.misc[kClsGreedy]);
-    // Top-k rows are split in two only when every item, halves included, is
-    // resident at once (halves that wait for a slot only delay their rows);
-    // greedy rows too when there is still room.  Second halves come last in
-    // block order.
+    // Top-k rows are split into S parts only when every item, parts included,
+    // is resident at once (parts that wait for a slot only delay their rows);
+    // greedy rows too when there is still room.  Parts after the first come
+    // last in block order.
     const u32 base_items = nf * s_full + n_whole + n_slab + n_greedy;
-    const u32 S = (p.split > 1 && base_items + (p.split - 1) * n_slab <= p.slots) ? p.split : 1u;
-    const u32 Sg = (S > 1 && base_items + (p.split - 1) * (n_slab + n_greedy) <= p.slots) ? p.split : 1u;
+    // Parts beyond half the resident slots cost more in joins than they gain
+    // (measured), so the split stops there.
+    const u32 room = p.slots / 2;
+    u32 S = 1, Sg = 1;
+    for (u32 c = p.split; c > 1 && S == 1; --c)
+        if (base_items + (c - 1) * n_slab <= room) S = c;
+    for (u32 c = S; c > 1 && Sg == 1; --c)
+        if (base_items + (S - 1) * n_slab + (c - 1) * n_greedy <= room) Sg = c;
     const u32 full_end = nf * s_full;
     const u32 whole_end = full_end + n_whole;
     const u32 first_end = whole_end + n_slab;
@@ -2782,6 +2830,7 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     if (s->s_ws < 1) s->s_ws = 1;
     if (s->s_ws > kMaxSegWs) s->s_ws = kMaxSegWs;
     size_t rb = (size_t)s->s_ws * (sizeof(PubC) + sizeof(PubF) + (size_t)kGSeg * sizeof(u64));
+    if (rb < kSplitBytes) rb = kSplitBytes;  // parts of a split top-k or greedy row
     rb = (rb + 255) & ~(size_t)255;
     s->rowbytes = (u32)rb;
     s->chunk = (u32)max_batch < kChunk ? (u32)max_batch : kChunk;
@@ -2852,9 +2901,12 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
         p.flags = s->flags;
-        // Top-k and greedy rows long enough for two full samples are split
-        // between two workgroups when the exchange area holds both halves.
-        p.split = (s->rowbytes >= kHalfBytes && nvec >= 2 * kStreamDepth * kBlock) ? 2u : 1u;
+        // Top-k and greedy rows may be split into up to kMaxSplit parts of at
+        // least kMinPartVec vectors (the kernel splits only when every part
+        // is resident at once).
+        const u32 by_len = nvec / kMinPartVec;
+        p.split = s->rowbytes >= kSplitBytes ? (by_len < kMaxSplit ? (by_len < 1 ? 1u : by_len) : kMaxSplit)
+                                             : 1u;
         p.slots = s->slots;
         if (p.stats &&
             hipMemsetAsync(p.stats + (size_t)kStatWords * c0, 0, sizeof(u32) * kStatWords * rows,
@@ -2862,8 +2914,11 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
             return TES_ERR_LAUNCH;
         // Enough blocks for every row to be top-p-only; the kernel knows the
         // actual mix, and blocks beyond the last item return at once.
+        // Split rows occur only when every item is resident, i.e. within
+        // the slots.
         const u32 per_row = s_full <= s->s_ws ? s_full : 1u;
-        const u32 grid = rows * (per_row > p.split ? per_row : p.split);
+        const u32 split_items = rows * p.split < s->slots ? rows * p.split : s->slots;
+        const u32 grid = rows * per_row > split_items ? rows * per_row : split_items;
         if (vec4)
             hipLaunchKernelGGL(tes_main_kernel<4>, dim3(grid), dim3(kBlock), 0, st, p);
         else
