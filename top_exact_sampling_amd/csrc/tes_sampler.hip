@@ -783,9 +783,11 @@ __device__ Sel radix_select(Smem& s, u32 n, Get get, u64 W, bool mass, u64 lo, u
 }
 
 // Select over sbuf(s)[0, n), n <= kSelCap (the digit tables sit above it).
-// One out-of-line copy: selects run once per row, with little else live.
-__device__ __noinline__ Sel select_buf(Smem& s, u32 n, u64 W, bool mass, u64 lo = 0,
-                                       u64 hi = kNoUpper) {
+// The finishes are inlined into the kernel: a call boundary makes the caller
+// and callee save registers to scratch memory, and reloading them costs a
+// memory round trip on every row's critical path (about 1 us per row).
+__device__ __forceinline__ Sel select_buf(Smem& s, u32 n, u64 W, bool mass, u64 lo = 0,
+                                          u64 hi = kNoUpper) {
     return radix_select(s, n, [&](u32 i, u64& c) { c = sbuf(s)[i]; return true; }, W, mass, lo, hi,
                         shcnt(s), shmass(s));
 }
@@ -1209,7 +1211,7 @@ struct BinView {
 // sorting their bin.  Returns false, with the buffer holding the same entries
 // in another order, when a bin it needs holds more than 64 entries or the
 // support holds +inf entries or has no mass; the caller then sorts.
-__device__ __noinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+__device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          Outcome& o, u32 wfill) {
     constexpr int J = kSlabCap / kBlock;
     static_assert(J * 64 == kSlabCap / kWaves, "a wave region is J entries per lane");
@@ -1291,7 +1293,7 @@ __device__ __noinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P,
 // the sub-bin holding W is sorted.  Larger bins go through the workgroup's
 // 2048-bin table (32 keys per bin), and the radix select decides when even
 // that bin holds more than 64 entries.
-__device__ __noinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
+__device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     const u32 fkey = (u32)(f + (int)kFineBase);
     u64* list = sbuf(s) + kSelCap;
     if (threadIdx.x == 0) s.ctr[2] = 0;
@@ -1675,7 +1677,7 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // Top-k rows (2 <= k <= 1024)
 // ---------------------------------------------------------------------------
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+__device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path = kPathSlab);
 
 // The smallest index of the row whose key is zero (NaN, negative, -0.0 or
@@ -2037,7 +2039,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // the best k when it holds more than a sort takes, sort it descending (padded
 // with zeros, which sort last) and finish on the first k positions.
 template <int VEC>
-__device__ __noinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
+__device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
@@ -2227,7 +2229,7 @@ __device__ __forceinline__ void fine_plan_wave(Smem& s, int nlist, u64 T, u64 u)
 }
 
 template <int VEC>
-__device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
+__device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
                                          u64 above_f, int fbT, int nlist, bool failed);
 
 template <int VEC>
@@ -2465,9 +2467,9 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
 }
 
 // Last segment of a top-p-only row: load every segment's gathered entries
-// and finish (out of line, once per row).
+// and finish.
 template <int VEC>
-__device__ __noinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
+__device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
                                          u64 above_f, int fbT, int nlist, bool failed) {
     const Params p = params_from(s);
     RowState* rs = ws_state(p, r);
