@@ -79,6 +79,60 @@ def cpu_baseline(w, min_wall=10.0, max_reps=40):
     }
 
 
+def graph_timing(step, copies, stream, calls=20, replays=10):
+    """Average duration of one call when `calls` calls (rotating over the
+    input copies) are captured in one HIP graph and replayed."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        step(0, side)  # the library's first use of this stream, outside capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for i in range(calls):
+            step(i, cap)
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()  # replays run on the current stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(replays):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * calls)
+
+
+def read_timing(tes, probs, nbytes, dev, stream, steps):
+    """Average duration of a plain read of one input copy (reference stream
+    kernel of the library), rotating over the copies like the timed calls."""
+    import torch
+
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def rd(i):
+        rc = tes.sampler_read_probe(probs[i % len(probs)].data_ptr(), nbytes, sink.data_ptr(),
+                                    dev.index or 0, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError("sampler_read_probe failed: %d" % rc)
+
+    for i in range(10):
+        rd(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        rd(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,9 +168,9 @@ def main():
     out = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, st=None):
         sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset, out_tokens=out,
-                       stream=stream)
+                       stream=stream if st is None else st)
 
     for i in range(args.warmup):
         step(i)
@@ -148,6 +202,12 @@ def main():
 
     alg_bytes = B * V * 4 + 12 * B
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    # The same calls replayed from one captured HIP graph (launch overhead
+    # removed), and a plain read of the same bytes by the library's reference
+    # stream kernel, on the same stream and input copies.
+    graph_ms = graph_timing(step, args.copies, stream)
+    read_ms = read_timing(tes, probs, B * V * 4, dev, stream, args.steps)
 
     parity = None
     if not args.no_parity:
@@ -184,6 +244,10 @@ def main():
             "renorm_out": None,
             "input_copies_rotated": args.copies,
             "kernel_ms_hip_events": round(kern_ms, 5),
+            "kernel_ms_graph_replay": round(graph_ms, 5),
+            "plain_read_ms_same_bytes": round(read_ms, 5),
+            "plain_read_GBps": round(B * V * 4 / (read_ms * 1e-3) / 1e9, 1),
+            "frac_of_plain_read": round(read_ms / kern_ms, 4),
             "parity_vs_oracle": parity,
         },
         "roofline": {

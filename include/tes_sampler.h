@@ -146,6 +146,20 @@ const char *sampler_status_string(int status);
  * device.  `host_out` holds 16 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);
 
+/* Reference measurement, not part of sampling: reads `bytes` bytes of device
+ * memory at `data` once with coalesced 16-byte loads (the access pattern of
+ * the sampler's row stream, with nothing computed) on `stream`, on HIP device
+ * `device`.  Timing it over the same bytes as a sampler call gives the plain
+ * read time of the device, the practical floor of a single-read sampler.
+ *   data    device, 16-byte aligned; bytes a multiple of 16 (0 is a no-op).
+ *   sink    device, one uint32; written only when the folded value of the
+ *           data equals a fixed constant (it exists so that no load can be
+ *           removed); its content is otherwise untouched.
+ * Returns TES_ERR_INVALID_ARGUMENT for null or misaligned pointers or sizes,
+ * TES_ERR_LAUNCH when the kernel cannot be enqueued. */
+int sampler_read_probe(const void *data, uint64_t bytes, uint32_t *sink, int device,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ TES_FLAG_SMALL_SEGMENTS = 8
 STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
-            "sampler_get_stats")
+            "sampler_get_stats", "sampler_read_probe")
 
 _lib = None
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.sampler_status_string.restype = ctypes.c_char_p
         L.sampler_get_stats.argtypes = [vp, vp, ctypes.c_int]
         L.sampler_get_stats.restype = ctypes.c_int
+        L.sampler_read_probe.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, vp]
+        L.sampler_read_probe.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -103,6 +105,11 @@ def sampler_get_stats(handle, B: int):
     if rc != TES_OK:
         raise TesError(rc, "sampler_get_stats")
     return out
+
+
+def sampler_read_probe(data_ptr: int, nbytes: int, sink_ptr: int, device: int, stream) -> int:
+    """Plain read of nbytes of device memory (reference timing); status code."""
+    return lib().sampler_read_probe(data_ptr, int(nbytes), sink_ptr, int(device), stream)
 
 
 # -- torch convenience (marshalling only) -----------------------------------

@@ -2757,6 +2757,35 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
 }
 
 
+
+// Reference stream: reads nvec 16-byte vectors once (coalesced, eight loads
+// per thread in flight, non-temporal like the sampler's row loads) and folds
+// them into one word, stored only when it equals a value no input is expected
+// to produce, so that no load can be dropped.  Its duration over the same
+// bytes is the plain read time the sampler's duration is compared with.
+__global__ __launch_bounds__(256) void tes_read_kernel(const f4* __restrict__ src, u64 nvec,
+                                                       u32* __restrict__ sink) {
+    constexpr int kU = 8;
+    const u64 stride = (u64)gridDim.x * 256u;
+    u32 acc = 0;
+    u64 i = (u64)blockIdx.x * 256u + threadIdx.x;
+    for (; i + (kU - 1) * stride < nvec; i += kU * stride) {
+        f4 v[kU];
+#pragma unroll
+        for (int j = 0; j < kU; ++j) v[j] = ld_stream(&src[i + j * stride]);
+#pragma unroll
+        for (int j = 0; j < kU; ++j)
+            acc ^= __float_as_uint(v[j][0]) ^ __float_as_uint(v[j][1]) ^
+                   __float_as_uint(v[j][2]) ^ __float_as_uint(v[j][3]);
+    }
+    for (; i < nvec; i += stride) {
+        const f4 v = ld_stream(&src[i]);
+        acc ^= __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^ __float_as_uint(v[2]) ^
+               __float_as_uint(v[3]);
+    }
+    if (acc == 0x7FC0DEADu) *sink = acc;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2965,6 +2994,23 @@ extern "C" const char* sampler_status_string(int status) {
         case TES_ERR_TOO_LARGE: return "batch or vocabulary above the sampler's limits";
         default: return "unknown status";
     }
+}
+
+extern "C" int sampler_read_probe(const void* data, uint64_t bytes, uint32_t* sink, int device,
+                                  void* stream) {
+    if (!data || !sink || device < 0 || ((uintptr_t)data & 15) || (bytes & 15) ||
+        ((uintptr_t)sink & 3))
+        return TES_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return TES_OK;
+    DeviceGuard g(device);
+    if (!g.ok) return TES_ERR_LAUNCH;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const u64 nvec = bytes / 16;
+    const u64 want = (nvec + 256 * 8 - 1) / (256 * 8);
+    const u32 grid = want < 8192 ? (u32)(want < 1 ? 1 : want) : 8192u;
+    hipLaunchKernelGGL(tes_read_kernel, dim3(grid), dim3(256), 0, st,
+                       reinterpret_cast<const f4*>(data), nvec, sink);
+    return hipGetLastError() == hipSuccess ? TES_OK : TES_ERR_LAUNCH;
 }
 
 extern "C" int sampler_get_stats(tes_sampler* s, uint32_t* host_out, int B) {
