@@ -32,6 +32,24 @@ KERNEL_SRC = os.path.join(ROOT, "top_exact_sampling_amd", "csrc", "tes_sampler.h
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tes_main_kernel_hetero_b256_v151936_traffic.txt")
 
 
+ROW_MIX = {
+    1: "k=50, p=0.9 on all rows",
+    2: "k~U{1..1024}, p~U[0.5,1.0]",
+    3: "64 greedy (k=1), 64 top-p only (k=V, p~U[0.8,0.99]), "
+       "128 k~U{20..1024} with p~U[0.7,1.0]",
+    4: "k~U{1..1024}, p~U[0.5,1.0]; 10 all-zero rows, 10 NaN/negative/-0.0 rows, "
+       "10 rows with 2-5 +inf",
+    5: "top-p only: k=V, p=0.95",
+}
+INPUT = {
+    1: "fp32 probs, softmax of 2*N(0,1) logits with 3 tokens boosted +10",
+    2: "fp32 probs, softmax of 2*N(0,1) logits with 1-8 tokens boosted U[8,15]",
+    3: "fp32 probs, softmax of 2*N(0,1) logits with 1-8 tokens boosted U[8,15]",
+    4: "fp32 probs of the same recipe quantised to multiples of 2^-20 and renormalised",
+    5: "fp32 probs, softmax of 0.5*N(0,1) logits (high entropy)",
+}
+
+
 def source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -139,6 +157,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4, help="rotating input copies (> MALL)")
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="input recipe (workloads.py); 3, the heterogeneous B=256, V=151,936 "
+                         "batch, is the headline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -157,12 +178,16 @@ def main():
     import top_exact_sampling_amd as tes
     import workloads
 
-    w = workloads.make(3)
+    w = workloads.make(args.workload)
     B, V = w.B, w.V
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sampler = tes.Sampler(0, max_batch=B, max_vocab=V)
-    probs = [torch.from_numpy(w.probs).to(dev) for _ in range(args.copies)]
+    # Rotating copies: at least twice the 256 MiB Infinity Cache in total
+    # (fewer for the large batches, whose single copy already exceeds it).
+    copies = max(1, min(args.copies, -(-2 * (256 << 20) // w.probs.nbytes)))
+    args.copies = copies
+    probs = [torch.from_numpy(w.probs).to(dev) for _ in range(copies)]
     top_k = torch.from_numpy(w.top_k).to(dev)
     top_p = torch.from_numpy(w.top_p).to(dev)
     out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -220,7 +245,7 @@ def main():
         parity = "bit-exact" if np.array_equal(gtok, otok) else \
             "MISMATCH on %d rows" % int((gtok != otok).sum())
 
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile() if args.workload == 3 else None
     line = {
         "metric": METRIC,
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -238,9 +263,8 @@ def main():
             "workload": w.name,
             "B": B,
             "V": V,
-            "row_mix": "64 greedy (k=1), 64 top-p only (k=V, p~U[0.8,0.99]), "
-                       "128 k~U{20..1024} with p~U[0.7,1.0]",
-            "input": "fp32 probs, softmax of 2*N(0,1) logits with 1-8 tokens boosted U[8,15]",
+            "row_mix": ROW_MIX[args.workload],
+            "input": INPUT[args.workload],
             "renorm_out": None,
             "input_copies_rotated": args.copies,
             "kernel_ms_hip_events": round(kern_ms, 5),
