@@ -427,3 +427,43 @@ def test_wide_topp_bins_stay_on_the_fast_path(sampler, orc):
     assert_parity(orc, probs, w.top_k[rows], w.top_p[rows], w.seed, w.offset, gtok, gren,
                   "wide top-p bins")
     assert np.all(st[:, 0] == 1), "rows left the fast path: %s" % np.flatnonzero(st[:, 0] != 1)
+
+
+def test_batches_longer_than_one_launch(sampler, orc):
+    # More rows than one launch takes (1024): the call enqueues several
+    # launches, each with its own row offset for the Philox counter, mixing
+    # every row class.
+    B, V = 2500, 4096
+    rng = np.random.default_rng(2500)
+    x = 2.0 * rng.standard_normal((B, V))
+    x[np.arange(B), rng.integers(0, V, size=B)] += 10.0
+    e = np.exp(x - x.max(1, keepdims=True))
+    probs = (e / e.sum(1, keepdims=True)).astype(np.float32)
+    ks = rng.choice(np.array([1, 7, 300, 1024, 2000, 0, V], np.int32), size=B)
+    ps = rng.uniform(0.3, 1.0, size=B).astype(np.float32)
+    log("[gpu] multi-launch batch B=%d V=%d" % (B, V))
+    gtok, gren = run_gpu(sampler, probs, ks, ps, 99, 7, renorm=True)
+    assert_parity(orc, probs, ks, ps, 99, 7, gtok, gren, "multi-launch")
+
+
+@pytest.mark.parametrize("trial", range(6))
+def test_random_shapes(sampler, orc, trial):
+    # Random batch and vocabulary sizes, row recipes and parameters, including
+    # out-of-range k and p.
+    rng = np.random.default_rng(1000 + trial)
+    B = int(rng.integers(1, 80))
+    V = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 20000)),
+                        int(rng.integers(20000, 140000))]))
+    scale = float(rng.choice([0.3, 2.0, 6.0]))
+    x = scale * rng.standard_normal((B, V))
+    e = np.exp(x - x.max(1, keepdims=True))
+    probs = (e / e.sum(1, keepdims=True)).astype(np.float32)
+    if rng.random() < 0.5:  # coarse values: many ties
+        probs = (np.round(probs * 2**12) / 2**12).astype(np.float32)
+    ks = rng.integers(-3, V + 5, size=B).astype(np.int32)
+    ks[rng.random(B) < 0.3] = 1
+    ps = rng.uniform(-0.2, 1.3, size=B).astype(np.float32)
+    seed, off = (int(v) for v in rng.integers(0, 2**63, size=2))
+    log("[gpu] random shapes trial %d B=%d V=%d" % (trial, B, V))
+    gtok, gren = run_gpu(sampler, probs, ks, ps, seed, off, renorm=True)
+    assert_parity(orc, probs, ks, ps, seed, off, gtok, gren, "random trial %d" % trial)
