@@ -1729,12 +1729,17 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     __syncthreads();
     for_each_vec<VEC, kPassDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
         const u32 span = kInfKey - theta;
+        // One append per vector: the lane's passing entries go to consecutive
+        // slots taken by one LDS atomic per wave.
+        u64 c[VEC];
+        u32 mask = 0;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-            wave_append(sbuf(s), valid && !closed && b - theta <= span, composite(b, iv * VEC + e),
-                        &s.ctr[3], 0, kSlabCap);
+            c[e] = composite(b, iv * VEC + e);
+            mask |= (valid && !closed && b - theta <= span) ? 1u << e : 0u;
         }
+        wave_append_n<VEC>(sbuf(s), mask, c, &s.ctr[3], 0, kSlabCap);
         __syncthreads();
         const u32 n = uni(s.ctr[3]);
         if (n > kHigh) {
