@@ -58,6 +58,9 @@ class Oracle:
             ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int]
         lib.oracle_topk_topp_sample.restype = ctypes.c_int
+        lib.oracle_support.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_support.restype = ctypes.c_int64
         self.lib = lib
         self.path = path
 
@@ -106,6 +109,30 @@ class Oracle:
         if rc:
             raise RuntimeError("oracle_topk_topp_sample failed: %d" % rc)
         return tok, ren, info
+
+
+def slab(orc: Oracle, probs, top_k, cap: int, renorm):
+    """Per row: the support's indices in sorted order (descending
+    probability, ascending index) and their renormalised weights taken from
+    ``renorm`` (the oracle's dense renorm_out), for rows whose support holds
+    at most ``cap`` entries; other rows get length -1.  Returns
+    (index[B][cap] filled with -1, weight[B][cap] filled with 0, length[B])."""
+    probs = np.ascontiguousarray(probs, dtype=np.float32)
+    B, V = probs.shape
+    idx = np.full((B, cap), -1, np.int32)
+    wgt = np.zeros((B, cap), np.float32)
+    length = np.full(B, -1, np.int32)
+    buf = np.zeros(max(cap, 1), np.int32)
+    for b in range(B):
+        k_eff = int(orc.lib.oracle_support(probs[b].ctypes.data, V, int(top_k[b]), cap,
+                                           buf.ctypes.data))
+        if k_eff < 0:
+            raise RuntimeError("oracle_support failed")
+        if k_eff <= cap:
+            idx[b, :k_eff] = buf[:k_eff]
+            wgt[b, :k_eff] = renorm[b, buf[:k_eff]]
+            length[b] = k_eff
+    return idx, wgt, length
 
 
 def load(path: str | None = None) -> Oracle:

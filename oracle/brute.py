@@ -67,6 +67,27 @@ def fixed_p(p: float) -> int:
     return max(1, int(r))
 
 
+def brute_support(row_bits, k: int):
+    """The support in its order: the indices whose rank (the number of
+    entries with a larger sanitised value, or an equal one at a lower index)
+    is below k_eff, by ascending rank.  No sort is involved."""
+    vals = [sanitized_value(_from_bits(int(v))) for v in row_bits]
+    V = len(vals)
+    k_eff = V if (k <= 0 or k >= V) else k
+    rank = []
+    for i in range(V):
+        r = 0
+        for j in range(V):
+            if _greater(vals[j], vals[i]) or (vals[j] == vals[i] and j < i):
+                r += 1
+        rank.append(r)
+    order = [None] * k_eff
+    for i in range(V):
+        if rank[i] < k_eff:
+            order[rank[i]] = i
+    return order
+
+
 def brute_row(row_bits, k: int, p: float, u: int):
     """Return (token, kept indices in sorted order, weights as Fractions).
 

@@ -240,6 +240,26 @@ extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, flo
 }
 
 // ---------------------------------------------------------------------------
+// The support S of one row in its sorted order (descending probability,
+// ascending index: the first k_eff entries of the stable sort of step 3),
+// written to out[0, min(k_eff, cap)); returns k_eff.  This is the order in
+// which the cake_sampling page ("Semantics") emits its slab.
+// ---------------------------------------------------------------------------
+extern "C" int64_t oracle_support(const float* row, int64_t V, int32_t top_k, int64_t cap,
+                                  int32_t* out) {
+    if (V <= 0 || row == nullptr || (cap > 0 && out == nullptr)) return -1;
+    std::vector<uint32_t> key(V);
+    for (int64_t i = 0; i < V; ++i) key[i] = sanitized_key(row[i]);
+    const int64_t k_eff = effective_k(top_k, V);
+    std::vector<int64_t> order(V);
+    std::iota(order.begin(), order.end(), (int64_t)0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return key[a] > key[b]; });
+    for (int64_t j = 0; j < k_eff && j < cap; ++j) out[j] = (int32_t)order[j];
+    return k_eff;
+}
+
+// ---------------------------------------------------------------------------
 // Batched entry: B rows of V entries, row-major.  Rows are split statically
 // across n_threads host threads (<= 0 means one).  renorm_out and info are
 // nullable; info holds 10 int64 per row.

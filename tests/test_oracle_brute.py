@@ -15,7 +15,7 @@ import struct
 import numpy as np
 import pytest
 
-from oracle.brute import brute_row
+from oracle.brute import brute_row, brute_support
 
 TWO64 = 1 << 64
 
@@ -149,3 +149,44 @@ def test_random_tiny_rows(orc):
         p = float(rng.random())
         u = int(rng.integers(0, 2**63)) * 2 + int(rng.integers(0, 2))
         _check(orc, bits, k, p, u)
+
+
+def _support(orc, row, k, cap):
+    import numpy as np
+
+    row = np.ascontiguousarray(row, dtype=np.float32)
+    out = np.full(max(cap, 1), -7, np.int32)
+    k_eff = int(orc.lib.oracle_support(row.ctypes.data, row.size, int(k), cap, out.ctypes.data))
+    return k_eff, out[: min(k_eff, cap)].tolist()
+
+
+def test_support_order_matches_rank_definition(orc):
+    # The exported support order (the slab order: descending probability,
+    # ascending index) against the O(V^2) rank definition, on rows of special
+    # values with heavy ties, for every k.
+    rng = np.random.default_rng(77)
+    for trial in range(120):
+        V = int(rng.integers(1, 9))
+        bits = [int(SPECIAL[i]) for i in rng.integers(0, len(SPECIAL), size=V)]
+        row = np.array(bits, np.uint32).view(np.float32)
+        for k in range(-1, V + 2):
+            want = brute_support(bits, k)
+            k_eff, got = _support(orc, row, k, V)
+            assert k_eff == len(want)
+            assert got == want, (bits, k)
+
+
+def test_support_order_matches_lexsort(orc):
+    # Library cross-check on larger rows: numpy's lexsort by (-value, index)
+    # of the sanitised values, truncated to k and to the capacity.
+    rng = np.random.default_rng(78)
+    for V, k, cap in ((1000, 50, 64), (5000, 700, 1024), (4096, 4096, 1024), (300, 0, 512)):
+        x = np.round(rng.random(V) * 64).astype(np.float32) / 64  # many ties
+        x[rng.choice(V, 5, replace=False)] = np.nan
+        x[rng.choice(V, 5, replace=False)] = -1.0
+        vals = np.where(np.isnan(x) | (np.signbit(x)), 0.0, x).astype(np.float64)
+        order = np.lexsort((np.arange(V), -vals))
+        k_eff = V if (k <= 0 or k >= V) else k
+        got_k, got = _support(orc, x, k, cap)
+        assert got_k == k_eff
+        assert got == order[: min(k_eff, cap)].tolist()
