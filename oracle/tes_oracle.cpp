@@ -139,6 +139,17 @@ static int64_t effective_k(int32_t k, int64_t V) {
     return k;
 }
 
+// Stable sort of the indices by key, descending (ties keep ascending index),
+// cut to the first k_eff: the support S in its order.
+static std::vector<int64_t> support_order(const std::vector<uint32_t>& key, int64_t k_eff) {
+    std::vector<int64_t> order(key.size());
+    std::iota(order.begin(), order.end(), (int64_t)0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return key[a] > key[b]; });
+    order.resize(k_eff);
+    return order;
+}
+
 // ---------------------------------------------------------------------------
 // One row, with the uniform u given explicitly.
 //
@@ -158,12 +169,8 @@ extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, flo
     const int64_t k_eff = effective_k(top_k, V);
     const uint64_t P = fixed_point_p(top_p);
 
-    // Step 3: stable sort by key, descending; ties keep ascending index.
-    std::vector<int64_t> order(V);
-    std::iota(order.begin(), order.end(), (int64_t)0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int64_t a, int64_t b) { return key[a] > key[b]; });
-    order.resize(k_eff);  // the support S
+    // Step 3: the support S in its sorted order.
+    std::vector<int64_t> order = support_order(key, k_eff);
 
     if (renorm) std::fill(renorm, renorm + V, 0.0f);
     int64_t inf_count = 0;
@@ -251,10 +258,7 @@ extern "C" int64_t oracle_support(const float* row, int64_t V, int32_t top_k, in
     std::vector<uint32_t> key(V);
     for (int64_t i = 0; i < V; ++i) key[i] = sanitized_key(row[i]);
     const int64_t k_eff = effective_k(top_k, V);
-    std::vector<int64_t> order(V);
-    std::iota(order.begin(), order.end(), (int64_t)0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int64_t a, int64_t b) { return key[a] > key[b]; });
+    const std::vector<int64_t> order = support_order(key, k_eff);
     for (int64_t j = 0; j < k_eff && j < cap; ++j) out[j] = (int32_t)order[j];
     return k_eff;
 }
