@@ -104,6 +104,43 @@ int topk_topp_sample(tes_sampler *s, const float *probs, int B, int V, const int
                      const float *top_p, uint64_t seed, uint64_t offset, int32_t *out_tokens,
                      float *renorm_out, void *stream);
 
+/* topk_topp_sample plus the slab export: the same sampling (same arguments,
+ * same outputs), and for every row whose support holds at most slab_cap
+ * entries, the support in its sorted order -- descending probability,
+ * ascending vocabulary index, the order in which the FlashInfer
+ * "cake_sampling" page (section "Semantics") emits its workspace slab and
+ * renormalised output -- with the renormalised weight of each entry.
+ *   slab_index   device, int32 [B][slab_cap]: row b's support indices in
+ *                sorted order at [b][0, len), -1 after them.
+ *   slab_renorm  device, fp32 [B][slab_cap]: the renormalised weight of
+ *                slab_index[b][j] (exactly the renorm_out value at that
+ *                index: q / M_p for kept entries, 1/m for kept +inf entries,
+ *                0 for support entries past the top-p cut and for zero-mass
+ *                rows), 0 after len.
+ *   slab_cap     1 .. 1024.
+ *   slab_len     device, int32 [B]: the support size k_eff, or -1 when it
+ *                exceeds slab_cap (then the row's slab is all -1 / 0).
+ *   route        device, uint32 [B] or NULL: the path that decided each row
+ *                (the codes of sampler_get_stats word [0]).
+ * The export reads every row once more (one extra pass over probs).  Errors
+ * as for topk_topp_sample, plus TES_ERR_INVALID_ARGUMENT for a slab_cap out
+ * of range or null / misaligned slab pointers. */
+int topk_topp_sample_slab(tes_sampler *s, const float *probs, int B, int V,
+                          const int32_t *top_k, const float *top_p, uint64_t seed,
+                          uint64_t offset, int32_t *out_tokens, float *renorm_out,
+                          int32_t *slab_index, float *slab_renorm, int slab_cap,
+                          int32_t *slab_len, uint32_t *route, void *stream);
+
+/* The path each row will take, from top_k in host memory, without launching
+ * anything (the role of the cake_sampling page's route report): 4 greedy
+ * (k_eff = 1), 0 top-k streaming (k_eff <= 1024), 1 top-p-only (k_eff = V),
+ * 3 whole-row passes (1024 < k_eff < V, or forced by the flags).  Data can
+ * still send a row to a fallback (codes 2 and 5 of sampler_get_stats); the
+ * route output of topk_topp_sample_slab reports the path actually taken.
+ *   top_k_host  host, int32 [B];  route_host  host, uint32 [B]. */
+int sampler_route(tes_sampler *s, int B, int V, const int32_t *top_k_host,
+                  uint32_t *route_host);
+
 /* Release the handle and its workspace.  NULL is accepted. */
 int sampler_destroy(tes_sampler *s);
 

@@ -53,3 +53,43 @@ def assert_parity(orc, probs, top_k, top_p, seed, offset, gtok, gren, label):
             rel = np.abs(gren[nzo].astype(np.float64) - oren[nzo]) / oren[nzo]
             assert rel.max() <= REL_TOL, "%s: renorm rel err %.3g" % (label, rel.max())
     return otok, info
+
+
+def run_gpu_slab(sampler, probs, top_k, top_p, seed, offset, cap):
+    """Run the sampler with the slab export; returns numpy (tokens, renorm,
+    slab_index, slab_renorm, slab_len, route)."""
+    import torch
+
+    B, V = probs.shape
+    pd = to_dev(probs, torch)
+    kd = to_dev(np.asarray(top_k, np.int32), torch)
+    qd = to_dev(np.asarray(top_p, np.float32), torch)
+    ren = torch.full((B, V), -1.0, dtype=torch.float32, device="cuda")
+    tok, si, sr, sl, rt = sampler.sample_slab(pd, kd, qd, seed, offset, cap, renorm_out=ren)
+    torch.cuda.synchronize()
+    return (tok.cpu().numpy(), ren.cpu().numpy(), si.cpu().numpy(), sr.cpu().numpy(),
+            sl.cpu().numpy(), rt.cpu().numpy().view(np.uint32))
+
+
+def assert_slab_parity(orc, probs, top_k, top_p, seed, offset, cap, out, label):
+    """Tokens and renorm_out as assert_parity; the slab against the oracle's
+    support order (bit-exact indices and lengths) and its renormalised weights
+    (1e-6 relative, zeros exact)."""
+    import oracle
+
+    gtok, gren, si, sr, sl, rt = out
+    otok, _ = assert_parity(orc, probs, top_k, top_p, seed, offset, gtok, gren, label)
+    _, oren, _ = orc.sample(probs, top_k, top_p, seed, offset, want_renorm=True)
+    oi, ow, ol = oracle.slab(orc, probs, top_k, cap, oren)
+    bad = np.flatnonzero(sl != ol)
+    assert bad.size == 0, "%s: slab length mismatch rows %s (gpu %s oracle %s)" % (
+        label, bad[:8], sl[bad[:8]], ol[bad[:8]])
+    bad = np.flatnonzero((si != oi).any(axis=1))
+    assert bad.size == 0, "%s: slab order mismatch on rows %s" % (label, bad[:8])
+    assert np.array_equal(sr == 0, ow == 0), label + ": slab zero pattern"
+    nz = ow != 0
+    if nz.any():
+        rel = np.abs(sr[nz].astype(np.float64) - ow[nz]) / ow[nz]
+        assert rel.max() <= REL_TOL, "%s: slab weight rel err %.3g" % (label, rel.max())
+    assert np.all(np.isin(rt, [0, 1, 2, 3, 4, 5])), label + ": route codes"
+    return otok

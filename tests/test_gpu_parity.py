@@ -467,3 +467,60 @@ def test_random_shapes(sampler, orc, trial):
     log("[gpu] random shapes trial %d B=%d V=%d" % (trial, B, V))
     gtok, gren = run_gpu(sampler, probs, ks, ps, seed, off, renorm=True)
     assert_parity(orc, probs, ks, ps, seed, off, gtok, gren, "random trial %d" % trial)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_slab_export(sampler, orc, cfg):
+    # The sorted support of every row with k_eff <= 1024 (its order is the
+    # cake_sampling slab order), the renormalised weights in that order, and
+    # the same tokens and renorm_out as the plain call.
+    from tests.gpu_util import assert_slab_parity, run_gpu_slab
+
+    w = wl(cfg)
+    log("[gpu] slab export config %d %s" % (cfg, w.name))
+    out = run_gpu_slab(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, 1024)
+    assert_slab_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, 1024, out, w.name)
+    st = sampler.stats(w.B)
+    assert np.array_equal(out[5], st[:, 0]), "route differs from the recorded paths"
+
+
+@pytest.mark.parametrize("V", [151936, 20000, 1000])
+def test_slab_export_edge_rows(sampler, variant_samplers, orc, V):
+    # Restream rows (zeros completing the support), ties, +inf, NaN, split
+    # rows and the forced whole-row and tiny-buffer paths, at capacities
+    # below and above the support sizes.
+    from tests.gpu_util import assert_slab_parity, run_gpu_slab
+
+    rng = np.random.default_rng(V + 31)
+    p1, k1, q1, _ = _restream_batch(V, rng)
+    p2, k2, q2, _ = _adversarial_batch(V, rng)
+    probs = np.concatenate([p1, p2])
+    ks = np.concatenate([k1, k2])
+    ps = np.concatenate([q1, q2])
+    for label, s in (("default", sampler), ("row_select", variant_samplers["row_select"]),
+                     ("tiny_buffer", variant_samplers["tiny_buffer"])):
+        for cap in (1024, 100):
+            log("[gpu] slab edge rows V=%d %s cap %d" % (V, label, cap))
+            out = run_gpu_slab(s, probs, ks, ps, 5, 9, cap)
+            assert_slab_parity(orc, probs, ks, ps, 5, 9, cap, out, "slab V=%d %s" % (V, label))
+
+
+def test_slab_export_split_rows(sampler, orc):
+    from tests.gpu_util import assert_slab_parity, run_gpu_slab
+
+    rng = np.random.default_rng(404)
+    probs, ks, ps, _ = _split_batch(151936, rng)
+    log("[gpu] slab export split rows")
+    out = run_gpu_slab(sampler, probs, ks, ps, 2, 3, 1024)
+    assert np.all(sampler.stats(len(ks))[:, 2] >= 2)
+    assert_slab_parity(orc, probs, ks, ps, 2, 3, 1024, out, "slab split rows")
+
+
+def test_route_report(sampler, variant_samplers):
+    V = 151936
+    ks = np.array([1, 2, 1024, 1025, V - 1, V, 0, -5, V + 7], np.int32)
+    want = [4, 0, 0, 3, 3, 1, 1, 1, 1]
+    assert sampler.route(V, ks).tolist() == want
+    assert variant_samplers["row_select"].route(V, ks).tolist() == [3] * len(ks)
+    # Greedy rows stay greedy for a one-entry vocabulary too (k_eff = V = 1).
+    assert sampler.route(1, np.array([1, 0, 5], np.int32)).tolist() == [4, 4, 4]

@@ -33,7 +33,7 @@ TES_FLAG_SMALL_SEGMENTS = 8
 STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
-            "sampler_get_stats", "sampler_read_probe")
+            "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route")
 
 _lib = None
 
@@ -67,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.sampler_get_stats.restype = ctypes.c_int
         L.sampler_read_probe.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, vp]
         L.sampler_read_probe.restype = ctypes.c_int
+        L.topk_topp_sample_slab.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
+                                            ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp,
+                                            ctypes.c_int, vp, vp, vp]
+        L.topk_topp_sample_slab.restype = ctypes.c_int
+        L.sampler_route.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.sampler_route.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -104,6 +110,30 @@ def sampler_get_stats(handle, B: int):
     rc = lib().sampler_get_stats(handle, out.ctypes.data, int(B))
     if rc != TES_OK:
         raise TesError(rc, "sampler_get_stats")
+    return out
+
+
+def topk_topp_sample_slab(handle, probs_ptr: int, B: int, V: int, top_k_ptr: int, top_p_ptr: int,
+                          seed: int, offset: int, out_tokens_ptr: int, renorm_ptr, slab_index_ptr: int,
+                          slab_renorm_ptr: int, slab_cap: int, slab_len_ptr: int, route_ptr,
+                          stream) -> int:
+    """Raw call with device pointers (ints); returns the status code."""
+    return lib().topk_topp_sample_slab(handle, probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
+                                       int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                       out_tokens_ptr, renorm_ptr, slab_index_ptr,
+                                       slab_renorm_ptr, int(slab_cap), slab_len_ptr, route_ptr,
+                                       stream)
+
+
+def sampler_route(handle, V: int, top_k_host):
+    """Per-row path codes from host top_k, without launching anything."""
+    import numpy as np
+
+    k = np.ascontiguousarray(top_k_host, dtype=np.int32)
+    out = np.zeros(k.size, np.uint32)
+    rc = lib().sampler_route(handle, int(k.size), int(V), k.ctypes.data, out.ctypes.data)
+    if rc != TES_OK:
+        raise TesError(rc, "sampler_route")
     return out
 
 
@@ -151,6 +181,37 @@ class Sampler:
         if rc != TES_OK:
             raise TesError(rc, "topk_topp_sample")
         return out_tokens
+
+    def sample_slab(self, probs, top_k, top_p, seed: int, offset: int, slab_cap: int,
+                    out_tokens=None, renorm_out=None, stream=None, want_route: bool = True):
+        """Sample and export each row's sorted support (see topk_topp_sample_slab);
+        returns (tokens, slab_index, slab_renorm, slab_len, route or None)."""
+        import torch
+
+        B, V = probs.shape
+        for t, dt in ((probs, torch.float32), (top_k, torch.int32), (top_p, torch.float32)):
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("expected contiguous %s on the GPU" % dt)
+        dev = probs.device
+        if out_tokens is None:
+            out_tokens = torch.empty(B, dtype=torch.int32, device=dev)
+        si = torch.empty((B, slab_cap), dtype=torch.int32, device=dev)
+        sr = torch.empty((B, slab_cap), dtype=torch.float32, device=dev)
+        sl = torch.empty(B, dtype=torch.int32, device=dev)
+        rt = torch.empty(B, dtype=torch.int32, device=dev) if want_route else None
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = topk_topp_sample_slab(self.handle, probs.data_ptr(), B, V, top_k.data_ptr(),
+                                   top_p.data_ptr(), seed, offset, out_tokens.data_ptr(),
+                                   renorm_out.data_ptr() if renorm_out is not None else None,
+                                   si.data_ptr(), sr.data_ptr(), slab_cap, sl.data_ptr(),
+                                   rt.data_ptr() if rt is not None else None, stream.cuda_stream)
+        if rc != TES_OK:
+            raise TesError(rc, "topk_topp_sample_slab")
+        return out_tokens, si, sr, sl, rt
+
+    def route(self, V: int, top_k_host):
+        return sampler_route(self.handle, V, top_k_host)
 
     def stats(self, B: int):
         return sampler_get_stats(self.handle, B)

@@ -118,13 +118,14 @@ struct RowState {  // zero between calls
 };
 static_assert(sizeof(RowState) == 64, "row state size");
 
-struct Decision {  // what renorm_out needs
+struct Decision {  // what renorm_out and the slab export need
     u32 kind;
     u32 m;
     u32 token;
     u32 path;
     u64 c_keep;  // kept entries have composite >= c_keep
     u64 M_p;     // kept mass (normal rows)
+    u64 c_k;     // the support is the entries with composite >= c_k (k_eff < V)
 };
 
 struct PubC {  // first exchange of a top-p-only segment (and its gather count)
@@ -297,6 +298,7 @@ struct Outcome {  // a resolved row
     u64 c_keep;  // kept entries have composite >= c_keep
     u64 M_p;     // kept mass (normal rows)
     u32 m;       // kept +inf entries (+inf rows)
+    u64 c_k;     // smallest composite of the support (0: the whole row)
 };
 
 // ---------------------------------------------------------------------------
@@ -1019,8 +1021,13 @@ __device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u3
         ninf_l += (in && key == kInfKey) ? 1u : 0u;
         msum += q[j];
     }
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        if (base + j == kk - 1) s.loc_above[3] = v[j];  // read after block_sum's barriers
     const u64 ninf = block_sum(s, ninf_l);
     Outcome o{};
+    const u64 c_k = uni(s.loc_above[3]);
+    o.c_k = c_k;
     if (threadIdx.x == 0) s.bc[0] = s.bc[1] = s.bc[2] = s.bc[3] = 0;
     if (ninf > 0) {
         // +inf entries sort first, in index order: keep them all, draw the t-th.
@@ -1243,8 +1250,11 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
         const u32 kd = (kkey >> kFineShift) - tbin;
         const int bk = (int)(kd < (u32)kTabBins ? kd : (u32)kTabBins - 1);
         bool ok = !has_inf && bv.load(bk);
-        u64 Mk = 0;
-        if (ok) Mk = bv.mass_above(bk) + read_lane(bv.inc, k - 1 - bv.st);
+        u64 Mk = 0, ck = 0;
+        if (ok) {
+            Mk = bv.mass_above(bk) + read_lane(bv.inc, k - 1 - bv.st);
+            ck = read_lane(bv.v, k - 1 - bv.st);
+        }
         ok = ok && Mk > 0;
         u64 cT = 0, Mp = 0, cd = 0;
         if (ok) {
@@ -1272,6 +1282,7 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
             s.bc[1] = cT;
             s.bc[2] = Mp;
             s.bc[3] = cd;
+            s.loc_above[3] = ck;
         }
     }
     __syncthreads();
@@ -1281,6 +1292,7 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
     o.c_keep = uni(s.bc[1]);
     o.M_p = uni(s.bc[2]);
     o.token = comp_index(uni(s.bc[3]));
+    o.c_k = uni(s.loc_above[3]);
     __syncthreads();
     return ok;
 }
@@ -1512,6 +1524,7 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
     Outcome o{};
     u64 lo = 0;
     if (k_eff < V) lo = select_row<VEC>(s, row, nvec, k_eff, false, 0, gather_cap).c;
+    o.c_k = lo;
     u64 mk = 0, ninf = 0, minidx = ~0ull;
     for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
         if (valid && composite(key, idx) >= lo) {
@@ -1562,6 +1575,7 @@ __device__ void finish_row(Smem& s, const Params& p, u32 r, const Outcome& o, u3
         *gp(&d->token) = o.token;
         *gp(&d->path) = path;
         *gp(&d->c_keep) = o.c_keep;
+        *gp(&d->c_k) = o.c_k;
         *gp(&d->M_p) = o.M_p;
         if (p.stats) {
             u32* st = p.stats + kStatWords * (size_t)(p.row_base + r);
@@ -1676,6 +1690,7 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     const u32 key = comp_key(cbest);
     o.token = comp_index(cbest);
     o.c_keep = cbest;
+    o.c_k = cbest;
     o.m = 1;
     o.M_p = key_mass(key);
     o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
@@ -1687,26 +1702,40 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // ---------------------------------------------------------------------------
 template <int VEC>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         u32 wfill, u32 path = kPathSlab);
+                                         u32 wfill, u32 path = kPathSlab, u64 c_k = ~0ull);
 
-// The smallest index of the row whose key is zero (NaN, negative, -0.0 or
-// +0.0), read in steps of one vector per thread until a step holds one; ~0u
-// when there is none.
+// The index of the m-th (m >= 1) entry of the row, in index order, whose key
+// is zero (NaN, negative, -0.0 or +0.0), read in steps of one vector per
+// thread until a step holds it; ~0u when the row has fewer than m.
 template <int VEC>
-__device__ u32 first_zero_index(Smem& s, const float* __restrict__ row, u32 nvec) {
+__device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, u32 m) {
     typedef typename VecT<VEC>::T VT;
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
+    u32 before = 0;  // zeros in the steps already read (workgroup-uniform)
     for (u32 v0 = 0; v0 < nvec; v0 += kBlock) {
         const u32 iv = v0 + threadIdx.x;
-        u64 best = ~0ull;
+        u32 zmask = 0;
         if (iv < nvec) {
             const VT x = ld_g(&rv[iv]);
 #pragma unroll
-            for (int e = VEC - 1; e >= 0; --e)
-                if (sanitize(__float_as_uint(VecT<VEC>::get(x, e))) == 0u) best = (u64)iv * VEC + e;
+            for (int e = 0; e < VEC; ++e)
+                zmask |= sanitize(__float_as_uint(VecT<VEC>::get(x, e))) == 0u ? 1u << e : 0u;
         }
-        best = block_min(s, best);
-        if (best != ~0ull) return (u32)best;
+        const u32 c = (u32)__popc(zmask);
+        const u32 ex = (u32)block_excl_scan(s, c);
+        if (threadIdx.x == kBlock - 1) s.ctr[2] = ex + c;
+        if (threadIdx.x == 0) s.misc[4] = ~0u;
+        __syncthreads();
+        if (c && before + ex < m && m <= before + ex + c) {
+            u32 need = m - before - ex, mm = zmask;  // the need-th set bit of the mask
+            while (--need) mm &= mm - 1;
+            s.misc[4] = iv * VEC + (u32)__builtin_ctz(mm);
+        }
+        __syncthreads();
+        const u32 hit = uni(s.misc[4]);
+        before += uni(s.ctr[2]);
+        __syncthreads();
+        if (hit != ~0u) return hit;
     }
     return ~0u;
 }
@@ -1779,17 +1808,26 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     // The binned finish's base: at most 1.0, so that +inf entries land in its
     // top bin, where it looks for them.
     const u32 tkey = n ? min(comp_key(mn), kOneKey) & ~0xFFFFu : 0u;
-    if (n >= k || (n > 0 && mass > 0)) {
-        // n < k: the zeros that complete the support change nothing.
-        slab_finish<VEC>(s, r, n, n >= k ? k : n, tkey, P, u, ~0u, kPathSlabFallback);
+    if (n >= k) {
+        slab_finish<VEC>(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
         return;
     }
-    // No mass in the support: its smallest index (n < k, so zeros complete it).
+    // n < k: the support ends with the k - n lowest-indexed zeros; its
+    // boundary is the last of them.
+    const u32 zk = mth_zero_index<VEC>(s, row, p.nvec, k - n);
+    const u64 c_k = composite(0u, zk);
+    if (n > 0 && mass > 0) {
+        // The zeros carry no mass: they change nothing else.
+        slab_finish<VEC>(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
+        return;
+    }
+    // No mass in the support: its smallest index.
     midx = block_min(s, midx);
-    const u32 z = first_zero_index<VEC>(s, row, p.nvec);
+    const u32 z = mth_zero_index<VEC>(s, row, p.nvec, 1);
     Outcome o{};
     o.kind = kZeroRow;
     o.token = (u32)(midx < (u64)z ? midx : (u64)z);
+    o.c_k = c_k;
     finish_row(s, p, r, o, kPathSlabFallback, n);
 }
 
@@ -2054,7 +2092,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // with zeros, which sort last) and finish on the first k positions.
 template <int VEC>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         u32 wfill, u32 path) {
+                                         u32 wfill, u32 path, u64 c_k) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
@@ -2064,6 +2102,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         Outcome ob;
         if (binned_topk(s, n, k, tkey, P, u, ob, wfill)) {
             stat_phase(p, r, 9, tp);
+            if (c_k != ~0ull) ob.c_k = c_k;
             finish_row(s, p, r, ob, path, gathered);
             return;
         }
@@ -2095,6 +2134,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         o = resolve_sorted<4>(s, v, k, P, u);
     }
     stat_phase(p, r, 9, tp);
+    if (c_k != ~0ull) o.c_k = c_k;
     finish_row(s, p, r, o, path, gathered);
 }
 
@@ -2776,6 +2816,95 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
 
 
 
+// Slab export: one workgroup per row writes the row's support in its sorted
+// order (descending probability, ascending index, the order in which the
+// cake_sampling page emits its slab) with the renormalised weight of each
+// entry (the renorm_out value at that index), for supports of at most `cap`
+// entries; other rows get length -1.  The support is every entry whose
+// composite is at least the row's boundary c_k (the whole row when k_eff = V),
+// collected in one pass over the row and sorted by a bitonic network in LDS.
+constexpr int kSlabThreads = 256;
+constexpr u32 kSlabExportMax = 1024;
+
+template <int VEC>
+__global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
+    const float* __restrict__ probs, u32 V, u32 nvec, const int32_t* __restrict__ top_k,
+    const Decision* __restrict__ dec, u32 cap, int32_t* __restrict__ slab_index,
+    float* __restrict__ slab_renorm, int32_t* __restrict__ slab_len, u32* __restrict__ route) {
+    typedef typename VecT<VEC>::T VT;
+    __shared__ u64 buf[kSlabExportMax];
+    __shared__ u32 cnt;
+    const u32 r = blockIdx.x;
+    const Decision d = dec[r];
+    const int32_t kr = top_k[r];
+    const u32 k_eff = (kr <= 0 || (u32)kr >= V) ? V : (u32)kr;
+    int32_t* oi = slab_index + (size_t)r * cap;
+    float* ow = slab_renorm + (size_t)r * cap;
+    if (threadIdx.x == 0) {
+        if (route) route[r] = d.path;
+        slab_len[r] = k_eff <= cap ? (int32_t)k_eff : -1;
+        cnt = 0;
+    }
+    if (k_eff > cap) {
+        for (u32 j = threadIdx.x; j < cap; j += kSlabThreads) {
+            oi[j] = -1;
+            ow[j] = 0.0f;
+        }
+        return;
+    }
+    const u64 lo = k_eff == V ? 0ull : d.c_k;
+    __syncthreads();
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
+    for (u32 iv = threadIdx.x; iv < nvec; iv += kSlabThreads) {
+        const VT x = rv[iv];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u64 c = composite(sanitize(__float_as_uint(VecT<VEC>::get(x, e))), iv * VEC + e);
+            if (c >= lo) {
+                const u32 pos = atomicAdd(&cnt, 1u);
+                if (pos < kSlabExportMax) buf[pos] = c;
+            }
+        }
+    }
+    __syncthreads();
+    const u32 n = cnt < k_eff ? cnt : k_eff;  // exactly k_eff for a consistent boundary
+    u32 n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (u32 i = n + threadIdx.x; i < n2; i += kSlabThreads) buf[i] = 0;
+    __syncthreads();
+    // Bitonic sort of buf[0, n2), descending (composites are unique; zeros pad).
+    for (u32 size = 2; size <= n2; size <<= 1) {
+        for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
+            for (u32 t = threadIdx.x; t < n2 / 2; t += kSlabThreads) {
+                const u32 i = 2 * t - (t & (stride - 1));  // lower element of the pair
+                const u32 j = i + stride;
+                const u64 a = buf[i], b = buf[j];
+                const bool desc = (i & size) == 0;
+                if (desc ? a < b : a > b) {
+                    buf[i] = b;
+                    buf[j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
+    const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
+    for (u32 j = threadIdx.x; j < cap; j += kSlabThreads) {
+        if (j < n) {
+            const u64 c = buf[j];
+            const u32 key = comp_key(c);
+            const bool kept = d.kind != kZeroRow && c >= d.c_keep;
+            oi[j] = (int32_t)comp_index(c);
+            ow[j] = !kept ? 0.0f
+                          : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
+        } else {
+            oi[j] = -1;
+            ow[j] = 0.0f;
+        }
+    }
+}
+
 // Reference stream: reads nvec 16-byte vectors once (coalesced, eight loads
 // per thread in flight, non-temporal like the sampler's row loads) and folds
 // them into one word, stored only when it equals a value no input is expected
@@ -2912,10 +3041,18 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     return TES_OK;
 }
 
-extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V,
-                                const int32_t* top_k, const float* top_p, uint64_t seed,
-                                uint64_t offset, int32_t* out_tokens, float* renorm_out,
-                                void* stream) {
+struct SlabOut {
+    int32_t* index;
+    float* renorm;
+    int32_t* len;
+    uint32_t* route;
+    u32 cap;
+};
+
+namespace {
+int sample_impl(tes_sampler* s, const float* probs, int B, int V, const int32_t* top_k,
+                const float* top_p, uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                float* renorm_out, const SlabOut* slab, void* stream) {
     if (!s || B < 0 || V < 1) return TES_ERR_INVALID_ARGUMENT;
     if (B > s->max_batch || V > s->max_vocab) return TES_ERR_TOO_LARGE;
     if (B == 0) return TES_OK;
@@ -2986,6 +3123,69 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
                                    p.probs, (u32)V, nvec, dec, ro);
             if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
         }
+        if (slab) {
+            const Decision* dec =
+                reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
+            const size_t o = (size_t)c0 * slab->cap;
+            if (vec4)
+                hipLaunchKernelGGL(tes_slab_kernel<4>, dim3(rows), dim3(kSlabThreads), 0, st,
+                                   p.probs, (u32)V, nvec, p.top_k, dec, slab->cap,
+                                   slab->index + o, slab->renorm + o, slab->len + c0,
+                                   slab->route ? slab->route + c0 : nullptr);
+            else
+                hipLaunchKernelGGL(tes_slab_kernel<1>, dim3(rows), dim3(kSlabThreads), 0, st,
+                                   p.probs, (u32)V, nvec, p.top_k, dec, slab->cap,
+                                   slab->index + o, slab->renorm + o, slab->len + c0,
+                                   slab->route ? slab->route + c0 : nullptr);
+            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        }
+    }
+    return TES_OK;
+}
+}  // namespace
+
+extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V,
+                                const int32_t* top_k, const float* top_p, uint64_t seed,
+                                uint64_t offset, int32_t* out_tokens, float* renorm_out,
+                                void* stream) {
+    return sample_impl(s, probs, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
+                       nullptr, stream);
+}
+
+extern "C" int topk_topp_sample_slab(tes_sampler* s, const float* probs, int B, int V,
+                                     const int32_t* top_k, const float* top_p, uint64_t seed,
+                                     uint64_t offset, int32_t* out_tokens, float* renorm_out,
+                                     int32_t* slab_index, float* slab_renorm, int slab_cap,
+                                     int32_t* slab_len, uint32_t* route, void* stream) {
+    if (B > 0 && (!slab_index || !slab_renorm || !slab_len)) return TES_ERR_INVALID_ARGUMENT;
+    if (slab_cap < 1 || slab_cap > (int)kSlabExportMax) return TES_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)slab_index & 3) || ((uintptr_t)slab_renorm & 3) || ((uintptr_t)slab_len & 3) ||
+        ((uintptr_t)route & 3))
+        return TES_ERR_INVALID_ARGUMENT;
+    const SlabOut slab{slab_index, slab_renorm, slab_len, route, (u32)slab_cap};
+    return sample_impl(s, probs, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out, &slab,
+                       stream);
+}
+
+extern "C" int sampler_route(tes_sampler* s, int B, int V, const int32_t* top_k_host,
+                             uint32_t* route_host) {
+    if (!s || B < 0 || V < 1 || (B > 0 && (!top_k_host || !route_host)))
+        return TES_ERR_INVALID_ARGUMENT;
+    if (B > s->max_batch || V > s->max_vocab) return TES_ERR_TOO_LARGE;
+    // Rows are 16-byte streamed when V % 4 == 0 (with an aligned base); the
+    // segment count of a top-p-only row follows from that.
+    const u32 nvec = (V % 4 == 0) ? (u32)V / 4 : (u32)V;
+    const u32 s_full = ceil_div(nvec, s->seg_full);
+    for (int b = 0; b < B; ++b) {
+        const int32_t k = top_k_host[b];
+        const u32 k_eff = (k <= 0 || k >= V) ? (u32)V : (u32)k;
+        u32 path;
+        if (s->flags & TES_FLAG_FORCE_ROW_SELECT) path = kPathWhole;
+        else if (k_eff == 1) path = kPathGreedy;
+        else if (k_eff <= kSlabMaxK) path = kPathSlab;
+        else if (k_eff == (u32)V && s_full <= s->s_ws) path = kPathFull;
+        else path = kPathWhole;
+        route_host[b] = path;
     }
     return TES_OK;
 }
