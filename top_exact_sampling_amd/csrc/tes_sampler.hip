@@ -2823,7 +2823,7 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
 // entries; other rows get length -1.  The support is every entry whose
 // composite is at least the row's boundary c_k (the whole row when k_eff = V),
 // collected in one pass over the row and sorted by a bitonic network in LDS.
-constexpr int kSlabThreads = 256;
+constexpr int kSlabThreads = 512;
 constexpr u32 kSlabExportMax = 1024;
 
 template <int VEC>
@@ -2854,15 +2854,35 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
     }
     const u64 lo = k_eff == V ? 0ull : d.c_k;
     __syncthreads();
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
-    for (u32 iv = threadIdx.x; iv < nvec; iv += kSlabThreads) {
-        const VT x = rv[iv];
+    if (k_eff == 1) {
+        // A one-entry support is the boundary itself: no pass over the row.
+        if (threadIdx.x == 0) {
+            buf[0] = lo;
+            cnt = 1;
+        }
+    } else {
+        // Eight loads per thread in flight: a single workgroup streams the row.
+        const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
+        constexpr u32 kU = 8;
+        for (u32 i0 = 0; i0 < nvec; i0 += kU * kSlabThreads) {
+            VT x[kU];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const u64 c = composite(sanitize(__float_as_uint(VecT<VEC>::get(x, e))), iv * VEC + e);
-            if (c >= lo) {
-                const u32 pos = atomicAdd(&cnt, 1u);
-                if (pos < kSlabExportMax) buf[pos] = c;
+            for (u32 j = 0; j < kU; ++j) {
+                const u32 iv = i0 + j * kSlabThreads + threadIdx.x;
+                x[j] = ld_stream(&rv[iv < nvec ? iv : nvec - 1]);
+            }
+#pragma unroll
+            for (u32 j = 0; j < kU; ++j) {
+                const u32 iv = i0 + j * kSlabThreads + threadIdx.x;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const u64 c =
+                        composite(sanitize(__float_as_uint(VecT<VEC>::get(x[j], e))), iv * VEC + e);
+                    if (iv < nvec && c >= lo) {
+                        const u32 pos = atomicAdd(&cnt, 1u);
+                        if (pos < kSlabExportMax) buf[pos] = c;
+                    }
+                }
             }
         }
     }
