@@ -57,6 +57,16 @@ def test_host_side_argument_validation():
         tes.sampler_create(0, 4, 100, flags=1 << 20)
     assert e.value.status == tes.TES_ERR_INVALID_ARGUMENT
     assert tes.sampler_destroy(None) == tes.TES_OK
+    # Slab export: no handle, or a capacity out of range.
+    assert tes.topk_topp_sample_slab(None, 0, 1, 10, 0, 0, 0, 0, 0, None, 16, 16, 8, 16, None,
+                                     None) == tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.lib().sampler_route(None, 1, 10, None, None) == tes.TES_ERR_INVALID_ARGUMENT
+    # Reference read: null, misaligned or ragged buffers.
+    assert tes.sampler_read_probe(0, 16, 64, 0, None) == tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.sampler_read_probe(8, 16, 64, 0, None) == tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.sampler_read_probe(16, 20, 64, 0, None) == tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.sampler_read_probe(16, 16, 0, 0, None) == tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.sampler_read_probe(16, 16, 64, -1, None) == tes.TES_ERR_INVALID_ARGUMENT
 
 
 def test_create_without_gpu_reports_no_device():

@@ -524,3 +524,18 @@ def test_route_report(sampler, variant_samplers):
     assert variant_samplers["row_select"].route(V, ks).tolist() == [3] * len(ks)
     # Greedy rows stay greedy for a one-entry vocabulary too (k_eff = V = 1).
     assert sampler.route(1, np.array([1, 0, 5], np.int32)).tolist() == [4, 4, 4]
+
+
+def test_read_probe_reads_and_leaves_the_sink(torch_cuda):
+    # The reference read kernel runs over ordinary data without writing its
+    # sink (the fold of these bytes is not the sentinel) and reports success.
+    torch = torch_cuda
+    x = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    log("[gpu] read probe")
+    rc = tes.sampler_read_probe(x.data_ptr(), x.numel() * 4, sink.data_ptr(), 0,
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == tes.TES_OK
+    assert tes.sampler_read_probe(x.data_ptr(), 0, sink.data_ptr(), 0, None) == tes.TES_OK
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
