@@ -156,7 +156,7 @@ struct Params {
     u32 rowbytes;   // bytes of the per-row exchange area
     u32 chunk;      // rows the workspace holds
     u32 flags;
-    u32 split;      // workgroups a top-k or greedy row may be split between (1 or 2)
+    u32 split;      // parts a top-k or greedy row may be split into (1 .. kMaxSplit)
     u32 slots;      // workgroups resident at once on the device
 };
 
@@ -1626,7 +1626,7 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     typedef typename VecT<VEC>::T VT;
     stat_start(p, r, S);
     const u64 tp = p.stats ? wall_clock64() : 0;
-    // This workgroup's part: the row, or half of it when split.
+    // This workgroup's part: the row, or one of its S parts when split.
     const u32 hv = (p.nvec + S - 1) / S;
     const u32 v0 = h * hv;
     const u32 nv = min(v0 + hv, p.nvec) - v0;
@@ -1743,7 +1743,7 @@ __device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, 
 // Exact single pass over the whole row for a top-k row (k <= kSlabMaxK) that
 // its sampled threshold could not decide: a sample with too few entries with a
 // mass, a candidate buffer that overflowed (long runs of equal values at the
-// threshold) or a split row whose halves did not join.  Every entry with key
+// threshold) or a split row whose parts did not join.  Every entry with key
 // >= theta0 (theta0 >= 1) is appended to the LDS buffer; whenever the buffer
 // could not take one more step, it is cut to the best k so far (a radix select)
 // and the threshold rises to one above the k-th key: the row is read in index
@@ -1831,30 +1831,30 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     finish_row(s, p, r, o, kPathSlabFallback, n);
 }
 
-// Streams its part of the row (the whole row, or half of it when the row is
-// split between two workgroups) once and keeps, in the LDS buffer, every entry
-// whose key is at or above a threshold key tkey > 0, chosen so that about
-// 1.5 k (and at least k) entries of the row pass.  The test is one subtraction
-// and one compare on the raw bits: sanitize(b) >= tkey exactly when tkey <= b
-// <= the bits of +inf.
+// Streams its part of the row (the whole row, or one of S <= kMaxSplit parts
+// when the row is split between S workgroups) once and keeps, in the LDS
+// buffer, every entry whose key is at or above a threshold key tkey > 0,
+// chosen so that about 1.5 k (2 k for more than two parts) of the row's share
+// pass.  The test is one subtraction and one compare on the raw bits:
+// sanitize(b) >= tkey exactly when tkey <= b <= the bits of +inf.
 //   The first kSampleDepth steps (2048 entries each, the first loads in
 //   flight) are a sample: their keys are counted in 1/128-octave bins before
 //   anything else happens, and tkey becomes the lower edge of the bin that
-//   holds the sample's j-th best, j = ceil(1.5 k n / V) + 12 for n sampled
-//   entries (j = k when the sample is the whole row).
+//   holds the sample's j-th best, j = ceil(c k n / V) + 12 for n sampled
+//   entries and c = 1.5 or 2 (j = k when the sample is the whole row).
 //   Then the part is streamed from its start with no barriers and no atomics:
 //   each wave appends to its own region of kSlabCap / 8 entries, at its
 //   running count (a scalar) plus the lane's rank among the wave's passing
 //   lanes (mbcnt of the element's ballot).  Entries beyond a region are
-//   counted but not written.  Afterwards the regions are packed together.
+//   counted but not written.
 // The buffer then holds exactly the part's entries at or above tkey.  A whole
-// row that kept at least k without overflowing holds the row's best k.  The
-// two halves of a split row publish their buffers and thresholds; the last to
-// arrive joins them, and with T = the larger threshold, every entry of the row
-// at or above T is in the union, so the union holds the row's best k when at
-// least k of its entries are at or above T.  Rows that fail these tests (or
-// whose sample holds fewer than j entries with a mass) are resolved by
-// whole-row passes.
+// row that kept at least k without overflowing holds the row's best k and is
+// finished from the wave regions directly.  The parts of a split row publish
+// their buffers and thresholds; the last to arrive keeps every part's entries
+// at or above T = the largest threshold (every entry of the row at or above T
+// is among them), which hold the row's best k when there are at least k of
+// them.  Rows that fail these tests (or whose sample holds fewer than j
+// entries with a mass) are decided by the compacting restream.
 template <int VEC>
 __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u32 h, u32 S) {
     const Params p = params_from(s);
@@ -1914,7 +1914,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     }
     __syncthreads();  // the histogram is dead; the buffer takes its place
     const bool no_tkey = tkey == 0;
-    if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the half reports itself unusable
+    if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the part reports itself unusable
     if (no_tkey && S == 1) {
         // Fewer than j sampled entries have a mass (a row of mostly zeros, or
         // a short row with fewer than k): one exact pass over every positive key.
