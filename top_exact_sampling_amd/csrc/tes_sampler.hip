@@ -2772,11 +2772,14 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     } else if (item < greedy_end) {
         const u32 i = (item - first_end) / Sg;
         const u32 r = uni((u32)s.rows[nf + n_whole + n_slab + i]);
-        // Greedy rows yield bandwidth unless they make up more than three
-        // quarters of the rows (measured: 75% greedy batch 41.3 -> 36.9 us,
-        // hetero batch 40.7 -> 39.4 us; an all-greedy batch keeps 29 us).
+        // Greedy rows yield bandwidth when the launch fills at least half
+        // the resident slots (below that HBM is not saturated and yielding
+        // only slows them: B=128 with 64 greedy rows 24.4 -> 27.2 us) and
+        // they make up at most three quarters of the rows (measured: 75%
+        // greedy B=256 batch 41.3 -> 36.9 us, hetero batch 40.7 -> 39.4 us;
+        // an all-greedy batch keeps 29 us).
         do_greedy<VEC>(s, r, item - first_end - i * Sg, Sg,
-                       n_greedy <= 3 * (n_slab + nf + n_whole));
+                       n_greedy <= 3 * (n_slab + nf + n_whole) && 2 * base_items >= p.slots);
     } else if (item < greedy_end + n_slab * (S - 1)) {
         const u32 i = (item - greedy_end) % n_slab, h = 1 + (item - greedy_end) / n_slab;
         const u32 r = uni((u32)s.rows[nf + n_whole + i]);
