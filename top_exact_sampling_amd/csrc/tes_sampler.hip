@@ -1211,6 +1211,69 @@ struct BinView {
     }
 };
 
+// One wave: the j-th smallest (0-based) vocabulary index among the entries
+// sbuf(s)[st, st + n), whose indices are distinct.  A radix select on the
+// index, 8 bits per round from the highest bit in which the indices differ,
+// counting into 256 LDS counters (the top-p-only rows' fine-mass array, unused
+// by top-k rows).  All 64 lanes must take part.
+__device__ __noinline__ u32 wave_nth_index(Smem& s, u32 st, u32 n, u32 j) {
+    u32* tab = reinterpret_cast<u32*>(s.finem);
+    static_assert(sizeof(s.finem) >= 256 * sizeof(u32), "256 counters fit");
+    const u32 lane = lane_id();
+    u64 lo = ~0ull, hi = 0;
+    for (u32 i = lane; i < n; i += 64) {
+        const u64 x = comp_index(sbuf(s)[st + i]);
+        lo = x < lo ? x : lo;
+        hi = x > hi ? x : hi;
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    const u32 diff = (u32)(lo ^ hi);
+    int sh = diff ? ((31 - __builtin_clz(diff)) & ~7) : 0;
+    u32 prefix = (u32)lo & ~((2u << (sh + 7)) - 1u);  // bits above the first round
+    if (sh + 8 >= 32) prefix = 0;
+    u32 pmask = sh + 8 >= 32 ? 0u : ~((1u << (sh + 8)) - 1u);
+    for (; sh >= 0; sh -= 8) {
+        for (u32 b = lane; b < 256u; b += 64) tab[b] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        for (u32 i0 = 0; i0 < n; i0 += 64) {
+            const u32 i = i0 + lane;
+            const u32 idx = i < n ? comp_index(sbuf(s)[st + i]) : 0u;
+            hist_add(tab, nullptr, false, i < n && (idx & pmask) == prefix, (idx >> sh) & 255u, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const u32 c0 = tab[4 * lane], c1 = tab[4 * lane + 1], c2 = tab[4 * lane + 2],
+                  c3 = tab[4 * lane + 3];
+        const u32 loc = c0 + c1 + c2 + c3;
+        const u32 incl = (u32)wave_incl_scan((u64)loc);
+        const u32 excl = incl - loc;
+        const u64 m = __builtin_amdgcn_ballot_w64(excl <= j && j < incl);
+        const int L = m ? (int)__builtin_ctzll(m) : 0;
+        u32 jj = j - (u32)__builtin_amdgcn_readlane((int)excl, L);
+        const u32 d0 = (u32)__builtin_amdgcn_readlane((int)c0, L);
+        const u32 d1 = (u32)__builtin_amdgcn_readlane((int)c1, L);
+        const u32 d2 = (u32)__builtin_amdgcn_readlane((int)c2, L);
+        u32 d = 4u * (u32)L;
+        if (jj >= d0) {
+            jj -= d0;
+            ++d;
+            if (jj >= d1) {
+                jj -= d1;
+                ++d;
+                if (jj >= d2) {
+                    jj -= d2;
+                    ++d;
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // reads done before the next clear
+        prefix |= d << sh;
+        pmask |= 255u << sh;
+        j = jj;
+    }
+    return prefix;
+}
+
 // Top-k finish from the candidate buffer sbuf(s)[0, n), k <= n <= kSlabCap,
 // which holds every entry of the row with key >= tkey (0 < tkey <= 1.0, a
 // multiple of 2^16).  Bins are 1/128-octave key ranges counted from tkey (bin
@@ -1249,32 +1312,75 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
         const u32 kkey = comp_key(sbuf(s)[k - 1]);
         const u32 kd = (kkey >> kFineShift) - tbin;
         const int bk = (int)(kd < (u32)kTabBins ? kd : (u32)kTabBins - 1);
-        bool ok = !has_inf && bv.load(bk);
+        // A bin of more than 64 entries (bv.load fails) whose entries all share
+        // one key (long runs of equal values) is ordered by index alone: its
+        // position j holds the j-th smallest index, found by a radix select on
+        // the index, and every entry has the same mass q, so mass positions
+        // are quotients.
+        auto tie_key = [&](int b, u32& key) {
+            const u32 st0 = bv.cnt_above(b), nb = bv.end_of(b) - st0;
+            key = comp_key(sbuf(s)[st0]);
+            bool same = true;
+            for (u32 i = lane; i < nb; i += 64) same = same && comp_key(sbuf(s)[st0 + i]) == key;
+            return __ballot(!same) == 0;
+        };
+        auto nth = [&](int b, u32 j) {
+            return wave_nth_index(s, bv.cnt_above(b), bv.end_of(b) - bv.cnt_above(b), j);
+        };
+        bool ok = !has_inf;
         u64 Mk = 0, ck = 0;
+        u32 key = 0;
         if (ok) {
-            Mk = bv.mass_above(bk) + read_lane(bv.inc, k - 1 - bv.st);
-            ck = read_lane(bv.v, k - 1 - bv.st);
+            if (bv.load(bk)) {
+                Mk = bv.mass_above(bk) + read_lane(bv.inc, k - 1 - bv.st);
+                ck = read_lane(bv.v, k - 1 - bv.st);
+            } else {
+                ok = tie_key(bk, key);
+                if (ok) {
+                    const u32 j = k - 1 - bv.cnt_above(bk);
+                    Mk = bv.mass_above(bk) + (u64)(j + 1) * key_mass(key);
+                    ck = composite(key, nth(bk, j));
+                }
+            }
         }
         ok = ok && Mk > 0;
         u64 cT = 0, Mp = 0, cd = 0;
         if (ok) {
             const u64 T = topp_threshold(P, Mk);
             const int bT = bv.find_mass(T);
-            ok = bv.load(bT);
-            const u64 base = ok ? bv.mass_above(bT) : 0;
-            const u64 mT = ok ? __ballot(base + bv.inc >= T) : 0;
-            ok = mT != 0;  // always set for a consistent table
+            const u64 base = bv.mass_above(bT);
+            if (bv.load(bT)) {
+                const u64 mT = __ballot(base + bv.inc >= T);
+                ok = mT != 0;  // always set for a consistent table
+                if (ok) {
+                    const u32 L = (u32)__builtin_ctzll(mT);
+                    cT = read_lane(bv.v, L);
+                    Mp = base + read_lane(bv.inc, L);
+                }
+            } else {
+                ok = tie_key(bT, key) && key_mass(key) > 0;
+                if (ok) {
+                    const u64 q = key_mass(key);
+                    const u32 j = (u32)((T - base + q - 1) / q) - 1;  // first with base + (j+1) q >= T
+                    cT = composite(key, nth(bT, j));
+                    Mp = base + (u64)(j + 1) * q;
+                }
+            }
             if (ok) {
-                const u32 L = (u32)__builtin_ctzll(mT);
-                cT = read_lane(bv.v, L);
-                Mp = base + read_lane(bv.inc, L);
                 const u64 t = __umul64hi(u, Mp);
                 const int bd = bv.find_mass(t + 1);
-                ok = bv.load(bd);
-                const u64 base2 = ok ? bv.mass_above(bd) : 0;
-                const u64 md = ok ? __ballot(base2 + bv.inc > t) : 0;
-                ok = md != 0;
-                if (ok) cd = read_lane(bv.v, (u32)__builtin_ctzll(md));
+                const u64 base2 = bv.mass_above(bd);
+                if (bv.load(bd)) {
+                    const u64 md = __ballot(base2 + bv.inc > t);
+                    ok = md != 0;
+                    if (ok) cd = read_lane(bv.v, (u32)__builtin_ctzll(md));
+                } else {
+                    ok = tie_key(bd, key) && key_mass(key) > 0;
+                    if (ok) {
+                        const u64 q = key_mass(key);
+                        cd = composite(key, nth(bd, (u32)((t - base2) / q)));  // first with base2 + (j+1) q > t
+                    }
+                }
             }
         }
         if (lane_id() == 0) {
