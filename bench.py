@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="input recipe (workloads.py); 3, the heterogeneous B=256, V=151,936 "
                          "batch, is the headline")
+    ap.add_argument("--input-dtype", choices=["fp32", "bf16"], default="fp32",
+                    help="row format: fp32 (the headline) or bf16 (topk_topp_sample_bf16, "
+                         "the same rows rounded to bf16)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -182,14 +185,25 @@ def main():
 
     w = workloads.make(args.workload)
     B, V = w.B, w.V
+    bf16 = args.input_dtype == "bf16"
+    if bf16:
+        # The same rows rounded to bf16; the oracle reads their exact fp32
+        # widening, which is what a bf16 entry means to the sampler.
+        t16 = torch.from_numpy(w.probs).to(torch.bfloat16)
+        w.probs = (t16.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16) \
+            .view(np.float32)
+    esize = 2 if bf16 else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sampler = tes.Sampler(0, max_batch=B, max_vocab=V)
     # Rotating copies: at least twice the 256 MiB Infinity Cache in total
     # (fewer for the large batches, whose single copy already exceeds it).
-    copies = max(1, min(args.copies, -(-2 * (256 << 20) // w.probs.nbytes)))
+    copies = max(1, min(args.copies, -(-2 * (256 << 20) // (B * V * esize))))
     args.copies = copies
-    probs = [torch.from_numpy(w.probs).to(dev) for _ in range(copies)]
+    if bf16:
+        probs = [t16.to(dev) for _ in range(copies)]
+    else:
+        probs = [torch.from_numpy(w.probs).to(dev) for _ in range(copies)]
     top_k = torch.from_numpy(w.top_k).to(dev)
     top_p = torch.from_numpy(w.top_p).to(dev)
     out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -227,14 +241,14 @@ def main():
     kern_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
-    alg_bytes = B * V * 4 + 12 * B
+    alg_bytes = B * V * esize + 12 * B
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
     # The same calls replayed from one captured HIP graph (launch overhead
     # removed), and a plain read of the same bytes by the library's reference
     # stream kernel, on the same stream and input copies.
     graph_ms = graph_timing(step, args.copies, stream)
-    read_ms = read_timing(tes, probs, B * V * 4, dev, stream, args.steps)
+    read_ms = read_timing(tes, probs, B * V * esize, dev, stream, args.steps)
 
     parity = None
     if not args.no_parity:
@@ -247,7 +261,7 @@ def main():
         parity = "bit-exact" if np.array_equal(gtok, otok) else \
             "MISMATCH on %d rows" % int((gtok != otok).sum())
 
-    traffic = traffic_from_profile() if args.workload == 3 else None
+    traffic = traffic_from_profile() if args.workload == 3 and not bf16 else None
     line = {
         "metric": METRIC,
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -266,13 +280,14 @@ def main():
             "B": B,
             "V": V,
             "row_mix": ROW_MIX[args.workload],
-            "input": INPUT[args.workload],
+            "input": INPUT[args.workload] + (", rounded to bf16" if bf16 else ""),
+            "input_dtype": args.input_dtype,
             "renorm_out": None,
             "input_copies_rotated": args.copies,
             "kernel_ms_hip_events": round(kern_ms, 5),
             "kernel_ms_graph_replay": round(graph_ms, 5),
             "plain_read_ms_same_bytes": round(read_ms, 5),
-            "plain_read_GBps": round(B * V * 4 / (read_ms * 1e-3) / 1e9, 1),
+            "plain_read_GBps": round(B * V * esize / (read_ms * 1e-3) / 1e9, 1),
             "frac_of_plain_read": round(read_ms / kern_ms, 4),
             "parity_vs_oracle": parity,
         },

@@ -104,6 +104,23 @@ int topk_topp_sample(tes_sampler *s, const float *probs, int B, int V, const int
                      const float *top_p, uint64_t seed, uint64_t offset, int32_t *out_tokens,
                      float *renorm_out, void *stream);
 
+/* topk_topp_sample over bfloat16 probability rows (the 16-bit format whose
+ * ordered encoding the SonicSampler page builds its keys from, section 3.4
+ * "Numerical Lexicographic Encoding"; its input there is bf16 logits).
+ * Each entry means exactly its widening to fp32 (the 16 bits become the
+ * upper half of an fp32 word); after that every step -- support, cutoff,
+ * draw, renormalisation -- is the fp32 method, so the tokens equal those of
+ * topk_topp_sample on the widened rows.  Half the bytes are read.
+ *   probs       device, bf16 bit patterns [B][V] row-major, contiguous;
+ *               16-byte aligned and V % 8 == 0 (TES_ERR_INVALID_ARGUMENT
+ *               otherwise).
+ *   renorm_out  device, fp32 [B][V] or NULL, 16-byte aligned when given.
+ * Every other argument, the ownership rules and the status codes are those
+ * of topk_topp_sample. */
+int topk_topp_sample_bf16(tes_sampler *s, const uint16_t *probs, int B, int V,
+                          const int32_t *top_k, const float *top_p, uint64_t seed,
+                          uint64_t offset, int32_t *out_tokens, float *renorm_out, void *stream);
+
 /* topk_topp_sample plus the slab export: the same sampling (same arguments,
  * same outputs), and for every row whose support holds at most slab_cap
  * entries, the support in its sorted order -- descending probability,

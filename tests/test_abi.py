@@ -47,6 +47,8 @@ def test_host_side_argument_validation():
     # None of these reach the device.
     assert tes.topk_topp_sample(None, 0, 1, 10, 0, 0, 0, 0, 0, None, None) == \
         tes.TES_ERR_INVALID_ARGUMENT
+    assert tes.topk_topp_sample_bf16(None, 0, 1, 16, 0, 0, 0, 0, 0, None, None) == \
+        tes.TES_ERR_INVALID_ARGUMENT
     with pytest.raises(tes.TesError) as e:
         tes.sampler_create(0, 0, 10)
     assert e.value.status == tes.TES_ERR_INVALID_ARGUMENT

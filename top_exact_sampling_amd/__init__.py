@@ -33,7 +33,8 @@ TES_FLAG_SMALL_SEGMENTS = 8
 STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
-            "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route")
+            "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route",
+            "topk_topp_sample_bf16")
 
 _lib = None
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.topk_topp_sample.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp,
                                        ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
         L.topk_topp_sample.restype = ctypes.c_int
+        L.topk_topp_sample_bf16.argtypes = L.topk_topp_sample.argtypes
+        L.topk_topp_sample_bf16.restype = ctypes.c_int
         L.sampler_destroy.argtypes = [vp]
         L.sampler_destroy.restype = ctypes.c_int
         L.sampler_status_string.argtypes = [ctypes.c_int]
@@ -97,6 +100,15 @@ def topk_topp_sample(handle, probs_ptr: int, B: int, V: int, top_k_ptr: int, top
     return lib().topk_topp_sample(handle, probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
                                   int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                   out_tokens_ptr, renorm_ptr, stream)
+
+
+def topk_topp_sample_bf16(handle, probs_ptr: int, B: int, V: int, top_k_ptr: int,
+                          top_p_ptr: int, seed: int, offset: int, out_tokens_ptr: int, renorm_ptr,
+                          stream) -> int:
+    """Raw call over bf16 rows with device pointers (ints); returns the status."""
+    return lib().topk_topp_sample_bf16(handle, probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
+                                       int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                       out_tokens_ptr, renorm_ptr, stream)
 
 
 def sampler_destroy(handle) -> int:
@@ -167,19 +179,22 @@ class Sampler:
         import torch
 
         B, V = probs.shape
-        for t, dt in ((probs, torch.float32), (top_k, torch.int32), (top_p, torch.float32)):
+        # fp32 rows, or bf16 rows (topk_topp_sample_bf16).
+        bf16 = probs.dtype == torch.bfloat16
+        pdt = torch.bfloat16 if bf16 else torch.float32
+        for t, dt in ((probs, pdt), (top_k, torch.int32), (top_p, torch.float32)):
             if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
                 raise ValueError("expected contiguous %s on the GPU" % dt)
         if out_tokens is None:
             out_tokens = torch.empty(B, dtype=torch.int32, device=probs.device)
         if stream is None:
             stream = torch.cuda.current_stream(probs.device)
-        rc = topk_topp_sample(self.handle, probs.data_ptr(), B, V, top_k.data_ptr(),
-                              top_p.data_ptr(), seed, offset, out_tokens.data_ptr(),
-                              renorm_out.data_ptr() if renorm_out is not None else None,
-                              stream.cuda_stream)
+        fn = topk_topp_sample_bf16 if bf16 else topk_topp_sample
+        rc = fn(self.handle, probs.data_ptr(), B, V, top_k.data_ptr(), top_p.data_ptr(), seed,
+                offset, out_tokens.data_ptr(),
+                renorm_out.data_ptr() if renorm_out is not None else None, stream.cuda_stream)
         if rc != TES_OK:
-            raise TesError(rc, "topk_topp_sample")
+            raise TesError(rc, fn.__name__)
         return out_tokens
 
     def sample_slab(self, probs, top_k, top_p, seed: int, offset: int, slab_cap: int,

@@ -842,6 +842,27 @@ struct VecT<1> {
     typedef float T;
     __device__ static float get(const T& v, int) { return v; }
 };
+// bf16 rows: eight values per 16-byte vector.  A bf16 value is the upper half
+// of an fp32 value with the same bits below zero, so its fp32 widening (the
+// bits shifted up by 16) is exact and every rule of the method applies to it
+// unchanged.
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+template <>
+struct VecT<8> {
+    typedef u4v T;
+    __device__ static float get(const T& v, int e) {
+        return __uint_as_float(((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
+    }
+};
+// Bytes per row entry: 2 for bf16 rows (VEC = 8), else 4.
+template <int VEC>
+constexpr size_t kEntryBytes = VEC == 8 ? 2 : 4;
+// Row r of the [B][V] matrix at `base`.
+template <int VEC>
+__device__ __forceinline__ const float* row_ptr(const float* base, size_t r, u32 V) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(base) +
+                                          r * V * kEntryBytes<VEC>);
+}
 
 // Row data is read once: non-temporal loads keep it from displacing the
 // exchanged words and the kernel's own code in L2.
@@ -1736,7 +1757,8 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     const u32 hv = (p.nvec + S - 1) / S;
     const u32 v0 = h * hv;
     const u32 nv = min(v0 + hv, p.nvec) - v0;
-    const float* part = p.probs + (size_t)r * p.V + (size_t)v0 * VEC;
+    const float* part =
+        reinterpret_cast<const float*>(reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V)) + v0);
     // The largest bits as signed integers: non-negative floats order as their
     // bits, negative ones (which count as zero) lie below all of them and NaN
     // bits above +inf.  Each lane keeps the first of its vectors holding its
@@ -1863,8 +1885,11 @@ template <int VEC>
 __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u64 P, u64 u) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
-    const float* row = p.probs + (size_t)r * p.V;
-    constexpr u32 kHigh = kSlabCap - kBlock * VEC;  // room for one more step
+    const float* row = row_ptr<VEC>(p.probs, r, p.V);
+    // Entries are appended kSub per thread at a time (an 8-entry vector in
+    // two halves), so the buffer keeps room for one more append.
+    constexpr int kSub = VEC > 4 ? 4 : VEC;
+    constexpr u32 kHigh = kSlabCap - kBlock * kSub;
     static_assert(kHigh >= kSlabMaxK, "a cut always has k entries to keep");
     u32 theta = theta0;  // workgroup-uniform
     bool closed = false;  // the k-th best so far is +inf: nothing later can enter
@@ -1872,30 +1897,41 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     if (threadIdx.x == 0) s.ctr[3] = 0;
     __syncthreads();
     for_each_vec<VEC, kPassDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
-        const u32 span = kInfKey - theta;
-        // One append per vector: the lane's passing entries go to consecutive
-        // slots taken by one LDS atomic per wave.
-        u64 c[VEC];
-        u32 mask = 0;
+        // After a cut within a step, entries with the k-th key still enter
+        // for the rest of the step (another thread's later half may hold a
+        // lower index); only at the step's end does the threshold rise above
+        // that key.
+        bool raise = false;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-            c[e] = composite(b, iv * VEC + e);
-            mask |= (valid && !closed && b - theta <= span) ? 1u << e : 0u;
-        }
-        wave_append_n<VEC>(sbuf(s), mask, c, &s.ctr[3], 0, kSlabCap);
-        __syncthreads();
-        const u32 n = uni(s.ctr[3]);
-        if (n > kHigh) {
-            __syncthreads();  // every thread has read the count
-            const u64 ck = select_slab(s, n, k);
-            const u32 kept = keep_above(s, n, ck);
-            const u32 kk = comp_key(ck);
-            closed = kk == kInfKey;
-            theta = closed ? kInfKey : kk + 1;
-            ++cuts;
-            if (threadIdx.x == 0) s.ctr[3] = kept;
+        for (int h0 = 0; h0 < VEC; h0 += kSub) {
+            const u32 span = kInfKey - theta;
+            // One append per half: the lane's passing entries go to
+            // consecutive slots taken by one LDS atomic per wave.
+            u64 c[kSub];
+            u32 mask = 0;
+#pragma unroll
+            for (int e = 0; e < kSub; ++e) {
+                const u32 b = __float_as_uint(VecT<VEC>::get(x, h0 + e));
+                c[e] = composite(b, iv * VEC + h0 + e);
+                mask |= (valid && !closed && b - theta <= span) ? 1u << e : 0u;
+            }
+            wave_append_n<kSub>(sbuf(s), mask, c, &s.ctr[3], 0, kSlabCap);
             __syncthreads();
+            const u32 n = uni(s.ctr[3]);
+            if (n > kHigh) {
+                __syncthreads();  // every thread has read the count
+                const u64 ck = select_slab(s, n, k);
+                const u32 kept = keep_above(s, n, ck);
+                theta = comp_key(ck);
+                raise = true;
+                ++cuts;
+                if (threadIdx.x == 0) s.ctr[3] = kept;
+                __syncthreads();
+            }
+        }
+        if (raise) {
+            closed = theta == kInfKey;
+            theta = closed ? kInfKey : theta + 1;
         }
     });
     __syncthreads();
@@ -1968,7 +2004,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     const u32 hv = (p.nvec + S - 1) / S;
     const u32 v0 = h * hv;
     const u32 nvec = min(v0 + hv, p.nvec) - v0;  // vectors of this part
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V) + v0;
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V)) + v0;
     // Issued before the stream so that its latency is hidden.
     const float top_p = ld_g(&p.top_p[r]);
     stat_start(p, r, S);
@@ -2396,7 +2432,7 @@ template <int VEC>
 __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, u32 nseg) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(p.probs + (size_t)r * p.V);
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V));
     const u32 sv = (p.nvec + nseg - 1) / nseg;
     const u32 v0 = seg * sv, v1 = min(v0 + sv, p.nvec);
     const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
@@ -2732,7 +2768,7 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
     }
     if (!fail && fb) stat_why(p, r, 32u);
     if (fb) {
-        o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, p.V, P, u, kSelCap);
+        o = resolve_row<VEC>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, p.V, P, u, kSelCap);
         path = kPathFullFallback;
     } else if (kind == kNormal) {
         // decided above
@@ -2770,7 +2806,7 @@ __device__ __attribute__((always_inline)) void do_whole(Smem& s, u32 r, u32 k_ef
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
     if (threadIdx.x == 0) s.npass = 0;
-    const Outcome o = resolve_row<VEC>(s, p.probs + (size_t)r * p.V, p.nvec, p.V, k_eff, P, u,
+    const Outcome o = resolve_row<VEC>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, k_eff, P, u,
                                        tiny ? 64u : kSelCap);
     stat_add(p, r, 3, uni(s.npass));
     finish_row(s, p, r, o, kPathWhole, 0);
@@ -2901,8 +2937,8 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
     typedef typename VecT<VEC>::T VT;
     const u32 r = blockIdx.y;
     const Decision d = dec[r];
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
-    VT* __restrict__ ov = reinterpret_cast<VT*>(out + (size_t)r * V);
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(probs, r, V));
+    float* __restrict__ orow = out + (size_t)r * V;
     const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
     const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
     for (u32 iv = blockIdx.x * 256 + threadIdx.x; iv < nvec; iv += gridDim.x * 256) {
@@ -2916,9 +2952,12 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
                          : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
         }
         if constexpr (VEC == 4) {
-            ov[iv] = f4{o[0], o[1], o[2], o[3]};
+            reinterpret_cast<f4*>(orow)[iv] = f4{o[0], o[1], o[2], o[3]};
+        } else if constexpr (VEC == 8) {
+            reinterpret_cast<f4*>(orow)[2 * iv] = f4{o[0], o[1], o[2], o[3]};
+            reinterpret_cast<f4*>(orow)[2 * iv + 1] = f4{o[4], o[5], o[6], o[7]};
         } else {
-            ov[iv] = o[0];
+            orow[iv] = o[0];
         }
     }
 }
@@ -2971,7 +3010,7 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
         }
     } else {
         // Eight loads per thread in flight: a single workgroup streams the row.
-        const VT* __restrict__ rv = reinterpret_cast<const VT*>(probs + (size_t)r * V);
+        const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(probs, r, V));
         constexpr u32 kU = 8;
         for (u32 i0 = 0; i0 < nvec; i0 += kU * kSlabThreads) {
             VT x[kU];
@@ -3179,7 +3218,32 @@ struct SlabOut {
 };
 
 namespace {
-int sample_impl(tes_sampler* s, const float* probs, int B, int V, const int32_t* top_k,
+// The kernels of one launch (one chunk of rows) for row vectors of VEC entries.
+template <int VEC>
+int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 rows, u32 V,
+                 u32 nvec, float* ro, const SlabOut* slab, size_t c0) {
+    hipLaunchKernelGGL(tes_main_kernel<VEC>, dim3(grid), dim3(kBlock), 0, st, p);
+    if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+    const Decision* dec =
+        reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
+    if (ro) {
+        const u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
+        hipLaunchKernelGGL(tes_renorm_kernel<VEC>, dim3(gx, rows), dim3(256), 0, st, p.probs, V,
+                           nvec, dec, ro);
+        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+    }
+    if (slab) {
+        const size_t o = c0 * slab->cap;
+        hipLaunchKernelGGL(tes_slab_kernel<VEC>, dim3(rows), dim3(kSlabThreads), 0, st, p.probs,
+                           V, nvec, p.top_k, dec, slab->cap, slab->index + o, slab->renorm + o,
+                           slab->len + c0, slab->route ? slab->route + c0 : nullptr);
+        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+    }
+    return TES_OK;
+}
+
+// probs holds fp32 entries, or bf16 entries when bf16 is set.
+int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, const int32_t* top_k,
                 const float* top_p, uint64_t seed, uint64_t offset, int32_t* out_tokens,
                 float* renorm_out, const SlabOut* slab, void* stream) {
     if (!s || B < 0 || V < 1) return TES_ERR_INVALID_ARGUMENT;
@@ -3189,17 +3253,22 @@ int sample_impl(tes_sampler* s, const float* probs, int B, int V, const int32_t*
     if (((uintptr_t)probs & 3) || ((uintptr_t)top_k & 3) || ((uintptr_t)top_p & 3) ||
         ((uintptr_t)out_tokens & 3) || ((uintptr_t)renorm_out & 3))
         return TES_ERR_INVALID_ARGUMENT;
-    const bool vec4 = (V % 4 == 0) && (((uintptr_t)probs & 15) == 0) &&
-                      (((uintptr_t)renorm_out & 15) == 0);
+    // Row vectors: eight bf16 entries (bf16 rows must allow them), four fp32
+    // entries when the rows and renorm_out allow 16-byte access, else one.
+    const bool aligned16 = (((uintptr_t)probs & 15) == 0) && (((uintptr_t)renorm_out & 15) == 0);
+    if (bf16 && (V % 8 != 0 || !aligned16)) return TES_ERR_INVALID_ARGUMENT;
+    const int vec = bf16 ? 8 : ((V % 4 == 0) && aligned16 ? 4 : 1);
+    const size_t entry_bytes = bf16 ? 2 : 4;
     DeviceGuard g(s->device);
     if (!g.ok) return TES_ERR_LAUNCH;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const u32 nvec = vec4 ? (u32)V / 4 : (u32)V;
+    const u32 nvec = (u32)V / (u32)vec;
     const u32 s_full = ceil_div(nvec, s->seg_full);
     for (int c0 = 0; c0 < B; c0 += (int)s->chunk) {
         const u32 rows = (u32)(B - c0) < s->chunk ? (u32)(B - c0) : s->chunk;
         Params p;
-        p.probs = probs + (size_t)c0 * V;
+        p.probs = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(probs) +
+                                                 (size_t)c0 * V * entry_bytes);
         p.top_k = top_k + c0;
         p.top_p = top_p + c0;
         p.out_tokens = out_tokens + c0;
@@ -3234,40 +3303,11 @@ int sample_impl(tes_sampler* s, const float* probs, int B, int V, const int32_t*
         const u32 per_row = s_full <= s->s_ws ? s_full : 1u;
         const u32 split_items = rows * p.split < s->slots ? rows * p.split : s->slots;
         const u32 grid = rows * per_row > split_items ? rows * per_row : split_items;
-        if (vec4)
-            hipLaunchKernelGGL(tes_main_kernel<4>, dim3(grid), dim3(kBlock), 0, st, p);
-        else
-            hipLaunchKernelGGL(tes_main_kernel<1>, dim3(grid), dim3(kBlock), 0, st, p);
-        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
-        if (renorm_out) {
-            const Decision* dec =
-                reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
-            const u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
-            float* ro = renorm_out + (size_t)c0 * V;
-            if (vec4)
-                hipLaunchKernelGGL(tes_renorm_kernel<4>, dim3(gx, rows), dim3(256), 0, st,
-                                   p.probs, (u32)V, nvec, dec, ro);
-            else
-                hipLaunchKernelGGL(tes_renorm_kernel<1>, dim3(gx, rows), dim3(256), 0, st,
-                                   p.probs, (u32)V, nvec, dec, ro);
-            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
-        }
-        if (slab) {
-            const Decision* dec =
-                reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
-            const size_t o = (size_t)c0 * slab->cap;
-            if (vec4)
-                hipLaunchKernelGGL(tes_slab_kernel<4>, dim3(rows), dim3(kSlabThreads), 0, st,
-                                   p.probs, (u32)V, nvec, p.top_k, dec, slab->cap,
-                                   slab->index + o, slab->renorm + o, slab->len + c0,
-                                   slab->route ? slab->route + c0 : nullptr);
-            else
-                hipLaunchKernelGGL(tes_slab_kernel<1>, dim3(rows), dim3(kSlabThreads), 0, st,
-                                   p.probs, (u32)V, nvec, p.top_k, dec, slab->cap,
-                                   slab->index + o, slab->renorm + o, slab->len + c0,
-                                   slab->route ? slab->route + c0 : nullptr);
-            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
-        }
+        float* ro = renorm_out ? renorm_out + (size_t)c0 * V : nullptr;
+        const int rc = vec == 8 ? launch_chunk<8>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
+                     : vec == 4 ? launch_chunk<4>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
+                                : launch_chunk<1>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0);
+        if (rc != TES_OK) return rc;
     }
     return TES_OK;
 }
@@ -3277,7 +3317,15 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
                                 const int32_t* top_k, const float* top_p, uint64_t seed,
                                 uint64_t offset, int32_t* out_tokens, float* renorm_out,
                                 void* stream) {
-    return sample_impl(s, probs, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
+    return sample_impl(s, probs, false, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
+                       nullptr, stream);
+}
+
+extern "C" int topk_topp_sample_bf16(tes_sampler* s, const uint16_t* probs, int B, int V,
+                                     const int32_t* top_k, const float* top_p, uint64_t seed,
+                                     uint64_t offset, int32_t* out_tokens, float* renorm_out,
+                                     void* stream) {
+    return sample_impl(s, probs, true, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
                        nullptr, stream);
 }
 
@@ -3292,8 +3340,8 @@ extern "C" int topk_topp_sample_slab(tes_sampler* s, const float* probs, int B, 
         ((uintptr_t)route & 3))
         return TES_ERR_INVALID_ARGUMENT;
     const SlabOut slab{slab_index, slab_renorm, slab_len, route, (u32)slab_cap};
-    return sample_impl(s, probs, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out, &slab,
-                       stream);
+    return sample_impl(s, probs, false, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
+                       &slab, stream);
 }
 
 extern "C" int sampler_route(tes_sampler* s, int B, int V, const int32_t* top_k_host,
