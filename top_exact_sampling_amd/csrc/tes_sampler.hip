@@ -1235,11 +1235,9 @@ struct BinView {
 // One wave: the j-th smallest (0-based) vocabulary index among the entries
 // sbuf(s)[st, st + n), whose indices are distinct.  A radix select on the
 // index, 8 bits per round from the highest bit in which the indices differ,
-// counting into 256 LDS counters (the top-p-only rows' fine-mass array, unused
-// by top-k rows).  All 64 lanes must take part.
-__device__ __noinline__ u32 wave_nth_index(Smem& s, u32 st, u32 n, u32 j) {
-    u32* tab = reinterpret_cast<u32*>(s.finem);
-    static_assert(sizeof(s.finem) >= 256 * sizeof(u32), "256 counters fit");
+// counting into 256 LDS counters at tab (outside the entries).  All 64 lanes
+// must take part.
+__device__ __noinline__ u32 wave_nth_index(Smem& s, u32* tab, u32 st, u32 n, u32 j) {
     const u32 lane = lane_id();
     u64 lo = ~0ull, hi = 0;
     for (u32 i = lane; i < n; i += 64) {
@@ -1346,7 +1344,11 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
             return __ballot(!same) == 0;
         };
         auto nth = [&](int b, u32 j) {
-            return wave_nth_index(s, bv.cnt_above(b), bv.end_of(b) - bv.cnt_above(b), j);
+            // The counters: the top-p-only rows' fine-mass array, unused by
+            // top-k rows.
+            static_assert(sizeof(s.finem) >= 256 * sizeof(u32), "256 counters fit");
+            return wave_nth_index(s, reinterpret_cast<u32*>(s.finem), bv.cnt_above(b),
+                                  bv.end_of(b) - bv.cnt_above(b), j);
         };
         bool ok = !has_inf;
         u64 Mk = 0, ck = 0;
@@ -1551,6 +1553,39 @@ __device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     const Sel r{uni(s.bc[1]), uni(s.bc[2])};
     __syncthreads();
     if (ok) return r;
+    // Bins whose entries all share one key (a bf16 row's fine bins each hold
+    // one value) rank them by index alone: with mass m per entry, W is
+    // reached by the j-th lowest index, j = ceil(W / m) - 1, and the j
+    // entries before it weigh j m.
+    if (wave_id() == 0) {
+        const u32 lane = lane_id();
+        u64 kmin = ~0ull, kmax = 0;
+        for (u32 i = lane; i < (nf < kSelCap ? nf : kSelCap); i += 64) {
+            const u64 kk = comp_key(list[i]);
+            kmin = kk < kmin ? kk : kmin;
+            kmax = kk > kmax ? kk : kmax;
+        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
+        const u64 m = nf ? key_mass((u32)kmin) : 0;
+        const bool tie = nf > 0 && nf <= kSelCap && kmin == kmax && m > 0 && W <= (u64)nf * m;
+        if (tie) {
+            const u32 j = W ? (u32)((W + m - 1) / m - 1) : 0u;
+            // The counters: the table area, past the list.
+            const u32 idx = wave_nth_index(s, reinterpret_cast<u32*>(shtab(s)), kSelCap, nf, j);
+            if (lane == 0) {
+                s.bc[1] = composite((u32)kmin, idx);
+                s.bc[2] = (u64)j * m;
+            }
+        }
+        if (lane == 0) s.misc[5] = tie ? 1u : 0u;
+    }
+    __syncthreads();
+    if (uni(s.misc[5])) {
+        const Sel t{uni(s.bc[1]), uni(s.bc[2])};
+        __syncthreads();
+        return t;
+    }
     return select_buf(s, n, W, true, fine_lo(f), fine_hi(f));
 }
 
