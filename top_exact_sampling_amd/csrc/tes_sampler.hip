@@ -70,6 +70,10 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kWavesPerSimd = 4;       // two workgroups per CU
 constexpr int kSlotsFull = 16;         // vectors per thread of a register-resident segment
 constexpr u32 kSegVecFull = kBlock * kSlotsFull;
+// Rows of 8-entry (bf16) vectors keep half as many vectors per thread, so that
+// a segment holds as many entries as one of fp32 rows.
+template <int VEC>
+constexpr int kSlots = VEC == 8 ? kSlotsFull / 2 : kSlotsFull;
 constexpr u32 kSegVecSmall = kBlock * 2;     // segment size under TES_FLAG_SMALL_SEGMENTS
 constexpr u32 kStreamDepth = 16;       // 16-byte loads per thread in flight when streaming
 constexpr u32 kPassDepth = 8;          // the same for the passes of whole-row selects
@@ -2482,9 +2486,9 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // as its load returns (loads are issued, and waited for, in order).
     for (int i = (int)threadIdx.x - 1; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
     __syncthreads();
-    VT x[kSlotsFull];
+    VT x[kSlots<VEC>];
 #pragma unroll
-    for (int d = 0; d < kSlotsFull; ++d) {
+    for (int d = 0; d < kSlots<VEC>; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
         x[d] = ld_stream(&rv[i < v1 ? i : v1 - 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -2501,7 +2505,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256, the largest float below 2^32
     u64 ninf = 0;
 #pragma unroll
-    for (int d = 0; d < kSlotsFull; ++d) {
+    for (int d = 0; d < kSlots<VEC>; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
         if (i < v1) {
             int mx = kIntMin;
@@ -2619,7 +2623,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         const u32 kR0 = ckey0(min(clo, chi)), wR = ckey1(max(clo, chi)) - kR0;
         u64* sreg = sbuf(s) + wave * kSpecReg;
 #pragma unroll
-        for (int d = 0; d < kSlotsFull; ++d) {
+        for (int d = 0; d < kSlots<VEC>; ++d) {
             const u32 i = v0 + d * kBlock + threadIdx.x;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -2685,10 +2689,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             if (spec_ok)
                 ng = filter_regions(s, kSpecReg, sfill, pred, garea, gcap);
             else
-                ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, pred, garea, gcap);
+                ng = gather_regs<VEC, kSlots<VEC>>(s, x, v0, v1, pred, garea, gcap);
         }
     } else if (!failed && kind == kInfRow) {
-        ng = gather_regs<VEC, kSlotsFull>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
+        ng = gather_regs<VEC, kSlots<VEC>>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
                                           garea, gcap);
     }
     if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
@@ -3298,7 +3302,8 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
     if (!g.ok) return TES_ERR_LAUNCH;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const u32 nvec = (u32)V / (u32)vec;
-    const u32 s_full = ceil_div(nvec, s->seg_full);
+    const u32 seg = vec == 8 ? s->seg_full / 2 : s->seg_full;  // vectors per segment
+    const u32 s_full = ceil_div(nvec, seg);
     for (int c0 = 0; c0 < B; c0 += (int)s->chunk) {
         const u32 rows = (u32)(B - c0) < s->chunk ? (u32)(B - c0) : s->chunk;
         Params p;
@@ -3315,7 +3320,7 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.nvec = nvec;
         p.rows = rows;
         p.row_base = (u32)c0;
-        p.seg_vec_full = s->seg_full;
+        p.seg_vec_full = seg;
         p.s_ws = s->s_ws;
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
