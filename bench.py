@@ -5,7 +5,8 @@ One step = one call of topk_topp_sample over the whole heterogeneous batch
 (B=256 rows, V=151,936 fp32 probabilities; 64 greedy rows, 64 top-p-only rows,
 128 rows with k in [20, 1024]), tokens only (renorm_out = NULL), inputs
 already resident in HBM.  Timed steps rotate over several copies of the
-input so that the 256 MiB Infinity Cache cannot serve a repeated read.
+input so that the 256 MiB Infinity Cache cannot serve a repeated read, and
+advance the Philox offset by one per call.
 
 Prints one JSON line: rows/s for the whole job, the kernel's achieved HBM
 bandwidth against the 8 TB/s peak (algorithmic bytes = B*V*4 + 12*B per
@@ -209,8 +210,10 @@ def main():
     out = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    # Call i draws with Philox offset w.offset + i, as a decode loop advances
+    # it, so that draw-dependent paths are sampled rather than one fixed draw.
     def step(i, st=None):
-        sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset, out_tokens=out,
+        sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i, out_tokens=out,
                        stream=stream if st is None else st)
 
     for i in range(args.warmup):

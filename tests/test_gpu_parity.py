@@ -539,3 +539,32 @@ def test_read_probe_reads_and_leaves_the_sink(torch_cuda):
     assert tes.sampler_read_probe(x.data_ptr(), 0, sink.data_ptr(), 0, None) == tes.TES_OK
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+def test_wide_draw_ranges_stay_on_the_fast_path(sampler, orc):
+    # Top-p-only rows whose few large entries sit many octaves above the
+    # bulk: before the boundary is known, a draw can fall anywhere from the
+    # large entries down to the bulk, a range of up to ~150 coarse bins that
+    # are almost all empty.  Only the bins with mass are exchanged, so these
+    # rows stay on the segment path.
+    B, V = 256, 151936
+    rng = np.random.default_rng(4242)
+    probs = np.empty((B, V), np.float32)
+    for b in range(B):
+        x = rng.standard_normal(V)
+        e = np.exp(x - x.max())
+        nb = int(rng.integers(1, 4))
+        big = rng.dirichlet(np.ones(nb)) * rng.uniform(0.3, 0.7)
+        row = e / e.sum() * (1.0 - big.sum())
+        row[rng.choice(V, nb, replace=False)] = big
+        probs[b] = row.astype(np.float32)
+    ks = np.full(B, V, np.int32)
+    ps = rng.uniform(0.85, 0.99, size=B).astype(np.float32)
+    for off in (0, 1, 2):
+        log("[gpu] wide draw ranges offset %d" % off)
+        gtok, gren = run_gpu(sampler, probs, ks, ps, 77, off, renorm=(off == 0))
+        st = sampler.stats(B)
+        log("[gpu]   paths %s" % np.bincount(st[:, 0], minlength=6).tolist())
+        assert_parity(orc, probs, ks, ps, 77, off, gtok, gren, "wide draw ranges %d" % off)
+        assert np.all(st[:, 0] == 1), "rows left the fast path: %s (why %s)" % (
+            np.flatnonzero(st[:, 0] != 1), st[st[:, 0] != 1, 7])

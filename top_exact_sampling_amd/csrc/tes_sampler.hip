@@ -2577,20 +2577,31 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         __syncthreads();
         const int cbT = (int)uni((u32)s.loc_bin[0]);
         const int chi = (int)uni((u32)s.loc_bin[1]), clo = (int)uni((u32)s.loc_bin[2]);
-        // Listed coarse bins: the boundary bin, then the draw range.
-        const int cnt = 1 + (chi - clo + 1) - ((cbT >= clo && cbT <= chi) ? 1 : 0);
+        // Listed coarse bins: the boundary bin, then the draw range's bins
+        // that hold mass, highest first.  A bin without mass holds neither
+        // position (a range from a few large entries down to the bulk of the
+        // row is mostly empty bins).
+        if (wave_id() == 0) {
+            const u32 lane = lane_id();
+            u32 q = 1;  // listed so far (wave-uniform)
+            if (lane == 0) s.flist[0] = cbT;
+            for (int b0 = chi; b0 >= clo; b0 -= 64) {
+                const int b = b0 - (int)lane;  // lane 0 takes the highest bin
+                const bool in = b >= clo && b != cbT && s.coarse[b] != 0;
+                const u64 m = __builtin_amdgcn_ballot_w64(in);
+                const u32 pos = q + mbcnt64(m);
+                if (in && pos < (u32)dmax) s.flist[pos] = b;
+                q += (u32)__popcll(m);
+            }
+            if (lane == 0) s.misc[6] = q;
+        }
+        __syncthreads();
+        const int cnt = (int)uni(s.misc[6]);
         if (cnt > dmax) {
             decidable = false;
             stat_why(p, r, 2u | (u32)min(cnt, 255) << 8);
         } else {
-            if (threadIdx.x == 0) {
-                int q = 0;
-                s.flist[q++] = cbT;
-                for (int b = chi; b >= clo; --b)
-                    if (b != cbT) s.flist[q++] = b;
-            }
             nlist = cnt;
-            __syncthreads();
             // Second exchange: this segment's fine bins of the listed coarse bins.
             PubF* pf = pub_f(p, r, seg);
             for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
