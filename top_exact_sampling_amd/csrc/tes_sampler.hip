@@ -1430,15 +1430,57 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
     return ok;
 }
 
+// Bins whose nf listed entries all share one key rank them by index alone:
+// with mass m per entry, the weight W (1 <= W <= nf m) is reached by the j-th
+// lowest index, j = ceil(W / m) - 1, and the j entries before it weigh j m.
+// True with the entry's composite in s.bc[1] and the weight above it in
+// s.bc[2] (the caller reads them, then synchronises); false when the keys
+// differ or carry no mass.  The list is sbuf(s)[kSelCap, kSelCap + nf); all
+// threads call it.
+__device__ __noinline__ bool tie_select(Smem& s, u32 nf, u64 W) {
+    const u64* list = sbuf(s) + kSelCap;
+    if (wave_id() == 0) {
+        const u32 lane = lane_id();
+        u64 kmin = ~0ull, kmax = 0;
+        for (u32 i = lane; i < (nf < kSelCap ? nf : kSelCap); i += 64) {
+            const u64 kk = comp_key(list[i]);
+            kmin = kk < kmin ? kk : kmin;
+            kmax = kk > kmax ? kk : kmax;
+        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
+        const u64 m = nf ? key_mass((u32)kmin) : 0ull;
+        const bool tie = nf > 0 && nf <= kSelCap && kmin == kmax && m > 0 && W <= (u64)nf * m;
+        if (tie) {
+            const u32 j = W ? (u32)((W + m - 1) / m - 1) : 0u;
+            // The counters: the table area, past the list.
+            const u32 idx = wave_nth_index(s, reinterpret_cast<u32*>(shtab(s)), kSelCap, nf, j);
+            if (lane == 0) {
+                s.bc[1] = composite((u32)kmin, idx);
+                s.bc[2] = (u64)j * m;
+            }
+        }
+        if (lane == 0) s.misc[5] = tie ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool tie = uni(s.misc[5]) != 0;
+    if (!tie) __syncthreads();
+    return tie;
+}
+
 // Mass select inside fine bin f (< kFineBins - 1) over sbuf(s)[0, n), n <=
 // kSelCap: the entry at which the bin's descending cumulative mass first
 // reaches W (1 <= W <= the bin's mass), with the bin's mass above it.  The
-// bin's entries are first compacted into a list.  Up to 64 of them are sorted
+// bin's entries are first compacted into a list.  A list whose entries share
+// one key is ranked by index (tie_select): for bf16 rows (kTieFirst) before
+// anything else when it holds more than 64, for fp32 rows only once the
+// attempts below fail.  Up to 64 entries are sorted
 // by one wave; up to 256 are split by one wave into 64 sub-bins of 1024 keys
 // (an LDS table of packed count and mass, scanned across the lanes) and only
 // the sub-bin holding W is sorted.  Larger bins go through the workgroup's
 // 2048-bin table (32 keys per bin), and the radix select decides when even
 // that bin holds more than 64 entries.
+template <bool kTieFirst>
 __device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     const u32 fkey = (u32)(f + (int)kFineBase);
     u64* list = sbuf(s) + kSelCap;
@@ -1451,6 +1493,13 @@ __device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     }
     __syncthreads();
     const u32 nf = uni(s.ctr[2]);
+    // Rows of bf16 entries: every fine bin holds one value, so a bin of more
+    // than 64 entries is a tie run, which the attempts below cannot split.
+    if (kTieFirst && nf > 64u && tie_select(s, nf, W)) {
+        const Sel t{uni(s.bc[1]), uni(s.bc[2])};
+        __syncthreads();
+        return t;
+    }
     bool ok = false;
     if (nf <= 256u) {
         if (wave_id() == 0) {
@@ -1557,35 +1606,7 @@ __device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
     const Sel r{uni(s.bc[1]), uni(s.bc[2])};
     __syncthreads();
     if (ok) return r;
-    // Bins whose entries all share one key (a bf16 row's fine bins each hold
-    // one value) rank them by index alone: with mass m per entry, W is
-    // reached by the j-th lowest index, j = ceil(W / m) - 1, and the j
-    // entries before it weigh j m.
-    if (wave_id() == 0) {
-        const u32 lane = lane_id();
-        u64 kmin = ~0ull, kmax = 0;
-        for (u32 i = lane; i < (nf < kSelCap ? nf : kSelCap); i += 64) {
-            const u64 kk = comp_key(list[i]);
-            kmin = kk < kmin ? kk : kmin;
-            kmax = kk > kmax ? kk : kmax;
-        }
-        kmin = wave_min(kmin);
-        kmax = wave_max(kmax);
-        const u64 m = nf ? key_mass((u32)kmin) : 0;
-        const bool tie = nf > 0 && nf <= kSelCap && kmin == kmax && m > 0 && W <= (u64)nf * m;
-        if (tie) {
-            const u32 j = W ? (u32)((W + m - 1) / m - 1) : 0u;
-            // The counters: the table area, past the list.
-            const u32 idx = wave_nth_index(s, reinterpret_cast<u32*>(shtab(s)), kSelCap, nf, j);
-            if (lane == 0) {
-                s.bc[1] = composite((u32)kmin, idx);
-                s.bc[2] = (u64)j * m;
-            }
-        }
-        if (lane == 0) s.misc[5] = tie ? 1u : 0u;
-    }
-    __syncthreads();
-    if (uni(s.misc[5])) {
+    if (!kTieFirst && tie_select(s, nf, W)) {
         const Sel t{uni(s.bc[1]), uni(s.bc[2])};
         __syncthreads();
         return t;
@@ -2792,7 +2813,7 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
         fb = n1 > kSelCap;
         if (!fb) {
             const bool binned = !tiny && fbT < kFineBins - 1;
-            const Sel sb = binned ? fine_select(s, n1, fbT, T - above_f)
+            const Sel sb = binned ? fine_select<VEC == 8>(s, n1, fbT, T - above_f)
                                   : select_buf(s, n1, T - above_f, true, fine_lo(fbT), fine_hi(fbT));
             tf = stat_phase(p, r, 15, tf);
             const u64 M_p = above_f + sb.above + key_mass(comp_key(sb.c));
@@ -2807,7 +2828,7 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
             fb = n2 > kSelCap;
             if (!fb) {
                 const Sel sd = (!tiny && fd < kFineBins - 1)
-                                   ? fine_select(s, n2, fd, t + 1 - above_d)
+                                   ? fine_select<VEC == 8>(s, n2, fd, t + 1 - above_d)
                                    : select_buf(s, n2, t + 1 - above_d, true, fine_lo(fd), fine_hi(fd));
                 o.kind = kNormal;
                 o.c_keep = sb.c;
