@@ -858,6 +858,34 @@ struct VecT<8> {
         return __uint_as_float(((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16);
     }
 };
+// Whether any entry of x, its bits read as a signed int, is >= tkey, for a
+// tkey that is a multiple of 2^16.  The eight entries of a bf16 vector are
+// compared as signed 16-bit halves (packed integer maxima): a widened entry
+// (h << 16) >= tkey exactly when the signed half h >= tkey >> 16.
+template <int VEC>
+__device__ __forceinline__ bool any_at_least(const typename VecT<VEC>::T& x, int tkey) {
+    if constexpr (VEC == 8) {
+        typedef short s2v __attribute__((ext_vector_type(2)));
+        auto halves = [](u32 w) {
+            s2v h;
+            __builtin_memcpy(&h, &w, sizeof(w));
+            return h;
+        };
+        auto hmax = [](s2v a, s2v b) { return a > b ? a : b; };  // v_pk_max_i16
+        const s2v c = hmax(hmax(halves(x.x), halves(x.y)), hmax(halves(x.z), halves(x.w)));
+        u32 m;
+        __builtin_memcpy(&m, &c, sizeof(m));
+        // The upper half compares in place (the lower bits cannot lift it
+        // past a multiple of 2^16); the lower half is moved up.
+        return max((int)m, (int)(m << 16)) >= tkey;
+    } else {
+        int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
+#pragma unroll
+        for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
+        return mx >= tkey;
+    }
+}
+
 // Bytes per row entry: 2 for bf16 rows (VEC = 8), else 4.
 template <int VEC>
 constexpr size_t kEntryBytes = VEC == 8 ? 2 : 4;
@@ -2138,10 +2166,8 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     auto append = [&](auto masked, const VT& x, u32 iv) {
         constexpr bool kMasked = decltype(masked)::value;
         const bool valid = !kMasked || iv < nvec;
-        int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
-#pragma unroll
-        for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
-        if (__builtin_amdgcn_ballot_w64(valid & (mx >= (int)tkey)) == 0) return;
+        static_assert(kFineShift == 16, "tkey is a multiple of 2^16");
+        if (__builtin_amdgcn_ballot_w64(valid & any_at_least<VEC>(x, (int)tkey)) == 0) return;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
