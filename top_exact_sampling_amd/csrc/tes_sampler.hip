@@ -2042,6 +2042,17 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
         slab_finish<VEC>(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
         return;
     }
+    if (n == 0 && theta0 == 1u) {
+        // No positive key anywhere: every entry is a zero, so the support is
+        // indices [0, k), its boundary index k - 1 and its token (the
+        // smallest index of a support without mass) 0.
+        Outcome o{};
+        o.kind = kZeroRow;
+        o.token = 0;
+        o.c_k = composite(0u, k - 1);
+        finish_row(s, p, r, o, kPathSlabFallback, 0);
+        return;
+    }
     // n < k: the support ends with the k - n lowest-indexed zeros; its
     // boundary is the last of them.
     const u32 zk = mth_zero_index<VEC>(s, row, p.nvec, k - n);
