@@ -13,6 +13,11 @@ bandwidth against the 8 TB/s peak (algorithmic bytes = B*V*4 + 12*B per
 launch divided by the kernel's average duration: one pair of HIP events on the
 launch stream brackets the timed region, which holds exactly one kernel launch
 per step), and the CPU oracle timed on the host cores as a baseline.
+
+Before the timed region the script replays the same calls from a captured HIP
+graph and times the library's plain read of the same bytes (both reported in
+the line); after it, it repeats the timed loop for a median and checks the
+tokens of one call against the oracle.
 """
 
 from __future__ import annotations
@@ -76,11 +81,25 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(w, min_wall=10.0, max_reps=40):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, min_wall=10.0, max_reps=40, single_wall=3.0):
+    """The oracle as it stands, on every host core this process may use (rows
+    split statically across threads), plus a one-thread figure on a bounded
+    prefix of the same batch."""
     import oracle
 
     orc = oracle.load()
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
     while True:
         orc.sample(w.probs, w.top_k, w.top_p, w.seed, w.offset + reps, n_threads=cores)
@@ -88,13 +107,26 @@ def cpu_baseline(w, min_wall=10.0, max_reps=40):
         wall = time.perf_counter() - t0
         if wall >= min_wall or reps >= max_reps:
             break
+    # One thread: rows in batch order until ~single_wall seconds have passed.
+    rows1, t1 = 0, time.perf_counter()
+    while rows1 < w.B:
+        n = min(8, w.B - rows1)
+        orc.sample(w.probs[rows1:rows1 + n], w.top_k[rows1:rows1 + n],
+                   w.top_p[rows1:rows1 + n], w.seed, w.offset, n_threads=1)
+        rows1 += n
+        if time.perf_counter() - t1 >= single_wall:
+            break
+    wall1 = time.perf_counter() - t1
     return {
         "value": round(reps * w.B / wall, 1),
         "unit": "rows/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "%d full passes over all %d rows of %s (stable sort per row, %d host threads)"
-                  % (reps, w.B, w.name, cores),
+        "sample": "%d full passes over all %d rows of %s (stable sort per row, %d host threads, "
+                  "%.1f s)" % (reps, w.B, w.name, cores, wall),
+        "cpu_model": cpu_model(),
+        "single_thread_rows_per_s": round(rows1 / wall1, 1),
+        "single_thread_sample": "first %d rows of the batch on one thread (%.1f s)" % (rows1, wall1),
     }
 
 
@@ -170,6 +202,11 @@ def main():
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--renorm", action="store_true",
+                    help="also write renorm_out (dense [B][V] fp32) in every timed call")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed repetitions of --steps calls; the first is the timed region of "
+                         "the line, the median over all is reported beside it")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -208,13 +245,14 @@ def main():
     top_k = torch.from_numpy(w.top_k).to(dev)
     top_p = torch.from_numpy(w.top_p).to(dev)
     out = torch.empty(B, dtype=torch.int32, device=dev)
+    ren = torch.empty((B, V), dtype=torch.float32, device=dev) if args.renorm else None
     stream = torch.cuda.current_stream(dev)
 
     # Call i draws with Philox offset w.offset + i, as a decode loop advances
     # it, so that draw-dependent paths are sampled rather than one fixed draw.
     def step(i, st=None):
         sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i, out_tokens=out,
-                       stream=stream if st is None else st)
+                       renorm_out=ren, stream=stream if st is None else st)
 
     for i in range(args.warmup):
         step(i)
@@ -228,30 +266,41 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Two reference measurements come first: the same calls replayed from one
+    # captured HIP graph (launch overhead removed), and a plain read of the
+    # same bytes by the library's reference stream kernel, on the same stream
+    # and input copies.  (Run before the timed region, they also bring the GPU
+    # to the clocks it keeps in a decode loop.)
+    graph_ms = graph_timing(step, args.copies, stream)
+    read_ms = read_timing(tes, probs, B * V * esize, dev, stream, max(args.steps, 200))
+
     # Timed region: exactly `steps` calls, back to back on the launch stream,
     # bracketed by one pair of HIP events on that stream (each call is one
-    # kernel launch, so the events give its average duration).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    # sampler launch, or two with renorm_out, so the events give the call's
+    # average duration).  Further repetitions of the same loop follow; their
+    # median is reported beside the first.
+    def timed_loop(first):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(first + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev0.elapsed_time(ev1) / args.steps
+
+    wall, kern_ms = timed_loop(0)
     ms_per_step = wall * 1e3 / args.steps
+    reps_ms = [kern_ms] + [timed_loop(args.steps * (j + 1))[1]
+                           for j in range(max(0, args.repeats - 1))]
+    kern_med = sorted(reps_ms)[len(reps_ms) // 2]
 
-    alg_bytes = B * V * esize + 12 * B
+    # Algorithmic bytes: the rows once, top_k, top_p and the token, plus the
+    # dense renorm_out write when requested.
+    alg_bytes = B * V * esize + 12 * B + (B * V * 4 if args.renorm else 0)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-
-    # The same calls replayed from one captured HIP graph (launch overhead
-    # removed), and a plain read of the same bytes by the library's reference
-    # stream kernel, on the same stream and input copies.
-    graph_ms = graph_timing(step, args.copies, stream)
-    read_ms = read_timing(tes, probs, B * V * esize, dev, stream, args.steps)
 
     parity = None
     if not args.no_parity:
@@ -264,7 +313,8 @@ def main():
         parity = "bit-exact" if np.array_equal(gtok, otok) else \
             "MISMATCH on %d rows" % int((gtok != otok).sum())
 
-    traffic = traffic_from_profile() if args.workload == 3 and not bf16 else None
+    traffic = traffic_from_profile() if args.workload == 3 and not bf16 and not args.renorm \
+        else None
     line = {
         "metric": METRIC,
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -276,7 +326,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u64",
+        "dtype": args.input_dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -285,9 +335,13 @@ def main():
             "row_mix": ROW_MIX[args.workload],
             "input": INPUT[args.workload] + (", rounded to bf16" if bf16 else ""),
             "input_dtype": args.input_dtype,
-            "renorm_out": None,
+            "renorm_out": "dense [B][V] fp32" if args.renorm else None,
+            "arithmetic": "u32 keys, u64 fixed-point masses, u128 products (integer decisions)",
+            "input_sha256": workloads.sha256_of(w),
             "input_copies_rotated": args.copies,
             "kernel_ms_hip_events": round(kern_ms, 5),
+            "kernel_ms_repeats": [round(x, 5) for x in reps_ms],
+            "kernel_ms_median": round(kern_med, 5),
             "kernel_ms_graph_replay": round(graph_ms, 5),
             "plain_read_ms_same_bytes": round(read_ms, 5),
             "plain_read_GBps": round(B * V * esize / (read_ms * 1e-3) / 1e9, 1),
@@ -301,6 +355,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE summary committed under "
+                               "profiles/ for this kernel source hash") if traffic else None,
         },
         "cpu_baseline": None if args.no_cpu else cpu_baseline(w),
     }

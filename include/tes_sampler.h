@@ -67,6 +67,11 @@ extern "C" {
 /* Cut top-p-only rows into segments of 4096 floats instead of 32768, so that
  * the cross-segment exchanges run on small vocabularies too. */
 #define TES_FLAG_SMALL_SEGMENTS 8u
+/* Make every bounded wait of the cross-workgroup exchanges report a timeout
+ * without polling, so that a top-p-only row cut into several segments takes
+ * the path that a timed-out exchange takes (its whole-row passes decide it).
+ * Outputs are unchanged; only the path differs. */
+#define TES_FLAG_NO_WAIT 16u
 
 typedef struct tes_sampler tes_sampler;
 

@@ -34,6 +34,14 @@ def sampler(torch_cuda):
 
 
 @pytest.fixture(scope="module")
+def plain_sampler(torch_cuda):
+    # The shipping configuration: no flags (no statistics, no forced paths).
+    s = tes.Sampler(0, max_batch=4096, max_vocab=1 << 18, flags=0)
+    yield s
+    s.close()
+
+
+@pytest.fixture(scope="module")
 def variant_samplers(torch_cuda):
     out = {
         "row_select": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_FORCE_ROW_SELECT),
@@ -58,25 +66,36 @@ def wl(cfg):
     return _WL[cfg]
 
 
+@pytest.mark.parametrize("which", ["stats", "plain"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_config_parity_with_renorm(sampler, orc, cfg):
+def test_config_parity_with_renorm(sampler, plain_sampler, orc, cfg, which):
     w = wl(cfg)
-    log("[gpu] config %d %s B=%d V=%d renorm" % (cfg, w.name, w.B, w.V))
-    gtok, gren = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=True)
+    s = sampler if which == "stats" else plain_sampler
+    log("[gpu] config %d %s B=%d V=%d renorm (%s sampler)" % (cfg, w.name, w.B, w.V, which))
+    gtok, gren = run_gpu(s, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=True)
     assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, gren, w.name)
-    st = sampler.stats(w.B)
-    log("[gpu]   paths %s, kinds %s, gathered max %d" % (
-        np.bincount(st[:, 0], minlength=5).tolist(), np.bincount(st[:, 1], minlength=3).tolist(),
-        st[:, 4].max()))
+    if which == "stats":
+        st = sampler.stats(w.B)
+        log("[gpu]   paths %s, kinds %s, gathered max %d" % (
+            np.bincount(st[:, 0], minlength=5).tolist(),
+            np.bincount(st[:, 1], minlength=3).tolist(), st[:, 4].max()))
 
 
+@pytest.mark.parametrize("which", ["stats", "plain"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_config_parity_tokens_only(sampler, orc, cfg):
-    # The launch the benchmark times: renorm_out = NULL.
+def test_config_parity_tokens_only(sampler, plain_sampler, orc, cfg, which):
+    # The launch the benchmark times: renorm_out = NULL, on the sampler the
+    # benchmark uses (no flags) and on the statistics sampler.
     w = wl(cfg)
-    log("[gpu] config %d %s tokens only" % (cfg, w.name))
-    gtok, _ = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=False)
+    s = sampler if which == "stats" else plain_sampler
+    log("[gpu] config %d %s tokens only (%s sampler)" % (cfg, w.name, which))
+    gtok, _ = run_gpu(s, w.probs, w.top_k, w.top_p, w.seed, w.offset, renorm=False)
     assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, gtok, None, w.name)
+    # A second offset on the shipping sampler: draw-dependent paths differ.
+    if which == "plain":
+        gtok, _ = run_gpu(s, w.probs, w.top_k, w.top_p, w.seed, w.offset + 17, renorm=False)
+        assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset + 17, gtok, None,
+                      w.name + " offset+17")
 
 
 @pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "row_select_tiny",
@@ -213,7 +232,9 @@ def test_seeds_and_offsets(sampler, orc):
         assert_parity(orc, w.probs, w.top_k, w.top_p, seed, off, gtok, None, "seed/offset")
 
 
-def test_determinism_streams_and_graph_replay(sampler, torch_cuda):
+def test_determinism_streams_and_graph_replay(plain_sampler, torch_cuda):
+    # The sampler without statistics: a captured call records kernel nodes only.
+    sampler = plain_sampler
     torch = torch_cuda
     w = wl(3)
     pd = torch.from_numpy(w.probs).cuda()
@@ -568,3 +589,45 @@ def test_wide_draw_ranges_stay_on_the_fast_path(sampler, orc):
         assert_parity(orc, probs, ks, ps, 77, off, gtok, gren, "wide draw ranges %d" % off)
         assert np.all(st[:, 0] == 1), "rows left the fast path: %s (why %s)" % (
             np.flatnonzero(st[:, 0] != 1), st[st[:, 0] != 1, 7])
+
+
+def test_exchange_timeout_fallback(orc, torch_cuda):
+    # Top-p-only rows cut into several segments exchange their histograms
+    # through bounded waits.  With TES_FLAG_NO_WAIT every wait that is not
+    # already satisfied gives up at once, so each such row takes the timeout
+    # path (failure flag, the last segment decides the row by whole-row
+    # passes, the row state is reset).  Tokens, kept sets and renorm_out must
+    # still equal the oracle's, and a second identical call (which starts
+    # from the reset row state) must agree too.
+    s = tes.Sampler(0, max_batch=1024, max_vocab=1 << 18,
+                    flags=tes.TES_FLAG_NO_WAIT | tes.TES_FLAG_STATS)
+    try:
+        w3, w5 = wl(3), wl(5)
+        rng = np.random.default_rng(77)
+        full3 = np.flatnonzero(w3.top_k >= w3.V)
+        rows3 = np.sort(np.concatenate([full3, rng.choice(np.flatnonzero(w3.top_k < w3.V), 16,
+                                                          replace=False)]))
+        rows5 = np.sort(rng.choice(w5.B, 24, replace=False))
+        adv, aks, aps, _ = _adversarial_batch(262144, np.random.default_rng(262144))
+        cases = [
+            ("hetero subset", np.ascontiguousarray(w3.probs[rows3]), w3.top_k[rows3],
+             w3.top_p[rows3], w3.seed, w3.offset),
+            ("speculative-verify subset", np.ascontiguousarray(w5.probs[rows5]), w5.top_k[rows5],
+             w5.top_p[rows5], w5.seed, w5.offset),
+            ("adversarial V=262144", adv, aks, aps, 9, 3),
+        ]
+        for label, probs, ks, ps, seed, off in cases:
+            V = probs.shape[1]
+            multi = np.asarray(ks) >= V  # top-p-only rows (several segments at these V)
+            for call in (1, 2):
+                log("[gpu] exchange timeout fallback: %s call %d rows %d" % (label, call,
+                                                                             len(ks)))
+                gtok, gren = run_gpu(s, probs, ks, ps, seed, off, renorm=True)
+                assert_parity(orc, probs, ks, ps, seed, off, gtok, gren,
+                              "timeout fallback %s call %d" % (label, call))
+                st = s.stats(len(ks))
+                assert np.all(st[multi, 2] >= 2), "top-p-only rows were not segmented"
+                assert np.all(st[multi, 0] == 2), "paths %s" % st[multi, 0]
+                assert np.all(st[multi, 7] & 5), "timeout bits %s" % st[multi, 7]
+    finally:
+        s.close()

@@ -29,6 +29,7 @@ TES_FLAG_FORCE_ROW_SELECT = 1
 TES_FLAG_TINY_BUFFER = 2
 TES_FLAG_STATS = 4
 TES_FLAG_SMALL_SEGMENTS = 8
+TES_FLAG_NO_WAIT = 16
 
 STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 

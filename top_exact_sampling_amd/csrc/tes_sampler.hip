@@ -625,11 +625,13 @@ __device__ void arrive_only(Smem& s, u32* ctr) {
 }
 
 // Wait until `n` workgroups have counted in at *ctr (bounded); returns false
-// on a timeout.
+// on a timeout.  Under TES_FLAG_NO_WAIT every wait reports a timeout without
+// polling, so the timeout path of the callers runs on ordinary inputs.
 __device__ bool wait_arrivals(Smem& s, u32* ctr, u32 n) {
     if (threadIdx.x == 0) {
-        u32 ok = 1, it = 0;
-        while (ld_dev(ctr) < n) {
+        const bool no_wait = (s.p.flags & TES_FLAG_NO_WAIT) != 0;
+        u32 ok = no_wait ? 0u : 1u, it = 0;
+        while (!no_wait && ld_dev(ctr) < n) {
             if (++it > kSpinLimit) {
                 ok = 0;
                 break;
@@ -3181,6 +3183,13 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
     }
 }
 
+// Clears n words at p.  The statistics are cleared by this kernel rather
+// than by a memset, so that a call that a caller captures into a HIP graph
+// records kernel nodes only.
+__global__ __launch_bounds__(256) void tes_clear_kernel(u32* __restrict__ p, u32 n) {
+    for (u32 i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
 // Reference stream: reads nvec 16-byte vectors once (coalesced, eight loads
 // per thread in flight, non-temporal like the sampler's row loads) and folds
 // them into one word, stored only when it equals a value no input is expected
@@ -3258,7 +3267,7 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     if (max_batch < 1 || max_vocab < 1 || max_vocab > (1 << 30) || device < 0)
         return TES_ERR_INVALID_ARGUMENT;
     if (flags & ~(TES_FLAG_FORCE_ROW_SELECT | TES_FLAG_TINY_BUFFER | TES_FLAG_STATS |
-                  TES_FLAG_SMALL_SEGMENTS))
+                  TES_FLAG_SMALL_SEGMENTS | TES_FLAG_NO_WAIT))
         return TES_ERR_INVALID_ARGUMENT;
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
@@ -3401,10 +3410,12 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.split = s->rowbytes >= kSplitBytes ? (by_len < kMaxSplit ? (by_len < 1 ? 1u : by_len) : kMaxSplit)
                                              : 1u;
         p.slots = s->slots;
-        if (p.stats &&
-            hipMemsetAsync(p.stats + (size_t)kStatWords * c0, 0, sizeof(u32) * kStatWords * rows,
-                           st) != hipSuccess)
-            return TES_ERR_LAUNCH;
+        if (p.stats) {
+            const u32 nw = kStatWords * rows;
+            hipLaunchKernelGGL(tes_clear_kernel, dim3(ceil_div(nw, 256) < 64 ? ceil_div(nw, 256) : 64),
+                               dim3(256), 0, st, p.stats + (size_t)kStatWords * c0, nw);
+            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        }
         // Enough blocks for every row to be top-p-only; the kernel knows the
         // actual mix, and blocks beyond the last item return at once.
         // Split rows occur only when every item is resident, i.e. within
