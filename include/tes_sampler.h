@@ -109,6 +109,27 @@ int topk_topp_sample(tes_sampler *s, const float *probs, int B, int V, const int
                      const float *top_p, uint64_t seed, uint64_t offset, int32_t *out_tokens,
                      float *renorm_out, void *stream);
 
+/* topk_topp_sample for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same sampling, outputs and argument rules, with no handle.
+ * Its workspace is one statically sized device array of the library (about
+ * 32 MiB per GPU, taken when the library is loaded and held until the process
+ * ends); the call allocates nothing.
+ *   device      the current HIP device (hipGetDevice) when the call is made.
+ *   V           1 .. 262144 (TES_ERR_TOO_LARGE above); any B >= 0 (batches
+ *               of more than 256 rows run as several launches).
+ *   stream      hipStream_t on the current device.
+ * The first call on a device sets up that device (architecture check, the
+ * array's device address) and clears the array's row states with a kernel
+ * on `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Returns TES_ERR_NO_DEVICE without a current
+ * device, TES_ERR_UNSUPPORTED_DEVICE when it is not gfx950, otherwise the
+ * statuses of topk_topp_sample. */
+int topk_topp_sample_noalloc(const float *probs, int B, int V, const int32_t *top_k,
+                             const float *top_p, uint64_t seed, uint64_t offset,
+                             int32_t *out_tokens, float *renorm_out, void *stream);
+
 /* topk_topp_sample over bfloat16 probability rows (the 16-bit format whose
  * ordered encoding the SonicSampler page builds its keys from, section 3.4
  * "Numerical Lexicographic Encoding"; its input there is bf16 logits).

@@ -35,7 +35,7 @@ STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
             "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route",
-            "topk_topp_sample_bf16")
+            "topk_topp_sample_bf16", "topk_topp_sample_noalloc")
 
 _lib = None
 
@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.topk_topp_sample.restype = ctypes.c_int
         L.topk_topp_sample_bf16.argtypes = L.topk_topp_sample.argtypes
         L.topk_topp_sample_bf16.restype = ctypes.c_int
+        L.topk_topp_sample_noalloc.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp,
+                                               ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
+        L.topk_topp_sample_noalloc.restype = ctypes.c_int
         L.sampler_destroy.argtypes = [vp]
         L.sampler_destroy.restype = ctypes.c_int
         L.sampler_status_string.argtypes = [ctypes.c_int]
@@ -110,6 +113,16 @@ def topk_topp_sample_bf16(handle, probs_ptr: int, B: int, V: int, top_k_ptr: int
     return lib().topk_topp_sample_bf16(handle, probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
                                        int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                        out_tokens_ptr, renorm_ptr, stream)
+
+
+def topk_topp_sample_noalloc(probs_ptr: int, B: int, V: int, top_k_ptr: int, top_p_ptr: int,
+                             seed: int, offset: int, out_tokens_ptr: int, renorm_ptr,
+                             stream) -> int:
+    """Raw call of the allocation-free entry point (no handle; the current
+    device), with device pointers (ints); returns the status code."""
+    return lib().topk_topp_sample_noalloc(probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
+                                          int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                          out_tokens_ptr, renorm_ptr, stream)
 
 
 def sampler_destroy(handle) -> int:

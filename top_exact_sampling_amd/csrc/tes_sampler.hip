@@ -53,9 +53,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <cstring>
-#include <type_traits>
+#include <mutex>
 #include <new>
+#include <type_traits>
 
 #include "tes_sampler.h"
 
@@ -3439,6 +3441,118 @@ extern "C" int topk_topp_sample(tes_sampler* s, const float* probs, int B, int V
                                 void* stream) {
     return sample_impl(s, probs, false, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
                        nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free entry point
+// ---------------------------------------------------------------------------
+// topk_topp_sample_noalloc keeps its workspace (row states, decisions and the
+// per-row exchange areas of up to kNoAllocRows rows, laid out exactly as a
+// handle's workspace) in one statically sized device array, so that a call
+// allocates nothing.  Its size is fixed by the largest vocabulary it serves;
+// batches of more rows run as several launches.
+namespace {
+constexpr u32 kNoAllocRows = 256;
+constexpr u32 kNoAllocMaxVocab = 1u << 18;
+constexpr u32 kNoAllocSegWs = (kNoAllocMaxVocab / 4 + kSegVecFull - 1) / kSegVecFull;
+constexpr size_t kNoAllocTopP =
+    (size_t)kNoAllocSegWs * (sizeof(PubC) + sizeof(PubF) + (size_t)kGSeg * sizeof(u64));
+constexpr size_t kNoAllocRowBytes =
+    ((kNoAllocTopP > kSplitBytes ? kNoAllocTopP : kSplitBytes) + 255) & ~(size_t)255;
+constexpr size_t kScratchBytes =
+    (size_t)kNoAllocRows * (sizeof(RowState) + sizeof(Decision) + kNoAllocRowBytes);
+static_assert(kNoAllocRows * sizeof(RowState) % 4 == 0, "row states clear as words");
+static_assert(kScratchBytes <= (40u << 20), "the scratch array stays modest");
+}  // namespace
+
+// One copy per GPU the library runs on, held until the process ends.  Host
+// code never uses this name as an address: the device address of each GPU's
+// copy comes from hipGetSymbolAddress (see noalloc_device).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+struct NoAllocDevice {
+    unsigned char* ptr;  // device address of this GPU's scratch array (null: not set up)
+    u32 slots;           // resident workgroups
+    bool clean;          // its row states were cleared by an executed (not captured) call
+};
+constexpr int kNoAllocDevices = 64;
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kNoAllocDevices];
+
+// Sets up device `dev` (current) on its first call: checks the architecture,
+// takes the scratch array's device address and clears its row states with a
+// kernel on `st` (row states must start at zero; the sampler leaves them at
+// zero after every row).  A clear recorded into a graph under capture does
+// not count: the next call that is not captured clears again.
+int noalloc_device(int dev, hipStream_t st, NoAllocDevice& out) {
+    if (dev < 0 || dev >= kNoAllocDevices) return TES_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoAllocDevice& e = g_noalloc[dev];
+    if (!e.ptr) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TES_ERR_NO_DEVICE;
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return TES_ERR_UNSUPPORTED_DEVICE;
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return TES_ERR_LAUNCH;
+        }
+        e.ptr = static_cast<unsigned char*>(ptr);
+        e.slots = 2u * (u32)(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1);
+        e.clean = false;
+    }
+    if (!e.clean) {
+        const u32 nw = (u32)(kNoAllocRows * sizeof(RowState) / 4);
+        hipLaunchKernelGGL(tes_clear_kernel, dim3(ceil_div(nw, 256)), dim3(256), 0, st,
+                           reinterpret_cast<u32*>(e.ptr), nw);
+        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+            e.clean = true;
+        else
+            (void)hipGetLastError();
+    }
+    out = e;
+    return TES_OK;
+}
+}  // namespace
+
+extern "C" int topk_topp_sample_noalloc(const float* probs, int B, int V, const int32_t* top_k,
+                                        const float* top_p, uint64_t seed, uint64_t offset,
+                                        int32_t* out_tokens, float* renorm_out, void* stream) {
+    if (B < 0 || V < 1) return TES_ERR_INVALID_ARGUMENT;
+    if ((u32)V > kNoAllocMaxVocab) return TES_ERR_TOO_LARGE;
+    if (B == 0) return TES_OK;
+    // Argument errors are reported before the device is touched.
+    if (!probs || !top_k || !top_p || !out_tokens) return TES_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)probs & 3) || ((uintptr_t)top_k & 3) || ((uintptr_t)top_p & 3) ||
+        ((uintptr_t)out_tokens & 3) || ((uintptr_t)renorm_out & 3))
+        return TES_ERR_INVALID_ARGUMENT;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TES_ERR_NO_DEVICE;
+    }
+    NoAllocDevice d{};
+    const int rc = noalloc_device(dev, reinterpret_cast<hipStream_t>(stream), d);
+    if (rc != TES_OK) return rc;
+    // A handle-shaped view of the scratch array (nothing is allocated).
+    tes_sampler view{};
+    view.device = dev;
+    view.max_batch = INT_MAX;
+    view.max_vocab = (int)kNoAllocMaxVocab;
+    view.flags = 0;
+    view.ws = d.ptr;
+    view.ws_bytes = kScratchBytes;
+    view.s_ws = kNoAllocSegWs;
+    view.rowbytes = (u32)kNoAllocRowBytes;
+    view.chunk = kNoAllocRows;
+    view.seg_full = kSegVecFull;
+    view.slots = d.slots;
+    view.d_stats = nullptr;
+    return sample_impl(&view, probs, false, B, V, top_k, top_p, seed, offset, out_tokens,
+                       renorm_out, nullptr, stream);
 }
 
 extern "C" int topk_topp_sample_bf16(tes_sampler* s, const uint16_t* probs, int B, int V,
