@@ -33,7 +33,10 @@ def build(force: bool = True, out: str | None = None, src: str | None = None) ->
     if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
         return out
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", tmp, src]
+    # -ffp-contract=off: every fp32 operation of the logit weights is the one
+    # written (no multiply-add fusion the source does not ask for).
+    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-shared", "-fPIC", "-pthread",
+           "-o", tmp, src]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -61,6 +64,20 @@ class Oracle:
         lib.oracle_support.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                        ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_support.restype = ctypes.c_int64
+        lib.oracle_exp_weight.argtypes = [ctypes.c_float]
+        lib.oracle_exp_weight.restype = ctypes.c_float
+        lib.oracle_logit_weights.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                             ctypes.c_void_p]
+        lib.oracle_logit_weights.restype = ctypes.c_int
+        lib.oracle_sample_row_minp.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+            ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_sample_row_minp.restype = ctypes.c_int
+        lib.oracle_topk_topp_sample_logits.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_topk_topp_sample_logits.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -75,15 +92,57 @@ class Oracle:
     def uniform_u64(self, seed: int, row: int, offset: int) -> int:
         return int(self.lib.oracle_uniform_u64(seed, row, offset))
 
+    # -- logit rows ---------------------------------------------------------
+    def exp_weight(self, s: float) -> float:
+        """E(s) of the logit-row weights (fp32 in, fp32 out)."""
+        return float(np.float32(self.lib.oracle_exp_weight(float(np.float32(s)))))
+
+    def logit_weights(self, row, tau: float):
+        """The fp32 weights of one logit row at temperature tau."""
+        row = np.ascontiguousarray(row, dtype=np.float32)
+        w = np.zeros(row.size, np.float32)
+        rc = self.lib.oracle_logit_weights(row.ctypes.data, row.size, float(np.float32(tau)),
+                                           w.ctypes.data)
+        if rc:
+            raise RuntimeError("oracle_logit_weights failed: %d" % rc)
+        return w
+
+    def sample_logits(self, logits, top_k, top_p, temperature, min_p, seed: int, offset: int,
+                      want_renorm: bool = False, want_info: bool = False,
+                      n_threads: int | None = None):
+        """Batched logit rows (temperature / min_p may be None: 1 and off)."""
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        B, V = logits.shape
+        top_k = np.ascontiguousarray(top_k, dtype=np.int32)
+        top_p = np.ascontiguousarray(top_p, dtype=np.float32)
+        tau = None if temperature is None else np.ascontiguousarray(temperature, np.float32)
+        mp = None if min_p is None else np.ascontiguousarray(min_p, np.float32)
+        tok = np.zeros(B, np.int32)
+        ren = np.zeros((B, V), np.float32) if want_renorm else None
+        info = np.zeros((B, 10), np.int64) if want_info else None
+        if n_threads is None:
+            n_threads = len(os.sched_getaffinity(0))
+        rc = self.lib.oracle_topk_topp_sample_logits(
+            logits.ctypes.data, B, V, top_k.ctypes.data, top_p.ctypes.data,
+            tau.ctypes.data if tau is not None else None,
+            mp.ctypes.data if mp is not None else None,
+            int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), tok.ctypes.data,
+            ren.ctypes.data if ren is not None else None,
+            info.ctypes.data if info is not None else None, int(n_threads))
+        if rc:
+            raise RuntimeError("oracle_topk_topp_sample_logits failed: %d" % rc)
+        return tok, ren, info
+
     # -- sampling -------------------------------------------------------------
-    def sample_row(self, row, top_k: int, top_p: float, u: int, want_renorm: bool = True):
+    def sample_row(self, row, top_k: int, top_p: float, u: int, want_renorm: bool = True,
+                   min_p: float = 0.0):
         row = np.ascontiguousarray(row, dtype=np.float32)
         V = row.size
         tok = np.zeros(1, np.int32)
         ren = np.zeros(V, np.float32) if want_renorm else None
         info = np.zeros(10, np.int64)
-        rc = self.lib.oracle_sample_row(
-            row.ctypes.data, V, int(top_k), float(top_p), int(u) & (2**64 - 1),
+        rc = self.lib.oracle_sample_row_minp(
+            row.ctypes.data, V, int(top_k), float(top_p), float(min_p), int(u) & (2**64 - 1),
             tok.ctypes.data, ren.ctypes.data if ren is not None else None, info.ctypes.data)
         if rc:
             raise RuntimeError("oracle_sample_row failed: %d" % rc)

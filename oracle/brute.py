@@ -88,11 +88,15 @@ def brute_support(row_bits, k: int):
     return order
 
 
-def brute_row(row_bits, k: int, p: float, u: int):
+def brute_row(row_bits, k: int, p: float, u: int, min_p: float = 0.0):
     """Return (token, kept indices in sorted order, weights as Fractions).
 
     ``row_bits`` is a sequence of fp32 bit patterns (ints), so NaN payloads,
-    -0.0 and denormals reach this function unchanged.
+    -0.0 and denormals reach this function unchanged.  ``min_p`` (theta) is
+    the min-p floor of SonicSampler eq. (11) on the fixed-point masses: an
+    entry of the support stays only if q_i >= theta * max q (exact rational
+    comparison), applied after top-k and top-p (the kept set is the
+    intersection of the two sets); theta NaN or <= 0 is off, > 1 counts as 1.
     """
     xs = [_from_bits(int(v)) for v in row_bits]
     V = len(xs)
@@ -125,6 +129,12 @@ def brute_row(row_bits, k: int, p: float, u: int):
 
     target = Fraction(fixed_p(p), TWO24) * M_k
     n = next(n for n in range(1, len(support) + 1) if sum(q[:n]) >= target)
+    theta = _f32(min_p)
+    if not math.isnan(theta) and theta > 0:
+        floor_mass = Fraction(min(theta, 1.0)) * max(q)
+        keep = [j for j in range(n) if q[j] >= floor_mass]  # the intersection
+        n = len(keep)
+        assert keep == list(range(n)), "the min-p set is a prefix of the sorted support"
     kept = support[:n]
     M_p = sum(q[:n])
     x = Fraction(u, TWO64)

@@ -32,6 +32,27 @@
 //      token = S[first j with S_incl(j) > t].
 //   9. renorm_out[b][S[j]] = fp32(q_j / M_p) for kept j, 0 elsewhere.
 //
+// Min-p (SonicSampler paper, appendix C.2, eq. (11)): with theta in (0, 1],
+// the support entries whose mass q_j >= theta * q_max (q_max = the largest
+// mass of the support, compared exactly) form a prefix of the sorted support;
+// it is applied after top-k and top-p, as the truncation epilogue of the
+// paper's stage-2 kernel lists them (TopK, TopP, MinP): the kept set is the
+// shorter of the top-p prefix and the min-p prefix.  theta NaN or <= 0 turns
+// it off; theta > 1 counts as 1.
+//
+// Logit rows (SonicSampler appendix C.1, temperature eq. (8), and the
+// softmax that turns logits into probabilities): x_i = logit, NaN counts as
+// -inf; M = max_i x_i.  Each entry gets the fp32 weight
+//   w_i = 1                          if x_i == M,
+//   w_i = E(fl(fl(x_i - M) * r))      otherwise,
+// with r = fp32(fp64(1 / tau)) (tau NaN or <= 0: r = +inf, the tau -> 0
+// limit; tau = +inf: r = 0) and E(s) the fp32 exponential of s <= 0 defined
+// below.  Rows with M = +inf weigh their +inf entries +inf and the rest 0;
+// rows with M = -inf (every entry -inf or NaN) weigh everything 0.  w is the
+// row's softmax(x / tau) scaled so that its largest entry is 1, and the row is
+// then sampled by steps 1-9 as a probability row (step 1 is the identity on
+// w; the scale cancels in every step).
+//
 // Parity is pinned by the tests in tests/test_oracle_*.py (brute force over
 // tiny rows with exact rationals, closed forms, Philox cross-checks against
 // the open-source PyTorch and rocRAND engines, exact draw boundaries and a
@@ -41,6 +62,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <numeric>
 #include <thread>
 #include <vector>
@@ -151,6 +173,86 @@ static std::vector<int64_t> support_order(const std::vector<uint32_t>& key, int6
 }
 
 // ---------------------------------------------------------------------------
+// E(s) for fp32 s <= 0: exp(s) evaluated with a fixed sequence of IEEE-754
+// fp32 operations (each correctly rounded: multiply, round-to-integer ties to
+// even, fused multiply-add, scaling by a power of two), so that any
+// implementation that performs the same operations gets the same bits.  The
+// method is Cody and Waite's argument reduction (W. J. Cody and W. Waite,
+// "Software Manual for the Elementary Functions", 1980): n = rint(s / ln 2),
+// f = s - n ln 2 with ln 2 split into a high and a low part, then
+// exp(f) by the Taylor polynomial sum_{j<=7} f^j / j! in Horner form, and
+// exp(s) = exp(f) * 2^n.  Results below 2^-125 (n < -125), NaN and s < -104
+// give 0, so no result is subnormal.
+// ---------------------------------------------------------------------------
+static float taylor_coefficient(int j) {
+    double f = 1.0;
+    for (int i = 2; i <= j; ++i) f *= (double)i;
+    return (float)(1.0 / f);  // the fp32 nearest 1/j! (checked exactly by the tests)
+}
+
+extern "C" float oracle_exp_weight(float s) {
+    if (!(s >= -104.0f)) return 0.0f;  // NaN, -inf and far below the smallest weight
+    const float log2e = 0x1.715476p+0f;     // fp32 nearest log2(e)
+    const float ln2_hi = 0x1.62e43p-1f;     // fp32 nearest ln(2)
+    const float ln2_lo = -0x1.05c61p-29f;   // fp32 nearest ln(2) - ln2_hi
+    const float n = std::nearbyint(s * log2e);
+    if (n < -125.0f) return 0.0f;
+    float f = std::fma(n, -ln2_hi, s);
+    f = std::fma(n, -ln2_lo, f);
+    float p = taylor_coefficient(7);
+    for (int j = 6; j >= 0; --j) p = std::fma(p, f, taylor_coefficient(j));
+    return std::ldexp(p, (int)n);
+}
+
+// The weights w[0, V) of one logit row (see the file header).
+extern "C" int oracle_logit_weights(const float* x, int64_t V, float tau, float* w) {
+    if (V <= 0 || !x || !w) return -1;
+    const float ninf = -std::numeric_limits<float>::infinity();
+    float M = ninf;
+    for (int64_t i = 0; i < V; ++i) {
+        const float xi = std::isnan(x[i]) ? ninf : x[i];
+        if (xi > M) M = xi;
+    }
+    if (M == std::numeric_limits<float>::infinity()) {
+        for (int64_t i = 0; i < V; ++i) w[i] = (x[i] == M) ? M : 0.0f;
+        return 0;
+    }
+    if (M == ninf) {
+        for (int64_t i = 0; i < V; ++i) w[i] = 0.0f;
+        return 0;
+    }
+    float r;
+    if (!(tau > 0.0f)) r = std::numeric_limits<float>::infinity();
+    else r = (float)(1.0 / (double)tau);  // 0 for tau = +inf
+    for (int64_t i = 0; i < V; ++i) {
+        const float xi = std::isnan(x[i]) ? ninf : x[i];
+        if (xi == M) {
+            w[i] = 1.0f;
+        } else {
+            const float d = xi - M;
+            const float sc = d * r;
+            w[i] = oracle_exp_weight(sc);
+        }
+    }
+    return 0;
+}
+
+// ceil(theta * qmax) for theta in (0, 1], exactly: theta = m * 2^e with an
+// integer m < 2^24.
+static uint64_t min_p_floor_mass(float theta, uint64_t qmax) {
+    int e = 0;
+    const double fr = std::frexp((double)theta, &e);  // theta = fr * 2^e, fr in [0.5, 1)
+    const uint64_t m = (uint64_t)std::ldexp(fr, 24);  // exact: theta has 24 bits
+    e -= 24;                                           // theta = m * 2^e, e < 0 here
+    const u128 prod = (u128)m * (u128)qmax;  // < 2^57
+    const int sh = -e;
+    if (sh >= 64) return prod != 0 ? 1 : 0;  // theta * qmax <= 2^-7: ceil is 1 (or 0)
+    const u128 q = prod >> sh;
+    const bool rem = (prod & (((u128)1 << sh) - 1)) != 0;
+    return (uint64_t)q + (rem ? 1 : 0);
+}
+
+// ---------------------------------------------------------------------------
 // One row, with the uniform u given explicitly.
 //
 // info (nullable, 10 x int64):
@@ -159,8 +261,9 @@ static std::vector<int64_t> support_order(const std::vector<uint32_t>& key, int6
 //   [6] M_p  [7] t  [8] position of the token in the sorted support
 //   [9] row kind: 0 normal, 1 +inf, 2 zero mass
 // ---------------------------------------------------------------------------
-extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, float top_p,
-                                 uint64_t u, int32_t* token, float* renorm, int64_t* info) {
+extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k, float top_p,
+                                      float min_p, uint64_t u, int32_t* token, float* renorm,
+                                      int64_t* info) {
     if (V <= 0 || row == nullptr || token == nullptr) return -1;
 
     std::vector<uint32_t> key(V);
@@ -220,6 +323,19 @@ extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, flo
         s_excl += q[kept];
         ++kept;
     }
+    // Min-p (off for theta NaN or <= 0): the support entries with
+    // q_j >= ceil(theta * q_max) are a prefix; keep the shorter prefix.
+    if (min_p > 0.0f) {
+        const float theta = min_p > 1.0f ? 1.0f : min_p;
+        const uint64_t floor_mass = min_p_floor_mass(theta, q[0]);  // q[0] = q_max
+        int64_t n_min_p = 0;
+        while (n_min_p < k_eff && q[n_min_p] >= floor_mass) ++n_min_p;
+        if (n_min_p < kept) {
+            kept = n_min_p;
+            s_excl = 0;
+            for (int64_t j = 0; j < kept; ++j) s_excl += q[j];
+        }
+    }
     const uint64_t M_p = s_excl;  // S_incl(J)
 
     // Step 8: inverse CDF on the kept prefix.
@@ -246,6 +362,11 @@ extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, flo
     return 0;
 }
 
+extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, float top_p,
+                                 uint64_t u, int32_t* token, float* renorm, int64_t* info) {
+    return oracle_sample_row_minp(row, V, top_k, top_p, 0.0f, u, token, renorm, info);
+}
+
 // ---------------------------------------------------------------------------
 // The support S of one row in its sorted order (descending probability,
 // ascending index: the first k_eff entries of the stable sort of step 3),
@@ -268,6 +389,50 @@ extern "C" int64_t oracle_support(const float* row, int64_t V, int32_t top_k, in
 // across n_threads host threads (<= 0 means one).  renorm_out and info are
 // nullable; info holds 10 int64 per row.
 // ---------------------------------------------------------------------------
+// Batched sampling of logit rows: per row the weights of oracle_logit_weights
+// (temperature[b], 1 when temperature is null), then the probability method
+// with min_p[b] (off when min_p is null).  renorm_out (nullable) receives the
+// renormalised kept weights, i.e. the final probabilities.
+extern "C" int oracle_topk_topp_sample_logits(const float* logits, int64_t B, int64_t V,
+                                              const int32_t* top_k, const float* top_p,
+                                              const float* temperature, const float* min_p,
+                                              uint64_t seed, uint64_t offset,
+                                              int32_t* out_tokens, float* renorm_out,
+                                              int64_t* info, int n_threads) {
+    if (B < 0 || V <= 0) return -1;
+    if (B == 0) return 0;
+    if (!logits || !top_k || !top_p || !out_tokens) return -1;
+    if (n_threads <= 0) n_threads = 1;
+    if ((int64_t)n_threads > B) n_threads = (int)B;
+    std::vector<int> status(n_threads, 0);
+    auto work = [&](int wk) {
+        std::vector<float> w(V);
+        int64_t r0 = B * wk / n_threads, r1 = B * (wk + 1) / n_threads;
+        for (int64_t b = r0; b < r1; ++b) {
+            const float tau = temperature ? temperature[b] : 1.0f;
+            int rc = oracle_logit_weights(logits + b * V, V, tau, w.data());
+            if (!rc) {
+                uint64_t u = oracle_uniform_u64(seed, (uint64_t)b, offset);
+                rc = oracle_sample_row_minp(w.data(), V, top_k[b], top_p[b],
+                                            min_p ? min_p[b] : 0.0f, u, out_tokens + b,
+                                            renorm_out ? renorm_out + b * V : nullptr,
+                                            info ? info + b * 10 : nullptr);
+            }
+            if (rc) status[wk] = rc;
+        }
+    };
+    if (n_threads == 1) {
+        work(0);
+    } else {
+        std::vector<std::thread> pool;
+        for (int wk = 0; wk < n_threads; ++wk) pool.emplace_back(work, wk);
+        for (auto& th : pool) th.join();
+    }
+    for (int st : status)
+        if (st) return st;
+    return 0;
+}
+
 extern "C" int oracle_topk_topp_sample(const float* probs, int64_t B, int64_t V,
                                        const int32_t* top_k, const float* top_p,
                                        uint64_t seed, uint64_t offset, int32_t* out_tokens,

@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import tests.test_oracle_brute as pb
+import tests.test_oracle_logits as pl
 import tests.test_oracle_philox as pp
 import tests.test_oracle_properties as pr
 
@@ -71,6 +72,33 @@ MUTATIONS = {
     "zero_mass_first_sorted": (
         "*token = (int32_t)*std::min_element(order.begin(), order.end());",
         "*token = (int32_t)order[0];"),
+    "min_p_floor_not_ceil": (
+        "return (uint64_t)q + (rem ? 1 : 0);",
+        "return (uint64_t)q;"),
+    "min_p_strict": (
+        "q[n_min_p] >= floor_mass",
+        "q[n_min_p] > floor_mass"),
+    "min_p_from_last_support_mass": (
+        "min_p_floor_mass(theta, q[0])",
+        "min_p_floor_mass(theta, q[k_eff - 1])"),
+    "min_p_cut_dropped": (
+        "if (n_min_p < kept) {",
+        "if (n_min_p > kept) {"),
+    "temperature_multiplies": (
+        "else r = (float)(1.0 / (double)tau);",
+        "else r = tau;"),
+    "tau_zero_not_the_limit": (
+        "if (!(tau > 0.0f)) r = std::numeric_limits<float>::infinity();",
+        "if (!(tau > 0.0f)) r = 1.0f;"),
+    "exp_low_part_dropped": (
+        "f = std::fma(n, -ln2_lo, f);",
+        "f = f + 0.0f;"),
+    "exp_taylor_degree_six": (
+        "float p = taylor_coefficient(7);",
+        "float p = 0.0f;"),
+    "logit_nan_counts_as_max": (
+        "const float xi = std::isnan(x[i]) ? ninf : x[i];\n        if (xi > M) M = xi;",
+        "const float xi = std::isnan(x[i]) ? -ninf : x[i];\n        if (xi > M) M = xi;"),
     "renorm_by_topk_mass": (
         "renorm[order[j]] = (float)((double)q[j] / (double)M_p);",
         "renorm[order[j]] = (float)((double)q[j] / (double)M_k);"),
@@ -88,6 +116,13 @@ def _pins(orc, torch_exe, rocrand_exe):
     yield lambda: pr.test_zero_mass_rows_return_smallest_support_index(orc)
     yield lambda: pr.test_masses_closed_form(orc)
     yield lambda: pr.test_equal_values_keep_ceil_pn(orc, 100, 0.77)
+    yield lambda: pl.test_exp_weight_within_one_ulp(orc)
+    yield lambda: pl.test_exp_weight_special_values(orc)
+    yield lambda: pl.test_logit_weights_against_float64_softmax(orc)
+    yield lambda: pl.test_logit_weight_rules(orc)
+    for theta in (0.2, 0.25, 0.5, 1.0):
+        yield lambda theta=theta: pl.test_min_p_against_brute_force(orc, theta)
+    yield lambda: pl.test_min_p_floor_exactly_on_a_mass(orc)
     if torch_exe:
         yield lambda: pp.test_block_function_matches_pytorch(orc, torch_exe)
         yield lambda: pp.test_row_uniform_mapping(orc, torch_exe)
@@ -122,8 +157,8 @@ def test_planted_mistake_is_caught(name, harnesses, tmp_path):
     mutated = tmp_path / "tes_oracle_mut.cpp"
     mutated.write_text(src.replace(old, new))
     lib = tmp_path / "liboracle_mut.so"
-    subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", str(lib),
-                    str(mutated)], check=True)
+    subprocess.run(["g++", "-O1", "-std=c++17", "-ffp-contract=off", "-shared", "-fPIC",
+                    "-pthread", "-o", str(lib), str(mutated)], check=True)
     mut = oracle.load(str(lib))
     for pin in _pins(mut, *harnesses):
         try:
