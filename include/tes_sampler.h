@@ -109,6 +109,34 @@ int topk_topp_sample(tes_sampler *s, const float *probs, int B, int V, const int
                      const float *top_p, uint64_t seed, uint64_t offset, int32_t *out_tokens,
                      float *renorm_out, void *stream);
 
+/* Sampling from fp32 logit rows with a per-row temperature and a min-p floor
+ * (SonicSampler paper, appendix C.1 "Temperature", eq. (8), and appendix C.2
+ * "Min-p", eqs. (11)-(12)).  Each row becomes fp32 weights: with M the row
+ * maximum (NaN counts as -inf) and r = fp32(fp64(1 / tau)), an entry equal to
+ * M weighs 1 and any other E((x - M) * r), E an fp32 exponential evaluated
+ * by a fixed sequence of correctly rounded fp32 operations (Cody-Waite
+ * reduction, degree-7 Taylor polynomial; within one ulp of exp, 0 below
+ * 2^-125), so the weights are bit-reproducible; tau NaN or <= 0 is the
+ * tau -> 0 limit (1 on every maximum, 0 elsewhere), tau = +inf weighs every
+ * finite entry 1; rows with a +inf logit weigh their +inf entries +inf (the
+ * +inf rule), rows of only -inf / NaN weigh everything 0.  The weights are
+ * softmax(x / tau) up to one scale factor, which every step cancels; the row
+ * is then sampled by steps 1-7 above, with min-p after top-p: the support
+ * entries with mass q < ceil(theta * q_max) (q_max the largest mass) are
+ * dropped from the kept prefix.  renorm_out holds the final probabilities.
+ *   logits       device, fp32 [B][V] row-major, contiguous, 4-byte aligned
+ *                (16-byte alignment and V % 4 == 0 enable 16-byte loads).
+ *   temperature  device, fp32 [B], or NULL (1 on every row).
+ *   min_p        device, fp32 [B], or NULL (off); theta NaN or <= 0 is off,
+ *                theta > 1 counts as 1.
+ * Every other argument, the ownership rules and the status codes are those
+ * of topk_topp_sample.  One extra read of the rows (their maxima) precedes
+ * the sampling kernel. */
+int topk_topp_sample_logits(tes_sampler *s, const float *logits, int B, int V,
+                            const int32_t *top_k, const float *top_p, const float *temperature,
+                            const float *min_p, uint64_t seed, uint64_t offset,
+                            int32_t *out_tokens, float *renorm_out, void *stream);
+
 /* topk_topp_sample for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same sampling, outputs and argument rules, with no handle.

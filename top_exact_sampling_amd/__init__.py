@@ -35,7 +35,7 @@ STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
             "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route",
-            "topk_topp_sample_bf16", "topk_topp_sample_noalloc")
+            "topk_topp_sample_bf16", "topk_topp_sample_noalloc", "topk_topp_sample_logits")
 
 _lib = None
 
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.topk_topp_sample_noalloc.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp,
                                                ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
         L.topk_topp_sample_noalloc.restype = ctypes.c_int
+        L.topk_topp_sample_logits.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                              ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
+        L.topk_topp_sample_logits.restype = ctypes.c_int
         L.sampler_destroy.argtypes = [vp]
         L.sampler_destroy.restype = ctypes.c_int
         L.sampler_status_string.argtypes = [ctypes.c_int]
@@ -123,6 +126,17 @@ def topk_topp_sample_noalloc(probs_ptr: int, B: int, V: int, top_k_ptr: int, top
     return lib().topk_topp_sample_noalloc(probs_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
                                           int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                           out_tokens_ptr, renorm_ptr, stream)
+
+
+def topk_topp_sample_logits(handle, logits_ptr: int, B: int, V: int, top_k_ptr: int,
+                            top_p_ptr: int, temperature_ptr, min_p_ptr, seed: int, offset: int,
+                            out_tokens_ptr: int, renorm_ptr, stream) -> int:
+    """Raw call over fp32 logit rows with device pointers (ints; temperature,
+    min_p and renorm may be None); returns the status code."""
+    return lib().topk_topp_sample_logits(handle, logits_ptr, int(B), int(V), top_k_ptr, top_p_ptr,
+                                         temperature_ptr, min_p_ptr, int(seed) & (2**64 - 1),
+                                         int(offset) & (2**64 - 1), out_tokens_ptr, renorm_ptr,
+                                         stream)
 
 
 def sampler_destroy(handle) -> int:
@@ -209,6 +223,33 @@ class Sampler:
                 renorm_out.data_ptr() if renorm_out is not None else None, stream.cuda_stream)
         if rc != TES_OK:
             raise TesError(rc, fn.__name__)
+        return out_tokens
+
+    def sample_logits(self, logits, top_k, top_p, seed: int, offset: int, temperature=None,
+                      min_p=None, out_tokens=None, renorm_out=None, stream=None):
+        """Sample fp32 logit rows (topk_topp_sample_logits); temperature and
+        min_p are per-row fp32 tensors or None."""
+        import torch
+
+        B, V = logits.shape
+        checks = [(logits, torch.float32), (top_k, torch.int32), (top_p, torch.float32)]
+        for t in (temperature, min_p):
+            if t is not None:
+                checks.append((t, torch.float32))
+        for t, dt in checks:
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("expected contiguous %s on the GPU" % dt)
+        if out_tokens is None:
+            out_tokens = torch.empty(B, dtype=torch.int32, device=logits.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(logits.device)
+        rc = topk_topp_sample_logits(
+            self.handle, logits.data_ptr(), B, V, top_k.data_ptr(), top_p.data_ptr(),
+            temperature.data_ptr() if temperature is not None else None,
+            min_p.data_ptr() if min_p is not None else None, seed, offset, out_tokens.data_ptr(),
+            renorm_out.data_ptr() if renorm_out is not None else None, stream.cuda_stream)
+        if rc != TES_OK:
+            raise TesError(rc, "topk_topp_sample_logits")
         return out_tokens
 
     def sample_slab(self, probs, top_k, top_p, seed: int, offset: int, slab_cap: int,

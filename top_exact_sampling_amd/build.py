@@ -16,6 +16,9 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     # Packed fp32 instructions are disabled for all device code on purpose.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The logit weights are a fixed sequence of IEEE fp32 operations: no
+    # multiply-add fusion beyond the written ones, subnormals kept.
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Wno-unused-command-line-argument",
 ]
 

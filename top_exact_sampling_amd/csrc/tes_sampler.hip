@@ -124,6 +124,13 @@ struct RowState {  // zero between calls
 };
 static_assert(sizeof(RowState) == 64, "row state size");
 
+// Logit rows: the row maximum, as partial maxima of up to kXParts parts of the
+// row written by the prologue kernel (order-preserving u32 encodings).
+constexpr u32 kXParts = 8;
+struct XMax {
+    u32 part[kXParts];
+};
+
 struct Decision {  // what renorm_out and the slab export need
     u32 kind;
     u32 m;
@@ -145,9 +152,11 @@ struct PubF {  // second exchange: fine bins of the listed coarse bins
 };
 
 struct Params {
-    const float* probs;  // first row of this launch
+    const float* probs;  // first row of this launch (probabilities, or logits)
     const int32_t* top_k;
     const float* top_p;
+    const float* temperature;  // logit rows: per-row temperature, or null (1)
+    const float* min_p;        // per-row min-p floor, or null (off)
     int32_t* out_tokens;
     u32* stats;          // per row, 8 words, or null
     unsigned char* ws;
@@ -164,6 +173,7 @@ struct Params {
     u32 flags;
     u32 split;      // parts a top-k or greedy row may be split into (1 .. kMaxSplit)
     u32 slots;      // workgroups resident at once on the device
+    u32 xparts;     // logit rows: partial maxima per row
 };
 
 __device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
@@ -172,8 +182,12 @@ __device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
 __device__ __forceinline__ Decision* ws_decision(const Params& p, u32 r) {
     return reinterpret_cast<Decision*>(p.ws + (size_t)p.chunk * sizeof(RowState)) + r;
 }
+__device__ __forceinline__ XMax* ws_xmax(const Params& p, u32 r) {
+    return reinterpret_cast<XMax*>(p.ws + (size_t)p.chunk * (sizeof(RowState) + sizeof(Decision))) + r;
+}
 __device__ __forceinline__ unsigned char* ws_row(const Params& p, u32 r) {
-    return p.ws + (size_t)p.chunk * (sizeof(RowState) + sizeof(Decision)) + (size_t)r * p.rowbytes;
+    return p.ws + (size_t)p.chunk * (sizeof(RowState) + sizeof(Decision) + sizeof(XMax)) +
+           (size_t)r * p.rowbytes;
 }
 __device__ __forceinline__ PubC* pub_c(const Params& p, u32 r, u32 seg) {
     return reinterpret_cast<PubC*>(ws_row(p, r)) + seg;
@@ -356,6 +370,32 @@ __device__ __forceinline__ u64 topp_threshold(u64 P, u64 M) {
     return T + ((lo & 0xFFFFFFull) != 0);
 }
 
+// Min-p (SonicSampler paper, appendix C.2, eq. (11), on the fixed-point
+// masses): the support keeps entries with q >= theta * q_max.  For theta in
+// (0, 1] the floor ceil(theta * q_max) is exact: theta = m * 2^-sh with an
+// integer m < 2^24, and q_max <= 2^32, so m * q_max fits 64 bits.  NaN and
+// theta <= 0 give 0 (off); theta > 1 counts as 1.
+__device__ __forceinline__ u64 minp_floor(float theta, u64 qmax) {
+    if (!(theta > 0.0f)) return 0;
+    const u32 b = __float_as_uint(theta >= 1.0f ? 1.0f : theta);
+    const u32 ex = b >> 23;
+    const u64 m = ex ? (u64)((b & 0x7FFFFFu) | 0x800000u) : (u64)(b & 0x7FFFFFu);
+    const int sh = 150 - (int)(ex ? ex : 1u);  // theta = m * 2^-sh
+    const u64 prod = m * qmax;
+    if (sh >= 64) return prod != 0 ? 1 : 0;
+    return (prod >> sh) + ((prod & ((1ull << sh) - 1)) != 0);
+}
+
+// The smallest key whose mass floor(x * 2^32) is at least F (F <= 2^32): the
+// bits of the smallest float >= F * 2^-32.
+__device__ __forceinline__ u32 minp_key(u64 F) {
+    if (F == 0) return 0;
+    if (F >= (1ull << 32)) return kOneKey;
+    float f = (float)F;                               // nearest
+    if ((double)f < (double)F) f = __uint_as_float(__float_as_uint(f) + 1u);  // round up
+    return __float_as_uint(f * 0x1p-32f);             // exact scaling (F >= 1)
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): key (seed lo, seed hi),
 // counter (offset lo, offset hi, row lo, row hi); returns word0 | word1 << 32.
 __device__ u64 philox_uniform(u64 seed, u64 row, u64 offset) {
@@ -397,6 +437,8 @@ __device__ __forceinline__ Params params_from(const Smem& s) {
     p.probs = reinterpret_cast<const float*>(uni((u64)s.p.probs));
     p.top_k = reinterpret_cast<const int32_t*>(uni((u64)s.p.top_k));
     p.top_p = reinterpret_cast<const float*>(uni((u64)s.p.top_p));
+    p.temperature = reinterpret_cast<const float*>(uni((u64)s.p.temperature));
+    p.min_p = reinterpret_cast<const float*>(uni((u64)s.p.min_p));
     p.out_tokens = reinterpret_cast<int32_t*>(uni((u64)s.p.out_tokens));
     p.stats = reinterpret_cast<u32*>(uni((u64)s.p.stats));
     p.ws = reinterpret_cast<unsigned char*>(uni((u64)s.p.ws));
@@ -413,6 +455,7 @@ __device__ __forceinline__ Params params_from(const Smem& s) {
     p.flags = uni(s.p.flags);
     p.split = uni(s.p.split);
     p.slots = uni(s.p.slots);
+    p.xparts = uni(s.p.xparts);
     return p;
 }
 
@@ -900,6 +943,92 @@ __device__ __forceinline__ const float* row_ptr(const float* base, size_t r, u32
                                           r * V * kEntryBytes<VEC>);
 }
 
+// ---------------------------------------------------------------------------
+// Logit rows
+// ---------------------------------------------------------------------------
+// A logit row is sampled as the row of fp32 weights w = softmax(x / tau)
+// scaled so that its largest entry is 1 (SonicSampler appendix C.1: the
+// temperature of eq. (8), then the softmax): w = wtop for x == M (the row
+// maximum; wtop = 1, or +inf when M = +inf), else E(fl(fl(x - M) * r)) with
+// r = fp32(fp64(1 / tau)) (+inf for tau NaN or <= 0, 0 for tau = +inf).  NaN
+// logits weigh 0, like -inf; a row whose entries are all -inf or NaN has M set
+// to NaN, so every weight is 0.  Every step after that is the probability
+// method applied to w (masses floor(w * 2^32); the scale cancels).
+//
+// E(s) is exp(s) for s <= 0 by a fixed sequence of IEEE-754 fp32 operations:
+// Cody and Waite's reduction n = rint(s log2 e), f = s - n ln2 (ln 2 in a high
+// and a low part, each step one fused multiply-add), the degree-7 Taylor
+// polynomial of exp(f) in Horner form (coefficients the fp32 values nearest
+// 1/j!), and the scaling by 2^n.  Results below 2^-125, NaN and s < -104 give
+// 0 (nothing subnormal).  Each operation is correctly rounded, so the weights
+// are bit-reproducible.
+struct RowXf {
+    float M;     // row maximum (NaN: every entry masked)
+    float r;     // 1 / temperature
+    float wtop;  // weight of the entries equal to M
+};
+
+__device__ __forceinline__ float exp_weight(float s) {
+    const float sc = fmaxf(s, -104.0f);  // NaN -> -104; the result is discarded below
+    const float n = rintf(sc * 0x1.715476p+0f);
+    float f = __builtin_fmaf(n, -0x1.62e43p-1f, sc);
+    f = __builtin_fmaf(n, 0x1.05c61p-29f, f);
+    float q = 0x1.a01a02p-13f;
+    q = __builtin_fmaf(q, f, 0x1.6c16c2p-10f);
+    q = __builtin_fmaf(q, f, 0x1.111112p-7f);
+    q = __builtin_fmaf(q, f, 0x1.555556p-5f);
+    q = __builtin_fmaf(q, f, 0x1.555556p-3f);
+    q = __builtin_fmaf(q, f, 0.5f);
+    q = __builtin_fmaf(q, f, 1.0f);
+    q = __builtin_fmaf(q, f, 1.0f);
+    const float w = __builtin_ldexpf(q, (int)n);
+    return (s >= -104.0f && n >= -125.0f) ? w : 0.0f;
+}
+
+__device__ __forceinline__ float logit_weight(const RowXf& t, float x) {
+    if (x == t.M) return t.wtop;
+    return exp_weight((x - t.M) * t.r);
+}
+
+// The weights of a loaded vector of a logit row (identity for probability
+// rows).  Applied where a vector is consumed, never where its load is issued,
+// so that loads stay in flight.
+template <int VEC, bool LG>
+__device__ __forceinline__ typename VecT<VEC>::T xform(const RowXf& t,
+                                                       const typename VecT<VEC>::T& x) {
+    if constexpr (!LG) {
+        return x;
+    } else {
+        static_assert(VEC == 4 || VEC == 1, "logit rows are fp32");
+        if constexpr (VEC == 4) {
+            return f4{logit_weight(t, x[0]), logit_weight(t, x[1]), logit_weight(t, x[2]),
+                      logit_weight(t, x[3])};
+        } else {
+            return logit_weight(t, x);
+        }
+    }
+}
+
+// Row maximum and temperature of logit row r (wave-uniform).
+template <bool LG>
+__device__ __forceinline__ RowXf row_xf(const Params& p, u32 r) {
+    RowXf t{0.0f, 0.0f, 1.0f};
+    if constexpr (LG) {
+        const XMax* xm = ws_xmax(p, r);
+        u32 e = 0;
+        for (u32 i = 0; i < p.xparts; ++i) e = max(e, uni(ld_g(&xm->part[i])));
+        const u32 bits = (e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e;  // order-preserving decode
+        const float tau = p.temperature ? ld_g(&p.temperature[r]) : 1.0f;
+        t.r = !(tau > 0.0f) ? __uint_as_float(kInfKey) : (float)(1.0 / (double)tau);
+        t.M = bits == 0xFF800000u ? __uint_as_float(0x7FC00000u) : __uint_as_float(bits);
+        t.wtop = bits == kInfKey ? __uint_as_float(kInfKey) : 1.0f;
+        t.M = __uint_as_float(uni(__float_as_uint(t.M)));
+        t.r = __uint_as_float(uni(__float_as_uint(t.r)));
+        t.wtop = __uint_as_float(uni(__float_as_uint(t.wtop)));
+    }
+    return t;
+}
+
 // Row data is read once: non-temporal loads keep it from displacing the
 // exchanged words and the kernel's own code in L2.
 template <typename T>
@@ -1066,7 +1195,8 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
 // Finish a row from its support sorted descending: positions [0, kk) of the
 // register arrays of sort_desc.
 template <int E>
-__device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u32 kk, u64 P, u64 u) {
+__device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u32 kk, u64 P, u64 u,
+                                                  float theta) {
     const u32 base = threadIdx.x * E;
     u64 q[E];
     u64 ninf_l = 0, msum = 0;
@@ -1114,7 +1244,20 @@ __device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u3
         o.token = (u32)block_min(s, mi);
         return o;
     }
-    const u64 T = topp_threshold(P, Mk);
+    u64 T = topp_threshold(P, Mk);
+    if (theta > 0.0f) {
+        // Min-p: the positions with q >= the floor are a prefix; the kept set
+        // ends where the inclusive mass reaches min(T, their mass).
+        u64 qm = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) qm = q[j] > qm ? q[j] : qm;
+        const u64 F = minp_floor(theta, block_max(s, qm));
+        u64 mf = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) mf += q[j] >= F ? q[j] : 0ull;
+        const u64 Mf = block_sum(s, mf);
+        T = Mf < T ? Mf : T;
+    }
     const u64 ex = block_excl_scan(s, msum);
     u64 acc = ex;
 #pragma unroll
@@ -1338,7 +1481,7 @@ __device__ __noinline__ u32 wave_nth_index(Smem& s, u32* tab, u32 st, u32 n, u32
 // in another order, when a bin it needs holds more than 64 entries or the
 // support holds +inf entries or has no mass; the caller then sorts.
 __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
-                                         Outcome& o, u32 wfill) {
+                                         Outcome& o, u32 wfill, float theta) {
     constexpr int J = kSlabCap / kBlock;
     static_assert(J * 64 == kSlabCap / kWaves, "a wave region is J entries per lane");
     const u32 tbin = tkey >> kFineShift;
@@ -1355,6 +1498,14 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
         c[j] = in ? sbuf(s)[i] : 0ull;
         const u32 d = (comp_key(c[j]) >> kFineShift) - tbin;
         dig[j] = in ? (int)(d < (u32)kTabBins ? d : (u32)kTabBins - 1) : -1;
+    }
+    // Min-p needs the row's largest key (the buffer holds the row's best k).
+    u32 kmax = 0;
+    if (theta > 0.0f) {
+        u64 km = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) km = comp_key(c[j]) > km ? comp_key(c[j]) : km;
+        kmax = (u32)block_max(s, km);
     }
     __syncthreads();  // the scatter overwrites the buffer
     const u64 total = bin_scatter<J>(s, c, dig, sbuf(s), regions);
@@ -1405,7 +1556,25 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
         ok = ok && Mk > 0;
         u64 cT = 0, Mp = 0, cd = 0;
         if (ok) {
-            const u64 T = topp_threshold(P, Mk);
+            u64 T = topp_threshold(P, Mk);
+            // Min-p: entries with key >= kf are a prefix of the support when
+            // kf lies above the k-th entry's key; the kept set then ends where
+            // the inclusive mass reaches min(T, their mass): the bins above
+            // kf's bin and the entries of kf's bin at or above kf.
+            const u64 F = minp_floor(theta, key_mass(kmax));
+            const u32 kf = minp_key(F);
+            if (F > 1 && kf > comp_key(ck)) {
+                const u32 fd = (kf >> kFineShift) - tbin;
+                const int bf = (int)(fd < (u32)kTabBins ? fd : (u32)kTabBins - 1);
+                const u32 st0 = bv.cnt_above(bf), en = bv.end_of(bf);
+                u64 part = 0;
+                for (u32 i = st0 + lane; i < en; i += 64) {
+                    const u32 kk = comp_key(sbuf(s)[i]);
+                    part += kk >= kf ? key_mass(kk) : 0ull;
+                }
+                const u64 Mf = bv.mass_above(bf) + wave_sum(part);
+                T = Mf < T ? Mf : T;
+            }
             const int bT = bv.find_mass(T);
             const u64 base = bv.mass_above(bT);
             if (bv.load(bT)) {
@@ -1649,9 +1818,10 @@ __device__ __forceinline__ Sel fine_select(Smem& s, u32 n, int f, u64 W) {
 // Calls f(x, iv, valid) for every vector x (index iv) of a row, one per thread
 // per round; every thread makes the same number of calls (valid is false past
 // the end of the row), so f may use wave collectives.  kG rounds of loads are
-// kept in flight.
-template <int VEC, u32 kG, typename F>
-__device__ __forceinline__ void for_each_vec(const float* __restrict__ row, u32 nvec, F f) {
+// kept in flight.  Logit rows (LG) hand f the vector's weights.
+template <int VEC, u32 kG, bool LG = false, typename F>
+__device__ __forceinline__ void for_each_vec(const float* __restrict__ row, u32 nvec, F f,
+                                             const RowXf& xf = RowXf{}) {
     typedef typename VecT<VEC>::T VT;
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
     const u32 nr = (nvec + kBlock - 1) / kBlock;
@@ -1666,7 +1836,7 @@ __device__ __forceinline__ void for_each_vec(const float* __restrict__ row, u32 
 #pragma unroll
         for (u32 d = 0; d < kG; ++d) {
             const u32 iv = (r0 + d) * kBlock + threadIdx.x;
-            f(pf[d], iv, iv < nvec);
+            f(xform<VEC, LG>(xf, pf[d]), iv, iv < nvec);
             pf[d] = ld_stream(&rv[min((r0 + d + kG) * kBlock + threadIdx.x, last)]);
             // Keep the refill here: hoisted above the other steps it would
             // turn the pipeline into load-all-then-wait.
@@ -1675,15 +1845,17 @@ __device__ __forceinline__ void for_each_vec(const float* __restrict__ row, u32 
     }
 }
 
-// Calls f(key, idx, valid) for every element of a row (sanitised key).
-template <int VEC, u32 kG = kPassDepth, typename F>
-__device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
+// Calls f(key, idx, valid) for every element of a row (sanitised key; the
+// weight's key for logit rows).
+template <int VEC, bool LG = false, u32 kG = kPassDepth, typename F>
+__device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f,
+                               const RowXf& xf = RowXf{}) {
     typedef typename VecT<VEC>::T VT;
-    for_each_vec<VEC, kG>(row, nvec, [&](const VT& x, u32 iv, bool valid) {
+    for_each_vec<VEC, kG, LG>(row, nvec, [&](const VT& x, u32 iv, bool valid) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             f(sanitize(__float_as_uint(VecT<VEC>::get(x, e))), iv * VEC + e, valid);
-    });
+    }, xf);
 }
 
 // ---------------------------------------------------------------------------
@@ -1692,9 +1864,9 @@ __device__ void for_each_entry(const float* __restrict__ row, u32 nvec, F f) {
 // Weighted radix select over the entries of the row with composite >= lo:
 // histogram one digit per pass; once the selected bucket holds at most
 // gather_cap (<= kSelCap) entries, gather it into LDS and finish there.
-template <int VEC>
+template <int VEC, bool LG>
 __device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass, u64 lo,
-                          u32 gather_cap) {
+                          u32 gather_cap, const RowXf& xf) {
     u64 prefix = 0, above = 0;
     for (int l = 0; l < 6; ++l) {
         const int sh = level_shift(l), wd = level_width(l);
@@ -1705,11 +1877,11 @@ __device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass,
             shmass(s)[b] = 0;
         }
         __syncthreads();
-        for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
+        for_each_entry<VEC, LG>(row, nvec, [&](u32 key, u32 idx, bool valid) {
             const u64 c = composite(key, idx);
             hist_add(shcnt(s), shmass(s), mass, valid && c >= lo && (c & hm) == prefix,
                      (u32)(c >> sh) & dmask, mass ? key_mass(key) : 0ull);
-        });
+        }, xf);
         if (threadIdx.x == 0) ++s.npass;
         __syncthreads();
         auto cf = [&](int b) { return (u64)shcnt(s)[b]; };
@@ -1721,11 +1893,11 @@ __device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass,
         if (g.cnt <= gather_cap || l == 5) {
             if (threadIdx.x == 0) s.ctr[3] = 0;
             __syncthreads();
-            for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
+            for_each_entry<VEC, LG>(row, nvec, [&](u32 key, u32 idx, bool valid) {
                 const u64 c = composite(key, idx);
                 wave_append(sbuf(s), valid && c >= lo && (c & m2) == prefix, c, &s.ctr[3], 0,
                             kSelCap);
-            });
+            }, xf);
             if (threadIdx.x == 0) ++s.npass;
             __syncthreads();
             const u32 n = uni(s.ctr[3]);
@@ -1737,21 +1909,23 @@ __device__ Sel select_row(Smem& s, const float* row, u32 nvec, u64 W, bool mass,
     return Sel{0, 0};  // not reached
 }
 
-template <int VEC>
-__device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec, u32 V, u32 k_eff, u64 P,
-                               u64 u, u32 gather_cap) {
+template <int VEC, bool LG>
+__device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec, u32 V, u32 k_eff,
+                                            u64 P, u64 u, u32 gather_cap, const RowXf& xf,
+                                            float theta) {
     Outcome o{};
     u64 lo = 0;
-    if (k_eff < V) lo = select_row<VEC>(s, row, nvec, k_eff, false, 0, gather_cap).c;
+    if (k_eff < V) lo = select_row<VEC, LG>(s, row, nvec, k_eff, false, 0, gather_cap, xf).c;
     o.c_k = lo;
-    u64 mk = 0, ninf = 0, minidx = ~0ull;
-    for_each_entry<VEC>(row, nvec, [&](u32 key, u32 idx, bool valid) {
+    u64 mk = 0, ninf = 0, minidx = ~0ull, kmax = 0;
+    for_each_entry<VEC, LG>(row, nvec, [&](u32 key, u32 idx, bool valid) {
         if (valid && composite(key, idx) >= lo) {
             mk += key_mass(key);
             ninf += key == kInfKey;
             minidx = idx < minidx ? idx : minidx;
+            kmax = key > kmax ? key : kmax;
         }
-    });
+    }, xf);
     if (threadIdx.x == 0) ++s.npass;
     const u64 M_k = block_sum(s, mk);
     const u64 m = block_sum(s, ninf);
@@ -1760,8 +1934,8 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
         const u64 t = __umul64hi(u, m);
         o.kind = kInfRow;
         o.m = (u32)m;
-        o.token = comp_index(select_row<VEC>(s, row, nvec, t + 1, false, 0, gather_cap).c);
-        o.c_keep = select_row<VEC>(s, row, nvec, m, false, 0, gather_cap).c;
+        o.token = comp_index(select_row<VEC, LG>(s, row, nvec, t + 1, false, 0, gather_cap, xf).c);
+        o.c_keep = select_row<VEC, LG>(s, row, nvec, m, false, 0, gather_cap, xf).c;
         return o;
     }
     if (M_k == 0) {
@@ -1769,11 +1943,25 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
         o.token = (u32)minidx;
         return o;
     }
-    const u64 T = topp_threshold(P, M_k);
-    const Sel bt = select_row<VEC>(s, row, nvec, T, true, lo, gather_cap);
+    u64 T = topp_threshold(P, M_k);
+    // Min-p: the support's entries with key >= kf (mass >= the floor) are a
+    // prefix; the kept set is the shorter of it and the top-p prefix, i.e.
+    // the first position whose inclusive mass reaches min(T, their mass).
+    const u64 F = minp_floor(theta, key_mass((u32)block_max(s, kmax)));
+    const u32 kf = minp_key(F);
+    if (F > 1 && kf > comp_key(lo)) {
+        u64 mf = 0;
+        for_each_entry<VEC, LG>(row, nvec, [&](u32 key, u32 idx, bool valid) {
+            if (valid && key >= kf) mf += key_mass(key);
+        }, xf);
+        if (threadIdx.x == 0) ++s.npass;
+        const u64 Mf = block_sum(s, mf);
+        T = Mf < T ? Mf : T;
+    }
+    const Sel bt = select_row<VEC, LG>(s, row, nvec, T, true, lo, gather_cap, xf);
     const u64 M_p = bt.above + key_mass(comp_key(bt.c));
     const u64 t = __umul64hi(u, M_p);
-    const Sel dr = select_row<VEC>(s, row, nvec, t + 1, true, lo, gather_cap);
+    const Sel dr = select_row<VEC, LG>(s, row, nvec, t + 1, true, lo, gather_cap, xf);
     o.kind = kNormal;
     o.c_keep = bt.c;
     o.M_p = M_p;
@@ -1839,10 +2027,11 @@ __device__ __forceinline__ u64 stat_phase(const Params& p, u32 r, int word, u64 
 // ---------------------------------------------------------------------------
 // Greedy rows (k = 1)
 // ---------------------------------------------------------------------------
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, u32 S, bool yield) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
+    const RowXf xf = row_xf<LG>(p, r);
     stat_start(p, r, S);
     const u64 tp = p.stats ? wall_clock64() : 0;
     // This workgroup's part: the row, or one of its S parts when split.
@@ -1871,25 +2060,25 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     // keeps only two loads in flight: its share of the bandwidth goes to those
     // rows, which then finish earlier, and it still ends before them.
     if (yield)
-        for_each_vec<VEC, kGreedyYieldDepth>(part, nv, vmax);
+        for_each_vec<VEC, kGreedyYieldDepth, LG>(part, nv, vmax, xf);
     else
-        for_each_vec<VEC, kStreamDepth>(part, nv, vmax);
+        for_each_vec<VEC, kStreamDepth, LG>(part, nv, vmax, xf);
     const int K = (int)((u32)block_max(s, (u64)((u32)best ^ 0x80000000u)) ^ 0x80000000u);
     u64 cbest;
     if (K > (int)kInfKey) {
         // NaN bits are the largest: take the exact maximum of the composites.
         u64 b = 0;
-        for_each_entry<VEC>(part, nv, [&](u32 key, u32 idx, bool valid) {
+        for_each_entry<VEC, LG>(part, nv, [&](u32 key, u32 idx, bool valid) {
             const u64 c = valid ? composite(key, v0 * VEC + idx) : 0ull;
             b = c > b ? c : b;
-        });
+        }, xf);
         cbest = block_max(s, b);
     } else if (K <= 0) {
         cbest = composite(0u, v0 * VEC);  // every entry counts as zero: the smallest index
     } else {
         u64 idx = ~0ull;
         if (best == K) {
-            const VT x = ld_g(&reinterpret_cast<const VT*>(part)[bvec]);
+            const VT x = xform<VEC, LG>(xf, ld_g(&reinterpret_cast<const VT*>(part)[bvec]));
 #pragma unroll
             for (int e = VEC - 1; e >= 0; --e)
                 if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K)
@@ -1920,15 +2109,15 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // ---------------------------------------------------------------------------
 // Top-k rows (2 <= k <= 1024)
 // ---------------------------------------------------------------------------
-template <int VEC>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path = kPathSlab, u64 c_k = ~0ull);
 
 // The index of the m-th (m >= 1) entry of the row, in index order, whose key
 // is zero (NaN, negative, -0.0 or +0.0), read in steps of one vector per
 // thread until a step holds it; ~0u when the row has fewer than m.
-template <int VEC>
-__device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, u32 m) {
+template <int VEC, bool LG>
+__device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, u32 m,
+                              const RowXf& xf) {
     typedef typename VecT<VEC>::T VT;
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
     u32 before = 0;  // zeros in the steps already read (workgroup-uniform)
@@ -1936,7 +2125,7 @@ __device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, 
         const u32 iv = v0 + threadIdx.x;
         u32 zmask = 0;
         if (iv < nvec) {
-            const VT x = ld_g(&rv[iv]);
+            const VT x = xform<VEC, LG>(xf, ld_g(&rv[iv]));
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 zmask |= sanitize(__float_as_uint(VecT<VEC>::get(x, e))) == 0u ? 1u << e : 0u;
@@ -1973,10 +2162,11 @@ __device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, 
 // also reaches zero keys takes the lowest-indexed zeros after them: they carry
 // no mass, so they are never kept or drawn, and only a support without mass
 // looks at them (its token is the smallest index in the support).
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u64 P, u64 u) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
+    const RowXf xf = row_xf<LG>(p, r);
     const float* row = row_ptr<VEC>(p.probs, r, p.V);
     // Entries are appended kSub per thread at a time (an 8-entry vector in
     // two halves), so the buffer keeps room for one more append.
@@ -1988,7 +2178,7 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     u32 cuts = 0;
     if (threadIdx.x == 0) s.ctr[3] = 0;
     __syncthreads();
-    for_each_vec<VEC, kPassDepth>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
+    for_each_vec<VEC, kPassDepth, LG>(row, p.nvec, [&](const VT& x, u32 iv, bool valid) {
         // After a cut within a step, entries with the k-th key still enter
         // for the rest of the step (another thread's later half may hold a
         // lower index); only at the step's end does the threshold rise above
@@ -2025,7 +2215,7 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
             closed = theta == kInfKey;
             theta = closed ? kInfKey : theta + 1;
         }
-    });
+    }, xf);
     __syncthreads();
     const u32 n = uni(s.ctr[3]);
     __syncthreads();
@@ -2043,7 +2233,7 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     // top bin, where it looks for them.
     const u32 tkey = n ? min(comp_key(mn), kOneKey) & ~0xFFFFu : 0u;
     if (n >= k) {
-        slab_finish<VEC>(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
+        slab_finish(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
         return;
     }
     if (n == 0 && theta0 == 1u) {
@@ -2059,16 +2249,16 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     }
     // n < k: the support ends with the k - n lowest-indexed zeros; its
     // boundary is the last of them.
-    const u32 zk = mth_zero_index<VEC>(s, row, p.nvec, k - n);
+    const u32 zk = mth_zero_index<VEC, LG>(s, row, p.nvec, k - n, xf);
     const u64 c_k = composite(0u, zk);
     if (n > 0 && mass > 0) {
         // The zeros carry no mass: they change nothing else.
-        slab_finish<VEC>(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
+        slab_finish(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
         return;
     }
     // No mass in the support: its smallest index.
     midx = block_min(s, midx);
-    const u32 z = mth_zero_index<VEC>(s, row, p.nvec, 1);
+    const u32 z = mth_zero_index<VEC, LG>(s, row, p.nvec, 1, xf);
     Outcome o{};
     o.kind = kZeroRow;
     o.token = (u32)(midx < (u64)z ? midx : (u64)z);
@@ -2100,10 +2290,11 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
 // is among them), which hold the row's best k when there are at least k of
 // them.  Rows that fail these tests (or whose sample holds fewer than j
 // entries with a mass) are decided by the compacting restream.
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u32 h, u32 S) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
+    const RowXf xf = row_xf<LG>(p, r);
     const u32 hv = (p.nvec + S - 1) / S;
     const u32 v0 = h * hv;
     const u32 nvec = min(v0 + hv, p.nvec) - v0;  // vectors of this part
@@ -2134,9 +2325,10 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 #pragma unroll
     for (u32 d = 0; d < kSampleDepth; ++d) {
         const bool valid = d * kBlock + threadIdx.x < nvec;
+        const VT xs = xform<VEC, LG>(xf, pf[d]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(pf[d], e)));
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(xs, e)));
             if (valid && key >= kMinMassKey) {
                 atomicAdd(&hist[fine_bin(key)], 1u);
                 ++nmass;
@@ -2163,8 +2355,8 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     if (no_tkey && S == 1) {
         // Fewer than j sampled entries have a mass (a row of mostly zeros, or
         // a short row with fewer than k): one exact pass over every positive key.
-        slab_restream<VEC>(s, r, k, 1u, fixed_p(top_p),
-                           philox_uniform(p.seed, p.row_base + r, p.offset));
+        slab_restream<VEC, LG>(s, r, k, 1u, fixed_p(top_p),
+                               philox_uniform(p.seed, p.row_base + r, p.offset));
         return;
     }
     const u32 span = kInfKey - tkey;
@@ -2178,8 +2370,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     // are below tkey has none; a wave with no such vector skips the rest.
     // (MASKED: lanes past the end of the part hold a copy of its last vector
     // and must append nothing.)
-    auto append = [&](auto masked, const VT& x, u32 iv) {
+    auto append = [&](auto masked, const VT& xraw, u32 iv) {
         constexpr bool kMasked = decltype(masked)::value;
+        const VT x = xform<VEC, LG>(xf, xraw);
         const bool valid = !kMasked || iv < nvec;
         static_assert(kFineShift == 16, "tkey is a multiple of 2^16");
         if (__builtin_amdgcn_ballot_w64(valid & any_at_least<VEC>(x, (int)tkey)) == 0) return;
@@ -2320,11 +2513,11 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         tbase = tmax;
     }
     if (!over && fill >= k) {
-        slab_finish<VEC>(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
+        slab_finish(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
     } else {
         // A whole row that counted at least k entries at or above its
         // threshold has its best k there; anything else starts from 1.
-        slab_restream<VEC>(s, r, k, (S == 1 && !no_tkey && fill >= k) ? tkey : 1u, P, u);
+        slab_restream<VEC, LG>(s, r, k, (S == 1 && !no_tkey && fill >= k) ? tkey : 1u, P, u);
     }
 }
 
@@ -2333,17 +2526,17 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // others (and every row under TES_FLAG_TINY_BUFFER) cut the buffer to exactly
 // the best k when it holds more than a sort takes, sort it descending (padded
 // with zeros, which sort last) and finish on the first k positions.
-template <int VEC>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path, u64 c_k) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
+    const float theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
     // wfill != ~0u: the entries are still in the stream's wave regions (this
     // wave's count), and the binned finish packs them.
     if (!(p.flags & TES_FLAG_TINY_BUFFER) && tkey > 0) {
         Outcome ob;
-        if (binned_topk(s, n, k, tkey, P, u, ob, wfill)) {
+        if (binned_topk(s, n, k, tkey, P, u, ob, wfill, theta)) {
             stat_phase(p, r, 9, tp);
             if (c_k != ~0ull) ob.c_k = c_k;
             finish_row(s, p, r, ob, path, gathered);
@@ -2364,17 +2557,17 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         u64 v[1];
         sort_desc<1>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<1>(s, v, k, P, u);
+        o = resolve_sorted<1>(s, v, k, P, u, theta);
     } else if (pad == 2 * kBlock) {
         u64 v[2];
         sort_desc<2>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<2>(s, v, k, P, u);
+        o = resolve_sorted<2>(s, v, k, P, u, theta);
     } else {
         u64 v[4];
         sort_desc<4>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<4>(s, v, k, P, u);
+        o = resolve_sorted<4>(s, v, k, P, u, theta);
     }
     stat_phase(p, r, 9, tp);
     if (c_k != ~0ull) o.c_k = c_k;
@@ -2525,14 +2718,15 @@ __device__ __forceinline__ void fine_plan_wave(Smem& s, int nlist, u64 T, u64 u)
     }
 }
 
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
                                          u64 above_f, int fbT, int nlist, bool failed);
 
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, u32 nseg) {
     const Params p = params_from(s);
     typedef typename VecT<VEC>::T VT;
+    const RowXf xf = row_xf<LG>(p, r);
     const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V));
     const u32 sv = (p.nvec + nseg - 1) / nseg;
     const u32 v0 = seg * sv, v1 = min(v0 + sv, p.nvec);
@@ -2569,6 +2763,8 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
 #pragma unroll
     for (int d = 0; d < kSlots<VEC>; ++d) {
         const u32 i = v0 + d * kBlock + threadIdx.x;
+        // Logit rows keep their weights in the registers from here on.
+        x[d] = xform<VEC, LG>(xf, x[d]);
         if (i < v1) {
             int mx = kIntMin;
 #pragma unroll
@@ -2771,12 +2967,12 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
     const bool last = arrive_last(s, &rs->ticket, nseg);
     stat_phase(p, r, 12, tp);
-    if (last) full_finish<VEC>(s, r, nseg, kind, nit, T, above_f, fbT, nlist, failed);
+    if (last) full_finish<VEC, LG>(s, r, nseg, kind, nit, T, above_f, fbT, nlist, failed);
 }
 
 // Last segment of a top-p-only row: load every segment's gathered entries
 // and finish.
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, u64 nit, u64 T,
                                          u64 above_f, int fbT, int nlist, bool failed) {
     const Params p = params_from(s);
@@ -2880,7 +3076,10 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
     }
     if (!fail && fb) stat_why(p, r, 32u);
     if (fb) {
-        o = resolve_row<VEC>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, p.V, P, u, kSelCap);
+        // (Rows with a min-p floor never take this path: their class is the
+        // whole-row passes.)
+        o = resolve_row<VEC, LG>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, p.V, P, u, kSelCap,
+                                 row_xf<LG>(p, r), 0.0f);
         path = kPathFullFallback;
     } else if (kind == kNormal) {
         // decided above
@@ -2910,7 +3109,7 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
 // ---------------------------------------------------------------------------
 // Whole-row items
 // ---------------------------------------------------------------------------
-template <int VEC>
+template <int VEC, bool LG>
 __device__ __attribute__((always_inline)) void do_whole(Smem& s, u32 r, u32 k_eff) {
     const Params p = params_from(s);
     stat_start(p, r, 1);
@@ -2918,8 +3117,9 @@ __device__ __attribute__((always_inline)) void do_whole(Smem& s, u32 r, u32 k_ef
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
     if (threadIdx.x == 0) s.npass = 0;
-    const Outcome o = resolve_row<VEC>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, k_eff, P, u,
-                                       tiny ? 64u : kSelCap);
+    const Outcome o = resolve_row<VEC, LG>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, k_eff, P,
+                                           u, tiny ? 64u : kSelCap, row_xf<LG>(p, r),
+                                           p.min_p ? ld_g(&p.min_p[r]) : 0.0f);
     stat_add(p, r, 3, uni(s.npass));
     finish_row(s, p, r, o, kPathWhole, 0);
 }
@@ -2932,11 +3132,14 @@ __device__ __forceinline__ u32 row_k_eff(const Params& p, u32 r) {
     return (k <= 0 || (u32)k >= p.V) ? p.V : (u32)k;
 }
 
-__device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full) {
+// Top-p-only rows with a min-p floor (theta > 0) are decided by the whole-row
+// passes: the exchanged histograms of the segments locate the top-p boundary
+// by mass only.
+__device__ __forceinline__ u32 row_class(const Params& p, u32 r, u32 k_eff, u32 s_full) {
     if (p.flags & TES_FLAG_FORCE_ROW_SELECT) return kClsWhole;
     if (k_eff == 1) return kClsGreedy;
     if (k_eff <= kSlabMaxK) return kClsSlab;
-    if (k_eff == p.V && s_full <= p.s_ws) return kClsFull;
+    if (k_eff == p.V && s_full <= p.s_ws && !(p.min_p && ld_g(&p.min_p[r]) > 0.0f)) return kClsFull;
     return kClsWhole;
 }
 
@@ -2947,7 +3150,7 @@ __device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full)
 // rows follow, one item each: whole-row rows, top-k rows, then greedy rows.
 // Blocks beyond the last item return at once.  No item loop: values live
 // across one would raise the register pressure of every path.
-template <int VEC>
+template <int VEC, bool LG>
 __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params p) {
     __shared__ Smem s;
     if (threadIdx.x == 0) {
@@ -2963,7 +3166,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     for (int j = 0; j < 2; ++j) {
         const u32 r = r0 + j;
         const u32 ke = r < p.rows ? row_k_eff(p, r) : 0u;
-        cls[j] = r < p.rows ? row_class(p, ke, s_full) : 4u;
+        cls[j] = r < p.rows ? row_class(p, r, ke, s_full) : 4u;
         if (cls[j] == kClsSlab) s.slab_k[r] = (u16)ke;
         if (cls[j] < 4) local += 1ull << (16 * cls[j]);
     }
@@ -3016,13 +3219,13 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     __syncthreads();
     if (item < full_end) {
         const u32 j = item / s_full;
-        do_full<VEC>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
+        do_full<VEC, LG>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
     } else if (item < whole_end) {
         const u32 r = uni((u32)s.rows[nf + (item - full_end)]);
-        do_whole<VEC>(s, r, row_k_eff(p, r));
+        do_whole<VEC, LG>(s, r, row_k_eff(p, r));
     } else if (item < first_end) {
         const u32 r = uni((u32)s.rows[nf + n_whole + (item - whole_end)]);
-        do_slab<VEC>(s, r, s.slab_k[r], 0, S);
+        do_slab<VEC, LG>(s, r, s.slab_k[r], 0, S);
     } else if (item < greedy_end) {
         const u32 i = (item - first_end) / Sg;
         const u32 r = uni((u32)s.rows[nf + n_whole + n_slab + i]);
@@ -3032,29 +3235,31 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
         // they make up at most three quarters of the rows (measured: 75%
         // greedy B=256 batch 41.3 -> 36.9 us, hetero batch 40.7 -> 39.4 us;
         // an all-greedy batch keeps 29 us).
-        do_greedy<VEC>(s, r, item - first_end - i * Sg, Sg,
+        do_greedy<VEC, LG>(s, r, item - first_end - i * Sg, Sg,
                        n_greedy <= 3 * (n_slab + nf + n_whole) && 2 * base_items >= p.slots);
     } else if (item < greedy_end + n_slab * (S - 1)) {
         const u32 i = (item - greedy_end) % n_slab, h = 1 + (item - greedy_end) / n_slab;
         const u32 r = uni((u32)s.rows[nf + n_whole + i]);
-        do_slab<VEC>(s, r, s.slab_k[r], h, S);
+        do_slab<VEC, LG>(s, r, s.slab_k[r], h, S);
     }
 }
 
-// renorm_out[r][i] = q_i / M_p for kept entries (1/m for kept +inf), else 0.
-template <int VEC>
-__global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict__ probs, u32 V,
-                                                         u32 nvec, const Decision* __restrict__ dec,
+// renorm_out[r][i] = q_i / M_p for kept entries (1/m for kept +inf), else 0
+// (q from the weights for logit rows).
+template <int VEC, bool LG>
+__global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decision* __restrict__ dec,
                                                          float* __restrict__ out) {
     typedef typename VecT<VEC>::T VT;
     const u32 r = blockIdx.y;
+    const u32 V = p.V, nvec = p.nvec;
     const Decision d = dec[r];
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(probs, r, V));
+    const RowXf xf = row_xf<LG>(p, r);
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, V));
     float* __restrict__ orow = out + (size_t)r * V;
     const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
     const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
     for (u32 iv = blockIdx.x * 256 + threadIdx.x; iv < nvec; iv += gridDim.x * 256) {
-        const VT x = rv[iv];
+        const VT x = xform<VEC, LG>(xf, rv[iv]);
         float o[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -3075,6 +3280,46 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(const float* __restrict
 }
 
 
+
+// Logit rows: the maximum of each of p.xparts parts of every row (NaN counts
+// as -inf), as an order-preserving u32 encoding (sign bit set for
+// non-negative values, all bits inverted for negative ones), so that the
+// sampling kernel takes the row maximum as the largest of the parts.
+template <int VEC>
+__global__ __launch_bounds__(256) void tes_rowmax_kernel(Params p) {
+    typedef typename VecT<VEC>::T VT;
+    static_assert(VEC == 4 || VEC == 1, "logit rows are fp32");
+    const u32 r = blockIdx.y, part = blockIdx.x;
+    const u32 pv = (p.nvec + p.xparts - 1) / p.xparts;
+    const u32 v0 = part * pv, v1 = min(v0 + pv, p.nvec);
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V));
+    auto enc = [](float x) {
+        const u32 b = x != x ? 0xFF800000u : __float_as_uint(x);
+        return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    };
+    u32 e = 0;
+    constexpr u32 kU = 4;
+    for (u32 i0 = v0; i0 < v1; i0 += kU * 256) {
+        VT x[kU];
+#pragma unroll
+        for (u32 j = 0; j < kU; ++j) {
+            const u32 iv = i0 + j * 256 + threadIdx.x;
+            x[j] = ld_stream(&rv[iv < v1 ? iv : v1 - 1]);
+        }
+#pragma unroll
+        for (u32 j = 0; j < kU; ++j)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) e = max(e, enc(VecT<VEC>::get(x[j], c)));
+    }
+    __shared__ u32 wm[4];
+    u32 m = e;
+#pragma unroll
+    for (u32 o = 32; o >= 1; o >>= 1) m = max(m, lane_xor(m, o));
+    if (lane_id() == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *gp(&ws_xmax(p, r)->part[part]) = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+}
 
 // Slab export: one workgroup per row writes the row's support in its sorted
 // order (descending probability, ascending index, the order in which the
@@ -3299,10 +3544,10 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     rb = (rb + 255) & ~(size_t)255;
     s->rowbytes = (u32)rb;
     s->chunk = (u32)max_batch < kChunk ? (u32)max_batch : kChunk;
-    const size_t per_row = sizeof(RowState) + sizeof(Decision) + rb;
+    const size_t per_row = sizeof(RowState) + sizeof(Decision) + sizeof(XMax) + rb;
     const size_t budget_rows = kWsBudget / per_row;
     if (budget_rows < s->chunk) s->chunk = budget_rows < 1 ? 1u : (u32)budget_rows;
-    s->ws_bytes = (size_t)s->chunk * (sizeof(RowState) + sizeof(Decision)) + (size_t)s->chunk * rb;
+    s->ws_bytes = (size_t)s->chunk * per_row;
     DeviceGuard g(device);
     if (!g.ok) {
         delete s;
@@ -3338,20 +3583,24 @@ struct SlabOut {
 
 namespace {
 // The kernels of one launch (one chunk of rows) for row vectors of VEC entries.
-template <int VEC>
+template <int VEC, bool LG>
 int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 rows, u32 V,
                  u32 nvec, float* ro, const SlabOut* slab, size_t c0) {
-    hipLaunchKernelGGL(tes_main_kernel<VEC>, dim3(grid), dim3(kBlock), 0, st, p);
+    if constexpr (LG) {
+        hipLaunchKernelGGL(tes_rowmax_kernel<VEC>, dim3(p.xparts, rows), dim3(256), 0, st, p);
+        if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+    }
+    hipLaunchKernelGGL((tes_main_kernel<VEC, LG>), dim3(grid), dim3(kBlock), 0, st, p);
     if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
     const Decision* dec =
         reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
     if (ro) {
         const u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
-        hipLaunchKernelGGL(tes_renorm_kernel<VEC>, dim3(gx, rows), dim3(256), 0, st, p.probs, V,
-                           nvec, dec, ro);
+        hipLaunchKernelGGL((tes_renorm_kernel<VEC, LG>), dim3(gx, rows), dim3(256), 0, st, p, dec,
+                           ro);
         if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
     }
-    if (slab) {
+    if (slab && !LG) {
         const size_t o = c0 * slab->cap;
         hipLaunchKernelGGL(tes_slab_kernel<VEC>, dim3(rows), dim3(kSlabThreads), 0, st, p.probs,
                            V, nvec, p.top_k, dec, slab->cap, slab->index + o, slab->renorm + o,
@@ -3361,17 +3610,22 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
     return TES_OK;
 }
 
-// probs holds fp32 entries, or bf16 entries when bf16 is set.
+// probs holds fp32 entries, or bf16 entries when bf16 is set, or fp32 logits
+// when logits is set (with the nullable per-row temperature; min_p, nullable,
+// applies to both kinds of rows).
 int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, const int32_t* top_k,
                 const float* top_p, uint64_t seed, uint64_t offset, int32_t* out_tokens,
-                float* renorm_out, const SlabOut* slab, void* stream) {
+                float* renorm_out, const SlabOut* slab, void* stream, bool logits = false,
+                const float* temperature = nullptr, const float* min_p = nullptr) {
     if (!s || B < 0 || V < 1) return TES_ERR_INVALID_ARGUMENT;
     if (B > s->max_batch || V > s->max_vocab) return TES_ERR_TOO_LARGE;
     if (B == 0) return TES_OK;
     if (!probs || !top_k || !top_p || !out_tokens) return TES_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)probs & 3) || ((uintptr_t)top_k & 3) || ((uintptr_t)top_p & 3) ||
-        ((uintptr_t)out_tokens & 3) || ((uintptr_t)renorm_out & 3))
+        ((uintptr_t)out_tokens & 3) || ((uintptr_t)renorm_out & 3) ||
+        ((uintptr_t)temperature & 3) || ((uintptr_t)min_p & 3))
         return TES_ERR_INVALID_ARGUMENT;
+    if (logits && (bf16 || slab)) return TES_ERR_INVALID_ARGUMENT;
     // Row vectors: eight bf16 entries (bf16 rows must allow them), four fp32
     // entries when the rows and renorm_out allow 16-byte access, else one.
     const bool aligned16 = (((uintptr_t)probs & 15) == 0) && (((uintptr_t)renorm_out & 15) == 0);
@@ -3391,6 +3645,8 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
                                                  (size_t)c0 * V * entry_bytes);
         p.top_k = top_k + c0;
         p.top_p = top_p + c0;
+        p.temperature = temperature ? temperature + c0 : nullptr;
+        p.min_p = min_p ? min_p + c0 : nullptr;
         p.out_tokens = out_tokens + c0;
         p.stats = (s->flags & TES_FLAG_STATS) ? s->d_stats : nullptr;
         p.ws = s->ws;
@@ -3412,6 +3668,15 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.split = s->rowbytes >= kSplitBytes ? (by_len < kMaxSplit ? (by_len < 1 ? 1u : by_len) : kMaxSplit)
                                              : 1u;
         p.slots = s->slots;
+        // Logit rows: parts per row of the row-maximum prologue (enough
+        // workgroups to fill the device for small batches).
+        {
+            const u32 want = ceil_div(2 * s->slots, rows);
+            const u32 by_len = ceil_div(nvec, 4 * 256);
+            u32 xp = want < kXParts ? want : kXParts;
+            xp = xp < by_len ? xp : by_len;
+            p.xparts = xp < 1 ? 1u : xp;
+        }
         if (p.stats) {
             const u32 nw = kStatWords * rows;
             hipLaunchKernelGGL(tes_clear_kernel, dim3(ceil_div(nw, 256) < 64 ? ceil_div(nw, 256) : 64),
@@ -3426,9 +3691,12 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         const u32 split_items = rows * p.split < s->slots ? rows * p.split : s->slots;
         const u32 grid = rows * per_row > split_items ? rows * per_row : split_items;
         float* ro = renorm_out ? renorm_out + (size_t)c0 * V : nullptr;
-        const int rc = vec == 8 ? launch_chunk<8>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
-                     : vec == 4 ? launch_chunk<4>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
-                                : launch_chunk<1>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0);
+        const int rc =
+            logits ? (vec == 4 ? launch_chunk<4, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
+                               : launch_chunk<1, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0))
+            : vec == 8 ? launch_chunk<8, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
+            : vec == 4 ? launch_chunk<4, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
+                       : launch_chunk<1, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0);
         if (rc != TES_OK) return rc;
     }
     return TES_OK;
@@ -3460,7 +3728,7 @@ constexpr size_t kNoAllocTopP =
 constexpr size_t kNoAllocRowBytes =
     ((kNoAllocTopP > kSplitBytes ? kNoAllocTopP : kSplitBytes) + 255) & ~(size_t)255;
 constexpr size_t kScratchBytes =
-    (size_t)kNoAllocRows * (sizeof(RowState) + sizeof(Decision) + kNoAllocRowBytes);
+    (size_t)kNoAllocRows * (sizeof(RowState) + sizeof(Decision) + sizeof(XMax) + kNoAllocRowBytes);
 static_assert(kNoAllocRows * sizeof(RowState) % 4 == 0, "row states clear as words");
 static_assert(kScratchBytes <= (40u << 20), "the scratch array stays modest");
 }  // namespace
@@ -3553,6 +3821,15 @@ extern "C" int topk_topp_sample_noalloc(const float* probs, int B, int V, const 
     view.d_stats = nullptr;
     return sample_impl(&view, probs, false, B, V, top_k, top_p, seed, offset, out_tokens,
                        renorm_out, nullptr, stream);
+}
+
+extern "C" int topk_topp_sample_logits(tes_sampler* s, const float* logits, int B, int V,
+                                       const int32_t* top_k, const float* top_p,
+                                       const float* temperature, const float* min_p,
+                                       uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                                       float* renorm_out, void* stream) {
+    return sample_impl(s, logits, false, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
+                       nullptr, stream, true, temperature, min_p);
 }
 
 extern "C" int topk_topp_sample_bf16(tes_sampler* s, const uint16_t* probs, int B, int V,
