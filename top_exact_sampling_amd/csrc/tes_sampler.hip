@@ -1194,7 +1194,7 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
 
 // Finish a row from its support sorted descending: positions [0, kk) of the
 // register arrays of sort_desc.
-template <int E>
+template <int E, bool MINP>
 __device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u32 kk, u64 P, u64 u,
                                                   float theta) {
     const u32 base = threadIdx.x * E;
@@ -1245,7 +1245,7 @@ __device__ __forceinline__ Outcome resolve_sorted(Smem& s, const u64 (&v)[E], u3
         return o;
     }
     u64 T = topp_threshold(P, Mk);
-    if (theta > 0.0f) {
+    if (MINP && theta > 0.0f) {
         // Min-p: the positions with q >= the floor are a prefix; the kept set
         // ends where the inclusive mass reaches min(T, their mass).
         u64 qm = 0;
@@ -1480,6 +1480,7 @@ __device__ __noinline__ u32 wave_nth_index(Smem& s, u32* tab, u32 st, u32 n, u32
 // sorting their bin.  Returns false, with the buffer holding the same entries
 // in another order, when a bin it needs holds more than 64 entries or the
 // support holds +inf entries or has no mass; the caller then sorts.
+template <bool MINP>
 __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          Outcome& o, u32 wfill, float theta) {
     constexpr int J = kSlabCap / kBlock;
@@ -1501,7 +1502,7 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
     }
     // Min-p needs the row's largest key (the buffer holds the row's best k).
     u32 kmax = 0;
-    if (theta > 0.0f) {
+    if (MINP && theta > 0.0f) {
         u64 km = 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) km = comp_key(c[j]) > km ? comp_key(c[j]) : km;
@@ -1561,9 +1562,9 @@ __device__ __forceinline__ bool binned_topk(Smem& s, u32 n, u32 k, u32 tkey, u64
             // kf lies above the k-th entry's key; the kept set then ends where
             // the inclusive mass reaches min(T, their mass): the bins above
             // kf's bin and the entries of kf's bin at or above kf.
-            const u64 F = minp_floor(theta, key_mass(kmax));
+            const u64 F = MINP ? minp_floor(theta, key_mass(kmax)) : 0ull;
             const u32 kf = minp_key(F);
-            if (F > 1 && kf > comp_key(ck)) {
+            if (MINP && F > 1 && kf > comp_key(ck)) {
                 const u32 fd = (kf >> kFineShift) - tbin;
                 const int bf = (int)(fd < (u32)kTabBins ? fd : (u32)kTabBins - 1);
                 const u32 st0 = bv.cnt_above(bf), en = bv.end_of(bf);
@@ -1923,7 +1924,7 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
             mk += key_mass(key);
             ninf += key == kInfKey;
             minidx = idx < minidx ? idx : minidx;
-            kmax = key > kmax ? key : kmax;
+            if (LG) kmax = key > kmax ? key : kmax;
         }
     }, xf);
     if (threadIdx.x == 0) ++s.npass;
@@ -1947,9 +1948,10 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
     // Min-p: the support's entries with key >= kf (mass >= the floor) are a
     // prefix; the kept set is the shorter of it and the top-p prefix, i.e.
     // the first position whose inclusive mass reaches min(T, their mass).
-    const u64 F = minp_floor(theta, key_mass((u32)block_max(s, kmax)));
+    // (Only logit launches carry min-p floors.)
+    const u64 F = LG ? minp_floor(theta, key_mass((u32)block_max(s, kmax))) : 0ull;
     const u32 kf = minp_key(F);
-    if (F > 1 && kf > comp_key(lo)) {
+    if (LG && F > 1 && kf > comp_key(lo)) {
         u64 mf = 0;
         for_each_entry<VEC, LG>(row, nvec, [&](u32 key, u32 idx, bool valid) {
             if (valid && key >= kf) mf += key_mass(key);
@@ -2109,6 +2111,7 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
 // ---------------------------------------------------------------------------
 // Top-k rows (2 <= k <= 1024)
 // ---------------------------------------------------------------------------
+template <bool MINP>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path = kPathSlab, u64 c_k = ~0ull);
 
@@ -2233,7 +2236,7 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     // top bin, where it looks for them.
     const u32 tkey = n ? min(comp_key(mn), kOneKey) & ~0xFFFFu : 0u;
     if (n >= k) {
-        slab_finish(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
+        slab_finish<LG>(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
         return;
     }
     if (n == 0 && theta0 == 1u) {
@@ -2253,7 +2256,7 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     const u64 c_k = composite(0u, zk);
     if (n > 0 && mass > 0) {
         // The zeros carry no mass: they change nothing else.
-        slab_finish(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
+        slab_finish<LG>(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
         return;
     }
     // No mass in the support: its smallest index.
@@ -2513,7 +2516,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         tbase = tmax;
     }
     if (!over && fill >= k) {
-        slab_finish(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
+        slab_finish<LG>(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
     } else {
         // A whole row that counted at least k entries at or above its
         // threshold has its best k there; anything else starts from 1.
@@ -2526,17 +2529,18 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
 // others (and every row under TES_FLAG_TINY_BUFFER) cut the buffer to exactly
 // the best k when it holds more than a sort takes, sort it descending (padded
 // with zeros, which sort last) and finish on the first k positions.
+template <bool MINP>
 __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tkey, u64 P, u64 u,
                                          u32 wfill, u32 path, u64 c_k) {
     const Params p = params_from(s);
     const u64 tp = p.stats ? wall_clock64() : 0;
     const u32 gathered = n;
-    const float theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
+    const float theta = (MINP && p.min_p) ? ld_g(&p.min_p[r]) : 0.0f;
     // wfill != ~0u: the entries are still in the stream's wave regions (this
     // wave's count), and the binned finish packs them.
     if (!(p.flags & TES_FLAG_TINY_BUFFER) && tkey > 0) {
         Outcome ob;
-        if (binned_topk(s, n, k, tkey, P, u, ob, wfill, theta)) {
+        if (binned_topk<MINP>(s, n, k, tkey, P, u, ob, wfill, theta)) {
             stat_phase(p, r, 9, tp);
             if (c_k != ~0ull) ob.c_k = c_k;
             finish_row(s, p, r, ob, path, gathered);
@@ -2557,17 +2561,17 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         u64 v[1];
         sort_desc<1>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<1>(s, v, k, P, u, theta);
+        o = resolve_sorted<1, MINP>(s, v, k, P, u, theta);
     } else if (pad == 2 * kBlock) {
         u64 v[2];
         sort_desc<2>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<2>(s, v, k, P, u, theta);
+        o = resolve_sorted<2, MINP>(s, v, k, P, u, theta);
     } else {
         u64 v[4];
         sort_desc<4>(s, v);
         ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<4>(s, v, k, P, u, theta);
+        o = resolve_sorted<4, MINP>(s, v, k, P, u, theta);
     }
     stat_phase(p, r, 9, tp);
     if (c_k != ~0ull) o.c_k = c_k;
@@ -3119,7 +3123,7 @@ __device__ __attribute__((always_inline)) void do_whole(Smem& s, u32 r, u32 k_ef
     if (threadIdx.x == 0) s.npass = 0;
     const Outcome o = resolve_row<VEC, LG>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, k_eff, P,
                                            u, tiny ? 64u : kSelCap, row_xf<LG>(p, r),
-                                           p.min_p ? ld_g(&p.min_p[r]) : 0.0f);
+                                           (LG && p.min_p) ? ld_g(&p.min_p[r]) : 0.0f);
     stat_add(p, r, 3, uni(s.npass));
     finish_row(s, p, r, o, kPathWhole, 0);
 }
@@ -3135,11 +3139,13 @@ __device__ __forceinline__ u32 row_k_eff(const Params& p, u32 r) {
 // Top-p-only rows with a min-p floor (theta > 0) are decided by the whole-row
 // passes: the exchanged histograms of the segments locate the top-p boundary
 // by mass only.
+template <bool LG>
 __device__ __forceinline__ u32 row_class(const Params& p, u32 r, u32 k_eff, u32 s_full) {
     if (p.flags & TES_FLAG_FORCE_ROW_SELECT) return kClsWhole;
     if (k_eff == 1) return kClsGreedy;
     if (k_eff <= kSlabMaxK) return kClsSlab;
-    if (k_eff == p.V && s_full <= p.s_ws && !(p.min_p && ld_g(&p.min_p[r]) > 0.0f)) return kClsFull;
+    if (k_eff == p.V && s_full <= p.s_ws && !(LG && p.min_p && ld_g(&p.min_p[r]) > 0.0f))
+        return kClsFull;
     return kClsWhole;
 }
 
@@ -3166,7 +3172,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     for (int j = 0; j < 2; ++j) {
         const u32 r = r0 + j;
         const u32 ke = r < p.rows ? row_k_eff(p, r) : 0u;
-        cls[j] = r < p.rows ? row_class(p, r, ke, s_full) : 4u;
+        cls[j] = r < p.rows ? row_class<LG>(p, r, ke, s_full) : 4u;
         if (cls[j] == kClsSlab) s.slab_k[r] = (u16)ke;
         if (cls[j] < 4) local += 1ull << (16 * cls[j]);
     }
@@ -3307,9 +3313,11 @@ __global__ __launch_bounds__(256) void tes_rowmax_kernel(Params p) {
             x[j] = ld_stream(&rv[iv < v1 ? iv : v1 - 1]);
         }
 #pragma unroll
-        for (u32 j = 0; j < kU; ++j)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) e = max(e, enc(VecT<VEC>::get(x[j], c)));
+        for (u32 j = 0; j < kU; ++j) {
+            u32 m = enc(VecT<VEC>::get(x[j], 0));
+            for (int c = 1; c < VEC; ++c) m = max(m, enc(VecT<VEC>::get(x[j], c)));
+            e = max(e, m);
+        }
     }
     __shared__ u32 wm[4];
     u32 m = e;
