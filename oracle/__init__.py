@@ -78,6 +78,15 @@ class Oracle:
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_topk_topp_sample_logits.restype = ctypes.c_int
+        lib.oracle_uniform_u64_hi.argtypes = [ctypes.c_uint64] * 3
+        lib.oracle_uniform_u64_hi.restype = ctypes.c_uint64
+        lib.oracle_spec_verify.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_spec_verify.restype = ctypes.c_int
+        lib.oracle_accept_draft.argtypes = [ctypes.c_uint64] * 4
+        lib.oracle_accept_draft.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -91,6 +100,37 @@ class Oracle:
 
     def uniform_u64(self, seed: int, row: int, offset: int) -> int:
         return int(self.lib.oracle_uniform_u64(seed, row, offset))
+
+    def uniform_u64_hi(self, seed: int, row: int, offset: int) -> int:
+        """Philox words 2 and 3 of the row's block (the acceptance uniform)."""
+        return int(self.lib.oracle_uniform_u64_hi(seed, row, offset))
+
+    # -- speculative verification --------------------------------------------
+    def spec_verify(self, target, Lt: int, top_k, top_p, draft, draft_tokens, target_map,
+                    seed: int, offset: int, n_threads: int | None = None):
+        """target [N*Lt][V], draft [N*L][V] (or [N][L][V]), draft_tokens [N][L],
+        target_map [N][L+1] or None; returns (out_tokens [N][L+1], accept_len [N])."""
+        target = np.ascontiguousarray(target, dtype=np.float32).reshape(-1, np.shape(target)[-1])
+        V = target.shape[1]
+        N = target.shape[0] // Lt
+        toks = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(N, -1)
+        L = toks.shape[1]
+        dr = np.ascontiguousarray(draft, dtype=np.float32).reshape(-1, V) if L else None
+        tk = np.ascontiguousarray(top_k, dtype=np.int32)
+        tp = np.ascontiguousarray(top_p, dtype=np.float32)
+        tm = None if target_map is None else np.ascontiguousarray(target_map, np.int32)
+        out = np.zeros((N, L + 1), np.int32)
+        acc = np.zeros(N, np.int32)
+        if n_threads is None:
+            n_threads = len(os.sched_getaffinity(0))
+        rc = self.lib.oracle_spec_verify(
+            target.ctypes.data, N, Lt, V, tk.ctypes.data, tp.ctypes.data,
+            dr.ctypes.data if dr is not None else None, L, toks.ctypes.data,
+            tm.ctypes.data if tm is not None else None, int(seed) & (2**64 - 1),
+            int(offset) & (2**64 - 1), out.ctypes.data, acc.ctypes.data, int(n_threads))
+        if rc:
+            raise RuntimeError("oracle_spec_verify failed: %d" % rc)
+        return out, acc
 
     # -- logit rows ---------------------------------------------------------
     def exp_weight(self, s: float) -> float:

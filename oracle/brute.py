@@ -145,3 +145,56 @@ def brute_row(row_bits, k: int, p: float, u: int, min_p: float = 0.0):
         if lo <= x < hi:
             return kept[j], kept, [Fraction(qj, M_p) for qj in q[:n]]
     raise AssertionError("u outside [0, 1)")
+
+
+def _mass(v):
+    """floor(min(v, 1) * 2^32) of a sanitised value (Fraction or inf)."""
+    if v is math.inf or v >= 1:
+        return TWO32
+    return math.floor(v * TWO32)
+
+
+def brute_spec_request(target_bits, ks, ps, draft_bits, tokens, pi, u_draw, u_acc):
+    """Speculative verification of one request with exact rationals
+    (SonicSampler appendix C.4, eqs. (15)-(16)).
+
+    target_bits[j] (fp32 bit patterns), ks[j], ps[j]: the request's target
+    rows; draft_bits[l], tokens[l]: draft distribution and token of position
+    l < L; pi[l] (l <= L): the target row of position l; u_draw[j] / u_acc[j]:
+    the 64-bit uniforms of target row j (its own draw / the acceptance test).
+    p_j = row j's final distribution (brute_row's kept weights; a zero-mass
+    row is the point mass on its token); q_l(x) = floor(min(y, 1) 2^32) / 2^32.
+    Position l's draft is accepted iff (u / 2^64) q_l(d) <= p(d); the first
+    rejection draws from max(0, p - q_l) normalised, by interval containment
+    of u_draw / 2^64 in vocabulary order (its own token if that is all zero);
+    with every draft accepted, the bonus is row pi[L]'s own token.
+    Returns (out tokens of length L + 1, accepted count)."""
+    L = len(tokens)
+    out = [-1] * (L + 1)
+    for l in range(L + 1):
+        j = pi[l]
+        tok, kept, w = brute_row(target_bits[j], ks[j], ps[j], u_draw[j])
+        p = dict(zip(kept, w)) if kept else {tok: Fraction(1)}
+        if l == L:
+            out[L] = tok
+            return out, L
+        ys = [sanitized_value(_from_bits(int(v))) for v in draft_bits[l]]
+        q = [Fraction(_mass(y), TWO32) for y in ys]
+        d = tokens[l]
+        if Fraction(u_acc[j], TWO64) * q[d] <= p.get(d, Fraction(0)):
+            out[l] = d
+            continue
+        r = [max(Fraction(0), p.get(x, Fraction(0)) - q[x]) for x in range(len(q))]
+        R = sum(r)
+        if R == 0:
+            out[l] = tok
+        else:
+            u = Fraction(u_draw[j], TWO64)
+            acc = Fraction(0)
+            for x in range(len(r)):
+                if acc / R <= u < (acc + r[x]) / R:
+                    out[l] = x
+                    break
+                acc += r[x]
+        return out, l
+    raise AssertionError("unreachable")

@@ -108,13 +108,18 @@ extern "C" void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2
     for (int i = 0; i < 4; ++i) out[i] = c[i];
 }
 
-// The 64-bit uniform of one row: counter = (offset, row), key = seed.
-extern "C" uint64_t oracle_uniform_u64(uint64_t seed, uint64_t row, uint64_t offset) {
+// The Philox block of one row: counter = (offset, row), key = seed.
+static void row_block(uint64_t seed, uint64_t row, uint64_t offset, uint32_t out[4]) {
     uint32_t ctr[4] = {(uint32_t)offset, (uint32_t)(offset >> 32), (uint32_t)row,
                        (uint32_t)(row >> 32)};
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-    uint32_t out[4];
     oracle_philox4x32_10(ctr, key, out);
+}
+
+// The 64-bit uniform of one row: words 0 and 1 of its block.
+extern "C" uint64_t oracle_uniform_u64(uint64_t seed, uint64_t row, uint64_t offset) {
+    uint32_t out[4];
+    row_block(seed, row, offset, out);
     return (uint64_t)out[0] | ((uint64_t)out[1] << 32);
 }
 
@@ -261,10 +266,14 @@ static uint64_t min_p_floor_mass(float theta, uint64_t qmax) {
 //   [6] M_p  [7] t  [8] position of the token in the sorted support
 //   [9] row kind: 0 normal, 1 +inf, 2 zero mass
 // ---------------------------------------------------------------------------
-extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k, float top_p,
-                                      float min_p, uint64_t u, int32_t* token, float* renorm,
-                                      int64_t* info) {
+// num / den (nullable): the row's final distribution as exact fractions,
+// num[x] / den for every vocabulary index x (q_j / M_p on the kept entries,
+// 1 / m on kept +inf entries, 1 / 1 on the token of a zero-mass row).
+static int sample_row_core(const float* row, int64_t V, int32_t top_k, float top_p, float min_p,
+                           uint64_t u, int32_t* token, float* renorm, int64_t* info,
+                           uint64_t* num, uint64_t* den) {
     if (V <= 0 || row == nullptr || token == nullptr) return -1;
+    if (num) std::fill(num, num + V, (uint64_t)0);
 
     std::vector<uint32_t> key(V);
     for (int64_t i = 0; i < V; ++i) key[i] = sanitized_key(row[i]);
@@ -290,6 +299,10 @@ extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k
             float w = (float)(1.0 / (double)inf_count);
             for (int64_t j = 0; j < inf_count; ++j) renorm[order[j]] = w;
         }
+        if (num) {
+            for (int64_t j = 0; j < inf_count; ++j) num[order[j]] = 1;
+            *den = (uint64_t)inf_count;
+        }
         sinfo[5] = inf_count;
         sinfo[7] = (int64_t)t;
         sinfo[8] = (int64_t)t;
@@ -309,6 +322,10 @@ extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k
     if (M_k == 0) {
         // Step 6: smallest vocabulary index present in the support.
         *token = (int32_t)*std::min_element(order.begin(), order.end());
+        if (num) {
+            num[*token] = 1;
+            *den = 1;
+        }
         sinfo[9] = 2;
         if (info) std::memcpy(info, sinfo, sizeof(sinfo));
         return 0;
@@ -353,6 +370,10 @@ extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k
         for (int64_t j = 0; j < kept; ++j)
             renorm[order[j]] = (float)((double)q[j] / (double)M_p);
     }
+    if (num) {
+        for (int64_t j = 0; j < kept; ++j) num[order[j]] = q[j];
+        *den = M_p;
+    }
     sinfo[4] = (int64_t)T;
     sinfo[5] = kept;
     sinfo[6] = (int64_t)M_p;
@@ -362,9 +383,157 @@ extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k
     return 0;
 }
 
+extern "C" int oracle_sample_row_minp(const float* row, int64_t V, int32_t top_k, float top_p,
+                                      float min_p, uint64_t u, int32_t* token, float* renorm,
+                                      int64_t* info) {
+    return sample_row_core(row, V, top_k, top_p, min_p, u, token, renorm, info, nullptr, nullptr);
+}
+
 extern "C" int oracle_sample_row(const float* row, int64_t V, int32_t top_k, float top_p,
                                  uint64_t u, int32_t* token, float* renorm, int64_t* info) {
     return oracle_sample_row_minp(row, V, top_k, top_p, 0.0f, u, token, renorm, info);
+}
+
+// ---------------------------------------------------------------------------
+// Speculative verification (SonicSampler paper, appendix C.4, eqs. (15) and
+// (16), and its draft-to-target mapping; the acceptance rule u * q(d) <= p(d)
+// of section 2).  N requests, each with L draft tokens d_l drawn by a draft
+// model from distributions q_l, and Lt target rows.  Draft position l (and
+// the bonus position L) reads target row pi(l) of its request (pi = the
+// identity when target_map is null).  With g = n * Lt + pi(l):
+//   p_g     = target row g's final distribution, by steps 1-9 with its
+//             top_k / top_p (num / den above);
+//   q_l(x)  = Q_x / 2^32, Q_x = floor(min(y_x, 1) * 2^32) of the sanitised
+//             draft probability y_x (the draft row as given, not
+//             renormalised);
+//   accept  d_l iff U_a * q_l(d_l) <= p_g(d_l) with U_a = u_a / 2^64, u_a =
+//             x2 | x3 << 32 of the Philox block of (seed, g, offset) (words
+//             0 and 1 are the row's own draw), compared exactly:
+//             u_a * Q_d * den <= num[d] * 2^96;
+//   on the first rejection at l, the correction token is drawn from
+//             max(0, p_g - q_l) (eq. (16)) by inverse CDF in vocabulary order:
+//             R_x = max(0, num[x] * 2^32 - Q_x * den), R = sum R_x,
+//             t = floor(u * R / 2^64) with u = x0 | x1 << 32 of row g's
+//             block, correction = the first x whose inclusive prefix of R
+//             exceeds t (R = 0: row g's own token);
+//   if every draft is accepted, the bonus token is the own token of target
+//             row pi(L).
+// out_tokens[n][0, L + 1) holds the accepted drafts, then the correction or
+// the bonus, then -1; accept_len[n] = the number of accepted drafts.  A
+// request whose map or draft tokens are out of range gets accept_len -1 and
+// all tokens -1.
+// ---------------------------------------------------------------------------
+extern "C" uint64_t oracle_uniform_u64_hi(uint64_t seed, uint64_t row, uint64_t offset) {
+    uint32_t out[4];
+    row_block(seed, row, offset, out);
+    return (uint64_t)out[2] | ((uint64_t)out[3] << 32);
+}
+
+// u * Q * den <= num * 2^96, exactly (u < 2^64, Q <= 2^32, den < 2^51, num <= 2^32).
+static bool accept_draft(uint64_t u, uint64_t Q, uint64_t den, uint64_t num) {
+    const u128 a = (u128)u * (u128)Q;             // < 2^96
+    const uint64_t a_hi = (uint64_t)(a >> 64), a_lo = (uint64_t)a;
+    const u128 lo_prod = (u128)a_lo * (u128)den;  // < 2^115
+    const u128 hi = (u128)a_hi * (u128)den + (lo_prod >> 64);  // the product >> 64
+    const uint64_t low = (uint64_t)lo_prod;                    // the product mod 2^64
+    const u128 rhs = (u128)num << 32;                          // num * 2^96 >> 64
+    return hi < rhs || (hi == rhs && low == 0);
+}
+
+extern "C" int oracle_accept_draft(uint64_t u, uint64_t Q, uint64_t den, uint64_t num) {
+    return accept_draft(u, Q, den, num) ? 1 : 0;
+}
+
+extern "C" int oracle_spec_verify(const float* target, int64_t N, int64_t Lt, int64_t V,
+                                  const int32_t* top_k, const float* top_p, const float* draft,
+                                  int64_t L, const int32_t* draft_tokens,
+                                  const int32_t* target_map, uint64_t seed, uint64_t offset,
+                                  int32_t* out_tokens, int32_t* accept_len, int n_threads) {
+    if (N < 0 || Lt <= 0 || V <= 0 || L < 0) return -1;
+    if (N == 0) return 0;
+    if (!target || !top_k || !top_p || !out_tokens || !accept_len) return -1;
+    if (L > 0 && (!draft || !draft_tokens)) return -1;
+    if (!target_map && Lt < L + 1) return -1;
+    if (n_threads <= 0) n_threads = 1;
+    if ((int64_t)n_threads > N) n_threads = (int)N;
+    std::vector<int> status(n_threads, 0);
+    auto work = [&](int wk) {
+        std::vector<uint64_t> num(V);
+        for (int64_t n = N * wk / n_threads; n < N * (wk + 1) / n_threads; ++n) {
+            int32_t* out = out_tokens + n * (L + 1);
+            for (int64_t l = 0; l <= L; ++l) out[l] = -1;
+            accept_len[n] = -1;
+            auto row_of = [&](int64_t l) {
+                return target_map ? (int64_t)target_map[n * (L + 1) + l] : l;
+            };
+            bool valid = true;
+            for (int64_t l = 0; l <= L; ++l) valid = valid && row_of(l) >= 0 && row_of(l) < Lt;
+            for (int64_t l = 0; l < L; ++l)
+                valid = valid && draft_tokens[n * L + l] >= 0 && draft_tokens[n * L + l] < V;
+            if (!valid) continue;
+            int64_t l = 0;
+            for (; l <= L; ++l) {
+                const int64_t g = n * Lt + row_of(l);
+                const uint64_t u = oracle_uniform_u64(seed, (uint64_t)g, offset);
+                int32_t tok = 0;
+                uint64_t den = 0;
+                int rc = sample_row_core(target + g * V, V, top_k[g], top_p[g], 0.0f, u, &tok,
+                                         nullptr, nullptr, num.data(), &den);
+                if (rc) {
+                    status[wk] = rc;
+                    break;
+                }
+                if (l == L) {  // every draft accepted: the bonus token
+                    out[L] = tok;
+                    accept_len[n] = (int32_t)L;
+                    break;
+                }
+                const float* y = draft + (n * L + l) * V;
+                const int32_t d = draft_tokens[n * L + l];
+                const uint64_t Qd = fixed_point_mass(sanitized_key(y[d]));
+                const uint64_t ua = oracle_uniform_u64_hi(seed, (uint64_t)g, offset);
+                if (accept_draft(ua, Qd, den, num[d])) {
+                    out[l] = d;
+                    continue;
+                }
+                // Rejected: the correction from max(0, p - q), vocabulary order.
+                u128 R = 0;
+                std::vector<u128> r(V);
+                for (int64_t x = 0; x < V; ++x) {
+                    const u128 a = (u128)num[x] << 32;
+                    const u128 b = (u128)fixed_point_mass(sanitized_key(y[x])) * (u128)den;
+                    r[x] = a > b ? a - b : 0;
+                    R += r[x];
+                }
+                int32_t corr = tok;
+                if (R > 0) {
+                    const uint64_t R_hi = (uint64_t)(R >> 64), R_lo = (uint64_t)R;
+                    const u128 t = (u128)u * R_hi + (((u128)u * R_lo) >> 64);  // floor(u R / 2^64)
+                    u128 acc = 0;
+                    for (int64_t x = 0; x < V; ++x) {
+                        acc += r[x];
+                        if (acc > t) {
+                            corr = (int32_t)x;
+                            break;
+                        }
+                    }
+                }
+                out[l] = corr;
+                accept_len[n] = (int32_t)l;
+                break;
+            }
+        }
+    };
+    if (n_threads == 1) {
+        work(0);
+    } else {
+        std::vector<std::thread> pool;
+        for (int wk = 0; wk < n_threads; ++wk) pool.emplace_back(work, wk);
+        for (auto& th : pool) th.join();
+    }
+    for (int st : status)
+        if (st) return st;
+    return 0;
 }
 
 // ---------------------------------------------------------------------------

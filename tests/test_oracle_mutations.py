@@ -16,6 +16,7 @@ import pytest
 import oracle
 import tests.test_oracle_brute as pb
 import tests.test_oracle_logits as pl
+import tests.test_oracle_spec as ps_
 import tests.test_oracle_philox as pp
 import tests.test_oracle_properties as pr
 
@@ -99,6 +100,27 @@ MUTATIONS = {
     "logit_nan_counts_as_max": (
         "const float xi = std::isnan(x[i]) ? ninf : x[i];\n        if (xi > M) M = xi;",
         "const float xi = std::isnan(x[i]) ? -ninf : x[i];\n        if (xi > M) M = xi;"),
+    "spec_accept_strict": (
+        "return hi < rhs || (hi == rhs && low == 0);",
+        "return hi < rhs;"),
+    "spec_residual_sign_swapped": (
+        "r[x] = a > b ? a - b : 0;",
+        "r[x] = b > a ? b - a : 0;"),
+    "spec_acceptance_uses_draw_words": (
+        "const uint64_t ua = oracle_uniform_u64_hi(seed, (uint64_t)g, offset);",
+        "const uint64_t ua = oracle_uniform_u64(seed, (uint64_t)g, offset);"),
+    "spec_map_ignored": (
+        "return target_map ? (int64_t)target_map[n * (L + 1) + l] : l;",
+        "return (int64_t)l;"),
+    "spec_zero_residual_gives_minus_one": (
+        "int32_t corr = tok;",
+        "int32_t corr = -1;"),
+    "spec_correction_draws_with_acceptance_uniform": (
+        "const u128 t = (u128)u * R_hi + (((u128)u * R_lo) >> 64);",
+        "const u128 t = (u128)ua * R_hi + (((u128)ua * R_lo) >> 64);"),
+    "spec_draft_mass_not_sanitised": (
+        "const uint64_t Qd = fixed_point_mass(sanitized_key(y[d]));",
+        "const uint64_t Qd = fixed_point_mass(sanitized_key(std::fabs(y[d])));"),
     "renorm_by_topk_mass": (
         "renorm[order[j]] = (float)((double)q[j] / (double)M_p);",
         "renorm[order[j]] = (float)((double)q[j] / (double)M_k);"),
@@ -123,6 +145,11 @@ def _pins(orc, torch_exe, rocrand_exe):
     for theta in (0.2, 0.25, 0.5, 1.0):
         yield lambda theta=theta: pl.test_min_p_against_brute_force(orc, theta)
     yield lambda: pl.test_min_p_floor_exactly_on_a_mass(orc)
+    for special in (False, True):
+        for use_map in (False, True):
+            yield lambda a=special, b=use_map: ps_.test_spec_verify_against_brute_force(orc, a, b)
+    yield lambda: ps_.test_acceptance_boundary(orc)
+    yield lambda: ps_.test_identical_distributions_accept_everything(orc)
     if torch_exe:
         yield lambda: pp.test_block_function_matches_pytorch(orc, torch_exe)
         yield lambda: pp.test_row_uniform_mapping(orc, torch_exe)
