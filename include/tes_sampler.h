@@ -137,6 +137,41 @@ int topk_topp_sample_logits(tes_sampler *s, const float *logits, int B, int V,
                             const float *min_p, uint64_t seed, uint64_t offset,
                             int32_t *out_tokens, float *renorm_out, void *stream);
 
+/* Speculative verification on the sampled target rows (SonicSampler paper,
+ * appendix C.4 "Speculative Verification", eqs. (15)-(16), and its
+ * "Draft-to-Target Mapping").  N requests; request n proposed L draft tokens
+ * d_l from draft distributions q_l and owns Lt target rows.  Draft position
+ * l (and the bonus position L) reads target row g = n * Lt + pi(l), pi =
+ * target_map[n][l] (the identity when target_map is NULL).  Each target row
+ * is first sampled as by topk_topp_sample (its own top_k / top_p; its final
+ * distribution p_g and its own token, drawn with Philox words 0-1 of row g).
+ * Then, for l = 0, 1, ...:
+ *   accept d_l  iff  u_a * q_l(d_l) <= p_g(d_l), compared exactly, with
+ *               u_a = (word2 | word3 << 32) / 2^64 of row g's Philox block and
+ *               q_l(x) = floor(min(y_x, 1) * 2^32) / 2^32 of the sanitised
+ *               draft probability y_x (the draft row as given);
+ *   at the first rejection, the correction token is drawn from
+ *               max(0, p_g - q_l) normalised, by integer inverse CDF in
+ *               vocabulary order with row g's own 64-bit uniform (its own
+ *               token when p_g <= q_l everywhere), and the request stops;
+ *   if every draft is accepted, the bonus token is row pi(L)'s own token.
+ *   target_probs  device, fp32 [N * Lt][V], as for topk_topp_sample.
+ *   top_k, top_p  device, [N * Lt], per target row.
+ *   draft_probs   device, fp32 [N][L][V]; 16-byte aligned when target_probs is
+ *                 16-byte aligned and V % 4 == 0.  NULL when L = 0.
+ *   draft_tokens  device, int32 [N][L].  NULL when L = 0.
+ *   target_map    device, int32 [N][L + 1], or NULL (then Lt >= L + 1).
+ *   out_tokens    device, int32 [N][L + 1]: the accepted drafts, then the
+ *                 correction or the bonus token, then -1.
+ *   accept_len    device, int32 [N]: the number of accepted drafts (0 .. L);
+ *                 -1 (and all tokens -1) for a request whose map entries lie
+ *                 outside [0, Lt) or whose draft tokens lie outside [0, V).
+ * L is 0 .. 63; N * Lt <= max_batch.  Status codes as for topk_topp_sample. */
+int spec_verify_sample(tes_sampler *s, const float *target_probs, int N, int Lt, int V,
+                       const int32_t *top_k, const float *top_p, const float *draft_probs, int L,
+                       const int32_t *draft_tokens, const int32_t *target_map, uint64_t seed,
+                       uint64_t offset, int32_t *out_tokens, int32_t *accept_len, void *stream);
+
 /* topk_topp_sample for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same sampling, outputs and argument rules, with no handle.

@@ -35,7 +35,8 @@ STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 
 EXPORTED = ("sampler_create", "topk_topp_sample", "sampler_destroy", "sampler_status_string",
             "sampler_get_stats", "sampler_read_probe", "topk_topp_sample_slab", "sampler_route",
-            "topk_topp_sample_bf16", "topk_topp_sample_noalloc", "topk_topp_sample_logits")
+            "topk_topp_sample_bf16", "topk_topp_sample_noalloc", "topk_topp_sample_logits",
+            "spec_verify_sample")
 
 _lib = None
 
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.topk_topp_sample_logits.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
                                               ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp]
         L.topk_topp_sample_logits.restype = ctypes.c_int
+        L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                                         vp, ctypes.c_int, vp, vp, ctypes.c_uint64,
+                                         ctypes.c_uint64, vp, vp, vp]
+        L.spec_verify_sample.restype = ctypes.c_int
         L.sampler_destroy.argtypes = [vp]
         L.sampler_destroy.restype = ctypes.c_int
         L.sampler_status_string.argtypes = [ctypes.c_int]
@@ -137,6 +142,19 @@ def topk_topp_sample_logits(handle, logits_ptr: int, B: int, V: int, top_k_ptr: 
                                          temperature_ptr, min_p_ptr, int(seed) & (2**64 - 1),
                                          int(offset) & (2**64 - 1), out_tokens_ptr, renorm_ptr,
                                          stream)
+
+
+def spec_verify_sample(handle, target_ptr: int, N: int, Lt: int, V: int, top_k_ptr: int,
+                       top_p_ptr: int, draft_ptr, L: int, draft_tokens_ptr, target_map_ptr,
+                       seed: int, offset: int, out_tokens_ptr: int, accept_len_ptr: int,
+                       stream) -> int:
+    """Raw speculative-verification call with device pointers (ints; the
+    target map may be None); returns the status code."""
+    return lib().spec_verify_sample(handle, target_ptr, int(N), int(Lt), int(V), top_k_ptr,
+                                    top_p_ptr, draft_ptr, int(L), draft_tokens_ptr,
+                                    target_map_ptr, int(seed) & (2**64 - 1),
+                                    int(offset) & (2**64 - 1), out_tokens_ptr, accept_len_ptr,
+                                    stream)
 
 
 def sampler_destroy(handle) -> int:
@@ -251,6 +269,37 @@ class Sampler:
         if rc != TES_OK:
             raise TesError(rc, "topk_topp_sample_logits")
         return out_tokens
+
+    def spec_verify(self, target, Lt: int, top_k, top_p, draft, draft_tokens, seed: int,
+                    offset: int, target_map=None, stream=None):
+        """Speculative verification (spec_verify_sample): target [N*Lt][V] fp32,
+        draft [N*L][V] fp32, draft_tokens [N][L] int32, target_map [N][L+1]
+        int32 or None.  Returns (out_tokens [N][L+1], accept_len [N])."""
+        import torch
+
+        V = target.shape[-1]
+        N = target.shape[0] // Lt
+        L = draft_tokens.shape[1]
+        checks = [(target, torch.float32), (top_k, torch.int32), (top_p, torch.float32),
+                  (draft, torch.float32), (draft_tokens, torch.int32)]
+        if target_map is not None:
+            checks.append((target_map, torch.int32))
+        for t, dt in checks:
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("expected contiguous %s on the GPU" % dt)
+        dev = target.device
+        out = torch.empty((N, L + 1), dtype=torch.int32, device=dev)
+        acc = torch.empty(N, dtype=torch.int32, device=dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = spec_verify_sample(self.handle, target.data_ptr(), N, Lt, V, top_k.data_ptr(),
+                                top_p.data_ptr(), draft.data_ptr() if L else None, L,
+                                draft_tokens.data_ptr() if L else None,
+                                target_map.data_ptr() if target_map is not None else None,
+                                seed, offset, out.data_ptr(), acc.data_ptr(), stream.cuda_stream)
+        if rc != TES_OK:
+            raise TesError(rc, "spec_verify_sample")
+        return out, acc
 
     def sample_slab(self, probs, top_k, top_p, seed: int, offset: int, slab_cap: int,
                     out_tokens=None, renorm_out=None, stream=None, want_route: bool = True):

@@ -397,7 +397,10 @@ __device__ __forceinline__ u32 minp_key(u64 F) {
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): key (seed lo, seed hi),
-// counter (offset lo, offset hi, row lo, row hi); returns word0 | word1 << 32.
+// counter (offset lo, offset hi, row lo, row hi).  A row's own draw uses
+// word0 | word1 << 32 (philox_uniform); the acceptance test of speculative
+// verification uses word2 | word3 << 32 of the same block (HI).
+template <bool HI = false>
 __device__ u64 philox_uniform(u64 seed, u64 row, u64 offset) {
     u32 x0 = (u32)offset, x1 = (u32)(offset >> 32), x2 = (u32)row, x3 = (u32)(row >> 32);
     u32 k0 = (u32)seed, k1 = (u32)(seed >> 32);
@@ -415,7 +418,7 @@ __device__ u64 philox_uniform(u64 seed, u64 row, u64 offset) {
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
-    return (u64)x0 | ((u64)x1 << 32);
+    return HI ? ((u64)x2 | ((u64)x3 << 32)) : ((u64)x0 | ((u64)x1 << 32));
 }
 
 // ---------------------------------------------------------------------------
@@ -539,16 +542,18 @@ __device__ __forceinline__ u64 wave_incl_scan(u64 x) {
     return x + off;
 }
 
-__device__ u64 block_sum(Smem& s, u64 v) {
+// Sum over the workgroup, through kWaves words of LDS at part.
+__device__ u64 block_sum_u64(u64* part, u64 v) {
     v = wave_sum(v);
-    if (lane_id() == 0) s.wpart[wave_id()] = v;
+    if (lane_id() == 0) part[wave_id()] = v;
     __syncthreads();
     u64 t = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += s.wpart[w];
+    for (int w = 0; w < kWaves; ++w) t += part[w];
     __syncthreads();
     return uni(t);
 }
+__device__ u64 block_sum(Smem& s, u64 v) { return block_sum_u64(s.wpart, v); }
 __device__ u64 block_min(Smem& s, u64 v) {
     v = wave_min(v);
     if (lane_id() == 0) s.wpart[wave_id()] = v;
@@ -570,16 +575,21 @@ __device__ u64 block_max(Smem& s, u64 v) {
     return uni(t);
 }
 
-__device__ __forceinline__ u64 block_excl_scan(Smem& s, u64 v) {
+// Exclusive prefix sum over the workgroup in thread order, through kWaves
+// words of LDS at part.
+__device__ __forceinline__ u64 block_excl_scan_u64(u64* part, u64 v) {
     const u64 x = wave_incl_scan(v);
     const u32 lane = lane_id();
-    if (lane == 63) s.wpart[wave_id()] = x;
+    if (lane == 63) part[wave_id()] = x;
     __syncthreads();
     u64 pre = 0;
     const u32 w0 = wave_id();
-    for (u32 w = 0; w < w0; ++w) pre += s.wpart[w];
+    for (u32 w = 0; w < w0; ++w) pre += part[w];
     __syncthreads();
     return pre + x - v;
+}
+__device__ __forceinline__ u64 block_excl_scan(Smem& s, u64 v) {
+    return block_excl_scan_u64(s.wpart, v);
 }
 
 // Append `c` at arr[base + slot] for every lane with pred set; slots come from
@@ -1977,7 +1987,7 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
 __device__ void finish_row(Smem& s, const Params& p, u32 r, const Outcome& o, u32 path,
                            u32 gathered) {
     if (threadIdx.x == 0) {
-        *gp(&p.out_tokens[r]) = (int32_t)o.token;
+        if (p.out_tokens) *gp(&p.out_tokens[r]) = (int32_t)o.token;
         Decision* d = ws_decision(p, r);
         *gp(&d->kind) = o.kind;
         *gp(&d->m) = o.m;
@@ -3287,6 +3297,270 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decisio
 
 
 
+// ---------------------------------------------------------------------------
+// Speculative verification epilogue
+// ---------------------------------------------------------------------------
+// SonicSampler paper, appendix C.4, eqs. (15)-(16), with its draft-to-target
+// mapping.  The target rows of a launch have already been decided by the
+// sampling kernel (their Decisions hold each row's final distribution): p(x)
+// = q_x / M_p on the kept entries of a normal row, 1 / m on the kept +inf
+// entries of a +inf row, 1 on the token of a zero-mass row.  One workgroup
+// per request:
+//   * wave 0 tests the L drafts at once, lane l: the draft's mass
+//     Q = floor(min(y_d, 1) * 2^32) in its draft row, p(d) = num / den in
+//     target row pi(l), and u * Q * den <= num * 2^96 with u = words 2 and 3
+//     of that row's Philox block, compared on three 64-bit limbs;
+//   * the first rejected position l draws its correction from
+//     R_x = max(0, num_x * 2^32 - Q_x * den) (the residual of eq. (16) scaled
+//     by 2^32 den): t = floor(u R / 2^64) with u = words 0 and 1 (the row's
+//     own draw, whose token is not used then), and the correction is the
+//     first x in vocabulary order whose inclusive prefix of R exceeds t.  The
+//     workgroup finds it by splitting the vocabulary range in eight, one
+//     range per wave (each wave sums its range's R; the range holding t is
+//     kept), until the range is one vector per thread, then a workgroup
+//     scan.  R = 0 (p <= q everywhere) takes the row's own token;
+//   * with every draft accepted, the bonus token is target row pi(L)'s own
+//     token.
+// A request whose map or draft tokens are out of range gets accept_len -1
+// and tokens -1.
+struct SpecArgs {
+    const float* draft;      // [nreq][L][V] draft probabilities (fp32)
+    const int32_t* tokens;   // [nreq][L] draft tokens
+    const int32_t* map;      // [nreq][L + 1] target row of each position, or null
+    int32_t* out;            // [nreq][L + 1] output tokens
+    int32_t* accept;         // [nreq] accepted drafts
+    u32 L;
+    u32 Lt;                  // target rows per request
+};
+
+__device__ __forceinline__ Decision load_decision(const Params& p, u32 r) {
+    const Decision* d = ws_decision(p, r);
+    Decision o;
+    o.kind = ld_g(&d->kind);
+    o.m = ld_g(&d->m);
+    o.token = ld_g(&d->token);
+    o.path = ld_g(&d->path);
+    o.c_keep = ld_g(&d->c_keep);
+    o.M_p = ld_g(&d->M_p);
+    o.c_k = ld_g(&d->c_k);
+    return o;
+}
+
+// Row r's p(x) = num / den from its Decision and entry x's key.
+__device__ __forceinline__ u64 dist_num(const Decision& d, u32 key, u32 x) {
+    if (d.kind == kZeroRow) return x == d.token ? 1ull : 0ull;
+    if (composite(key, x) < d.c_keep) return 0;
+    return d.kind == kInfRow ? 1ull : key_mass(key);
+}
+__device__ __forceinline__ u64 dist_den(const Decision& d) {
+    return d.kind == kNormal ? d.M_p : (d.kind == kInfRow ? (u64)d.m : 1ull);
+}
+
+// u * Q * den <= num * 2^96 on 64-bit limbs (Q <= 2^32, den < 2^51, num <= 2^32).
+__device__ __forceinline__ bool draft_accepted(u64 u, u64 Q, u64 den, u64 num) {
+    const u64 m0 = u * Q, m1 = __umul64hi(u, Q);  // u Q = m1:m0, m1 < 2^32
+    const u64 p0 = m0 * den, c0 = __umul64hi(m0, den);
+    const u64 t1 = m1 * den, t2 = __umul64hi(m1, den);
+    const u64 p1 = t1 + c0;
+    const u64 p2 = t2 + (p1 < t1 ? 1ull : 0ull);  // u Q den = p2:p1:p0
+    const u64 r2 = num >> 32, r1 = num << 32;     // num 2^96 = r2:r1:0
+    if (p2 != r2) return p2 < r2;
+    if (p1 != r1) return p1 < r1;
+    return p0 == 0;
+}
+
+typedef unsigned __int128 u128;
+
+// R_x as hi / lo 32-bit parts of a value <= 2^64: hi = R >> 32 (<= 2^32),
+// lo = R & (2^32 - 1); sums of up to 2^18 of each stay below 2^51.
+__device__ __forceinline__ void residual_parts(u64 num, u64 Q, u64 den, u64& hi, u64& lo) {
+    const u64 a1 = num >> 32, a0 = num << 32;              // num 2^32
+    const u64 b0 = Q * den, b1 = __umul64hi(Q, den);       // Q den
+    const bool pos = a1 > b1 || (a1 == b1 && a0 > b0);
+    const u64 d0 = a0 - b0, d1 = a1 - b1 - (a0 < b0 ? 1ull : 0ull);  // a - b when pos
+    hi = pos ? ((d1 << 32) | (d0 >> 32)) : 0ull;
+    lo = pos ? (d0 & 0xFFFFFFFFull) : 0ull;
+}
+__device__ __forceinline__ u128 from_parts(u64 hi, u64 lo) { return ((u128)hi << 32) + lo; }
+
+template <int VEC>
+__global__ __launch_bounds__(kBlock) void tes_verify_kernel(Params p, SpecArgs a) {
+    typedef typename VecT<VEC>::T VT;
+    __shared__ u64 wsum[2][kWaves];
+    __shared__ u64 wpart[kWaves];
+    __shared__ u32 res[4];
+    const u32 n = blockIdx.x;
+    const u32 lane = lane_id(), wave = wave_id();
+    const u32 L = a.L, Lt = a.Lt, V = p.V;
+    int32_t* out = a.out + (size_t)n * (L + 1);
+    // Wave 0: validate the request, test every draft, find the first rejection.
+    if (wave == 0) {
+        const u32 l = lane;
+        int j = 0;
+        bool bad = false;
+        if (l <= L) {
+            j = a.map ? ld_g(&a.map[(size_t)n * (L + 1) + l]) : (int)l;
+            bad = j < 0 || (u32)j >= Lt;
+        }
+        int32_t d = 0;
+        if (l < L) {
+            d = ld_g(&a.tokens[(size_t)n * L + l]);
+            bad = bad || d < 0 || (u32)d >= V;
+        }
+        const bool any_bad = __ballot(bad) != 0;
+        bool acc = true;
+        if (!any_bad && l < L) {
+            const u32 r = n * Lt + (u32)j;
+            const Decision dec = load_decision(p, r);
+            const float* trow = row_ptr<1>(p.probs, r, V);
+            const u32 key = sanitize(__float_as_uint(ld_g(&trow[d])));
+            const float* drow = a.draft + ((size_t)n * L + l) * V;
+            const u64 Q = key_mass(sanitize(__float_as_uint(ld_g(&drow[d]))));
+            const u64 ua = philox_uniform<true>(p.seed, p.row_base + r, p.offset);
+            acc = draft_accepted(ua, Q, dist_den(dec), dist_num(dec, key, (u32)d));
+        }
+        const u64 rej = __ballot(l < L && !acc);
+        const u32 first = rej ? (u32)__builtin_ctzll(rej) : L;  // accepted drafts
+        const u32 jf = (u32)__builtin_amdgcn_readlane(j, (int)(first < 64 ? first : 0));
+        if (any_bad) {
+            if (l <= L) out[l] = -1;
+            if (l == 0) a.accept[n] = -1;
+        } else {
+            if (l < first) out[l] = d;
+            if (l > first && l <= L) out[l] = -1;
+            if (l == 0) {
+                a.accept[n] = (int32_t)first;
+                res[0] = first;
+                res[1] = n * Lt + jf;  // the row of the rejection, or of the bonus
+                if (first == L) out[L] = (int32_t)ld_g(&ws_decision(p, n * Lt + jf)->token);
+            }
+        }
+        if (l == 0) res[2] = any_bad ? 1u : 0u;
+    }
+    __syncthreads();
+    const u32 first = res[0];
+    if (res[2] != 0 || first >= L) return;  // marked, or every draft accepted (bonus written)
+    // The correction at position `first`, from target row r and draft row `first`.
+    const u32 r = res[1];
+    const Decision dec = load_decision(p, r);
+    const u64 den = dist_den(dec);
+    const VT* __restrict__ tv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, V));
+    const VT* __restrict__ dv =
+        reinterpret_cast<const VT*>(a.draft + ((size_t)n * L + first) * V);
+    // Residual parts of vector iv, summed over its entries.
+    auto vec_parts = [&](u32 iv, u64& hi, u64& lo) {
+        const VT x = ld_g(&tv[iv]);
+        const VT y = ld_g(&dv[iv]);
+        hi = lo = 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x, e)));
+            const u64 Q = key_mass(sanitize(__float_as_uint(VecT<VEC>::get(y, e))));
+            u64 h, l2;
+            residual_parts(dist_num(dec, key, iv * VEC + e), Q, den, h, l2);
+            hi += h;
+            lo += l2;
+        }
+    };
+    u32 v0 = 0, v1 = p.nvec;
+    u128 t = 0;
+    bool have_t = false;
+    while (true) {
+        const u32 nv = v1 - v0;
+        if (nv <= kBlock) break;
+        // Each wave sums one eighth of the range.
+        const u32 sub = (nv + kWaves - 1) / kWaves;
+        const u32 w0 = min(v0 + wave * sub, v1), w1 = min(w0 + sub, v1);
+        u64 hi = 0, lo = 0;
+#pragma unroll 4
+        for (u32 iv = w0 + lane; iv < w1; iv += 64) {
+            u64 h, l2;
+            vec_parts(iv, h, l2);
+            hi += h;
+            lo += l2;
+        }
+        hi = wave_sum(hi);
+        lo = wave_sum(lo);
+        if (lane == 0) {
+            wsum[0][wave] = hi;
+            wsum[1][wave] = lo;
+        }
+        __syncthreads();
+        u128 tot[kWaves];
+        u128 all = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            tot[w] = from_parts(wsum[0][w], wsum[1][w]);
+            all += tot[w];
+        }
+        __syncthreads();
+        if (!have_t) {
+            if (all == 0) {  // p <= q everywhere: the row's own token
+                if (threadIdx.x == 0) out[first] = (int32_t)dec.token;
+                return;
+            }
+            // t = floor(u * R / 2^64), R = all < 2^83.
+            const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+            const u64 R0 = (u64)all, R1 = (u64)(all >> 64);
+            const u64 c = __umul64hi(u, R0);
+            t = (u128)u * R1 + c;
+            have_t = true;
+        }
+        u32 k = 0;
+        u128 before = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w) {
+            if (k == (u32)w && before + tot[w] <= t) {
+                before += tot[w];
+                k = (u32)w + 1;
+            }
+        }
+        t -= before;
+        const u32 n0 = min(v0 + k * sub, v1);
+        v1 = min(n0 + sub, v1);
+        v0 = n0;
+    }
+    // One vector per thread: a workgroup scan of the residual parts.
+    const u32 iv = v0 + threadIdx.x;
+    u64 hi = 0, lo = 0;
+    if (iv < v1) vec_parts(iv, hi, lo);
+    if (!have_t) {
+        // The whole row fits one round: its total decides t.
+        const u64 th = block_sum_u64(wpart, hi), tl = block_sum_u64(wpart, lo);
+        const u128 all = from_parts(th, tl);
+        if (all == 0) {
+            if (threadIdx.x == 0) out[first] = (int32_t)dec.token;
+            return;
+        }
+        const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+        t = (u128)u * (u64)(all >> 64) + __umul64hi(u, (u64)all);
+    }
+    const u64 eh = block_excl_scan_u64(wpart, hi), el = block_excl_scan_u64(wpart, lo);
+    const u128 pre = from_parts(eh, el), own = from_parts(hi, lo);
+    if (threadIdx.x == 0) res[3] = 0xFFFFFFFFu;
+    __syncthreads();
+    if (iv < v1 && pre <= t && t < pre + own) {
+        const VT x = ld_g(&tv[iv]);
+        const VT y = ld_g(&dv[iv]);
+        u128 acc = pre;
+        u32 hit = iv * VEC + VEC - 1;
+        for (int e = 0; e < VEC; ++e) {
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x, e)));
+            const u64 Q = key_mass(sanitize(__float_as_uint(VecT<VEC>::get(y, e))));
+            u64 h, l2;
+            residual_parts(dist_num(dec, key, iv * VEC + e), Q, den, h, l2);
+            acc += from_parts(h, l2);
+            if (acc > t) {
+                hit = iv * VEC + e;
+                break;
+            }
+        }
+        res[3] = hit;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) out[first] = (int32_t)res[3];
+}
+
 // Logit rows: the maximum of each of p.xparts parts of every row (NaN counts
 // as -inf), as an order-preserving u32 encoding (sign bit set for
 // non-negative values, all bits inverted for negative ones), so that the
@@ -3593,7 +3867,7 @@ namespace {
 // The kernels of one launch (one chunk of rows) for row vectors of VEC entries.
 template <int VEC, bool LG>
 int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 rows, u32 V,
-                 u32 nvec, float* ro, const SlabOut* slab, size_t c0) {
+                 u32 nvec, float* ro, const SlabOut* slab, size_t c0, const SpecArgs* spec) {
     if constexpr (LG) {
         hipLaunchKernelGGL(tes_rowmax_kernel<VEC>, dim3(p.xparts, rows), dim3(256), 0, st, p);
         if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
@@ -3608,6 +3882,21 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
                            ro);
         if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
     }
+    if constexpr (!LG && VEC != 8) {
+        if (spec) {
+            // The requests whose target rows this launch decided.
+            const size_t n0 = c0 / spec->Lt;
+            SpecArgs a = *spec;
+            a.draft = spec->draft ? spec->draft + n0 * spec->L * (size_t)V : nullptr;
+            a.tokens = spec->tokens ? spec->tokens + n0 * spec->L : nullptr;
+            a.map = spec->map ? spec->map + n0 * (spec->L + 1) : nullptr;
+            a.out = spec->out + n0 * (spec->L + 1);
+            a.accept = spec->accept + n0;
+            hipLaunchKernelGGL(tes_verify_kernel<VEC>, dim3(rows / spec->Lt), dim3(kBlock), 0, st, p,
+                               a);
+            if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
+        }
+    }
     if (slab && !LG) {
         const size_t o = c0 * slab->cap;
         hipLaunchKernelGGL(tes_slab_kernel<VEC>, dim3(rows), dim3(kSlabThreads), 0, st, p.probs,
@@ -3621,19 +3910,24 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
 // probs holds fp32 entries, or bf16 entries when bf16 is set, or fp32 logits
 // when logits is set (with the nullable per-row temperature; min_p, nullable,
 // applies to both kinds of rows).
+// With spec (speculative verification), B counts target rows (Lt per
+// request), launches take whole requests, and the verification kernel
+// follows each launch; out_tokens is not used (the outputs are spec's).
 int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, const int32_t* top_k,
                 const float* top_p, uint64_t seed, uint64_t offset, int32_t* out_tokens,
                 float* renorm_out, const SlabOut* slab, void* stream, bool logits = false,
-                const float* temperature = nullptr, const float* min_p = nullptr) {
+                const float* temperature = nullptr, const float* min_p = nullptr,
+                const SpecArgs* spec = nullptr) {
     if (!s || B < 0 || V < 1) return TES_ERR_INVALID_ARGUMENT;
     if (B > s->max_batch || V > s->max_vocab) return TES_ERR_TOO_LARGE;
     if (B == 0) return TES_OK;
-    if (!probs || !top_k || !top_p || !out_tokens) return TES_ERR_INVALID_ARGUMENT;
+    if (!probs || !top_k || !top_p || (!out_tokens && !spec)) return TES_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)probs & 3) || ((uintptr_t)top_k & 3) || ((uintptr_t)top_p & 3) ||
         ((uintptr_t)out_tokens & 3) || ((uintptr_t)renorm_out & 3) ||
         ((uintptr_t)temperature & 3) || ((uintptr_t)min_p & 3))
         return TES_ERR_INVALID_ARGUMENT;
     if (logits && (bf16 || slab)) return TES_ERR_INVALID_ARGUMENT;
+    if (spec && (logits || bf16 || slab)) return TES_ERR_INVALID_ARGUMENT;
     // Row vectors: eight bf16 entries (bf16 rows must allow them), four fp32
     // entries when the rows and renorm_out allow 16-byte access, else one.
     const bool aligned16 = (((uintptr_t)probs & 15) == 0) && (((uintptr_t)renorm_out & 15) == 0);
@@ -3646,8 +3940,11 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
     const u32 nvec = (u32)V / (u32)vec;
     const u32 seg = vec == 8 ? s->seg_full / 2 : s->seg_full;  // vectors per segment
     const u32 s_full = ceil_div(nvec, seg);
-    for (int c0 = 0; c0 < B; c0 += (int)s->chunk) {
-        const u32 rows = (u32)(B - c0) < s->chunk ? (u32)(B - c0) : s->chunk;
+    // Rows per launch (whole requests under spec).
+    const u32 step = spec ? (s->chunk / spec->Lt) * spec->Lt : s->chunk;
+    if (step == 0) return TES_ERR_TOO_LARGE;
+    for (int c0 = 0; c0 < B; c0 += (int)step) {
+        const u32 rows = (u32)(B - c0) < step ? (u32)(B - c0) : step;
         Params p;
         p.probs = reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(probs) +
                                                  (size_t)c0 * V * entry_bytes);
@@ -3655,7 +3952,7 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.top_p = top_p + c0;
         p.temperature = temperature ? temperature + c0 : nullptr;
         p.min_p = min_p ? min_p + c0 : nullptr;
-        p.out_tokens = out_tokens + c0;
+        p.out_tokens = out_tokens ? out_tokens + c0 : nullptr;
         p.stats = (s->flags & TES_FLAG_STATS) ? s->d_stats : nullptr;
         p.ws = s->ws;
         p.seed = seed;
@@ -3700,11 +3997,13 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         const u32 grid = rows * per_row > split_items ? rows * per_row : split_items;
         float* ro = renorm_out ? renorm_out + (size_t)c0 * V : nullptr;
         const int rc =
-            logits ? (vec == 4 ? launch_chunk<4, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
-                               : launch_chunk<1, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0))
-            : vec == 8 ? launch_chunk<8, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
-            : vec == 4 ? launch_chunk<4, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0)
-                       : launch_chunk<1, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0);
+            logits ? (vec == 4 ? launch_chunk<4, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab,
+                                                       c0, spec)
+                               : launch_chunk<1, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab,
+                                                       c0, spec))
+            : vec == 8 ? launch_chunk<8, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0, spec)
+            : vec == 4 ? launch_chunk<4, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0, spec)
+                       : launch_chunk<1, false>(s, p, st, grid, rows, (u32)V, nvec, ro, slab, c0, spec);
         if (rc != TES_OK) return rc;
     }
     return TES_OK;
@@ -3838,6 +4137,30 @@ extern "C" int topk_topp_sample_logits(tes_sampler* s, const float* logits, int 
                                        float* renorm_out, void* stream) {
     return sample_impl(s, logits, false, B, V, top_k, top_p, seed, offset, out_tokens, renorm_out,
                        nullptr, stream, true, temperature, min_p);
+}
+
+extern "C" int spec_verify_sample(tes_sampler* s, const float* target_probs, int N, int Lt,
+                                  int V, const int32_t* top_k, const float* top_p,
+                                  const float* draft_probs, int L, const int32_t* draft_tokens,
+                                  const int32_t* target_map, uint64_t seed, uint64_t offset,
+                                  int32_t* out_tokens, int32_t* accept_len, void* stream) {
+    if (!s || N < 0 || Lt < 1 || V < 1 || L < 0 || L > 63) return TES_ERR_INVALID_ARGUMENT;
+    if (!target_map && Lt < L + 1) return TES_ERR_INVALID_ARGUMENT;
+    if ((int64_t)N * Lt > s->max_batch || V > s->max_vocab) return TES_ERR_TOO_LARGE;
+    if (N == 0) return TES_OK;
+    if (!out_tokens || !accept_len || (L > 0 && (!draft_probs || !draft_tokens)))
+        return TES_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)out_tokens & 3) || ((uintptr_t)accept_len & 3) ||
+        ((uintptr_t)draft_tokens & 3) || ((uintptr_t)target_map & 3))
+        return TES_ERR_INVALID_ARGUMENT;
+    // The verification reads draft rows with the target rows' vector width.
+    const bool t16 = ((uintptr_t)target_probs & 15) == 0 && V % 4 == 0;
+    const bool d16 = ((uintptr_t)draft_probs & 15) == 0;
+    if (L > 0 && t16 && !d16) return TES_ERR_INVALID_ARGUMENT;
+    if (L > 0 && ((uintptr_t)draft_probs & 3)) return TES_ERR_INVALID_ARGUMENT;
+    SpecArgs a{draft_probs, draft_tokens, target_map, out_tokens, accept_len, (u32)L, (u32)Lt};
+    return sample_impl(s, target_probs, false, N * Lt, V, top_k, top_p, seed, offset, nullptr,
+                       nullptr, nullptr, stream, false, nullptr, nullptr, &a);
 }
 
 extern "C" int topk_topp_sample_bf16(tes_sampler* s, const uint16_t* probs, int B, int V,

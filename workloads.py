@@ -27,7 +27,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "CONFIGS", "make", "make_logits", "softmax64", "sha256_of"]
+__all__ = ["Workload", "SpecWorkload", "CONFIGS", "make", "make_logits", "make_spec",
+           "softmax64", "sha256_of"]
 
 
 @dataclass
@@ -208,6 +209,45 @@ def make_logits(cfg: int) -> Workload:
     w.temperature = tau
     w.min_p = mp
     return w
+
+
+@dataclass
+class SpecWorkload:
+    name: str
+    target: np.ndarray        # float32 [N * Lt][V] target probabilities
+    top_k: np.ndarray         # int32 [N * Lt]
+    top_p: np.ndarray         # float32 [N * Lt]
+    draft: np.ndarray         # float32 [N * L][V] draft probabilities
+    draft_tokens: np.ndarray  # int32 [N][L]
+    Lt: int
+    seed: int
+    offset: int
+
+
+def make_spec(cfg: int = 5, L: int = 7, sigma: float = 0.5) -> SpecWorkload:
+    """Speculative-verification inputs on config ``cfg``'s rows: each request
+    owns L + 1 consecutive target rows (its draft positions and the bonus
+    position).  The draft distribution of position l is a perturbed copy of
+    its target row, softmax(log p + sigma * N(0, 1)) in float64, cast to fp32,
+    and the draft token is drawn from it; both from a generator seeded
+    seed + 104729.  (Config 5, 512 rows, is 64 requests of 7 drafts.)"""
+    w = CONFIGS[cfg]()
+    Lt = L + 1
+    N = w.B // Lt
+    rng = np.random.default_rng(w.seed + 104729)
+    V = w.V
+    draft = np.empty((N * L, V), np.float32)
+    toks = np.empty((N, L), np.int32)
+    for n in range(N):
+        lp = np.log(np.maximum(w.probs[n * Lt:n * Lt + L].astype(np.float64), 1e-300))
+        q = softmax64(lp + sigma * rng.standard_normal((L, V)))
+        draft[n * L:(n + 1) * L] = q.astype(np.float32)
+        for l in range(L):
+            toks[n, l] = rng.choice(V, p=q[l] / q[l].sum())
+    rows = N * Lt
+    return SpecWorkload("spec_%s_L%d" % (w.name, L), np.ascontiguousarray(w.probs[:rows]),
+                        w.top_k[:rows].copy(), w.top_p[:rows].copy(), draft, toks, Lt, w.seed,
+                        w.offset)
 
 
 def sha256_of(w: Workload) -> str:
