@@ -92,38 +92,35 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, min_wall=10.0, max_reps=40, single_wall=3.0):
+def cpu_baseline(name, B, call, min_wall=10.0, max_reps=40, single_wall=3.0):
     """The oracle as it stands, on every host core this process may use (rows
     split statically across threads), plus a one-thread figure on a bounded
-    prefix of the same batch."""
-    import oracle
-
-    orc = oracle.load()
+    prefix of the same batch.  call(lo, hi, n_threads, offset) runs the
+    oracle on rows (or requests) [lo, hi)."""
     cores = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
     while True:
-        orc.sample(w.probs, w.top_k, w.top_p, w.seed, w.offset + reps, n_threads=cores)
+        call(0, B, cores, reps)
         reps += 1
         wall = time.perf_counter() - t0
         if wall >= min_wall or reps >= max_reps:
             break
     # One thread: rows in batch order until ~single_wall seconds have passed.
     rows1, t1 = 0, time.perf_counter()
-    while rows1 < w.B:
-        n = min(8, w.B - rows1)
-        orc.sample(w.probs[rows1:rows1 + n], w.top_k[rows1:rows1 + n],
-                   w.top_p[rows1:rows1 + n], w.seed, w.offset, n_threads=1)
+    while rows1 < B:
+        n = min(8, B - rows1)
+        call(rows1, rows1 + n, 1, 0)
         rows1 += n
         if time.perf_counter() - t1 >= single_wall:
             break
     wall1 = time.perf_counter() - t1
     return {
-        "value": round(reps * w.B / wall, 1),
+        "value": round(reps * B / wall, 1),
         "unit": "rows/s",
         "cores": cores,
         "kind": "oracle",
         "sample": "%d full passes over all %d rows of %s (stable sort per row, %d host threads, "
-                  "%.1f s)" % (reps, w.B, w.name, cores, wall),
+                  "%.1f s)" % (reps, B, name, cores, wall),
         "cpu_model": cpu_model(),
         "single_thread_rows_per_s": round(rows1 / wall1, 1),
         "single_thread_sample": "first %d rows of the batch on one thread (%.1f s)" % (rows1, wall1),
@@ -192,9 +189,14 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--copies", type=int, default=4, help="rotating input copies (> MALL)")
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
                     help="input recipe (workloads.py); 3, the heterogeneous B=256, V=151,936 "
-                         "batch, is the headline")
+                         "batch, is the headline (5 for --mode spec)")
+    ap.add_argument("--mode", choices=["probs", "logits", "spec"], default="probs",
+                    help="probs: topk_topp_sample (the headline); logits: "
+                         "topk_topp_sample_logits on the recipe's logits with per-row "
+                         "temperature and min-p; spec: spec_verify_sample, requests of 7 drafts "
+                         "and 8 target rows over the recipe's rows")
     ap.add_argument("--input-dtype", choices=["fp32", "bf16"], default="fp32",
                     help="row format: fp32 (the headline) or bf16 (topk_topp_sample_bf16, "
                          "the same rows rounded to bf16)")
@@ -221,9 +223,23 @@ def main():
     import top_exact_sampling_amd as tes
     import workloads
 
-    w = workloads.make(args.workload)
-    B, V = w.B, w.V
+    if args.workload is None:
+        args.workload = 5 if args.mode == "spec" else 3
+    import oracle
+
     bf16 = args.input_dtype == "bf16"
+    if bf16 and args.mode != "probs":
+        raise SystemExit("--input-dtype bf16 applies to --mode probs only")
+    if args.mode == "spec":
+        sw = workloads.make_spec(args.workload)
+        w = workloads.make(args.workload)  # the target rows (same inputs)
+        B = sw.target.shape[0]
+        w.probs, w.top_k, w.top_p = sw.target, sw.top_k, sw.top_p
+    elif args.mode == "logits":
+        w = workloads.make_logits(args.workload)
+    else:
+        w = workloads.make(args.workload)
+    B, V = w.B, w.V
     if bf16:
         # The same rows rounded to bf16; the oracle reads their exact fp32
         # widening, which is what a bf16 entry means to the sampler.
@@ -247,12 +263,57 @@ def main():
     out = torch.empty(B, dtype=torch.int32, device=dev)
     ren = torch.empty((B, V), dtype=torch.float32, device=dev) if args.renorm else None
     stream = torch.cuda.current_stream(dev)
+    orc = oracle.load()
 
     # Call i draws with Philox offset w.offset + i, as a decode loop advances
     # it, so that draw-dependent paths are sampled rather than one fixed draw.
-    def step(i, st=None):
-        sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i, out_tokens=out,
-                       renorm_out=ren, stream=stream if st is None else st)
+    if args.mode == "probs":
+        def step(i, st=None):
+            sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i,
+                           out_tokens=out, renorm_out=ren, stream=stream if st is None else st)
+
+        def oracle_call(lo, hi, nt, off):
+            return orc.sample(w.probs[lo:hi], w.top_k[lo:hi], w.top_p[lo:hi], w.seed,
+                              w.offset + off, n_threads=nt)[0]
+    elif args.mode == "logits":
+        tau = torch.from_numpy(w.temperature).to(dev)
+        mp = torch.from_numpy(w.min_p).to(dev)
+
+        def step(i, st=None):
+            sampler.sample_logits(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i,
+                                  temperature=tau, min_p=mp, out_tokens=out, renorm_out=ren,
+                                  stream=stream if st is None else st)
+
+        def oracle_call(lo, hi, nt, off):
+            return orc.sample_logits(w.probs[lo:hi], w.top_k[lo:hi], w.top_p[lo:hi],
+                                     w.temperature[lo:hi], w.min_p[lo:hi], w.seed,
+                                     w.offset + off, n_threads=nt)[0]
+    else:
+        if args.renorm:
+            raise SystemExit("--renorm does not apply to --mode spec")
+        Lt = sw.Lt
+        N = B // Lt
+        L = sw.draft_tokens.shape[1]
+        draft = torch.from_numpy(sw.draft).to(dev)
+        dtok = torch.from_numpy(sw.draft_tokens).to(dev)
+        sout = torch.empty((N, L + 1), dtype=torch.int32, device=dev)
+        sacc = torch.empty(N, dtype=torch.int32, device=dev)
+
+        def step(i, st=None):
+            rc = tes.spec_verify_sample(sampler.handle, probs[i % args.copies].data_ptr(), N, Lt,
+                                        V, top_k.data_ptr(), top_p.data_ptr(), draft.data_ptr(),
+                                        L, dtok.data_ptr(), None, w.seed, w.offset + i,
+                                        sout.data_ptr(), sacc.data_ptr(),
+                                        (stream if st is None else st).cuda_stream)
+            if rc != 0:
+                raise RuntimeError("spec_verify_sample failed: %d" % rc)
+
+        def oracle_call(lo, hi, nt, off):
+            r0, r1 = lo // Lt * Lt, -(-hi // Lt) * Lt
+            n0, n1 = r0 // Lt, r1 // Lt
+            return orc.spec_verify(sw.target[r0:r1], Lt, sw.top_k[r0:r1], sw.top_p[r0:r1],
+                                   sw.draft[n0 * L:n1 * L], sw.draft_tokens[n0:n1], None, w.seed,
+                                   w.offset + off, n_threads=nt)
 
     for i in range(args.warmup):
         step(i)
@@ -297,24 +358,34 @@ def main():
                            for j in range(max(0, args.repeats - 1))]
     kern_med = sorted(reps_ms)[len(reps_ms) // 2]
 
-    # Algorithmic bytes: the rows once, top_k, top_p and the token, plus the
-    # dense renorm_out write when requested.
-    alg_bytes = B * V * esize + 12 * B + (B * V * 4 if args.renorm else 0)
-    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-
+    # Algorithmic bytes: the rows once, top_k, top_p and the token (and the
+    # temperature and min-p of logit rows), plus the dense renorm_out write
+    # when requested.  Speculative verification: the target rows once, the
+    # drafts' 4-byte lookups, and for each request with a rejection its
+    # draft row and target row once more (the correction's residual); the
+    # rejections are counted on the call checked below.
+    per_row = {"probs": 12, "logits": 20, "spec": 12}[args.mode]
+    alg_bytes = B * V * esize + per_row * B + (B * V * 4 if args.renorm else 0)
     parity = None
-    if not args.no_parity:
-        import oracle
-
-        step(0)
-        torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    if args.mode == "spec":
+        oout, oacc = oracle_call(0, B, len(os.sched_getaffinity(0)), 0)
+        rejected = int((oacc < L).sum())
+        alg_bytes += N * L * 12 + rejected * 2 * V * 4
+        if not args.no_parity:
+            same = np.array_equal(sout.cpu().numpy(), oout) and np.array_equal(sacc.cpu().numpy(),
+                                                                               oacc)
+            parity = "bit-exact" if same else "MISMATCH"
+    elif not args.no_parity:
+        otok = oracle_call(0, B, len(os.sched_getaffinity(0)), 0)
         gtok = out.cpu().numpy()
-        otok, _, _ = oracle.load().sample(w.probs, w.top_k, w.top_p, w.seed, w.offset)
         parity = "bit-exact" if np.array_equal(gtok, otok) else \
             "MISMATCH on %d rows" % int((gtok != otok).sum())
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
-    traffic = traffic_from_profile() if args.workload == 3 and not bf16 and not args.renorm \
-        else None
+    traffic = traffic_from_profile() if (args.workload == 3 and not bf16 and not args.renorm
+                                         and args.mode == "probs") else None
     line = {
         "metric": METRIC,
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -332,12 +403,20 @@ def main():
             "workload": w.name,
             "B": B,
             "V": V,
-            "row_mix": ROW_MIX[args.workload],
-            "input": INPUT[args.workload] + (", rounded to bf16" if bf16 else ""),
+            "mode": args.mode,
+            "row_mix": ROW_MIX[args.workload] + (
+                "; temperature ~U[0.5,1.5] (5% 0, 5% 1), min_p 0 on half the rows else "
+                "~U[0.005,0.3]" if args.mode == "logits" else "") + (
+                "; %d requests of %d drafts, %d target rows each, draft rows "
+                "softmax(log p + 0.5 N(0,1))" % (B // sw.Lt, sw.Lt - 1, sw.Lt)
+                if args.mode == "spec" else ""),
+            "input": (INPUT[args.workload] + (", rounded to bf16" if bf16 else "")) if
+            args.mode != "logits" else "fp32 logits of the same recipe, before the softmax",
             "input_dtype": args.input_dtype,
             "renorm_out": "dense [B][V] fp32" if args.renorm else None,
             "arithmetic": "u32 keys, u64 fixed-point masses, u128 products (integer decisions)",
-            "input_sha256": workloads.sha256_of(w),
+            "input_sha256": workloads.sha256_of(w) if args.mode != "spec" else
+            workloads.sha256_of(w) + "+draft",
             "input_copies_rotated": args.copies,
             "kernel_ms_hip_events": round(kern_ms, 5),
             "kernel_ms_repeats": [round(x, 5) for x in reps_ms],
@@ -358,7 +437,7 @@ def main():
             "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE summary committed under "
                                "profiles/ for this kernel source hash") if traffic else None,
         },
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(w),
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(w.name, B, oracle_call),
     }
     sampler.close()
     print(json.dumps(line), flush=True)

@@ -145,6 +145,7 @@ struct PubC {  // first exchange of a top-p-only segment (and its gather count)
     u64 M;
     u64 ninf;
     u64 ng;      // entries gathered for the final selects (written last)
+    u64 mf;      // logit rows with a min-p floor: mass of the entries at or above it
     u64 coarse[kCoarseBins];
 };
 struct PubF {  // second exchange: fine bins of the listed coarse bins
@@ -271,7 +272,7 @@ struct Smem {
     Params p;                  // this launch's parameters (copied from the kernel arguments)
     alignas(16) unsigned char region[kRegionBytes];
     u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
-    u64 csum[2];               // summed mass and +inf count of a top-p-only row
+    u64 csum[3];               // summed mass, +inf count and min-p mass of a top-p-only row
     u64 loc_above[4];          // results of the bin lookups (coarse and fine plans, fine_locate)
     int loc_bin[4];
     u32 gn[kMaxSegWs];         // entries each segment of a top-p-only row gathered
@@ -1037,6 +1038,41 @@ __device__ __forceinline__ RowXf row_xf(const Params& p, u32 r) {
         t.wtop = __uint_as_float(uni(__float_as_uint(t.wtop)));
     }
     return t;
+}
+
+// Order-preserving u32 encoding of fp32 values (sign bit set for
+// non-negative values, all bits inverted for negative ones) and its inverse.
+__device__ __forceinline__ u32 ord_enc(float x) {
+    const u32 b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float ord_dec(u32 e) {
+    return __uint_as_float((e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e);
+}
+
+// The smallest logit x <= M (in value order) whose weight's bits are at least
+// wkey - 1, for 2 <= wkey <= the bits of the row's top weight.  The fp32
+// exponential is monotone up to one ulp (its value never falls more than one
+// ulp below its value at any smaller argument, checked over every argument),
+// so every logit whose weight reaches wkey is >= this x: the streams test the
+// raw logits against it and compute weights only for those that pass.  One
+// wave, 64 candidates per round (six rounds for 32 bits); all lanes of the
+// wave take part and get the same result.
+__device__ __noinline__ float logit_x_threshold(const RowXf& t, u32 wkey) {
+    u32 lo = ord_enc(__uint_as_float(0xFF800000u));  // -inf: weight 0, fails
+    u32 hi = ord_enc(t.M);                           // M: the top weight, passes
+    const u32 lane = lane_id();
+    while (hi - lo > 1u) {
+        const u32 step = (hi - lo + 63u) / 64u;
+        const u32 e = min(lo + (lane + 1u) * step, hi);
+        const bool pass = __float_as_uint(logit_weight(t, ord_dec(e))) >= wkey - 1u;
+        const u64 m = __ballot(pass) | (1ull << 63);  // lane 63 reaches hi
+        const u32 L = (u32)__builtin_ctzll(m);
+        const u32 nhi = min(lo + (L + 1u) * step, hi);
+        lo = L ? min(lo + L * step, hi) : lo;
+        hi = nhi;
+    }
+    return ord_dec(hi);
 }
 
 // Row data is read once: non-temporal loads keep it from displacing the
@@ -2052,51 +2088,84 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     const u32 nv = min(v0 + hv, p.nvec) - v0;
     const float* part =
         reinterpret_cast<const float*>(reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, p.V)) + v0);
-    // The largest bits as signed integers: non-negative floats order as their
-    // bits, negative ones (which count as zero) lie below all of them and NaN
-    // bits above +inf.  Each lane keeps the first of its vectors holding its
-    // largest value; the part's smallest index holding the maximum comes from
-    // reloading those vectors afterwards.
-    int best = kIntMin;
-    u32 bvec = 0;
-    auto vmax = [&](const VT& x, u32 iv, bool valid) {
-        int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
-#pragma unroll
-        for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
-        const bool up = valid && mx > best;
-        best = up ? mx : best;
-        bvec = up ? iv : bvec;
-    };
-    // A greedy row needs almost no work after its stream, so when it shares
-    // the device with rows that do (top-k finishes, top-p exchanges), it
-    // keeps only two loads in flight: its share of the bandwidth goes to those
-    // rows, which then finish earlier, and it still ends before them.
-    if (yield)
-        for_each_vec<VEC, kGreedyYieldDepth, LG>(part, nv, vmax, xf);
-    else
-        for_each_vec<VEC, kStreamDepth, LG>(part, nv, vmax, xf);
-    const int K = (int)((u32)block_max(s, (u64)((u32)best ^ 0x80000000u)) ^ 0x80000000u);
     u64 cbest;
-    if (K > (int)kInfKey) {
-        // NaN bits are the largest: take the exact maximum of the composites.
-        u64 b = 0;
-        for_each_entry<VEC, LG>(part, nv, [&](u32 key, u32 idx, bool valid) {
-            const u64 c = valid ? composite(key, v0 * VEC + idx) : 0ull;
-            b = c > b ? c : b;
-        }, xf);
-        cbest = block_max(s, b);
-    } else if (K <= 0) {
-        cbest = composite(0u, v0 * VEC);  // every entry counts as zero: the smallest index
-    } else {
-        u64 idx = ~0ull;
-        if (best == K) {
-            const VT x = xform<VEC, LG>(xf, ld_g(&reinterpret_cast<const VT*>(part)[bvec]));
+    if constexpr (LG) {
+        // Logit rows: the largest weight is the top weight (1 at the row
+        // maximum, +inf in rows with +inf logits) and the token is the
+        // smallest index whose weight equals it.  Those entries are among
+        // the logits >= x1; only their weights are computed.  A row with
+        // every logit masked (no entry passes) has only zero weights: its
+        // smallest index.
+        const u32 wtop = __float_as_uint(xf.wtop);
+        const float x1 = logit_x_threshold(xf, wtop);
+        u64 bidx = ~0ull;
+        auto vfind = [&](const VT& x, u32 iv, bool valid) {
+            float mx = VecT<VEC>::get(x, 0);
 #pragma unroll
-            for (int e = VEC - 1; e >= 0; --e)
-                if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K)
-                    idx = (u64)(v0 + bvec) * VEC + e;
+            for (int e = 1; e < VEC; ++e) mx = fmaxf(mx, VecT<VEC>::get(x, e));
+            if (valid && mx >= x1) {
+#pragma unroll
+                for (int e = VEC - 1; e >= 0; --e) {
+                    const float xv = VecT<VEC>::get(x, e);
+                    if (xv >= x1 && __float_as_uint(logit_weight(xf, xv)) == wtop) {
+                        const u64 i = (u64)(v0 + iv) * VEC + e;
+                        bidx = i < bidx ? i : bidx;
+                    }
+                }
+            }
+        };
+        if (yield)
+            for_each_vec<VEC, kGreedyYieldDepth>(part, nv, vfind);
+        else
+            for_each_vec<VEC, kStreamDepth>(part, nv, vfind);
+        const u64 idx = block_min(s, bidx);
+        cbest = idx == ~0ull ? composite(0u, v0 * VEC) : composite(wtop, (u32)idx);
+    } else {
+        // The largest bits as signed integers: non-negative floats order as their
+        // bits, negative ones (which count as zero) lie below all of them and NaN
+        // bits above +inf.  Each lane keeps the first of its vectors holding its
+        // largest value; the part's smallest index holding the maximum comes from
+        // reloading those vectors afterwards.
+        int best = kIntMin;
+        u32 bvec = 0;
+        auto vmax = [&](const VT& x, u32 iv, bool valid) {
+            int mx = (int)__float_as_uint(VecT<VEC>::get(x, 0));
+#pragma unroll
+            for (int e = 1; e < VEC; ++e) mx = max(mx, (int)__float_as_uint(VecT<VEC>::get(x, e)));
+            const bool up = valid && mx > best;
+            best = up ? mx : best;
+            bvec = up ? iv : bvec;
+        };
+        // A greedy row needs almost no work after its stream, so when it shares
+        // the device with rows that do (top-k finishes, top-p exchanges), it
+        // keeps only two loads in flight: its share of the bandwidth goes to those
+        // rows, which then finish earlier, and it still ends before them.
+        if (yield)
+            for_each_vec<VEC, kGreedyYieldDepth, LG>(part, nv, vmax, xf);
+        else
+            for_each_vec<VEC, kStreamDepth, LG>(part, nv, vmax, xf);
+        const int K = (int)((u32)block_max(s, (u64)((u32)best ^ 0x80000000u)) ^ 0x80000000u);
+        if (K > (int)kInfKey) {
+            // NaN bits are the largest: take the exact maximum of the composites.
+            u64 b = 0;
+            for_each_entry<VEC, LG>(part, nv, [&](u32 key, u32 idx, bool valid) {
+                const u64 c = valid ? composite(key, v0 * VEC + idx) : 0ull;
+                b = c > b ? c : b;
+            }, xf);
+            cbest = block_max(s, b);
+        } else if (K <= 0) {
+            cbest = composite(0u, v0 * VEC);  // every entry counts as zero: the smallest index
+        } else {
+            u64 idx = ~0ull;
+            if (best == K) {
+                const VT x = xform<VEC, LG>(xf, ld_g(&reinterpret_cast<const VT*>(part)[bvec]));
+#pragma unroll
+                for (int e = VEC - 1; e >= 0; --e)
+                    if ((int)__float_as_uint(VecT<VEC>::get(x, e)) == K)
+                        idx = (u64)(v0 + bvec) * VEC + e;
+            }
+            cbest = composite((u32)K, (u32)block_min(s, idx));
         }
-        cbest = composite((u32)K, (u32)block_min(s, idx));
     }
     if (S > 1) {
         RowState* rs = ws_state(p, r);
@@ -2373,6 +2442,9 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         return;
     }
     const u32 span = kInfKey - tkey;
+    // Logit rows: the weights at or above tkey belong to logits >= xb.
+    float xb = 0.0f;
+    if constexpr (LG) xb = logit_x_threshold(xf, tkey);
     u64 tq = stat_phase(p, r, 11, tp);
     constexpr u32 kRegion = kSlabCap / kWaves;
     const u32 wave = uni(wave_id());
@@ -2383,15 +2455,27 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     // are below tkey has none; a wave with no such vector skips the rest.
     // (MASKED: lanes past the end of the part hold a copy of its last vector
     // and must append nothing.)
-    auto append = [&](auto masked, const VT& xraw, u32 iv) {
+    auto append = [&](auto masked, const VT& x, u32 iv) {
         constexpr bool kMasked = decltype(masked)::value;
-        const VT x = xform<VEC, LG>(xf, xraw);
         const bool valid = !kMasked || iv < nvec;
         static_assert(kFineShift == 16, "tkey is a multiple of 2^16");
-        if (__builtin_amdgcn_ballot_w64(valid & any_at_least<VEC>(x, (int)tkey)) == 0) return;
+        if constexpr (LG) {
+            // Raw logits first (NaN never passes); weights only for those
+            // at or above xb.
+            float mx = VecT<VEC>::get(x, 0);
+#pragma unroll
+            for (int e = 1; e < VEC; ++e) mx = fmaxf(mx, VecT<VEC>::get(x, e));
+            if (__builtin_amdgcn_ballot_w64(valid & (mx >= xb)) == 0) return;
+        } else {
+            if (__builtin_amdgcn_ballot_w64(valid & any_at_least<VEC>(x, (int)tkey)) == 0) return;
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+            u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+            if constexpr (LG) {
+                const float xv = VecT<VEC>::get(x, e);
+                b = xv >= xb ? __float_as_uint(logit_weight(xf, xv)) : 0u;
+            }
             // Passing bits are keys: no sanitising.
             const u64 m = __builtin_amdgcn_ballot_w64(valid & (b - tkey <= span));
             if (m) {
@@ -2798,7 +2882,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // Accumulators of the exchanges (ordered by the barriers below).
     for (int i = threadIdx.x; i < kCoarseBins; i += kBlock) s.coarse[i] = 0;
     for (int i = threadIdx.x; i < kDMax * 16; i += kBlock) s.finem[i] = 0;
-    if (threadIdx.x < 2) s.csum[threadIdx.x] = 0;
+    if (threadIdx.x < 3) s.csum[threadIdx.x] = 0;
     __syncthreads();
     if (threadIdx.x == 0) {
         u64& top = shfine(s)[kFineBins - 1];
@@ -2809,6 +2893,26 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     for (int i = threadIdx.x; i < kFineBins; i += kBlock) M += shfine(s)[i];
     M = block_sum(s, M);
     ninf = block_sum(s, ninf);
+    // Min-p on logit rows: the largest mass is that of the top weight 1
+    // (2^32), so the floor and its key are known before any exchange; each
+    // segment adds up the mass of its entries at or above the floor's key
+    // (the registers hold the weights).
+    u64 mf = 0;
+    float theta = 0.0f;
+    if constexpr (LG) theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
+    const u32 kf = minp_key(minp_floor(theta, 1ull << 32));
+    if (LG && kf > 1u) {
+#pragma unroll
+        for (int d = 0; d < kSlots<VEC>; ++d) {
+            const u32 i = v0 + d * kBlock + threadIdx.x;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
+                mf += (i < v1 && b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
+            }
+        }
+        mf = block_sum(s, mf);
+    }
     tp = stat_phase(p, r, 8, tp);
 
     // First exchange: this segment's mass, +inf count and coarse histogram.
@@ -2822,6 +2926,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if (threadIdx.x == 0) {
         st_dev(&pc->M, M);
         st_dev(&pc->ninf, ninf);
+        st_dev(&pc->mf, mf);
     }
     const bool ok = arrive_wait(s, &rs->arrive_a, nseg);
     tp = stat_phase(p, r, 9, tp);
@@ -2829,11 +2934,12 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // Every segment sums the exchange and takes the same decisions.  The
     // counter was acquired, so the published words are read with ordinary
     // loads that can be in flight together.
-    static_assert(sizeof(PubC) == 8 * (3 + kCoarseBins), "PubC is M, ninf, ng, coarse[]");
-    sum_words(reinterpret_cast<const u64*>(pub_c(p, r, 0)), sizeof(PubC) / 8, nseg, 3 + kCoarseBins,
+    static_assert(sizeof(PubC) == 8 * (4 + kCoarseBins), "PubC is M, ninf, ng, mf, coarse[]");
+    sum_words(reinterpret_cast<const u64*>(pub_c(p, r, 0)), sizeof(PubC) / 8, nseg, 4 + kCoarseBins,
               [&](u32 i, u64 v) {
                   if (i < 2) s.csum[i] = v;
-                  else if (i >= 3) s.coarse[i - 3] = v;
+                  else if (i == 3) s.csum[2] = v;
+                  else if (i >= 4) s.coarse[i - 4] = v;
               });
     __syncthreads();
     const u64 Mt = uni(s.csum[0]);
@@ -2841,7 +2947,13 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     const u32 kind = nit > 0 ? kInfRow : (Mt == 0 ? kZeroRow : kNormal);
-    const u64 T = kind == kNormal ? topp_threshold(P, Mt) : 0;
+    u64 T = kind == kNormal ? topp_threshold(P, Mt) : 0;
+    // Min-p: the kept set ends where the inclusive mass reaches min(T, the
+    // mass at or above the floor), which every later step takes as its T.
+    if (LG && kf > 1u) {
+        const u64 Mf = uni(s.csum[2]);
+        T = Mf < T ? Mf : T;
+    }
     int nlist = 0;
     bool decidable = ok;
     if (ok && kind == kNormal) {
@@ -3090,10 +3202,8 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
     }
     if (!fail && fb) stat_why(p, r, 32u);
     if (fb) {
-        // (Rows with a min-p floor never take this path: their class is the
-        // whole-row passes.)
         o = resolve_row<VEC, LG>(s, row_ptr<VEC>(p.probs, r, p.V), p.nvec, p.V, p.V, P, u, kSelCap,
-                                 row_xf<LG>(p, r), 0.0f);
+                                 row_xf<LG>(p, r), (LG && p.min_p) ? ld_g(&p.min_p[r]) : 0.0f);
         path = kPathFullFallback;
     } else if (kind == kNormal) {
         // decided above
@@ -3146,16 +3256,11 @@ __device__ __forceinline__ u32 row_k_eff(const Params& p, u32 r) {
     return (k <= 0 || (u32)k >= p.V) ? p.V : (u32)k;
 }
 
-// Top-p-only rows with a min-p floor (theta > 0) are decided by the whole-row
-// passes: the exchanged histograms of the segments locate the top-p boundary
-// by mass only.
-template <bool LG>
-__device__ __forceinline__ u32 row_class(const Params& p, u32 r, u32 k_eff, u32 s_full) {
+__device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full) {
     if (p.flags & TES_FLAG_FORCE_ROW_SELECT) return kClsWhole;
     if (k_eff == 1) return kClsGreedy;
     if (k_eff <= kSlabMaxK) return kClsSlab;
-    if (k_eff == p.V && s_full <= p.s_ws && !(LG && p.min_p && ld_g(&p.min_p[r]) > 0.0f))
-        return kClsFull;
+    if (k_eff == p.V && s_full <= p.s_ws) return kClsFull;
     return kClsWhole;
 }
 
@@ -3182,7 +3287,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     for (int j = 0; j < 2; ++j) {
         const u32 r = r0 + j;
         const u32 ke = r < p.rows ? row_k_eff(p, r) : 0u;
-        cls[j] = r < p.rows ? row_class<LG>(p, r, ke, s_full) : 4u;
+        cls[j] = r < p.rows ? row_class(p, ke, s_full) : 4u;
         if (cls[j] == kClsSlab) s.slab_k[r] = (u16)ke;
         if (cls[j] < 4) local += 1ull << (16 * cls[j]);
     }
