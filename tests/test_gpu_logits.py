@@ -37,6 +37,7 @@ def samplers(torch_cuda):
         "tiny_buffer": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_TINY_BUFFER),
         "small_segments": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS),
         "no_wait": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_NO_WAIT),
+        "row_topp": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_ROW_TOPP),
     }
     yield out
     for s in out.values():
@@ -105,7 +106,8 @@ def test_logit_config_parity(samplers, orc, torch_cuda, cfg, renorm):
                                               np.bincount(st[:, 1], minlength=3).tolist()))
 
 
-@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "small_segments", "no_wait"])
+@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "small_segments", "no_wait",
+                                     "row_topp"])
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_logit_forced_paths(samplers, orc, torch_cuda, variant, cfg):
     w = wl(cfg)
@@ -172,7 +174,7 @@ def _edge_logit_batch(V, rng):
 def test_logit_edge_rows(samplers, orc, torch_cuda, V):
     rng = np.random.default_rng(V + 101)
     x, ks, ps, taus, mps = _edge_logit_batch(V, rng)
-    for which in ("plain", "row_select", "tiny_buffer", "small_segments"):
+    for which in ("plain", "row_select", "tiny_buffer", "small_segments", "row_topp"):
         log("[gpu] logit edge rows V=%d rows=%d sampler=%s" % (V, len(ks), which))
         gtok, gren = run_logits(torch_cuda, samplers[which], x, ks, ps, taus, mps, 11, 5)
         assert_logit_parity(orc, x, ks, ps, taus, mps, 11, 5, gtok, gren,
@@ -212,7 +214,7 @@ def test_logit_min_p_binds_on_every_path(samplers, orc, torch_cuda):
     ps = np.full(B, 1.0, np.float32)
     taus = rng.uniform(0.7, 1.3, B).astype(np.float32)
     mps = rng.uniform(0.02, 0.4, B).astype(np.float32)
-    for which in ("plain", "tiny_buffer", "stats"):
+    for which in ("plain", "tiny_buffer", "stats", "row_topp"):
         log("[gpu] min-p binding rows sampler=%s" % which)
         gtok, gren = run_logits(torch_cuda, samplers[which], x, ks, ps, taus, mps, 21, 0)
         assert_logit_parity(orc, x, ks, ps, taus, mps, 21, 0, gtok, gren,

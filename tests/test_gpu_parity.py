@@ -51,6 +51,9 @@ def variant_samplers(torch_cuda):
         "small_segments": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS),
         "small_tiny": tes.Sampler(
             0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS | tes.TES_FLAG_TINY_BUFFER),
+        "row_topp": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_ROW_TOPP | tes.TES_FLAG_STATS),
+        "row_topp_tiny": tes.Sampler(
+            0, 4096, 1 << 18, tes.TES_FLAG_ROW_TOPP | tes.TES_FLAG_TINY_BUFFER),
     }
     yield out
     for s in out.values():
@@ -99,7 +102,8 @@ def test_config_parity_tokens_only(sampler, plain_sampler, orc, cfg, which):
 
 
 @pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "row_select_tiny",
-                                     "small_segments", "small_tiny"])
+                                     "small_segments", "small_tiny", "row_topp",
+                                     "row_topp_tiny"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_forced_paths_agree(variant_samplers, orc, variant, cfg):
     w = wl(cfg)
@@ -188,14 +192,16 @@ def test_adversarial_rows(sampler, variant_samplers, orc, V):
     for label, s in (("default", sampler), ("row_select", variant_samplers["row_select"]),
                      ("tiny_buffer", variant_samplers["tiny_buffer"]),
                      ("small_segments", variant_samplers["small_segments"]),
-                     ("small_tiny", variant_samplers["small_tiny"])):
+                     ("small_tiny", variant_samplers["small_tiny"]),
+                     ("row_topp", variant_samplers["row_topp"]),
+                     ("row_topp_tiny", variant_samplers["row_topp_tiny"])):
         log("[gpu] adversarial V=%d rows=%d sampler=%s" % (V, len(names), label))
         gtok, gren = run_gpu(s, probs, ks, ps, 9, 3, renorm=True)
         assert_parity(orc, probs, ks, ps, 9, 3, gtok, gren, "adversarial V=%d %s" % (V, label))
 
 
 @pytest.mark.parametrize("V", [1, 2, 3, 7, 999, 1000, 1024, 1025, 4097, 8191, 8192, 8193, 40000])
-def test_ragged_vocab_sizes(sampler, orc, V):
+def test_ragged_vocab_sizes(sampler, variant_samplers, orc, V):
     rng = np.random.default_rng(V + 17)
     B = 24
     x = 2.0 * rng.standard_normal((B, V))
@@ -205,9 +211,11 @@ def test_ragged_vocab_sizes(sampler, orc, V):
     ks = rng.integers(-2, V + 3, size=B).astype(np.int32)
     ks[:4] = [1, V, 0, 1024]
     ps = rng.uniform(0.3, 1.0, size=B).astype(np.float32)
-    log("[gpu] ragged V=%d" % V)
-    gtok, gren = run_gpu(sampler, probs, ks, ps, 3, 11, renorm=True)
-    assert_parity(orc, probs, ks, ps, 3, 11, gtok, gren, "ragged V=%d" % V)
+    for label in ("default", "row_topp"):
+        s = sampler if label == "default" else variant_samplers[label]
+        log("[gpu] ragged V=%d sampler=%s" % (V, label))
+        gtok, gren = run_gpu(s, probs, ks, ps, 3, 11, renorm=True)
+        assert_parity(orc, probs, ks, ps, 3, 11, gtok, gren, "ragged V=%d %s" % (V, label))
 
 
 def test_unaligned_rows_use_scalar_path(sampler, orc, torch_cuda):
@@ -450,6 +458,35 @@ def test_wide_topp_bins_stay_on_the_fast_path(sampler, orc):
     assert np.all(st[:, 0] == 1), "rows left the fast path: %s" % np.flatnonzero(st[:, 0] != 1)
 
 
+def test_oversubscribed_topp_rows_take_the_row_path(sampler, variant_samplers, orc):
+    # The speculative-verify shape holds more top-p-only segments than the
+    # device keeps resident workgroups: its top-p-only rows are decided by
+    # one workgroup each (path 6) without exchanges, and agree with the
+    # oracle at two offsets; the same rows through the forced flag agree
+    # with the segmented path's tokens.
+    w = wl(5)
+    topp = np.flatnonzero((w.top_k <= 0) | (w.top_k >= w.V))
+    for off in (w.offset, w.offset + 5):
+        log("[gpu] oversubscribed top-p rows offset %d" % off)
+        gtok, gren = run_gpu(sampler, w.probs, w.top_k, w.top_p, w.seed, off, renorm=True)
+        st = sampler.stats(w.B)
+        log("[gpu]   paths %s gathered max %d passes max %d" % (
+            np.bincount(st[:, 0], minlength=7).tolist(), st[topp, 4].max(), st[topp, 3].max()))
+        assert_parity(orc, w.probs, w.top_k, w.top_p, w.seed, off, gtok, gren,
+                      "oversubscribed offset %d" % off)
+        assert np.all(st[topp, 2] == 1), "top-p-only rows were segmented"
+        assert np.mean(st[topp, 0] == 6) >= 0.95, np.bincount(st[topp, 0], minlength=7)
+    rows = topp[:48]
+    probs = np.ascontiguousarray(w.probs[rows])
+    log("[gpu] forced row path on %d top-p-only rows" % rows.size)
+    gtok, gren = run_gpu(variant_samplers["row_topp"], probs, w.top_k[rows], w.top_p[rows],
+                         w.seed, w.offset, renorm=True)
+    st = variant_samplers["row_topp"].stats(rows.size)
+    assert_parity(orc, probs, w.top_k[rows], w.top_p[rows], w.seed, w.offset, gtok, gren,
+                  "forced row path")
+    assert np.all(st[:, 2] == 1) and np.mean(st[:, 0] == 6) >= 0.95, st[:, 0]
+
+
 def test_batches_longer_than_one_launch(sampler, orc):
     # More rows than one launch takes (1024): the call enqueues several
     # launches, each with its own row offset for the Philox counter, mixing
@@ -468,7 +505,7 @@ def test_batches_longer_than_one_launch(sampler, orc):
 
 
 @pytest.mark.parametrize("trial", range(6))
-def test_random_shapes(sampler, orc, trial):
+def test_random_shapes(sampler, variant_samplers, orc, trial):
     # Random batch and vocabulary sizes, row recipes and parameters, including
     # out-of-range k and p.
     rng = np.random.default_rng(1000 + trial)
@@ -485,9 +522,12 @@ def test_random_shapes(sampler, orc, trial):
     ks[rng.random(B) < 0.3] = 1
     ps = rng.uniform(-0.2, 1.3, size=B).astype(np.float32)
     seed, off = (int(v) for v in rng.integers(0, 2**63, size=2))
-    log("[gpu] random shapes trial %d B=%d V=%d" % (trial, B, V))
-    gtok, gren = run_gpu(sampler, probs, ks, ps, seed, off, renorm=True)
-    assert_parity(orc, probs, ks, ps, seed, off, gtok, gren, "random trial %d" % trial)
+    for label in ("default", "row_topp"):
+        s = sampler if label == "default" else variant_samplers[label]
+        log("[gpu] random shapes trial %d B=%d V=%d sampler=%s" % (trial, B, V, label))
+        gtok, gren = run_gpu(s, probs, ks, ps, seed, off, renorm=True)
+        assert_parity(orc, probs, ks, ps, seed, off, gtok, gren,
+                      "random trial %d %s" % (trial, label))
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 4])
@@ -566,8 +606,9 @@ def test_wide_draw_ranges_stay_on_the_fast_path(sampler, orc):
     # Top-p-only rows whose few large entries sit many octaves above the
     # bulk: before the boundary is known, a draw can fall anywhere from the
     # large entries down to the bulk, a range of up to ~150 coarse bins that
-    # are almost all empty.  Only the bins with mass are exchanged, so these
-    # rows stay on the segment path.
+    # are almost all empty.  Only the bins with mass are exchanged (or, in
+    # the one-workgroup row path this batch takes, listed), so these rows
+    # stay on a fast path.
     B, V = 256, 151936
     rng = np.random.default_rng(4242)
     probs = np.empty((B, V), np.float32)
@@ -587,8 +628,9 @@ def test_wide_draw_ranges_stay_on_the_fast_path(sampler, orc):
         st = sampler.stats(B)
         log("[gpu]   paths %s" % np.bincount(st[:, 0], minlength=6).tolist())
         assert_parity(orc, probs, ks, ps, 77, off, gtok, gren, "wide draw ranges %d" % off)
-        assert np.all(st[:, 0] == 1), "rows left the fast path: %s (why %s)" % (
-            np.flatnonzero(st[:, 0] != 1), st[st[:, 0] != 1, 7])
+        slow = ~np.isin(st[:, 0], (1, 6))
+        assert not slow.any(), "rows left the fast path: %s (why %s)" % (
+            np.flatnonzero(slow), st[slow, 7])
 
 
 def test_exchange_timeout_fallback(orc, torch_cuda):

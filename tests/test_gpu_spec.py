@@ -33,6 +33,7 @@ def samplers(torch_cuda):
         "tiny_buffer": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_TINY_BUFFER),
         "small_segments": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS),
         "no_wait": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_NO_WAIT),
+        "row_topp": tes.Sampler(0, 4096, 1 << 18, tes.TES_FLAG_ROW_TOPP),
     }
     yield out
     for s in out.values():
@@ -86,7 +87,8 @@ def test_spec_verify_parity(samplers, orc, torch_cuda, cfg):
         log("[gpu]   accepted lengths %s" % np.bincount(oacc, minlength=w.Lt).tolist())
 
 
-@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "small_segments", "no_wait"])
+@pytest.mark.parametrize("variant", ["row_select", "tiny_buffer", "small_segments", "no_wait",
+                                     "row_topp"])
 def test_spec_verify_forced_paths(samplers, orc, torch_cuda, variant):
     w = wl(2)
     log("[gpu] spec verify %s on %s" % (variant, w.name))

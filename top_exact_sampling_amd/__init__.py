@@ -30,6 +30,7 @@ TES_FLAG_TINY_BUFFER = 2
 TES_FLAG_STATS = 4
 TES_FLAG_SMALL_SEGMENTS = 8
 TES_FLAG_NO_WAIT = 16
+TES_FLAG_ROW_TOPP = 32
 
 STAT_WORDS = 16  # uint32 per row returned by sampler_get_stats
 

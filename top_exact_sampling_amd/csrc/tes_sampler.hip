@@ -107,7 +107,7 @@ enum RowKind : u32 { kNormal = 0, kInfRow = 1, kZeroRow = 2 };
 enum RowClass : u32 { kClsFull = 0, kClsWhole = 1, kClsSlab = 2, kClsGreedy = 3 };
 enum RowPath : u32 {
     kPathSlab = 0, kPathFull = 1, kPathFullFallback = 2, kPathWhole = 3, kPathGreedy = 4,
-    kPathSlabFallback = 5
+    kPathSlabFallback = 5, kPathFullRow = 6
 };
 enum RowFlag : u32 { kFlagFail = 1u };
 constexpr int kStatWords = 16;  // per-row debug statistics (TES_FLAG_STATS)
@@ -996,9 +996,10 @@ __device__ __forceinline__ float exp_weight(float s) {
     return (s >= -104.0f && n >= -125.0f) ? w : 0.0f;
 }
 
+// Branch free (a per-entry branch costs more than the exponential it skips).
 __device__ __forceinline__ float logit_weight(const RowXf& t, float x) {
-    if (x == t.M) return t.wtop;
-    return exp_weight((x - t.M) * t.r);
+    const float w = exp_weight((x - t.M) * t.r);
+    return x == t.M ? t.wtop : w;
 }
 
 // The weights of a loaded vector of a logit row (identity for probability
@@ -3231,6 +3232,697 @@ __device__ __forceinline__ void full_finish(Smem& s, u32 r, u32 nseg, u32 kind, 
 }
 
 // ---------------------------------------------------------------------------
+// Top-p-only rows decided by one workgroup each
+// ---------------------------------------------------------------------------
+// When a launch holds more top-p-only segments than the device keeps resident
+// workgroups (large batches of long rows, such as the speculative-verify
+// shape), the segments of a row would wait for each other across rounds of
+// dispatch.  Such rows are decided by one workgroup each, with no exchange,
+// in one pass over the row:
+//   * The pass visits the row's rounds (kBlock vectors each) interleaved, so
+//     that any prefix of the visit is spread over the whole row, and builds
+//     the exact fine mass histogram, the +inf count and the min-p mass.
+//   * After 1/16, 1/4 and 1/2 of the row, the histogram so far predicts the
+//     fine bins that can hold the boundary (where the descending cumulative
+//     mass reaches T) and the draw (position u * M_p): the bins whose
+//     cumulative mass so far lies within z = 4.5 standard errors of the
+//     predicted fraction (binomial, with the effective size (sum x)^2 /
+//     sum x^2 of the weights seen and the finite-population factor), the
+//     draw's widened for the boundary's uncertainty and by a bin each side.
+//     Each prediction is intersected with the previous one.  From the first
+//     prediction on, every wave appends its entries of the predicted bins to
+//     its own region of the row's exchange area (unused on this path; no
+//     atomics), and a wave whose region is three quarters full drops what a
+//     narrower prediction no longer holds.
+//   * After the last prediction the rounds visited before the first one are
+//     visited again, for their entries of the predicted bins only.
+//   * T, the boundary's bin and the draw range then follow from the exact
+//     histogram.  When the predictions covered the boundary's bin, the
+//     boundary and the draw are selected among the appended entries (those
+//     of the needed bins are moved into LDS in one read when they fit).  A
+//     bin the predictions missed costs one more pass that appends exactly
+//     the bins needed: the result is the same either way.
+// An empty intersection or a full region restarts the predictions (the
+// second visit then reaches further).  Entries beyond a region after the
+// exact pass too go to the whole-row passes.
+constexpr u32 kRowList = kCoarseBins;  // listed draw bins (s.coarse / s.cabove / s.finem)
+// Rounds in flight in the row pass.
+template <bool LG>
+constexpr u32 kRowDepth = 8;
+static_assert(kRowList <= kDMax * 16, "draw-bin masses fit s.finem");
+static_assert(5 * kWaves <= kCoarseBins, "fused reductions fit s.coarse");
+
+// The appended entries of a row: kWaves regions of wcap slots at gbuf, wave
+// w's first s.gn[w] slots in use (written by this workgroup before a
+// barrier).  Calls f(c, valid) for all of them, taken as one sequence with
+// eight loads per thread in flight (every thread makes the same calls).
+template <typename F>
+__device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 wcap, F f) {
+    u32 off[kWaves + 1];
+    off[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) off[w + 1] = off[w] + uni(s.gn[w]);
+    const u32 n = off[kWaves];
+    for (u32 i0 = 0; i0 < n; i0 += 8 * kBlock) {
+        u64 c[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const u32 i = i0 + k * kBlock + threadIdx.x;
+            // slot of sequence entry i: region w holds entries [off[w], off[w + 1])
+            u32 base = 0;
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                if (i >= off[w]) base = (u32)w * wcap - off[w];
+            c[k] = i < n ? gbuf[base + i] : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f(c[k], i0 + k * kBlock + threadIdx.x < n);
+    }
+}
+
+// Select among the appended entries with composite in [lo, hi): at which the
+// descending cumulative weight (mass, or one per entry) reaches W, with the
+// weight above it.  Up to lcap of them are compacted into LDS and selected
+// there (fine bin f >= 0 with mass weights takes the binned fine select).
+// More, in a fine bin with mass weights: a 2048-bin mass table over the
+// next 11 key bits finds the sub-bin holding W, whose entries are selected
+// in LDS.  Otherwise (ties beyond a buffer, +inf runs) a radix select reads
+// the appended entries once per digit.
+template <bool kTieFirst>
+__device__ Sel gather_select(Smem& s, const u64* gbuf, u32 wcap, u64 lo, u64 hi, int f, u64 W,
+                             bool mass, u32 lcap) {
+    auto collect = [&](auto pred) -> u32 {
+        if (threadIdx.x == 0) s.ctr[3] = 0;
+        __syncthreads();
+        for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+            wave_append(sbuf(s), v && c >= lo && c < hi && pred(c), c, &s.ctr[3], 0, kSelCap);
+        });
+        __syncthreads();
+        const u32 n = uni(s.ctr[3]);
+        __syncthreads();
+        return n;
+    };
+    const u32 nb = collect([](u64) { return true; });
+    if (nb <= lcap)
+        return (f >= 0 && mass) ? fine_select<kTieFirst>(s, nb, f, W)
+                                : select_buf(s, nb, W, mass, lo, hi);
+    if (f >= 0 && mass) {
+        constexpr int kSubShift = kFineShift - 11;
+        u32* hc = shcnt(s);
+        u64* hm = shmass(s);
+        for (int b = threadIdx.x; b < 2048; b += kBlock) {
+            hc[b] = 0;
+            hm[b] = 0;
+        }
+        __syncthreads();
+        for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+            const u32 key = comp_key(c);
+            hist_add(hc, hm, true, v && c >= lo && c < hi, (key >> kSubShift) & 2047u, key_mass(key));
+        });
+        __syncthreads();
+        const Digit g = find_desc(s, 2048, W, [&](int b) { return hm[b]; },
+                                  [&](int b) { return (u64)hc[b]; });
+        const u32 d = g.d;
+        const u32 n2 = collect([&](u64 c) { return ((comp_key(c) >> kSubShift) & 2047u) == d; });
+        if (n2 <= kSelCap) {
+            const Sel r = select_buf(s, n2, W - g.above, true);
+            return Sel{r.c, g.above + r.above};
+        }
+    }
+    // Sequence entry i of the appended entries (as for_each_gathered).
+    u32 off[kWaves + 1];
+    off[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) off[w + 1] = off[w] + uni(s.gn[w]);
+    return radix_select(s, off[kWaves], [&](u32 i, u64& c) {
+        u32 base = 0;
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            if (i >= off[w]) base = (u32)w * wcap - off[w];
+        c = gbuf[base + i];
+        return true;
+    }, W, mass, lo, hi, shcnt(s), shmass(s));
+}
+
+// Key range [fkey0(f), fkey1(f)) of fine bin f (the top bin ends at +inf
+// inclusive: NaN and negative bits lie above it and are never taken).
+__device__ __forceinline__ u32 fkey0(int f) { return (u32)(f + (int)kFineBase) << kFineShift; }
+__device__ __forceinline__ u32 fkey1(int f) {
+    return f == kFineBins - 1 ? kInfKey + 1 : (u32)(f + 1 + (int)kFineBase) << kFineShift;
+}
+
+// Up to two key ranges [k, k + w) (w = 0: empty).
+struct KeyWin {
+    u32 k0, w0, k1, w1;
+    __device__ bool has(u32 b) const { return (b - k0 < w0) | (b - k1 < w1); }
+    __device__ bool covers(int f) const {
+        const u32 a = fkey0(f), e = fkey1(f) - 1;
+        return (a - k0 < w0 && e - k0 < w0) || (a - k1 < w1 && e - k1 < w1);
+    }
+};
+__device__ __forceinline__ KeyWin bins_win(int a0, int b0, int a1, int b1) {
+    KeyWin w{0, 0, 0, 0};
+    if (a0 <= b0) w.k0 = fkey0(a0), w.w0 = fkey1(b0) - fkey0(a0);
+    if (a1 <= b1) w.k1 = fkey0(a1), w.w1 = fkey1(b1) - fkey0(a1);
+    return w;
+}
+
+// Streams visited rounds j in [0, jb) (jb a multiple of kRowDepth<LG>, read at
+// every step: it may grow) of a row visited in interleaved order: eight lanes
+// each walk one eighth of the row, so visited round j < nj is row round
+// (j & 7) * S8 + (j >> 3) (S8 rounds per eighth; past the row: invalid) and
+// visited round j >= nj is visited round j - nj again.  f(x, iv, valid,
+// first) is called for every vector of each round by every thread (first:
+// j < nj); tick(j) after every kRowDepth<LG> rounds (j rounds visited).
+template <int VEC, bool LG, typename F, typename G>
+__device__ __forceinline__ void stream_rounds(const float* __restrict__ row, u32 nvec, u32 S8,
+                                              const u32& jb, F f, G tick, const RowXf& xf) {
+    typedef typename VecT<VEC>::T VT;
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row);
+    const u32 nr = (nvec + kBlock - 1) / kBlock;
+    const u32 nj = 8 * S8;
+    auto vec_of = [&](u32 j) -> u32 {
+        const u32 jj = j < nj ? j : j - nj;
+        const u32 rd = (jj & 7) * S8 + (jj >> 3);
+        return (j < jb && rd < nr) ? rd * kBlock + threadIdx.x : nvec;
+    };
+    constexpr u32 kD = kRowDepth<LG>;
+    VT pf[kD];
+#pragma unroll
+    for (u32 d = 0; d < kD; ++d) {
+        pf[d] = ld_stream(&rv[min(vec_of(d), nvec - 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (u32 j0 = 0; j0 < jb; j0 += kD) {
+#pragma unroll
+        for (u32 d = 0; d < kD; ++d) {
+            const u32 iv = vec_of(j0 + d);
+            f(xform<VEC, LG>(xf, pf[d]), iv, iv < nvec, j0 + d < nj);
+            pf[d] = ld_stream(&rv[min(vec_of(j0 + d + kD), nvec - 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        tick(j0 + kD);
+    }
+}
+
+// A u64 as the nearest-ish float (two conversions and a fused add).
+__device__ __forceinline__ float u64f(u64 x) {
+    return fmaf((float)(u32)(x >> 32), 0x1p32f, (float)(u32)x);
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int VEC, bool LG>
+__device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
+    const Params p = params_from(s);
+    typedef typename VecT<VEC>::T VT;
+    const RowXf xf = row_xf<LG>(p, r);
+    const float* row = row_ptr<VEC>(p.probs, r, p.V);
+    const float top_p = ld_g(&p.top_p[r]);
+    float theta = 0.0f;
+    if constexpr (LG) theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
+    // Logit rows: the largest mass is that of the top weight 1 (2^32).
+    const u32 kf = LG ? minp_key(minp_floor(theta, 1ull << 32)) : 0u;
+    const bool minp = LG && kf > 1u;
+    const bool tiny = p.flags & TES_FLAG_TINY_BUFFER;
+    // Appended entries: one region of wcap slots per wave, filled without
+    // atomics (each wave keeps its own count).
+    u64* gbuf = reinterpret_cast<u64*>(ws_row(p, r));
+    const u32 wcap = (tiny ? 64u : (u32)(p.rowbytes / sizeof(u64))) / kWaves;
+    u64* wreg = gbuf + (size_t)wave_id() * wcap;
+    u32 wcnt = 0;  // this wave's appended entries (may pass wcap: counted, not written)
+    const u32 lcap = tiny ? 32u : kSelCap;
+    const u64 P = fixed_p(top_p);
+    const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+    stat_start(p, r, 1);
+    u64 tp = p.stats ? wall_clock64() : 0;
+    if (threadIdx.x == 0) s.npass = 0;
+
+    // Fine binning of the segments, branch free: bin (key >> 16) - base
+    // clamped to [-1, kFineBins - 1] (-1 is the discard slot) and mass
+    // floor(x * 2^32) clamped to [0, 2^32 - 256]; the top bin's sum is then
+    // turned into count * 2^32.
+    constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256
+    auto bin_add = [&](u32 b) -> u32 {
+        const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, -1), kFineBins - 1);
+        const u32 q = (u32)fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
+        atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)q);
+        return q;
+    };
+    auto wb = [&](int b) { return shfine(s)[b]; };
+
+    const u32 nr = (p.nvec + kBlock - 1) / kBlock;
+    const u32 S8 = (nr + 7) / 8;
+    const u32 nj = 8 * S8;  // visited rounds (some past the row when nr % 8 != 0)
+    // Predictions after j1 = nj/16 (at least kRowDepth<LG>) rounds, then after
+    // 4 j1 and 8 j1 (a quarter and half of the row).
+    constexpr u32 kD = kRowDepth<LG>;
+    const u32 j1 = max(kD, (nj / 16) / kD * kD);
+    const bool predict = nr >= 32;
+    u32 next_upd = predict ? j1 : ~0u;
+
+    // Prediction state (uniform): the bin ranges [tl, th] (boundary) and
+    // [dl, dh] (draw), or the +inf window; appended since round j_start.
+    KeyWin win{0, 0, 0, 0};
+    int tl = 0, th = -1, dl = 0, dh = -1;
+    bool started = false, infwin = false;
+    u32 j_start = 0;
+    u64 ninf = 0, mf = 0;
+
+    for (int i = (int)threadIdx.x - 1; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
+    __syncthreads();
+
+    // Appends this lane's entries c[e] with bit e of mask set to the wave's
+    // region (slots in lane order from a prefix sum over the lanes' counts).
+    auto append = [&](u32 mask, const u64 (&c)[VEC]) {
+        const u32 cnt = (u32)__popc(mask);
+        u32 pre = 0, tot = 0;
+#pragma unroll
+        for (int b = 0; (1 << b) <= VEC; ++b) {
+            const u64 bb = __ballot((cnt >> b) & 1u);
+            pre += mbcnt64(bb) << b;
+            tot += (u32)__popcll(bb) << b;
+        }
+        u32 pos = wcnt + pre;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if ((mask >> e) & 1u) {
+                if (pos < wcap) wreg[pos] = c[e];
+                ++pos;
+            }
+        }
+        wcnt += tot;
+    };
+    // Keeps, in place, this wave's appended entries inside win (one wave:
+    // each chunk of 64 * 8 slots is loaded before any of its kept entries is
+    // stored, and stores never pass the slots loaded).
+    auto compact = [&]() {
+        __threadfence_block();
+        const u32 n = wcnt;
+        u32 kept = 0;
+        for (u32 c0 = 0; c0 < n; c0 += 8 * 64) {
+            u64 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const u32 i = c0 + k * 64 + lane_id();
+                v[k] = i < n ? wreg[i] : 0ull;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const u32 i = c0 + k * 64 + lane_id();
+                const bool keep = i < n && win.has(comp_key(v[k]));
+                const u64 bm = __ballot(keep);
+                if (keep) wreg[kept + mbcnt64(bm)] = v[k];
+                kept += (u32)__popcll(bm);
+            }
+        }
+        wcnt = kept;
+    };
+
+    constexpr int kPer = (kFineBins + kBlock - 1) / kBlock;
+    auto update = [&](u32 j) {
+        __syncthreads();  // the histogram and the appends of rounds < j are complete
+        // This thread's bins (descending, as find_desc takes them); the
+        // waves' totals of the mass, +inf count, min-p mass and squares so
+        // far and the thread's exclusive mass prefix take one barrier.
+        // (The prediction is a heuristic: fp32 arithmetic is ample for it.)
+        const int top = kFineBins - 1 - (int)threadIdx.x * kPer;
+        u64 lm = 0;
+        float x2 = 0.0f;  // sum of squared weights x = q / 2^32: a bin's mass times its middle weight
+#pragma unroll
+        for (int jj = 0; jj < kPer; ++jj) {
+            if (top - jj >= 0) {
+                const u64 m = shfine(s)[top - jj];
+                lm += m;
+                x2 += u64f(m) * 0x1p-32f * __uint_as_float(fkey0(top - jj) + (1u << (kFineShift - 1)));
+            }
+        }
+        const u64 inc = wave_incl_scan(lm);
+        const u64 w1 = wave_sum(ninf), w2 = minp ? wave_sum(mf) : 0ull;
+        const float w3 = wave_sum_f32(x2);
+        const u32 wv = wave_id();
+        if (lane_id() == 63) s.coarse[5 * wv + 0] = inc;
+        if (lane_id() == 0) {
+            s.coarse[5 * wv + 1] = w1;
+            s.coarse[5 * wv + 2] = w2;
+            s.coarse[5 * wv + 3] = (u64)__float_as_uint(w3);
+            s.coarse[5 * wv + 4] = wcnt > wcap;
+        }
+        __syncthreads();
+        u64 Ms = 0, pre = 0, ni = 0, mfs = 0, over = 0;
+        float sx2 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const u64 tw = s.coarse[5 * w + 0];
+            Ms += tw;
+            pre += (u32)w < wv ? tw : 0ull;
+            ni += s.coarse[5 * w + 1];
+            mfs += s.coarse[5 * w + 2];
+            sx2 += __uint_as_float((u32)s.coarse[5 * w + 3]);
+            over += s.coarse[5 * w + 4];
+        }
+        Ms = uni(Ms), ni = uni(ni), mfs = uni(mfs);
+        const u64 ex = pre + inc - lm;  // mass of the bins above this thread's
+        const bool lost = uni(over) != 0;
+        if (ni > 0) {
+            // A +inf row keeps its +inf entries: append those from here on.
+            if (!infwin || lost) {
+                infwin = started = true;
+                j_start = j;
+                win = KeyWin{kInfKey, 1, 0, 0};
+                wcnt = 0;
+            }
+        } else if (Ms > 0) {
+            u64 Ts = topp_threshold(P, Ms);
+            if (minp) Ts = mfs < Ts ? mfs : Ts;
+            Ts = Ts < 1 ? 1 : Ts;
+            const float Md = u64f(Ms);
+            const float Mx = Md * 0x1p-32f;
+            const float neff = sx2 > 0.0f ? fmaxf(1.0f, Mx * Mx / sx2) : 1.0f;
+            // Share of the row not seen yet (entries per visited round).
+            const float seen = fminf(1.0f, (float)j * (float)(kBlock * VEC) / (float)p.V);
+            const float fpc = sqrtf(fmaxf(0.0f, 1.0f - seen));
+            const float ud = u64f(u) * 0x1p-64f;
+            const float FT = u64f(Ts) / Md, FD = ud * FT;
+            const float sT = sqrtf(FT * (1.0f - FT) / neff) * fpc;
+            const float sD = sqrtf(FD * (1.0f - FD) / neff) * fpc;
+            constexpr float z = 4.5f;
+            auto clampW = [&](float w) -> u64 {
+                if (!(w >= 1.0f)) return 1ull;
+                if (w >= Md) return Ms;
+                const float hi = floorf(w * 0x1p-32f);
+                return ((u64)(u32)hi << 32) + (u64)(u32)fmaxf(w - hi * 0x1p32f, 0.0f);
+            };
+            // Margins: the boundary's, and the draw's, which also moves with
+            // the kept mass M_p (from T up to T plus the boundary bin's mass:
+            // allowed for as twice the boundary margin, and one bin on either
+            // side of the draw's range).
+            const float mT = (z * sT + 2.0f / neff) * Md;
+            const float Tf = u64f(Ts), td = ud * Tf;
+            const float mD = (z * (sD + ud * sT) + 2.0f / neff) * Md + ud * 2.0f * mT;
+            const u64 Wq[4] = {clampW(Tf - mT), clampW(Tf + mT), clampW(td - mD), clampW(td + mD)};
+            // The bins where the cumulative mass reaches each target.
+            u64 acc = ex;
+#pragma unroll
+            for (int jj = 0; jj < kPer; ++jj) {
+                const int b = top - jj;
+                if (b >= 0) {
+                    const u64 w = shfine(s)[b];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (acc < Wq[k] && Wq[k] <= acc + w) s.loc_bin[k] = b;
+                    acc += w;
+                }
+            }
+            __syncthreads();
+            const int nth = (int)uni((u32)s.loc_bin[0]), ntl = (int)uni((u32)s.loc_bin[1]);
+            const int ndh = min((int)uni((u32)s.loc_bin[2]) + 1, kFineBins - 1);
+            const int ndl = max((int)uni((u32)s.loc_bin[3]) - 1, 0);
+            const int ttl = max(tl, ntl), tth = min(th, nth), tdl = max(dl, ndl), tdh = min(dh, ndh);
+            if (!started || infwin || lost || (ttl > tth && tdl > tdh)) {
+                // (Re)start: the appended entries are dropped.
+                tl = ntl, th = nth, dl = ndl, dh = ndh;
+                started = true;
+                infwin = false;
+                j_start = j;
+                win = bins_win(tl, th, dl, dh);
+                wcnt = 0;
+            } else {
+                const bool narrower = ttl != tl || tth != th || tdl != dl || tdh != dh;
+                tl = ttl, th = tth, dl = tdl, dh = tdh;
+                win = bins_win(tl, th, dl, dh);
+                // A wave whose region is three quarters full drops what the
+                // narrower prediction no longer needs.
+                if (narrower && 4 * wcnt > 3 * wcap) compact();
+            }
+        }
+        __syncthreads();
+        next_upd = next_upd == j1 ? 4 * j1 : (next_upd == 4 * j1 ? 8 * j1 : ~0u);
+        if (next_upd != ~0u && next_upd >= nj) next_upd = ~0u;
+    };
+
+    // The pass: exact histogram, +inf count, min-p mass, predicted bins;
+    // then, once the predictions are final, the rounds visited before the
+    // first one again (their entries of the predicted bins only).
+    u32 jend = nj;
+    stream_rounds<VEC, LG>(row, p.nvec, S8, jend, [&](const VT& x, u32 iv, bool valid, bool first) {
+        u32 mask = 0;
+        int mx = kIntMin;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+            mask |= (valid && win.has(b)) ? 1u << e : 0u;
+            if (valid && first) {
+                mx = max(mx, (int)b);
+                bin_add(b);
+                if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
+            }
+        }
+        if (mx >= (int)kInfKey) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x, e)) == kInfKey;
+        }
+        if (__ballot(mask != 0) == 0) return;
+        u64 c[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) c[e] = composite(__float_as_uint(VecT<VEC>::get(x, e)), iv * VEC + e);
+        append(mask, c);
+    }, [&](u32 j) {
+        if (j == next_upd) {
+            const u64 t0 = p.stats ? wall_clock64() : 0;
+            update(j);
+            jend = nj + (started ? j_start : 0);
+            stat_phase(p, r, 9, t0);
+        }
+    }, xf);
+    if (threadIdx.x == 0) ++s.npass;
+    // Publishes the waves' counts to s.gn (and returns whether all fit).
+    auto publish = [&]() -> bool {
+        if (lane_id() == 0) s.gn[wave_id()] = wcnt;
+        __syncthreads();
+        u32 mx = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = max(mx, s.gn[w]);
+        mx = uni(mx);
+        __syncthreads();  // s.gn is rewritten by the next publication
+        return mx <= wcap;
+    };
+    const bool fits = publish();
+    if (threadIdx.x == 0) {
+        u64& top = shfine(s)[kFineBins - 1];
+        top = (top / (u64)kTopMass) << 32;
+    }
+    __syncthreads();
+    u64 M = 0;
+    for (int i = threadIdx.x; i < kFineBins; i += kBlock) M += shfine(s)[i];
+    M = block_sum(s, M);
+    ninf = block_sum(s, ninf);
+    if (minp) mf = block_sum(s, mf);
+    const bool chain = started && fits;
+    if (!chain) stat_why(p, r, 1u << 16);
+    tp = stat_phase(p, r, 8, tp);
+
+    // Appends the entries taken by pred to the waves' regions in one pass
+    // over the row, from empty regions; returns whether every region held
+    // its entries (the counts are in s.gn).
+    auto take = [&](auto pred) {
+        return [&, pred](const VT& x, u32 iv, bool valid) {
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) any = any || pred(__float_as_uint(VecT<VEC>::get(x, e)));
+            if (__ballot(valid && any) == 0) return;
+            u32 mask = 0;
+            u64 c[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+                mask |= (valid && pred(b)) ? 1u << e : 0u;
+                c[e] = composite(b, iv * VEC + e);
+            }
+            append(mask, c);
+        };
+    };
+    auto pass = [&](auto pred) -> bool {
+        wcnt = 0;
+        for_each_vec<VEC, kStreamDepth, LG>(row, p.nvec, take(pred), xf);
+        if (threadIdx.x == 0) ++s.npass;
+        return publish();
+    };
+    // (s.gn holds the last publication until the next one.)
+    auto total = [&]() {
+        u32 n = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) n += s.gn[w];
+        return uni(n);
+    };
+    const u32 nfin = total();
+
+    // Decide.
+    Outcome o{};
+    bool fb = false;
+    u32 gathered = nfin;
+    if (ninf > 0) {
+        // +inf rows keep their +inf entries: the t-th in index order.
+        const bool ok = (chain && infwin) || pass([](u32 b) { return b == kInfKey; });
+        gathered = total();
+        if (ok) {
+            const u64 lo = (u64)kInfKey << 32, hi = (u64)(kInfKey + 1) << 32;
+            const u64 t = __umul64hi(u, ninf);
+            o.kind = kInfRow;
+            o.m = (u32)ninf;
+            o.token = comp_index(gather_select<VEC == 8>(s, gbuf, wcap, lo, hi, -1, t + 1, false, lcap).c);
+            u64 mn = ~0ull;
+            for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+                mn = (v && c >= lo && c < mn) ? c : mn;
+            });
+            o.c_keep = block_min(s, mn);
+        } else {
+            fb = true;
+        }
+    } else if (M == 0) {
+        o.kind = kZeroRow;
+        o.token = 0;  // the support is the whole row: its smallest index
+    } else {
+        u64 T = topp_threshold(P, M);
+        // Min-p: the kept set ends where the inclusive mass reaches
+        // min(T, the mass at or above the floor).
+        if (minp) T = mf < T ? mf : T;
+        const Digit gT = find_desc(s, kFineBins, T, wb, wb);
+        const int fbT = (int)gT.d;
+        const u64 aboveT = gT.above;
+        const u64 mT = uni(shfine(s)[fbT]);
+        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, aboveT + mT);
+        const Digit g1 = find_desc(s, kFineBins, t_lo + 1, wb, wb);
+        const Digit g2 = find_desc(s, kFineBins, t_hi + 1, wb, wb);
+        const int bhi = (int)g1.d, blo = (int)g2.d;  // the draw's fine bins, bhi >= blo >= fbT
+        // The non-empty bins of [blo, bhi] with their masses and the mass
+        // above each, highest first (one wave, 64 bins per step).
+        if (wave_id() == 0) {
+            const u32 lane = lane_id();
+            u64 base = g1.above;
+            u32 q = 0;
+            for (int b0 = bhi; b0 >= blo; b0 -= 64) {
+                const int b = b0 - (int)lane;
+                const bool in = b >= blo;
+                const u64 m = in ? shfine(s)[b] : 0ull;
+                const u64 inc = wave_incl_scan(m);
+                const bool ne = in && m != 0;
+                const u64 bm = __ballot(ne);
+                const u32 pos = q + mbcnt64(bm);
+                if (ne && pos < kRowList) {
+                    s.coarse[pos] = (u64)b;
+                    s.cabove[pos] = base + inc - m;
+                    s.finem[pos] = m;
+                }
+                q += (u32)__popcll(bm);
+                base += read_lane(inc, 63);
+            }
+            if (lane == 0) s.misc[6] = q;
+        }
+        __syncthreads();
+        const u32 nlist = uni(s.misc[6]);
+        tp = stat_phase(p, r, 10, tp);
+        // Bins whose entries are all appended: inside both ha and hb.
+        KeyWin need = bins_win(fbT, fbT, blo, bhi);
+        // Bins whose entries are all appended: inside both ha and hb.
+        KeyWin ha = need, hb = win;
+        bool ok = chain && win.covers(fbT);
+        if (!ok) {
+            stat_why(p, r, 1u << 17);
+            // One pass for the boundary's bin and the draw range; if they
+            // overflow, the boundary's bin alone (the draw's follows).
+            hb = KeyWin{0, 0xFFFFFFFFu, 0, 0};
+            ok = nlist <= kRowList && pass([&](u32 b) { return need.has(b); });
+            if (!ok) {
+                need.w1 = 0;
+                ok = pass([&](u32 b) { return need.has(b); });
+            }
+            ha = need;
+        }
+        gathered = total();
+        fb = !ok;
+        // One read of the appended entries puts those of the needed bins
+        // into LDS when they fit; otherwise each select reads them.
+        auto collect_need = [&]() -> u32 {
+            if (threadIdx.x == 0) s.ctr[3] = 0;
+            __syncthreads();
+            for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+                wave_append(sbuf(s), v && ha.has(comp_key(c)) && hb.has(comp_key(c)), c, &s.ctr[3],
+                            0, kSelCap);
+            });
+            __syncthreads();
+            const u32 n = uni(s.ctr[3]);
+            __syncthreads();
+            return n;
+        };
+        auto select_bin = [&](u32 nl, int f, u64 W) -> Sel {
+            const bool bin = !tiny && f < kFineBins - 1;
+            if (nl <= lcap)
+                return bin ? fine_select<VEC == 8>(s, nl, f, W)
+                           : select_buf(s, nl, W, true, fine_lo(f), fine_hi(f));
+            return gather_select<VEC == 8>(s, gbuf, wcap, fine_lo(f), fine_hi(f), bin ? f : -1, W,
+                                           true, lcap);
+        };
+        if (!fb) {
+            u32 nl = collect_need();
+            const Sel sb = select_bin(nl, fbT, T - aboveT);
+            const u64 M_p = aboveT + sb.above + key_mass(comp_key(sb.c));
+            const u64 t = __umul64hi(u, M_p);
+            // The listed bin holding draw position t + 1.
+            if (threadIdx.x == 0) {
+                s.loc_bin[0] = -1;
+                s.loc_above[0] = 0;
+            }
+            __syncthreads();
+            for (u32 i = threadIdx.x; i < min(nlist, kRowList); i += kBlock) {
+                const u64 a = s.cabove[i], m = s.finem[i];
+                if (a < t + 1 && t + 1 <= a + m) {
+                    s.loc_bin[0] = (int)s.coarse[i];
+                    s.loc_above[0] = a;
+                }
+            }
+            __syncthreads();
+            const int fd = (int)uni((u32)s.loc_bin[0]);
+            const u64 above_d = uni(s.loc_above[0]);
+            __syncthreads();
+            if (fd < 0) {
+                fb = true;  // the draw lies outside the listed bins: not for a consistent histogram
+            } else {
+                if (!(ha.covers(fd) && hb.covers(fd))) {
+                    stat_why(p, r, 1u << 18);
+                    ha = bins_win(fd, fd, 0, -1);
+                    hb = KeyWin{0, 0xFFFFFFFFu, 0, 0};
+                    ok = pass([&](u32 b) { return ha.has(b); });
+                    gathered = total();
+                    if (ok) nl = collect_need();
+                }
+                fb = !ok;
+                if (!fb) {
+                    const Sel sd = select_bin(nl, fd, t + 1 - above_d);
+                    o.kind = kNormal;
+                    o.c_keep = sb.c;
+                    o.M_p = M_p;
+                    o.token = comp_index(sd.c);
+                }
+            }
+        }
+    }
+    u32 path = kPathFullRow;
+    if (fb) {
+        stat_why(p, r, 1u << 19);
+        o = resolve_row<VEC, LG>(s, row, p.nvec, p.V, p.V, P, u, kSelCap, xf, theta);
+        path = kPathFullFallback;
+    }
+    stat_add(p, r, 3, uni(s.npass));
+    stat_phase(p, r, 13, tp);
+    finish_row(s, p, r, o, path, gathered);
+}
+
+// ---------------------------------------------------------------------------
 // Whole-row items
 // ---------------------------------------------------------------------------
 template <int VEC, bool LG>
@@ -3267,7 +3959,9 @@ __device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full)
 // One work item per workgroup, in block order.  Items [0, nf * S) are the
 // segments of the nf top-p-only rows, S consecutive items per row: blocks are
 // dispatched in order, so the segments of a row start together and wait for
-// each other only briefly (the waits are bounded all the same).  The other
+// each other only briefly (the waits are bounded all the same).  When the
+// launch's items would not all be resident at once, S is 1 and each such
+// row is decided by its one workgroup (two passes, no exchange).  The other
 // rows follow, one item each: whole-row rows, top-k rows, then greedy rows.
 // Blocks beyond the last item return at once.  No item loop: values live
 // across one would raise the register pressure of every path.
@@ -3323,7 +4017,13 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     // is resident at once (parts that wait for a slot only delay their rows);
     // greedy rows too when there is still room.  Parts after the first come
     // last in block order.
-    const u32 base_items = nf * s_full + n_whole + n_slab + n_greedy;
+    // Top-p-only rows are cut into s_full segments while every item of the
+    // launch is resident at once; otherwise each is decided by one
+    // workgroup in two passes over the row (or under TES_FLAG_ROW_TOPP).
+    const bool row_topp = (p.flags & TES_FLAG_ROW_TOPP) ||
+                          nf * s_full + n_whole + n_slab + n_greedy > p.slots;
+    const u32 segs = row_topp ? 1u : s_full;
+    const u32 base_items = nf * segs + n_whole + n_slab + n_greedy;
     // Parts beyond half the resident slots cost more in joins than they gain
     // (measured), so the split stops there.
     const u32 room = p.slots / 2;
@@ -3332,15 +4032,19 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
         if (base_items + (c - 1) * n_slab <= room) S = c;
     for (u32 c = S; c > 1 && Sg == 1; --c)
         if (base_items + (S - 1) * n_slab + (c - 1) * n_greedy <= room) Sg = c;
-    const u32 full_end = nf * s_full;
+    const u32 full_end = nf * segs;
     const u32 whole_end = full_end + n_whole;
     const u32 first_end = whole_end + n_slab;
     const u32 greedy_end = first_end + n_greedy * Sg;
     const u32 item = blockIdx.x;
     __syncthreads();
     if (item < full_end) {
-        const u32 j = item / s_full;
-        do_full<VEC, LG>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
+        if (row_topp) {
+            do_rowtopp<VEC, LG>(s, uni((u32)s.rows[item]));
+        } else {
+            const u32 j = item / s_full;
+            do_full<VEC, LG>(s, uni((u32)s.rows[j]), item - j * s_full, s_full);
+        }
     } else if (item < whole_end) {
         const u32 r = uni((u32)s.rows[nf + (item - full_end)]);
         do_whole<VEC, LG>(s, r, row_k_eff(p, r));
@@ -3901,7 +4605,7 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     if (max_batch < 1 || max_vocab < 1 || max_vocab > (1 << 30) || device < 0)
         return TES_ERR_INVALID_ARGUMENT;
     if (flags & ~(TES_FLAG_FORCE_ROW_SELECT | TES_FLAG_TINY_BUFFER | TES_FLAG_STATS |
-                  TES_FLAG_SMALL_SEGMENTS | TES_FLAG_NO_WAIT))
+                  TES_FLAG_SMALL_SEGMENTS | TES_FLAG_NO_WAIT | TES_FLAG_ROW_TOPP))
         return TES_ERR_INVALID_ARGUMENT;
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
@@ -3928,6 +4632,8 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     if (s->s_ws > kMaxSegWs) s->s_ws = kMaxSegWs;
     size_t rb = (size_t)s->s_ws * (sizeof(PubC) + sizeof(PubF) + (size_t)kGSeg * sizeof(u64));
     if (rb < kSplitBytes) rb = kSplitBytes;  // parts of a split top-k or greedy row
+    // One-workgroup top-p rows append up to one entry in eight of the row.
+    if (rb < (size_t)max_vocab) rb = (size_t)max_vocab;
     rb = (rb + 255) & ~(size_t)255;
     s->rowbytes = (u32)rb;
     s->chunk = (u32)max_batch < kChunk ? (u32)max_batch : kChunk;
@@ -4096,10 +4802,14 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         // Enough blocks for every row to be top-p-only; the kernel knows the
         // actual mix, and blocks beyond the last item return at once.
         // Split rows occur only when every item is resident, i.e. within
-        // the slots.
+        // the slots.  Segmented rows too: a launch whose items would exceed
+        // the slots decides its top-p-only rows one item each, so there are
+        // never more than max(rows, slots) items.
         const u32 per_row = s_full <= s->s_ws ? s_full : 1u;
         const u32 split_items = rows * p.split < s->slots ? rows * p.split : s->slots;
-        const u32 grid = rows * per_row > split_items ? rows * per_row : split_items;
+        const u32 g_all = rows * per_row > split_items ? rows * per_row : split_items;
+        const u32 g_cap = rows > s->slots ? rows : s->slots;
+        const u32 grid = g_all < g_cap ? g_all : g_cap;
         float* ro = renorm_out ? renorm_out + (size_t)c0 * V : nullptr;
         const int rc =
             logits ? (vec == 4 ? launch_chunk<4, true>(s, p, st, grid, rows, (u32)V, nvec, ro, slab,
