@@ -2435,13 +2435,10 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     __syncthreads();  // the histogram is dead; the buffer takes its place
     const bool no_tkey = tkey == 0;
     if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the part reports itself unusable
-    if (no_tkey && S == 1) {
-        // Fewer than j sampled entries have a mass (a row of mostly zeros, or
-        // a short row with fewer than k): one exact pass over every positive key.
-        slab_restream<VEC, LG>(s, r, k, 1u, fixed_p(top_p),
-                               philox_uniform(p.seed, p.row_base + r, p.offset));
-        return;
-    }
+    // Fewer than j sampled entries have a mass (a row of mostly zeros, or a
+    // short row with fewer than k): a whole row streams every positive key
+    // (its entries, if they fit, are then the whole support's mass).
+    if (no_tkey && S == 1) tkey = 1u;
     const u32 span = kInfKey - tkey;
     // Logit rows: the weights at or above tkey belong to logits >= xb.
     float xb = 0.0f;
@@ -2518,7 +2515,8 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     // A whole row headed for the binned finish leaves its entries in the
     // regions (that finish reads them there); otherwise the regions are
     // packed together.
-    const bool direct = S == 1 && !over && fill >= k && !(p.flags & TES_FLAG_TINY_BUFFER);
+    const bool direct =
+        S == 1 && !over && fill >= k && !no_tkey && !(p.flags & TES_FLAG_TINY_BUFFER);
     if (!direct) {
         constexpr int kPerLane = kRegion / 64;
         u64 mine[kPerLane];
@@ -2611,7 +2609,17 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         tbase = tmax;
     }
     if (!over && fill >= k) {
-        slab_finish<LG>(s, r, fill, k, tbase, P, u, direct ? wfill : ~0u);
+        // (Every positive key: no bin base for the binned finish.)
+        slab_finish<LG>(s, r, fill, k, no_tkey ? 0u : tbase, P, u, direct ? wfill : ~0u);
+    } else if (no_tkey && S == 1 && !over && fill == 0) {
+        // No positive key anywhere: every entry is a zero, so the support is
+        // indices [0, k), its boundary index k - 1 and its token (the
+        // smallest index of a support without mass) 0.
+        Outcome o{};
+        o.kind = kZeroRow;
+        o.token = 0;
+        o.c_k = composite(0u, k - 1);
+        finish_row(s, p, r, o, kPathSlab, 0);
     } else {
         // A whole row that counted at least k entries at or above its
         // threshold has its best k there; anything else starts from 1.
