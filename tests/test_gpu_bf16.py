@@ -42,6 +42,7 @@ def variants(torch_cuda):
         "tiny_buffer": tes.Sampler(0, 1024, 1 << 18, tes.TES_FLAG_TINY_BUFFER),
         "small_tiny": tes.Sampler(
             0, 1024, 1 << 18, tes.TES_FLAG_SMALL_SEGMENTS | tes.TES_FLAG_TINY_BUFFER),
+        "row_topp": tes.Sampler(0, 1024, 1 << 18, tes.TES_FLAG_ROW_TOPP),
     }
     yield out
     for s in out.values():

@@ -487,6 +487,26 @@ def test_oversubscribed_topp_rows_take_the_row_path(sampler, variant_samplers, o
     assert np.all(st[:, 2] == 1) and np.mean(st[:, 0] == 6) >= 0.95, st[:, 0]
 
 
+def test_row_path_tie_runs(sampler, variant_samplers, orc):
+    # Quantised rows (multiples of 2^-20, as in the ties-and-edges recipe)
+    # as top-p-only rows on the one-workgroup path: every fine bin holds one
+    # value, and the boundary's and the draw's bins hold thousands of equal
+    # entries, more than a select buffer takes, so they are selected by rank
+    # in index order.
+    w = wl(4)
+    cls = w.meta["row_class"]
+    rows = np.flatnonzero(cls == "plain")[:24]
+    probs = np.ascontiguousarray(w.probs[rows])
+    ks = np.full(rows.size, w.V, np.int32)
+    ps = np.random.default_rng(44).uniform(0.3, 0.99, rows.size).astype(np.float32)
+    for off in (0, 1):
+        for label in ("default", "row_topp"):
+            s = sampler if label == "default" else variant_samplers[label]
+            log("[gpu] tie runs on top-p-only rows offset %d sampler=%s" % (off, label))
+            gtok, gren = run_gpu(s, probs, ks, ps, 5, off, renorm=True)
+            assert_parity(orc, probs, ks, ps, 5, off, gtok, gren, "tie runs %s %d" % (label, off))
+
+
 def test_batches_longer_than_one_launch(sampler, orc):
     # More rows than one launch takes (1024): the call enqueues several
     # launches, each with its own row offset for the Philox counter, mixing

@@ -3312,13 +3312,16 @@ __device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 
 // descending cumulative weight (mass, or one per entry) reaches W, with the
 // weight above it.  Up to lcap of them are compacted into LDS and selected
 // there (fine bin f >= 0 with mass weights takes the binned fine select).
-// More, in a fine bin with mass weights: a 2048-bin mass table over the
-// next 11 key bits finds the sub-bin holding W, whose entries are selected
-// in LDS.  Otherwise (ties beyond a buffer, +inf runs) a radix select reads
-// the appended entries once per digit.
+// More of them sharing one key (a run of ties; every fine bin of a bf16 row
+// is one value): the W-th weight lies in the entry of rank m = ceil(W / q)
+// in index order, found through a 2048-bin count table over the top 11 of
+// the ibits index bits.  More, in a fine bin with mass weights: a 2048-bin
+// mass table over the next 11 key bits finds the sub-bin holding W.  Either
+// way the entries of that one table bin are selected in LDS.  Otherwise a
+// radix select reads the appended entries once per digit.
 template <bool kTieFirst>
 __device__ Sel gather_select(Smem& s, const u64* gbuf, u32 wcap, u64 lo, u64 hi, int f, u64 W,
-                             bool mass, u32 lcap) {
+                             bool mass, u32 lcap, u32 ibits) {
     auto collect = [&](auto pred) -> u32 {
         if (threadIdx.x == 0) s.ctr[3] = 0;
         __syncthreads();
@@ -3334,7 +3337,36 @@ __device__ Sel gather_select(Smem& s, const u64* gbuf, u32 wcap, u64 lo, u64 hi,
     if (nb <= lcap)
         return (f >= 0 && mass) ? fine_select<kTieFirst>(s, nb, f, W)
                                 : select_buf(s, nb, W, mass, lo, hi);
-    if (f >= 0 && mass) {
+    u64 kmn = ~0ull, kmx = 0;
+    for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+        const bool in = v && c >= lo && c < hi;
+        kmn = in && comp_key(c) < kmn ? comp_key(c) : kmn;
+        kmx = in && comp_key(c) > kmx ? comp_key(c) : kmx;
+    });
+    kmn = block_min(s, kmn);
+    kmx = block_max(s, kmx);
+    if (kmn == kmx) {
+        // One key: equal weights q, and descending composites are ascending
+        // indices, so the digit is taken from the complemented index.
+        const u64 q = mass ? key_mass((u32)kmn) : 1ull;
+        const u64 m = (W + q - 1) / q;
+        const u32 sh = ibits > 11 ? ibits - 11 : 0u;
+        u32* hc = shcnt(s);
+        for (int b = threadIdx.x; b < 2048; b += kBlock) hc[b] = 0;
+        __syncthreads();
+        for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
+            hist_add(hc, nullptr, false, v && c >= lo && c < hi, ((u32)c >> sh) & 2047u, 0);
+        });
+        __syncthreads();
+        auto cf = [&](int b) { return (u64)hc[b]; };
+        const Digit g = find_desc(s, 2048, m, cf, cf);
+        const u32 d = g.d;
+        const u32 n2 = collect([&](u64 c) { return (((u32)c >> sh) & 2047u) == d; });
+        if (n2 <= kSelCap) {
+            const Sel r = select_buf(s, n2, m - g.above, false);
+            return Sel{r.c, (m - 1) * q};
+        }
+    } else if (f >= 0 && mass) {
         constexpr int kSubShift = kFineShift - 11;
         u32* hc = shcnt(s);
         u64* hm = shmass(s);
@@ -3464,6 +3496,7 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     u64* wreg = gbuf + (size_t)wave_id() * wcap;
     u32 wcnt = 0;  // this wave's appended entries (may pass wcap: counted, not written)
     const u32 lcap = tiny ? 32u : kSelCap;
+    const u32 ibits = 32u - (u32)__clz((int)max(p.V - 1u, 1u));  // bits of an index
     const u64 P = fixed_p(top_p);
     const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
     stat_start(p, r, 1);
@@ -3679,20 +3712,23 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     u32 jend = nj;
     stream_rounds<VEC, LG>(row, p.nvec, S8, jend, [&](const VT& x, u32 iv, bool valid, bool first) {
         u32 mask = 0;
-        int mx = kIntMin;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-            mask |= (valid && win.has(b)) ? 1u << e : 0u;
-            if (valid && first) {
+        for (int e = 0; e < VEC; ++e)
+            mask |= (valid && win.has(__float_as_uint(VecT<VEC>::get(x, e)))) ? 1u << e : 0u;
+        if (first) {
+            // Branch free: a lane past the row adds nothing to the discard slot.
+            int mx = kIntMin;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 b = valid ? __float_as_uint(VecT<VEC>::get(x, e)) : 0u;
                 mx = max(mx, (int)b);
                 bin_add(b);
                 if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
             }
-        }
-        if (mx >= (int)kInfKey) {
+            if (mx >= (int)kInfKey) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x, e)) == kInfKey;
+                for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x, e)) == kInfKey;
+            }
         }
         if (__ballot(mask != 0) == 0) return;
         u64 c[VEC];
@@ -3782,7 +3818,8 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
             const u64 t = __umul64hi(u, ninf);
             o.kind = kInfRow;
             o.m = (u32)ninf;
-            o.token = comp_index(gather_select<VEC == 8>(s, gbuf, wcap, lo, hi, -1, t + 1, false, lcap).c);
+            o.token = comp_index(
+                gather_select<VEC == 8>(s, gbuf, wcap, lo, hi, -1, t + 1, false, lcap, ibits).c);
             u64 mn = ~0ull;
             for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
                 mn = (v && c >= lo && c < mn) ? c : mn;
@@ -3873,7 +3910,7 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
                 return bin ? fine_select<VEC == 8>(s, nl, f, W)
                            : select_buf(s, nl, W, true, fine_lo(f), fine_hi(f));
             return gather_select<VEC == 8>(s, gbuf, wcap, fine_lo(f), fine_hi(f), bin ? f : -1, W,
-                                           true, lcap);
+                                           true, lcap, ibits);
         };
         if (!fb) {
             u32 nl = collect_need();
