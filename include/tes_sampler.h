@@ -267,7 +267,9 @@ const char *sampler_status_string(int status);
  *       5 top-k row decided by one compacting pass over the whole row
  *         (its sampled threshold could not decide it: too few sampled
  *         entries with a mass, or a run of equal values that overflowed
- *         the candidate buffer);
+ *         the candidate buffer),
+ *       6 top-p-only row decided by one workgroup (TES_FLAG_ROW_TOPP, or a
+ *         launch with more top-p-only segments than resident workgroups);
  *   [1] kind: 0 normal, 1 +inf row, 2 zero-mass row;
  *   [2] segments the row was cut into;
  *   [3] candidate-buffer compactions (paths 0 and 5) or passes over the row
@@ -281,6 +283,10 @@ const char *sampler_status_string(int status);
  *       bits 8..15), 4 second exchange timed out, 8 inconsistent fine bins,
  *       16 a segment gathered too many entries, 32 too many in total (these
  *       for top-p-only rows), 64 a top-k row's binned finish needed a sort;
+ *       path 6: 1 << 16 its appended entries overflowed (or it never
+ *       predicted its bins), 1 << 17 the boundary's bin was not appended
+ *       whole, 1 << 18 nor the draw's,
+ *       1 << 19 it fell back to whole-row passes (path 2);
  *   [8..15] wall-clock ticks spent in successive phases, summed over the
  *       row's workgroups: greedy [8] whole item; top-k [8] streaming,
  *       [9] the finish, [11] the sampled first part, [13] the rest of the
@@ -288,7 +294,10 @@ const char *sampler_status_string(int status);
  *       sorts; top-p-only [8] loads and histogram, [9] first exchange,
  *       [10] its analysis and the second publication, [11] second exchange,
  *       [12] gather and arrival, [13] the last segment's finish, [14] its
- *       loads, [15] its boundary select; other words 0.
+ *       loads, [15] its boundary select; other words 0.  Exception: with
+ *       renorm_out, [10] of a top-k or greedy row holds the number of kept
+ *       entries it recorded (renorm_out's row is then written without
+ *       reading the row again).
  * The wall clock is the device's constant 100 MHz counter.  Synchronises the
  * device.  `host_out` holds 16 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);

@@ -82,6 +82,14 @@ def test_config_parity_with_renorm(sampler, plain_sampler, orc, cfg, which):
         log("[gpu]   paths %s, kinds %s, gathered max %d" % (
             np.bincount(st[:, 0], minlength=5).tolist(),
             np.bincount(st[:, 1], minlength=3).tolist(), st[:, 4].max()))
+        # Top-k and greedy rows record their kept entries (stats word 10), and
+        # renorm_out's row is written from that list without a second read:
+        # the list holds exactly the row's nonzero renorm entries.
+        listed = np.isin(st[:, 0], [0, 4, 5])
+        nz = np.count_nonzero(np.asarray(gren).reshape(w.B, w.V), axis=1)
+        bad = np.flatnonzero(listed & (st[:, 10] != nz))
+        assert bad.size == 0, "kept lists differ from renorm_out: rows %s" % bad[:8]
+        log("[gpu]   %d rows written from kept lists" % int(listed.sum()))
 
 
 @pytest.mark.parametrize("which", ["stats", "plain"])

@@ -139,6 +139,8 @@ struct Decision {  // what renorm_out and the slab export need
     u64 c_keep;  // kept entries have composite >= c_keep
     u64 M_p;     // kept mass (normal rows)
     u64 c_k;     // the support is the entries with composite >= c_k (k_eff < V)
+    u32 nlist;   // with renorm_out: entries in the row's kept list, or kNoList
+    u32 pad;
 };
 
 struct PubC {  // first exchange of a top-p-only segment (and its gather count)
@@ -175,6 +177,7 @@ struct Params {
     u32 split;      // parts a top-k or greedy row may be split into (1 .. kMaxSplit)
     u32 slots;      // workgroups resident at once on the device
     u32 xparts;     // logit rows: partial maxima per row
+    u32 klist;      // renorm_out requested: rows that can record their kept lists
 };
 
 __device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
@@ -460,6 +463,7 @@ __device__ __forceinline__ Params params_from(const Smem& s) {
     p.split = uni(s.p.split);
     p.slots = uni(s.p.slots);
     p.xparts = uni(s.p.xparts);
+    p.klist = uni(s.p.klist);
     return p;
 }
 
@@ -2021,8 +2025,50 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
 // ---------------------------------------------------------------------------
 // Row completion
 // ---------------------------------------------------------------------------
+// Kept lists, recorded only when renorm_out is requested: a top-k or greedy
+// row, whose kept entries are all at hand when it finishes, writes their
+// composites (in no particular order) to the start of its exchange area and
+// their number to its Decision, so that the renorm kernel writes the row
+// without reading it again.  A row without mass keeps nothing (an empty
+// list); other rows (top-p-only rows) record kNoList and are re-read.
+constexpr u32 kNoList = ~0u;
+__device__ __forceinline__ u64* kept_list(const Params& p, u32 r) {
+    return reinterpret_cast<u64*>(ws_row(p, r));
+}
+// Writes the entries c[j] >= c_keep held by the workgroup's threads to row
+// r's kept list and returns their number.  Entries below c_keep (zero
+// padding included; c_keep > 0) are skipped.  All threads call it; the
+// exchange area must no longer be read by anyone.
+template <int J>
+__device__ u32 emit_kept(Smem& s, const Params& p, u32 r, const u64 (&c)[J], u64 c_keep) {
+    u32 cnt = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) cnt += c[j] >= c_keep ? 1u : 0u;
+    const u64 x = wave_incl_scan((u64)cnt);
+    if (lane_id() == 63) s.wpart[wave_id()] = x;
+    __syncthreads();
+    u64 pre = 0, tot = 0;
+    const u32 w0 = wave_id();
+#pragma unroll
+    for (u32 w = 0; w < (u32)kWaves; ++w) {
+        const u64 t = s.wpart[w];
+        pre += w < w0 ? t : 0ull;
+        tot += t;
+    }
+    __syncthreads();
+    TES_GLOBAL u64* list = gp(kept_list(p, r));
+    u32 pos = (u32)(pre + x) - cnt;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const bool take = c[j] >= c_keep;
+        if (take) list[pos] = c[j];
+        pos += take ? 1u : 0u;
+    }
+    return (u32)tot;
+}
+
 __device__ void finish_row(Smem& s, const Params& p, u32 r, const Outcome& o, u32 path,
-                           u32 gathered) {
+                           u32 gathered, u32 nlist = kNoList) {
     if (threadIdx.x == 0) {
         if (p.out_tokens) *gp(&p.out_tokens[r]) = (int32_t)o.token;
         Decision* d = ws_decision(p, r);
@@ -2033,12 +2079,15 @@ __device__ void finish_row(Smem& s, const Params& p, u32 r, const Outcome& o, u3
         *gp(&d->c_keep) = o.c_keep;
         *gp(&d->c_k) = o.c_k;
         *gp(&d->M_p) = o.M_p;
+        const u32 nl = o.kind == kZeroRow ? 0u : nlist;
+        *gp(&d->nlist) = nl;
         if (p.stats) {
             u32* st = p.stats + kStatWords * (size_t)(p.row_base + r);
             *gp(&st[0]) = path;
             *gp(&st[1]) = o.kind;
             *gp(&st[4]) = gathered;
             *gp(&st[5]) = (u32)wall_clock64();
+            if (nlist != kNoList) *gp(&st[10]) = nl;
         }
     }
 }
@@ -2185,7 +2234,9 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     o.m = 1;
     o.M_p = key_mass(key);
     o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
-    finish_row(s, p, r, o, kPathGreedy, 0);
+    // The kept entry is the token.
+    if (p.klist && threadIdx.x == 0) *gp(kept_list(p, r)) = cbest;
+    finish_row(s, p, r, o, kPathGreedy, 0, p.klist ? 1u : kNoList);
 }
 
 // ---------------------------------------------------------------------------
@@ -2646,7 +2697,19 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         if (binned_topk<MINP>(s, n, k, tkey, P, u, ob, wfill, theta)) {
             stat_phase(p, r, 9, tp);
             if (c_k != ~0ull) ob.c_k = c_k;
-            finish_row(s, p, r, ob, path, gathered);
+            u32 nl = kNoList;
+            if (p.klist && ob.kind != kZeroRow) {
+                // The binned finish left the n entries packed at the buffer's start.
+                constexpr int J = kSlabCap / kBlock;
+                u64 c[J];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const u32 i = threadIdx.x + (u32)j * kBlock;
+                    c[j] = i < n ? sbuf(s)[i] : 0ull;
+                }
+                nl = emit_kept<J>(s, p, r, c, ob.c_keep);
+            }
+            finish_row(s, p, r, ob, path, gathered, nl);
             return;
         }
         stat_why(p, r, 64u);
@@ -2660,25 +2723,28 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
     __syncthreads();
     u64 ts = stat_phase(p, r, 14, tp);
     Outcome o;
+    u32 nl = kNoList;
+    // The sorted entries (zeros past n) stay in the threads' registers.
+    auto sorted = [&](auto& v) {
+        constexpr int E = sizeof(v) / sizeof(u64);
+        sort_desc<E>(s, v);
+        ts = stat_phase(p, r, 15, ts);
+        o = resolve_sorted<E, MINP>(s, v, k, P, u, theta);
+        if (p.klist && o.kind != kZeroRow) nl = emit_kept<E>(s, p, r, v, o.c_keep);
+    };
     if (pad == kBlock) {
         u64 v[1];
-        sort_desc<1>(s, v);
-        ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<1, MINP>(s, v, k, P, u, theta);
+        sorted(v);
     } else if (pad == 2 * kBlock) {
         u64 v[2];
-        sort_desc<2>(s, v);
-        ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<2, MINP>(s, v, k, P, u, theta);
+        sorted(v);
     } else {
         u64 v[4];
-        sort_desc<4>(s, v);
-        ts = stat_phase(p, r, 15, ts);
-        o = resolve_sorted<4, MINP>(s, v, k, P, u, theta);
+        sorted(v);
     }
     stat_phase(p, r, 9, tp);
     if (c_k != ~0ull) o.c_k = c_k;
-    finish_row(s, p, r, o, path, gathered);
+    finish_row(s, p, r, o, path, gathered, nl);
 }
 
 // ---------------------------------------------------------------------------
@@ -4121,29 +4187,30 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
 }
 
 // renorm_out[r][i] = q_i / M_p for kept entries (1/m for kept +inf), else 0
-// (q from the weights for logit rows).
+// (q from the weights for logit rows).  Each workgroup writes one contiguous
+// range of at most kRenormSpan entries of a row.  A row with a kept list is
+// written without being read: the list's entries in the range are stored by
+// the threads that read them from the list and marked in an LDS bitmap, then
+// the range's other entries are stored as zeros (each entry has one writer).
+// Rows without a list are read, and each entry tested against c_keep.
+constexpr u32 kRenormSpan = 32768;
 template <int VEC, bool LG>
 __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decision* __restrict__ dec,
                                                          float* __restrict__ out) {
     typedef typename VecT<VEC>::T VT;
+    __shared__ u32 marks[kRenormSpan / 32];
     const u32 r = blockIdx.y;
     const u32 V = p.V, nvec = p.nvec;
     const Decision d = dec[r];
-    const RowXf xf = row_xf<LG>(p, r);
-    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, V));
+    const u32 per = (nvec + gridDim.x - 1) / gridDim.x;
+    const u32 v0 = min(blockIdx.x * per, nvec), v1 = min(v0 + per, nvec);
     float* __restrict__ orow = out + (size_t)r * V;
     const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
     const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
-    for (u32 iv = blockIdx.x * 256 + threadIdx.x; iv < nvec; iv += gridDim.x * 256) {
-        const VT x = xform<VEC, LG>(xf, rv[iv]);
-        float o[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x, e)));
-            const bool kept = d.kind != kZeroRow && composite(key, iv * VEC + e) >= d.c_keep;
-            o[e] = !kept ? 0.0f
-                         : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
-        }
+    auto value = [&](u32 key) {
+        return d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv);
+    };
+    auto store = [&](u32 iv, const float (&o)[VEC]) {
         if constexpr (VEC == 4) {
             reinterpret_cast<f4*>(orow)[iv] = f4{o[0], o[1], o[2], o[3]};
         } else if constexpr (VEC == 8) {
@@ -4152,6 +4219,47 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decisio
         } else {
             orow[iv] = o[0];
         }
+    };
+    if (d.nlist != kNoList && (v1 - v0) * VEC <= kRenormSpan) {
+        const u32 e0 = v0 * VEC, e1 = v1 * VEC;
+        for (u32 i = threadIdx.x; i < kRenormSpan / 32; i += 256) marks[i] = 0;
+        __syncthreads();
+        const u64* list = kept_list(p, r);
+        for (u32 i = threadIdx.x; i < d.nlist; i += 256) {
+            const u64 c = ld_g(&list[i]);
+            const u32 idx = comp_index(c);
+            if (idx >= e0 && idx < e1) {
+                atomicOr(&marks[(idx - e0) >> 5], 1u << ((idx - e0) & 31));
+                orow[idx] = value(comp_key(c));
+            }
+        }
+        __syncthreads();
+        for (u32 iv = v0 + threadIdx.x; iv < v1; iv += 256) {
+            const u32 off = (iv - v0) * VEC;
+            const u32 m = (marks[off >> 5] >> (off & 31)) & ((1u << VEC) - 1u);
+            if (m == 0) {
+                const float z[VEC] = {};
+                store(iv, z);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (!((m >> e) & 1u)) orow[(size_t)iv * VEC + e] = 0.0f;
+            }
+        }
+        return;
+    }
+    const RowXf xf = row_xf<LG>(p, r);
+    const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(p.probs, r, V));
+    for (u32 iv = v0 + threadIdx.x; iv < v1; iv += 256) {
+        const VT x = xform<VEC, LG>(xf, rv[iv]);
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const u32 key = sanitize(__float_as_uint(VecT<VEC>::get(x, e)));
+            const bool kept = d.kind != kZeroRow && composite(key, iv * VEC + e) >= d.c_keep;
+            o[e] = kept ? value(key) : 0.0f;
+        }
+        store(iv, o);
     }
 }
 
@@ -4739,7 +4847,11 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
     const Decision* dec =
         reinterpret_cast<const Decision*>(s->ws + (size_t)s->chunk * sizeof(RowState));
     if (ro) {
-        const u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
+        // About four vectors per thread, at most 64 workgroups per row unless
+        // a workgroup's range would exceed kRenormSpan entries.
+        const u32 gmin = ceil_div(nvec, kRenormSpan / (u32)VEC);
+        u32 gx = ceil_div(nvec, 256 * 4) < 64 ? ceil_div(nvec, 256 * 4) : 64;
+        gx = gx < gmin ? gmin : gx;
         hipLaunchKernelGGL((tes_renorm_kernel<VEC, LG>), dim3(gx, rows), dim3(256), 0, st, p, dec,
                            ro);
         if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
@@ -4828,6 +4940,7 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
         p.flags = s->flags;
+        p.klist = renorm_out ? 1u : 0u;
         // Top-k and greedy rows may be split into up to kMaxSplit parts of at
         // least kMinPartVec vectors (the kernel splits only when every part
         // is resident at once).
