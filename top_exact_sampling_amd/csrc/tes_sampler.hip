@@ -177,7 +177,6 @@ struct Params {
     u32 split;      // parts a top-k or greedy row may be split into (1 .. kMaxSplit)
     u32 slots;      // workgroups resident at once on the device
     u32 xparts;     // logit rows: partial maxima per row
-    u32 klist;      // renorm_out requested: rows that can record their kept lists
 };
 
 __device__ __forceinline__ RowState* ws_state(const Params& p, u32 r) {
@@ -463,7 +462,6 @@ __device__ __forceinline__ Params params_from(const Smem& s) {
     p.split = uni(s.p.split);
     p.slots = uni(s.p.slots);
     p.xparts = uni(s.p.xparts);
-    p.klist = uni(s.p.klist);
     return p;
 }
 
@@ -1030,9 +1028,12 @@ template <bool LG>
 __device__ __forceinline__ RowXf row_xf(const Params& p, u32 r) {
     RowXf t{0.0f, 0.0f, 1.0f};
     if constexpr (LG) {
+        // The parts' loads issue together (indices past the last part reread it).
         const XMax* xm = ws_xmax(p, r);
         u32 e = 0;
-        for (u32 i = 0; i < p.xparts; ++i) e = max(e, uni(ld_g(&xm->part[i])));
+#pragma unroll
+        for (u32 i = 0; i < kXParts; ++i) e = max(e, ld_g(&xm->part[min(i, p.xparts - 1)]));
+        e = uni(e);
         const u32 bits = (e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e;  // order-preserving decode
         const float tau = p.temperature ? ld_g(&p.temperature[r]) : 1.0f;
         t.r = !(tau > 0.0f) ? __uint_as_float(kInfKey) : (float)(1.0 / (double)tau);
@@ -1122,29 +1123,28 @@ __device__ __forceinline__ u32 filter_regions(Smem& s, u32 reg, u32 n, Pred pred
     return total;
 }
 
-// Collects the composites of this workgroup's register-resident entries whose
-// raw bits satisfy pred (which must accept only bits <= those of +inf, i.e.
-// keys that sanitising leaves unchanged) and writes the first `cap`
-// (<= kSelCap) of them to
-// out[0, cap) with device-coherent stores.  Each wave first appends to its
-// own LDS region of kSelCap / 8 entries (scalar running count plus the lane's
-// rank in the element's ballot, no atomics); the regions are then packed.
-// Returns how many there are, which may exceed cap (or be reported as cap + 1
-// when a wave's region overflowed).
-template <int VEC, int NS, typename Pred>
-__device__ __forceinline__ u32 gather_regs(Smem& s, const typename VecT<VEC>::T (&x)[NS], u32 v0,
-                                           u32 v1, Pred pred, u64* out, u32 cap) {
+// Collects the composites of this workgroup's entries of a segment whose raw
+// bits satisfy pred (which must accept only bits <= those of +inf, i.e. keys
+// that sanitising leaves unchanged) and writes the first `cap` (<= kSelCap)
+// of them to out[0, cap) with device-coherent stores.  each(f) calls f(x,
+// i, in) for every vector x (index i, in: inside the segment) the thread
+// holds, the same number of times in every thread.  Each wave first appends
+// to its own LDS region of kSelCap / 8 entries (scalar running count plus the
+// lane's rank in the element's ballot, no atomics); the regions are then
+// packed.  Returns how many there are, which may exceed cap (or be reported
+// as cap + 1 when a wave's region overflowed).
+template <int VEC, typename Each, typename Pred>
+__device__ __forceinline__ u32 gather_seg(Smem& s, Each each, Pred pred, u64* out, u32 cap) {
+    typedef typename VecT<VEC>::T VT;
     constexpr u32 kReg = kSelCap / kWaves;
     const u32 wave = uni(wave_id());
     u64* const reg = sbuf(s) + wave * kReg;
     u32 wfill = 0;
-#pragma unroll
-    for (int d = 0; d < NS; ++d) {
-        const u32 i = v0 + d * kBlock + threadIdx.x;
+    each([&](const VT& x, u32 i, bool in) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const u32 key = __float_as_uint(VecT<VEC>::get(x[d], e));
-            const bool take = i < v1 && pred(key);
+            const u32 key = __float_as_uint(VecT<VEC>::get(x, e));
+            const bool take = in && pred(key);
             const u64 m = __ballot(take);
             if (m) {
                 const u32 pos = wfill + mbcnt64(m);
@@ -1152,7 +1152,7 @@ __device__ __forceinline__ u32 gather_regs(Smem& s, const typename VecT<VEC>::T 
                 wfill += (u32)__popcll(m);
             }
         }
-    }
+    });
     if (lane_id() == 0) s.gn[wave] = wfill;
     __syncthreads();
     u32 total = 0, before = 0;
@@ -2032,6 +2032,11 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
 // without reading it again.  A row without mass keeps nothing (an empty
 // list); other rows (top-p-only rows) record kNoList and are re-read.
 constexpr u32 kNoList = ~0u;
+// Launch flag (beside the sampler's TES_FLAG_* bits, which never use it):
+// renorm_out was requested.  (A flag rather than another parameter word: the
+// parameters sit in LDS ahead of the work regions, whose placement the
+// streams' bank conflicts are sensitive to.)
+constexpr u32 kFlagKeepList = 0x80000000u;
 __device__ __forceinline__ u64* kept_list(const Params& p, u32 r) {
     return reinterpret_cast<u64*>(ws_row(p, r));
 }
@@ -2235,8 +2240,8 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     o.M_p = key_mass(key);
     o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
     // The kept entry is the token.
-    if (p.klist && threadIdx.x == 0) *gp(kept_list(p, r)) = cbest;
-    finish_row(s, p, r, o, kPathGreedy, 0, p.klist ? 1u : kNoList);
+    if ((p.flags & kFlagKeepList) && threadIdx.x == 0) *gp(kept_list(p, r)) = cbest;
+    finish_row(s, p, r, o, kPathGreedy, 0, (p.flags & kFlagKeepList) ? 1u : kNoList);
 }
 
 // ---------------------------------------------------------------------------
@@ -2698,7 +2703,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
             stat_phase(p, r, 9, tp);
             if (c_k != ~0ull) ob.c_k = c_k;
             u32 nl = kNoList;
-            if (p.klist && ob.kind != kZeroRow) {
+            if ((p.flags & kFlagKeepList) && ob.kind != kZeroRow) {
                 // The binned finish left the n entries packed at the buffer's start.
                 constexpr int J = kSlabCap / kBlock;
                 u64 c[J];
@@ -2730,7 +2735,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         sort_desc<E>(s, v);
         ts = stat_phase(p, r, 15, ts);
         o = resolve_sorted<E, MINP>(s, v, k, P, u, theta);
-        if (p.klist && o.kind != kZeroRow) nl = emit_kept<E>(s, p, r, v, o.c_keep);
+        if ((p.flags & kFlagKeepList) && o.kind != kZeroRow) nl = emit_kept<E>(s, p, r, v, o.c_keep);
     };
     if (pad == kBlock) {
         u64 v[1];
@@ -2915,13 +2920,36 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // as its load returns (loads are issued, and waited for, in order).
     for (int i = (int)threadIdx.x - 1; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
     __syncthreads();
-    VT x[kSlots<VEC>];
+    // Probability rows hold the segment in registers from here to the
+    // candidate collection after the second publication.  Logit rows stream
+    // it twice instead (their weights are computed where a vector is
+    // consumed): the weights' arithmetic on top of the held segment would
+    // exceed the registers, and the spills serialise the loads.
+    VT x[LG ? 1 : kSlots<VEC>];
+    if constexpr (!LG) {
 #pragma unroll
-    for (int d = 0; d < kSlots<VEC>; ++d) {
-        const u32 i = v0 + d * kBlock + threadIdx.x;
-        x[d] = ld_stream(&rv[i < v1 ? i : v1 - 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int d = 0; d < kSlots<VEC>; ++d) {
+            const u32 i = v0 + d * kBlock + threadIdx.x;
+            x[d] = ld_stream(&rv[i < v1 ? i : v1 - 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    const float* seg_row = reinterpret_cast<const float*>(rv + v0);
+    // Visits the segment: f(x, i, in) for each vector x (weights for logit
+    // rows) of index i the thread holds (in: inside the segment).
+    auto seg_each = [&](auto f) {
+        if constexpr (LG) {
+            for_each_vec<VEC, kPassDepth, true>(seg_row, v1 - v0, [&](const VT& w, u32 iv, bool valid) {
+                f(w, v0 + iv, valid);
+            }, xf);
+        } else {
+#pragma unroll
+            for (int d = 0; d < kSlots<VEC>; ++d) {
+                const u32 i = v0 + d * kBlock + threadIdx.x;
+                f(x[d], i, i < v1);
+            }
+        }
+    };
     // Branch-free binning of the raw bits: the bin index (key >> 16) - base
     // clamped to [-1, kFineBins - 1] sends keys below 2^-32 to the discard
     // slot and keys >= 1.0, +inf, NaN and negative bits to the top bin; the
@@ -2933,27 +2961,33 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     // only by waves that hold one.
     constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256, the largest float below 2^32
     u64 ninf = 0;
-#pragma unroll
-    for (int d = 0; d < kSlots<VEC>; ++d) {
-        const u32 i = v0 + d * kBlock + threadIdx.x;
-        // Logit rows keep their weights in the registers from here on.
-        x[d] = xform<VEC, LG>(xf, x[d]);
-        if (i < v1) {
+    // Min-p on logit rows: the largest mass is that of the top weight 1
+    // (2^32), so the floor and its key are known up front; the segment adds
+    // up the mass of its entries at or above the floor's key as it bins them.
+    u64 mf = 0;
+    float theta = 0.0f;
+    if constexpr (LG) theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
+    const u32 kf = minp_key(minp_floor(theta, 1ull << 32));
+    const bool minp = LG && kf > 1u;
+    auto hist_vec = [&](const VT& w, bool in) {
+        if (in) {
             int mx = kIntMin;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
+                const u32 b = __float_as_uint(VecT<VEC>::get(w, e));
                 mx = max(mx, (int)b);
                 const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, -1), kFineBins - 1);
                 const float q = fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
                 atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)(u32)q);
+                if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
             }
             if (__ballot(mx >= (int)kInfKey)) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x[d], e)) == kInfKey;
+                for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(w, e)) == kInfKey;
             }
         }
-    }
+    };
+    seg_each([&](const VT& w, u32, bool in) { hist_vec(w, in); });
     // Accumulators of the exchanges (ordered by the barriers below).
     for (int i = threadIdx.x; i < kCoarseBins; i += kBlock) s.coarse[i] = 0;
     for (int i = threadIdx.x; i < kDMax * 16; i += kBlock) s.finem[i] = 0;
@@ -2968,26 +3002,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     for (int i = threadIdx.x; i < kFineBins; i += kBlock) M += shfine(s)[i];
     M = block_sum(s, M);
     ninf = block_sum(s, ninf);
-    // Min-p on logit rows: the largest mass is that of the top weight 1
-    // (2^32), so the floor and its key are known before any exchange; each
-    // segment adds up the mass of its entries at or above the floor's key
-    // (the registers hold the weights).
-    u64 mf = 0;
-    float theta = 0.0f;
-    if constexpr (LG) theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
-    const u32 kf = minp_key(minp_floor(theta, 1ull << 32));
-    if (LG && kf > 1u) {
-#pragma unroll
-        for (int d = 0; d < kSlots<VEC>; ++d) {
-            const u32 i = v0 + d * kBlock + threadIdx.x;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
-                mf += (i < v1 && b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
-            }
-        }
-        mf = block_sum(s, mf);
-    }
+    if (minp) mf = block_sum(s, mf);
     tp = stat_phase(p, r, 8, tp);
 
     // First exchange: this segment's mass, +inf count and coarse histogram.
@@ -3092,21 +3107,20 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         const u32 kB0 = ckey0(cb), wB = ckey1(cb) - kB0;
         const u32 kR0 = ckey0(min(clo, chi)), wR = ckey1(max(clo, chi)) - kR0;
         u64* sreg = sbuf(s) + wave * kSpecReg;
-#pragma unroll
-        for (int d = 0; d < kSlots<VEC>; ++d) {
-            const u32 i = v0 + d * kBlock + threadIdx.x;
+        auto collect = [&](const VT& w, u32 i, bool in) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const u32 b = __float_as_uint(VecT<VEC>::get(x[d], e));
-                const bool take = (i < v1) & ((b - kB0 < wB) | (b - kR0 < wR));
+                const u32 b = __float_as_uint(VecT<VEC>::get(w, e));
+                const bool take = in & ((b - kB0 < wB) | (b - kR0 < wR));
                 const u64 m = __builtin_amdgcn_ballot_w64(take);
                 if (m) {
-                    if ((i < v1) & ((b - kB0 < wB) | (b - kR0 < wR)))
+                    if (in & ((b - kB0 < wB) | (b - kR0 < wR)))
                         sreg[min(sfill + mbcnt64(m), kSpecReg - 1)] = composite(b, i * VEC + e);
                     sfill += (u32)__popcll(m);
                 }
             }
-        }
+        };
+        seg_each(collect);
         if (lane_id() == 0) s.gn[32 + wave] = sfill;  // read after the barriers below
     }
     const bool ok2 = wait_arrivals(s, &rs->arrive_b, nseg);
@@ -3159,11 +3173,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             if (spec_ok)
                 ng = filter_regions(s, kSpecReg, sfill, pred, garea, gcap);
             else
-                ng = gather_regs<VEC, kSlots<VEC>>(s, x, v0, v1, pred, garea, gcap);
+                ng = gather_seg<VEC>(s, seg_each, pred, garea, gcap);
         }
     } else if (!failed && kind == kInfRow) {
-        ng = gather_regs<VEC, kSlots<VEC>>(s, x, v0, v1, [&](u32 key) { return key == kInfKey; },
-                                          garea, gcap);
+        ng = gather_seg<VEC>(s, seg_each, [&](u32 key) { return key == kInfKey; }, garea, gcap);
     }
     if (threadIdx.x == 0) st_dev(&pc->ng, (u64)ng);
     const bool last = arrive_last(s, &rs->ticket, nseg);
@@ -4940,7 +4953,7 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
         p.flags = s->flags;
-        p.klist = renorm_out ? 1u : 0u;
+        if (renorm_out) p.flags |= kFlagKeepList;
         // Top-k and greedy rows may be split into up to kMaxSplit parts of at
         // least kMinPartVec vectors (the kernel splits only when every part
         // is resident at once).
