@@ -448,6 +448,43 @@ def test_restream_rows(sampler, orc, V):
     assert (st[:, 0] == 5).sum() >= 8, "the compacting pass did not run"
 
 
+@pytest.mark.parametrize("B", [20, 200])
+def test_rows_with_fewer_positive_keys_than_k(sampler, orc, B):
+    # A top-k row with fewer positive keys than k (mostly zeros, as a logit
+    # row at temperature 0 has) is decided by its first stream, split (B=20:
+    # eight parts per row) or not (B=200), without the compacting pass.
+    rng = np.random.default_rng(B + 71)
+    V = 20000
+    probs = np.zeros((B, V), np.float32)
+    ks = np.empty(B, np.int32)
+    short = np.zeros(B, bool)
+    for b in range(B):
+        m = int(rng.integers(0, 900))
+        idx = rng.choice(V, m, replace=False)
+        kind = b % 5
+        if kind == 0:
+            probs[b, idx] = rng.random(m).astype(np.float32) + 0.01
+        elif kind == 1:
+            probs[b, idx] = np.float32(1.0 / max(m, 1))  # ties
+        elif kind == 2:
+            probs[b, idx] = np.float32(1e-12)  # positive keys without a mass
+        elif kind == 3:
+            probs[b, idx] = rng.random(m).astype(np.float32)
+            probs[b, idx[:2]] = np.inf
+        else:
+            probs[b, idx] = rng.random(m).astype(np.float32)
+            probs[b, rng.choice(V, 3)] = -1.0
+        ks[b] = int(rng.integers(m + 1, 1025)) if m < 1024 else 1024
+        short[b] = m < ks[b] and ks[b] >= 2
+    ps = rng.uniform(0.3, 1.0, B).astype(np.float32)
+    log("[gpu] rows with fewer positive keys than k, B=%d" % B)
+    gtok, gren = run_gpu(sampler, probs, ks, ps, 17, 5, renorm=True)
+    st = sampler.stats(B)
+    log("[gpu]   paths %s" % np.bincount(st[:, 0], minlength=6).tolist())
+    assert_parity(orc, probs, ks, ps, 17, 5, gtok, gren, "fewer positives B=%d" % B)
+    assert np.all(st[short, 0] == 0), "rows took paths %s" % np.unique(st[short, 0])
+
+
 def test_wide_topp_bins_stay_on_the_fast_path(sampler, orc):
     # High-entropy rows at the speculative-verify shape gather more boundary
     # and draw entries than one buffer holds; the finish takes them one fine

@@ -2288,6 +2288,52 @@ __device__ u32 mth_zero_index(Smem& s, const float* __restrict__ row, u32 nvec, 
     return ~0u;
 }
 
+// A top-k row whose buffer sbuf(s)[0, n) holds every entry of the row with a
+// positive key, n < k: the support is those n entries and the k - n
+// lowest-indexed zeros, the last of which is its boundary.  The zeros carry
+// no mass, so they are never kept or drawn; only a support without mass
+// looks at them (its token is the smallest index in it).
+template <int VEC, bool LG>
+__device__ __noinline__ void slab_short(Smem& s, u32 r, u32 n, u32 k, u64 P, u64 u, u32 path) {
+    const Params p = params_from(s);
+    const RowXf xf = row_xf<LG>(p, r);
+    const float* row = row_ptr<VEC>(p.probs, r, p.V);
+    if (n == 0) {
+        // No positive key anywhere: the support is indices [0, k), its
+        // boundary index k - 1 and its token 0.
+        Outcome o{};
+        o.kind = kZeroRow;
+        o.token = 0;
+        o.c_k = composite(0u, k - 1);
+        finish_row(s, p, r, o, path, 0);
+        return;
+    }
+    u64 mn = ~0ull, mass = 0, midx = ~0ull;
+    for (u32 i = threadIdx.x; i < n; i += kBlock) {
+        const u64 c = sbuf(s)[i];
+        mn = c < mn ? c : mn;
+        mass += key_mass(comp_key(c));
+        midx = comp_index(c) < midx ? comp_index(c) : midx;
+    }
+    mn = block_min(s, mn);
+    mass = block_sum(s, mass);
+    const u32 zk = mth_zero_index<VEC, LG>(s, row, p.nvec, k - n, xf);
+    const u64 c_k = composite(0u, zk);
+    if (mass > 0) {
+        // The binned finish's base: at most 1.0, so that +inf entries land in
+        // its top bin, where it looks for them.
+        slab_finish<LG>(s, r, n, n, min(comp_key(mn), kOneKey) & ~0xFFFFu, P, u, ~0u, path, c_k);
+        return;
+    }
+    midx = block_min(s, midx);
+    const u32 z = mth_zero_index<VEC, LG>(s, row, p.nvec, 1, xf);
+    Outcome o{};
+    o.kind = kZeroRow;
+    o.token = (u32)(midx < (u64)z ? midx : (u64)z);
+    o.c_k = c_k;
+    finish_row(s, p, r, o, path, n);
+}
+
 // Exact single pass over the whole row for a top-k row (k <= kSlabMaxK) that
 // its sampled threshold could not decide: a sample with too few entries with a
 // mass, a candidate buffer that overflowed (long runs of equal values at the
@@ -2359,50 +2405,18 @@ __device__ __noinline__ void slab_restream(Smem& s, u32 r, u32 k, u32 theta0, u6
     const u32 n = uni(s.ctr[3]);
     __syncthreads();
     stat_add(p, r, 3, cuts);
-    u64 mn = ~0ull, mass = 0, midx = ~0ull;
-    for (u32 i = threadIdx.x; i < n; i += kBlock) {
-        const u64 c = sbuf(s)[i];
-        mn = c < mn ? c : mn;
-        mass += key_mass(comp_key(c));
-        midx = comp_index(c) < midx ? comp_index(c) : midx;
+    if (n < k) {
+        // Fewer than k positive keys (theta0 = 1: from a threshold the row
+        // has at least k): the buffer holds every one of them.
+        slab_short<VEC, LG>(s, r, n, k, P, u, kPathSlabFallback);
+        return;
     }
+    u64 mn = ~0ull;
+    for (u32 i = threadIdx.x; i < n; i += kBlock) mn = sbuf(s)[i] < mn ? sbuf(s)[i] : mn;
     mn = block_min(s, mn);
-    mass = block_sum(s, mass);
     // The binned finish's base: at most 1.0, so that +inf entries land in its
     // top bin, where it looks for them.
-    const u32 tkey = n ? min(comp_key(mn), kOneKey) & ~0xFFFFu : 0u;
-    if (n >= k) {
-        slab_finish<LG>(s, r, n, k, tkey, P, u, ~0u, kPathSlabFallback);
-        return;
-    }
-    if (n == 0 && theta0 == 1u) {
-        // No positive key anywhere: every entry is a zero, so the support is
-        // indices [0, k), its boundary index k - 1 and its token (the
-        // smallest index of a support without mass) 0.
-        Outcome o{};
-        o.kind = kZeroRow;
-        o.token = 0;
-        o.c_k = composite(0u, k - 1);
-        finish_row(s, p, r, o, kPathSlabFallback, 0);
-        return;
-    }
-    // n < k: the support ends with the k - n lowest-indexed zeros; its
-    // boundary is the last of them.
-    const u32 zk = mth_zero_index<VEC, LG>(s, row, p.nvec, k - n, xf);
-    const u64 c_k = composite(0u, zk);
-    if (n > 0 && mass > 0) {
-        // The zeros carry no mass: they change nothing else.
-        slab_finish<LG>(s, r, n, n, tkey, P, u, ~0u, kPathSlabFallback, c_k);
-        return;
-    }
-    // No mass in the support: its smallest index.
-    midx = block_min(s, midx);
-    const u32 z = mth_zero_index<VEC, LG>(s, row, p.nvec, 1, xf);
-    Outcome o{};
-    o.kind = kZeroRow;
-    o.token = (u32)(midx < (u64)z ? midx : (u64)z);
-    o.c_k = c_k;
-    finish_row(s, p, r, o, kPathSlabFallback, n);
+    slab_finish<LG>(s, r, n, k, min(comp_key(mn), kOneKey) & ~0xFFFFu, P, u, ~0u, kPathSlabFallback);
 }
 
 // Streams its part of the row (the whole row, or one of S <= kMaxSplit parts
@@ -2490,11 +2504,10 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
     }
     __syncthreads();  // the histogram is dead; the buffer takes its place
     const bool no_tkey = tkey == 0;
-    if (no_tkey && S > 1) tkey = kInfKey;  // stream on; the part reports itself unusable
     // Fewer than j sampled entries have a mass (a row of mostly zeros, or a
-    // short row with fewer than k): a whole row streams every positive key
-    // (its entries, if they fit, are then the whole support's mass).
-    if (no_tkey && S == 1) tkey = 1u;
+    // short row with fewer than k): the part streams every positive key (if
+    // they fit, the row's positive entries are then all at hand).
+    if (no_tkey) tkey = 1u;
     const u32 span = kInfKey - tkey;
     // Logit rows: the weights at or above tkey belong to logits >= xb.
     float xb = 0.0f;
@@ -2602,7 +2615,7 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         // candidates at or above the largest threshold T.
         RowState* rs = ws_state(p, r);
         HalfPub* mine = half_pub(p, r, h);
-        over = over || no_tkey || fill > kHalfCap;
+        over = over || fill > kHalfCap;
         if (!over) {
             u64* dst = half_cands(p, r, h);
             for (u32 i = threadIdx.x; i < fill; i += kBlock) st_dev(&dst[i], sbuf(s)[i]);
@@ -2660,22 +2673,19 @@ __device__ __attribute__((always_inline)) void do_slab(Smem& s, u32 r, u32 k, u3
         __syncthreads();
         fill = uni(s.ctr[3]);
         __syncthreads();
-        // At least k of them: the row's best k are among them.
-        over = over || fill > kSlabCap || fill < k;
+        over = over || fill > kSlabCap;
         tbase = tmax;
     }
+    // Every part streamed every positive key (thresholds of sampled parts
+    // are bin edges, far above 1) and nothing overflowed: the buffer holds
+    // all of the row's positive entries.
+    const bool all_pos = !over && tbase == 1u;
     if (!over && fill >= k) {
-        // (Every positive key: no bin base for the binned finish.)
-        slab_finish<LG>(s, r, fill, k, no_tkey ? 0u : tbase, P, u, direct ? wfill : ~0u);
-    } else if (no_tkey && S == 1 && !over && fill == 0) {
-        // No positive key anywhere: every entry is a zero, so the support is
-        // indices [0, k), its boundary index k - 1 and its token (the
-        // smallest index of a support without mass) 0.
-        Outcome o{};
-        o.kind = kZeroRow;
-        o.token = 0;
-        o.c_k = composite(0u, k - 1);
-        finish_row(s, p, r, o, kPathSlab, 0);
+        // (At least k entries at or above the threshold: the row's best k are
+        // among them.  Every positive key: no bin base for the binned finish.)
+        slab_finish<LG>(s, r, fill, k, tbase > 1u ? tbase : 0u, P, u, direct ? wfill : ~0u);
+    } else if (all_pos) {
+        slab_short<VEC, LG>(s, r, fill, k, P, u, kPathSlab);
     } else {
         // A whole row that counted at least k entries at or above its
         // threshold has its best k there; anything else starts from 1.
