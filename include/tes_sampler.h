@@ -283,9 +283,8 @@ const char *sampler_status_string(int status);
  *       bits 8..15), 4 second exchange timed out, 8 inconsistent fine bins,
  *       16 a segment gathered too many entries, 32 too many in total (these
  *       for top-p-only rows), 64 a top-k row's binned finish needed a sort;
- *       path 6: 1 << 16 its appended entries overflowed (or it never
- *       predicted its bins), 1 << 17 the boundary's bin was not appended
- *       whole, 1 << 18 nor the draw's,
+ *       path 6: 1 << 16 its appended entries overflowed, 1 << 17 the
+ *       boundary's bin was not appended whole, 1 << 18 nor the draw's,
  *       1 << 19 it fell back to whole-row passes (path 2);
  *   [8..15] wall-clock ticks spent in successive phases, summed over the
  *       row's workgroups: greedy [8] whole item; top-k [8] streaming,

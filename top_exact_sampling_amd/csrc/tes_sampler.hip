@@ -272,7 +272,12 @@ constexpr int kRegionBytes = 48 * 1024;
 
 struct Smem {
     Params p;                  // this launch's parameters (copied from the kernel arguments)
-    alignas(16) unsigned char region[kRegionBytes];
+    // Discard slots of the fine mass histograms, one per lane (slot -1 - lane
+    // of shfine; slot -1 is the region's first word): entries below the
+    // lowest bin (zeros) are added there, so a row of mostly zeros does not
+    // send every lane's atomic to one address.  Never read.
+    alignas(16) u64 discard[64];
+    unsigned char region[kRegionBytes];
     u64 coarse[kCoarseBins];   // summed coarse masses of a top-p-only row
     u64 csum[3];               // summed mass, +inf count and min-p mass of a top-p-only row
     u64 loc_above[4];          // results of the bin lookups (coarse and fine plans, fine_locate)
@@ -291,6 +296,9 @@ struct Smem {
     u32 npass;                 // passes over the row of the current item (statistics)
 };
 static_assert((kFineBins + 1) * 8 <= kRegionBytes, "fine histogram fits the region");
+static_assert(offsetof(Smem, region) == offsetof(Smem, discard) + sizeof(u64) * 64 &&
+                  offsetof(Smem, region) % 16 == 0,
+              "the discard slots sit just below the fine histogram's slot -1");
 
 __device__ __forceinline__ u64* sbuf(Smem& s) { return reinterpret_cast<u64*>(s.region); }
 __device__ __forceinline__ const u64* sbuf(const Smem& s) {
@@ -2961,8 +2969,9 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         }
     };
     // Branch-free binning of the raw bits: the bin index (key >> 16) - base
-    // clamped to [-1, kFineBins - 1] sends keys below 2^-32 to the discard
-    // slot and keys >= 1.0, +inf, NaN and negative bits to the top bin; the
+    // clamped to [-1 - lane, kFineBins - 1] sends keys below 2^-32 to the
+    // lane's discard slot and keys >= 1.0, +inf, NaN and negative bits to the
+    // top bin; the
     // mass floor(x * 2^32) clamped to [0, 2^32 - 256] is zero for NaN and
     // negatives, exact below 1.0, and 2^32 - 256 from 1.0 up, so the top bin
     // ends holding (2^32 - 256) times its count, whose mass is count * 2^32.
@@ -2979,6 +2988,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if constexpr (LG) theta = p.min_p ? ld_g(&p.min_p[r]) : 0.0f;
     const u32 kf = minp_key(minp_floor(theta, 1ull << 32));
     const bool minp = LG && kf > 1u;
+    const int dslot = -1 - (int)lane_id();  // this lane's discard slot
     auto hist_vec = [&](const VT& w, bool in) {
         if (in) {
             int mx = kIntMin;
@@ -2986,7 +2996,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             for (int e = 0; e < VEC; ++e) {
                 const u32 b = __float_as_uint(VecT<VEC>::get(w, e));
                 mx = max(mx, (int)b);
-                const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, -1), kFineBins - 1);
+                const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, dslot), kFineBins - 1);
                 const float q = fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
                 atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)(u32)q);
                 if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
@@ -3597,12 +3607,13 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     if (threadIdx.x == 0) s.npass = 0;
 
     // Fine binning of the segments, branch free: bin (key >> 16) - base
-    // clamped to [-1, kFineBins - 1] (-1 is the discard slot) and mass
-    // floor(x * 2^32) clamped to [0, 2^32 - 256]; the top bin's sum is then
-    // turned into count * 2^32.
+    // clamped to [-1 - lane, kFineBins - 1] (below 0: the lane's discard
+    // slot) and mass floor(x * 2^32) clamped to [0, 2^32 - 256]; the top
+    // bin's sum is then turned into count * 2^32.
     constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256
+    const int dslot = -1 - (int)lane_id();
     auto bin_add = [&](u32 b) -> u32 {
-        const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, -1), kFineBins - 1);
+        const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, dslot), kFineBins - 1);
         const u32 q = (u32)fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
         atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)q);
         return q;
@@ -3621,9 +3632,15 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
 
     // Prediction state (uniform): the bin ranges [tl, th] (boundary) and
     // [dl, dh] (draw), or the +inf window; appended since round j_start.
-    KeyWin win{0, 0, 0, 0};
-    int tl = 0, th = -1, dl = 0, dh = -1;
-    bool started = false, infwin = false;
+    // Before any prediction the window is the top bin (keys from 1.0 up: a
+    // probability row's entries of 1.0 or more, a logit row's entries at its
+    // maximum), appended from the first round.  A row whose mass all lies
+    // there (a logit row at temperature 0, a one-hot row) then needs no
+    // prediction, even when no update sees its mass.
+    constexpr int kTop = kFineBins - 1;
+    int tl = kTop, th = kTop, dl = kTop, dh = kTop;
+    KeyWin win = bins_win(tl, th, dl, dh);
+    bool started = true, infwin = false;
     u32 j_start = 0;
     u64 ninf = 0, mf = 0;
 
