@@ -120,7 +120,8 @@ struct RowState {  // zero between calls
     u32 arrive_b;  // top-p-only: second exchange
     u32 ticket;    // last-arriver ticket
     u32 flags;     // kFlagFail
-    u32 pad[12];
+    u32 vticket;   // speculative verification: last-arriver ticket of a request's chunks
+    u32 pad[11];
 };
 static_assert(sizeof(RowState) == 64, "row state size");
 
@@ -4430,17 +4431,20 @@ __global__ __launch_bounds__(kBlock) void tes_verify_kernel(Params p, SpecArgs a
         const u64 rej = __ballot(l < L && !acc);
         const u32 first = rej ? (u32)__builtin_ctzll(rej) : L;  // accepted drafts
         const u32 jf = (u32)__builtin_amdgcn_readlane(j, (int)(first < 64 ? first : 0));
+        // (Every chunk's workgroup takes the same decisions; chunk 0 writes them.)
+        const bool writer = blockIdx.y == 0;
         if (any_bad) {
-            if (l <= L) out[l] = -1;
-            if (l == 0) a.accept[n] = -1;
+            if (writer && l <= L) out[l] = -1;
+            if (writer && l == 0) a.accept[n] = -1;
         } else {
-            if (l < first) out[l] = d;
-            if (l > first && l <= L) out[l] = -1;
+            if (writer && l < first) out[l] = d;
+            if (writer && l > first && l <= L) out[l] = -1;
             if (l == 0) {
-                a.accept[n] = (int32_t)first;
+                if (writer) a.accept[n] = (int32_t)first;
                 res[0] = first;
                 res[1] = n * Lt + jf;  // the row of the rejection, or of the bonus
-                if (first == L) out[L] = (int32_t)ld_g(&ws_decision(p, n * Lt + jf)->token);
+                if (writer && first == L)
+                    out[L] = (int32_t)ld_g(&ws_decision(p, n * Lt + jf)->token);
             }
         }
         if (l == 0) res[2] = any_bad ? 1u : 0u;
@@ -4473,6 +4477,64 @@ __global__ __launch_bounds__(kBlock) void tes_verify_kernel(Params p, SpecArgs a
     u32 v0 = 0, v1 = p.nvec;
     u128 t = 0;
     bool have_t = false;
+    const u32 S = gridDim.y;
+    if (S > 1) {
+        // The vocabulary is cut into S chunks, one workgroup each: each sums
+        // its chunk's residual and publishes it in the exchange area of the
+        // request's first target row; the last to arrive locates t among
+        // the chunks and searches on within its chunk.
+        const u32 cv = (p.nvec + S - 1) / S;
+        const u32 c0 = min(blockIdx.y * cv, p.nvec), c1 = min(c0 + cv, p.nvec);
+        u64 hi = 0, lo = 0;
+#pragma unroll 4
+        for (u32 iv = c0 + threadIdx.x; iv < c1; iv += kBlock) {
+            u64 h, l2;
+            vec_parts(iv, h, l2);
+            hi += h;
+            lo += l2;
+        }
+        hi = block_sum_u64(wpart, hi);
+        lo = block_sum_u64(wpart, lo);
+        u64* pub = reinterpret_cast<u64*>(ws_row(p, n * Lt));
+        if (threadIdx.x == 0) {
+            st_dev(&pub[2 * blockIdx.y], hi);
+            st_dev(&pub[2 * blockIdx.y + 1], lo);
+        }
+        vm_wait();
+        __syncthreads();
+        RowState* rs = ws_state(p, n * Lt);
+        if (threadIdx.x == 0) {
+            const u32 tk = add_dev(&rs->vticket, 1u);
+            res[3] = tk == S - 1 ? 1u : 0u;
+            if (tk == S - 1) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                st_dev(&rs->vticket, 0u);  // zero between calls
+            }
+        }
+        __syncthreads();
+        if (res[3] == 0) return;
+        u128 all = 0;
+        for (u32 q = 0; q < S; ++q) all += from_parts(ld_g(&pub[2 * q]), ld_g(&pub[2 * q + 1]));
+        if (all == 0) {  // p <= q everywhere: the row's own token
+            if (threadIdx.x == 0) out[first] = (int32_t)dec.token;
+            return;
+        }
+        const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+        t = (u128)u * (u64)(all >> 64) + __umul64hi(u, (u64)all);
+        have_t = true;
+        u32 k = 0;
+        u128 before = 0;
+        for (u32 q = 0; q + 1 < S; ++q) {
+            const u128 m = from_parts(ld_g(&pub[2 * q]), ld_g(&pub[2 * q + 1]));
+            if (k == q && before + m <= t) {
+                before += m;
+                k = q + 1;
+            }
+        }
+        t -= before;
+        v0 = min(k * cv, p.nvec);
+        v1 = min(v0 + cv, p.nvec);
+    }
     while (true) {
         const u32 nv = v1 - v0;
         if (nv <= kBlock) break;
@@ -4906,7 +4968,13 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
             a.map = spec->map ? spec->map + n0 * (spec->L + 1) : nullptr;
             a.out = spec->out + n0 * (spec->L + 1);
             a.accept = spec->accept + n0;
-            hipLaunchKernelGGL(tes_verify_kernel<VEC>, dim3(rows / spec->Lt), dim3(kBlock), 0, st, p,
+            // Chunks per request: enough workgroups to fill the device (at
+            // most eight, and none for rows of one round).
+            const u32 nreq = rows / spec->Lt;
+            u32 S = s->slots / nreq;
+            S = S > 8 ? 8u : (S < 1 ? 1u : S);
+            if (nvec <= 2 * kBlock) S = 1;
+            hipLaunchKernelGGL(tes_verify_kernel<VEC>, dim3(nreq, S), dim3(kBlock), 0, st, p,
                                a);
             if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
         }
