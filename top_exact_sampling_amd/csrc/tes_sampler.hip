@@ -1073,7 +1073,7 @@ __device__ __forceinline__ float ord_dec(u32 e) {
 // raw logits against it and compute weights only for those that pass.  One
 // wave, 64 candidates per round (six rounds for 32 bits); all lanes of the
 // wave take part and get the same result.
-__device__ __noinline__ float logit_x_threshold(const RowXf& t, u32 wkey) {
+__device__ __attribute__((always_inline)) float logit_x_threshold(const RowXf& t, u32 wkey) {
     u32 lo = ord_enc(__uint_as_float(0xFF800000u));  // -inf: weight 0, fails
     u32 hi = ord_enc(t.M);                           // M: the top weight, passes
     const u32 lane = lane_id();
