@@ -642,12 +642,12 @@ __device__ __forceinline__ void wave_append_n(u64* arr, u32 mask, const u64 (&c)
     if ((int)lane_id() == leader) pos0 = atomicAdd(ctr, tot);
     pos0 = (u32)__builtin_amdgcn_readlane((int)pos0, leader);
     u32 pos = base + pos0 + pre;
+    // (One condition per store and a branch-free position.)
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-        if ((mask >> e) & 1u) {
-            if (pos < cap) arr[pos] = c[e];
-            ++pos;
-        }
+        const bool take = (mask >> e) & 1u;
+        if (take && pos < cap) arr[pos] = c[e];
+        pos += take ? 1u : 0u;
     }
 }
 
@@ -3382,10 +3382,11 @@ static_assert(5 * kWaves <= kCoarseBins, "fused reductions fit s.coarse");
 
 // The appended entries of a row: kWaves regions of `stride` slots at gbuf,
 // wave w's first s.gn[w] slots in use (written by this workgroup before a
-// barrier).  Calls f(c, valid) for all of them, taken as one sequence with
-// eight loads per thread in flight (every thread makes the same calls).
-template <typename F>
-__device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 stride, F f) {
+// barrier), taken as one sequence with eight loads per thread in flight.
+// Calls g(c, vmask) for each thread's batch of eight (bit k of vmask: c[k]
+// is an entry), the same number of times in every thread.
+template <typename G>
+__device__ __forceinline__ void for_each_gathered8(Smem& s, const u64* gbuf, u32 stride, G g) {
     u32 off[kWaves + 1];
     off[0] = 0;
 #pragma unroll
@@ -3393,6 +3394,7 @@ __device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 
     const u32 n = off[kWaves];
     for (u32 i0 = 0; i0 < n; i0 += 8 * kBlock) {
         u64 c[8];
+        u32 vm = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const u32 i = i0 + k * kBlock + threadIdx.x;
@@ -3402,10 +3404,30 @@ __device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 
             for (int w = 1; w < kWaves; ++w)
                 if (i >= off[w]) base = (u32)w * stride - off[w];
             c[k] = i < n ? ld_g(&gbuf[base + i]) : 0ull;
+            vm |= i < n ? 1u << k : 0u;
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) f(c[k], i0 + k * kBlock + threadIdx.x < n);
+        g(c, vm);
     }
+}
+// The same, calling f(c, valid) for each entry.
+template <typename F>
+__device__ __forceinline__ void for_each_gathered(Smem& s, const u64* gbuf, u32 stride, F f) {
+    for_each_gathered8(s, gbuf, stride, [&](const u64 (&c)[8], u32 vm) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f(c[k], ((vm >> k) & 1u) != 0);
+    });
+}
+// Appends the gathered entries that satisfy pred to sbuf(s) at s.ctr[3] (which
+// the caller has cleared), up to kSelCap: one LDS atomic per wave and batch
+// of eight (per-entry appends queued each batch behind eight round trips).
+template <typename Pred>
+__device__ __forceinline__ void append_gathered(Smem& s, const u64* gbuf, u32 stride, Pred pred) {
+    for_each_gathered8(s, gbuf, stride, [&](const u64 (&c)[8], u32 vm) {
+        u32 mask = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) mask |= (((vm >> k) & 1u) && pred(c[k])) ? 1u << k : 0u;
+        wave_append_n<8>(sbuf(s), mask, c, &s.ctr[3], 0, kSelCap);
+    });
 }
 
 // Select among the appended entries with composite in [lo, hi): at which the
@@ -3425,9 +3447,7 @@ __device__ Sel gather_select(Smem& s, const u64* gbuf, u32 stride, u64 lo, u64 h
     auto collect = [&](auto pred) -> u32 {
         if (threadIdx.x == 0) s.ctr[3] = 0;
         __syncthreads();
-        for_each_gathered(s, gbuf, stride, [&](u64 c, bool v) {
-            wave_append(sbuf(s), v && c >= lo && c < hi && pred(c), c, &s.ctr[3], 0, kSelCap);
-        });
+        append_gathered(s, gbuf, stride, [&](u64 c) { return c >= lo && c < hi && pred(c); });
         __syncthreads();
         const u32 n = uni(s.ctr[3]);
         __syncthreads();
@@ -4008,10 +4028,8 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
         auto collect_need = [&]() -> u32 {
             if (threadIdx.x == 0) s.ctr[3] = 0;
             __syncthreads();
-            for_each_gathered(s, gbuf, wcap, [&](u64 c, bool v) {
-                wave_append(sbuf(s), v && ha.has(comp_key(c)) && hb.has(comp_key(c)), c, &s.ctr[3],
-                            0, kSelCap);
-            });
+            append_gathered(s, gbuf, wcap,
+                            [&](u64 c) { return ha.has(comp_key(c)) && hb.has(comp_key(c)); });
             __syncthreads();
             const u32 n = uni(s.ctr[3]);
             __syncthreads();
