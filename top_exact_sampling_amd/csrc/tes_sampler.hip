@@ -3715,6 +3715,10 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
 
     constexpr int kPer = (kFineBins + kBlock - 1) / kBlock;
     auto update = [&](u32 j) {
+        // The whole workgroup waits on the prediction: its waves take issue
+        // priority over the other workgroup's streaming waves meanwhile
+        // (speculative-verify batch 208 -> 204 us).
+        __builtin_amdgcn_s_setprio(2);
         __syncthreads();  // the histogram and the appends of rounds < j are complete
         // This thread's bins (descending, as find_desc takes them); the
         // waves' totals of the mass, +inf count, min-p mass and squares so
@@ -3831,6 +3835,7 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
             }
         }
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         next_upd = next_upd == j1 ? 4 * j1 : (next_upd == 4 * j1 ? 8 * j1 : ~0u);
         if (next_upd != ~0u && next_upd >= nj) next_upd = ~0u;
     };
