@@ -4503,26 +4503,30 @@ __global__ __launch_bounds__(kBlock) void tes_verify_kernel(Params p, SpecArgs a
     bool have_t = false;
     const u32 S = gridDim.y;
     if (S > 1) {
-        // The vocabulary is cut into S chunks, one workgroup each: each sums
-        // its chunk's residual and publishes it in the exchange area of the
-        // request's first target row; the last to arrive locates t among
-        // the chunks and searches on within its chunk.
+        // The vocabulary is cut into S chunks, one workgroup each, and each
+        // chunk into eighths, one wave each: every wave sums its eighth's
+        // residual and publishes it in the exchange area of the request's
+        // first target row; the last workgroup to arrive locates t among the
+        // 8 S parts and searches on within its part.
         const u32 cv = (p.nvec + S - 1) / S;
         const u32 c0 = min(blockIdx.y * cv, p.nvec), c1 = min(c0 + cv, p.nvec);
+        const u32 sub = (cv + kWaves - 1) / kWaves;
+        const u32 w0 = min(c0 + wave * sub, c1), w1 = min(w0 + sub, c1);
         u64 hi = 0, lo = 0;
 #pragma unroll 4
-        for (u32 iv = c0 + threadIdx.x; iv < c1; iv += kBlock) {
+        for (u32 iv = w0 + lane; iv < w1; iv += 64) {
             u64 h, l2;
             vec_parts(iv, h, l2);
             hi += h;
             lo += l2;
         }
-        hi = block_sum_u64(wpart, hi);
-        lo = block_sum_u64(wpart, lo);
+        hi = wave_sum(hi);
+        lo = wave_sum(lo);
         u64* pub = reinterpret_cast<u64*>(ws_row(p, n * Lt));
-        if (threadIdx.x == 0) {
-            st_dev(&pub[2 * blockIdx.y], hi);
-            st_dev(&pub[2 * blockIdx.y + 1], lo);
+        const u32 part = blockIdx.y * kWaves + wave;
+        if (lane == 0) {
+            st_dev(&pub[2 * part], hi);
+            st_dev(&pub[2 * part + 1], lo);
         }
         vm_wait();
         __syncthreads();
@@ -4537,27 +4541,45 @@ __global__ __launch_bounds__(kBlock) void tes_verify_kernel(Params p, SpecArgs a
         }
         __syncthreads();
         if (res[3] == 0) return;
-        u128 all = 0;
-        for (u32 q = 0; q < S; ++q) all += from_parts(ld_g(&pub[2 * q]), ld_g(&pub[2 * q + 1]));
-        if (all == 0) {  // p <= q everywhere: the row's own token
+        // Parts in order: wave 0 holds parts lane, 64 + lane (S * 8 <= 64).
+        static_assert(kWaves * 8 <= 64, "every part fits one wave's lanes");
+        const u32 np = S * kWaves;
+        if (wave == 0) {
+            const u64 ph = lane < np ? ld_g(&pub[2 * lane]) : 0ull;
+            const u64 pl = lane < np ? ld_g(&pub[2 * lane + 1]) : 0ull;
+            // Inclusive prefix of the parts as u128 from the 32-bit-part sums.
+            const u64 ih = wave_incl_scan(ph), il = wave_incl_scan(pl);
+            const u128 inc = from_parts(ih, il), own = from_parts(ph, pl);
+            const u128 all = from_parts(read_lane(ih, 63), read_lane(il, 63));
+            u128 tt = 0;
+            if (all != 0) {
+                const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
+                tt = (u128)u * (u64)(all >> 64) + __umul64hi(u, (u64)all);
+            }
+            // The part whose inclusive prefix first exceeds t.
+            const u64 hit = __ballot(lane < np && all != 0 && inc > tt);
+            const u32 k = hit ? (u32)__builtin_ctzll(hit) : 0u;
+            const u128 before = inc - own;
+            if (lane == k) {
+                res[0] = all == 0 ? 1u : 0u;
+                wsum[0][0] = (u64)(tt - before);
+                wsum[0][1] = (u64)((tt - before) >> 64);
+                res[1] = k;
+            }
+        }
+        __syncthreads();
+        if (res[0] != 0) {  // p <= q everywhere: the row's own token
             if (threadIdx.x == 0) out[first] = (int32_t)dec.token;
             return;
         }
-        const u64 u = philox_uniform(p.seed, p.row_base + r, p.offset);
-        t = (u128)u * (u64)(all >> 64) + __umul64hi(u, (u64)all);
+        t = ((u128)wsum[0][1] << 64) | wsum[0][0];
         have_t = true;
-        u32 k = 0;
-        u128 before = 0;
-        for (u32 q = 0; q + 1 < S; ++q) {
-            const u128 m = from_parts(ld_g(&pub[2 * q]), ld_g(&pub[2 * q + 1]));
-            if (k == q && before + m <= t) {
-                before += m;
-                k = q + 1;
-            }
-        }
-        t -= before;
-        v0 = min(k * cv, p.nvec);
-        v1 = min(v0 + cv, p.nvec);
+        // Part k: eighth k % 8 of chunk k / 8, as its wave summed it.
+        const u32 k = res[1];
+        const u32 q0 = min((k / kWaves) * cv, p.nvec), q1 = min(q0 + cv, p.nvec);
+        v0 = min(q0 + (k % kWaves) * sub, q1);
+        v1 = min(v0 + sub, q1);
+        __syncthreads();
     }
     while (true) {
         const u32 nv = v1 - v0;
