@@ -72,9 +72,10 @@ extern "C" {
  * the path that a timed-out exchange takes (its whole-row passes decide it).
  * Outputs are unchanged; only the path differs. */
 #define TES_FLAG_NO_WAIT 16u
-/* Decide every top-p-only row by one workgroup in two passes over the row
- * (the path taken anyway when a launch holds more top-p-only segments than
- * the device keeps resident workgroups). */
+/* Decide every top-p-only row by one workgroup in one pass over the row
+ * (plus a second visit of its first sixteenth), with no exchange between
+ * workgroups: the path taken anyway when a launch holds more top-p-only
+ * segments than the device keeps resident workgroups. */
 #define TES_FLAG_ROW_TOPP 32u
 
 typedef struct tes_sampler tes_sampler;

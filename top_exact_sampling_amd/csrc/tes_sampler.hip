@@ -16,7 +16,8 @@
 //     the stable descending sort does.
 //   * One work item per 512-thread workgroup (two per CU), in block order:
 //     the segments of the top-p-only rows (k >= V) first, cut into
-//     register-resident segments of at most 8192 16-byte vectors and placed
+//     segments of at most 8192 16-byte vectors (held in registers for
+//     probability rows, streamed twice for logit rows) and placed
 //     consecutively so that a row's segments run at the same time; then
 //     whole-row rows, top-k rows and greedy rows, one item each (top-k rows,
 //     and greedy rows if there is still room, become two items when every
@@ -39,16 +40,20 @@
 //     histogram names the coarse bin of the top-p boundary and the coarse bins
 //     the draw can fall in, and the fine bins of just those coarse bins then
 //     name the fine boundary bin and the fine draw bins.  Every segment
-//     gathers the entries of those few fine bins from its registers and the
-//     last segment to arrive finishes with binned selects.  The row is read
-//     once.  This is the exact-integer analogue of the pivot and
+//     gathers the entries of those few fine bins (from its registers, or a
+//     second read of its part for logit rows) and the last segment to arrive
+//     finishes with binned selects.  This is the exact-integer analogue of the pivot and
 //     sigma-truncation searches of the Qrita paper (sections 3.1-3.2): the
 //     boundary is found by mass, never by sorting the nucleus.
+//   * Top-p-only rows of launches whose segments would not all be resident
+//     at once: one workgroup per row, one pass that bins every entry and
+//     appends those of predicted bins, then selects among them.
 //   * Rows with 1024 < k < V, and any row whose fast path cannot decide
 //     (over-full gather, too many draw bins, an exchange that times out), are
 //     resolved by one workgroup with exact multi-pass radix selects over the
 //     whole row.
-//   * renorm_out is written by a second kernel from the per-row decision.
+//   * renorm_out is written by a second kernel from the per-row decision
+//     (and, for top-k and greedy rows, their recorded kept entries).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -4143,7 +4148,7 @@ __device__ __forceinline__ u32 row_class(const Params& p, u32 k_eff, u32 s_full)
 // dispatched in order, so the segments of a row start together and wait for
 // each other only briefly (the waits are bounded all the same).  When the
 // launch's items would not all be resident at once, S is 1 and each such
-// row is decided by its one workgroup (two passes, no exchange).  The other
+// row is decided by its one workgroup (one pass, no exchange).  The other
 // rows follow, one item each: whole-row rows, top-k rows, then greedy rows.
 // Blocks beyond the last item return at once.  No item loop: values live
 // across one would raise the register pressure of every path.
@@ -4201,7 +4206,7 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
     // last in block order.
     // Top-p-only rows are cut into s_full segments while every item of the
     // launch is resident at once; otherwise each is decided by one
-    // workgroup in two passes over the row (or under TES_FLAG_ROW_TOPP).
+    // workgroup in one pass over the row (or under TES_FLAG_ROW_TOPP).
     const bool row_topp = (p.flags & TES_FLAG_ROW_TOPP) ||
                           nf * s_full + n_whole + n_slab + n_greedy > p.slots;
     const u32 segs = row_topp ? 1u : s_full;
@@ -4337,9 +4342,9 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decisio
 // mapping.  The target rows of a launch have already been decided by the
 // sampling kernel (their Decisions hold each row's final distribution): p(x)
 // = q_x / M_p on the kept entries of a normal row, 1 / m on the kept +inf
-// entries of a +inf row, 1 on the token of a zero-mass row.  One workgroup
-// per request:
-//   * wave 0 tests the L drafts at once, lane l: the draft's mass
+// entries of a +inf row, 1 on the token of a zero-mass row.  S workgroups
+// per request (S = 1 when requests fill the device):
+//   * wave 0 of each tests the L drafts at once, lane l: the draft's mass
 //     Q = floor(min(y_d, 1) * 2^32) in its draft row, p(d) = num / den in
 //     target row pi(l), and u * Q * den <= num * 2^96 with u = words 2 and 3
 //     of that row's Philox block, compared on three 64-bit limbs;
@@ -4347,11 +4352,13 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decisio
 //     R_x = max(0, num_x * 2^32 - Q_x * den) (the residual of eq. (16) scaled
 //     by 2^32 den): t = floor(u R / 2^64) with u = words 0 and 1 (the row's
 //     own draw, whose token is not used then), and the correction is the
-//     first x in vocabulary order whose inclusive prefix of R exceeds t.  The
-//     workgroup finds it by splitting the vocabulary range in eight, one
-//     range per wave (each wave sums its range's R; the range holding t is
-//     kept), until the range is one vector per thread, then a workgroup
-//     scan.  R = 0 (p <= q everywhere) takes the row's own token;
+//     first x in vocabulary order whose inclusive prefix of R exceeds t.
+//     With S > 1 each wave sums R over its eighth of its workgroup's S-th
+//     of the vocabulary and publishes it; the last workgroup to arrive
+//     keeps the part holding t.  Within the range, a workgroup splits it in
+//     eight, one eighth per wave (each wave sums its eighth's R; the eighth
+//     holding t is kept), until the range is one vector per thread, then a
+//     workgroup scan.  R = 0 (p <= q everywhere) takes the row's own token;
 //   * with every draft accepted, the bonus token is target row pi(L)'s own
 //     token.
 // A request whose map or draft tokens are out of range gets accept_len -1
