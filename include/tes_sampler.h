@@ -85,8 +85,9 @@ typedef struct tes_sampler tes_sampler;
  *   max_batch  largest B any later call may pass (>= 1).
  *   max_vocab  largest V any later call may pass (1 .. 2^30).
  *   flags      TES_FLAG_* bits.
- * The handle owns its (small) device workspace, allocated here and released
- * by sampler_destroy.  Returns TES_ERR_NO_DEVICE when no GPU is present,
+ * The handle owns its device workspace (at most about 512 MiB; batches of
+ * more rows than it holds run as several launches), allocated here and
+ * released by sampler_destroy.  Returns TES_ERR_NO_DEVICE when no GPU is present,
  * TES_ERR_UNSUPPORTED_DEVICE when the device is not gfx950. */
 int sampler_create(tes_sampler **out, int device, int max_batch, int max_vocab,
                    unsigned flags);
@@ -281,7 +282,8 @@ const char *sampler_status_string(int status);
  *       row started;
  *   [7] why a row left its fast path (bits): 1 first exchange timed out,
  *       2 the draw spans more coarse bins than are exchanged (their count in
- *       bits 8..15), 4 second exchange timed out, 8 inconsistent fine bins,
+ *       bits 8..15), 4 second exchange timed out (fp32 rows; bf16 rows
+ *       have no second exchange), 8 inconsistent fine bins,
  *       16 a segment gathered too many entries, 32 too many in total (these
  *       for top-p-only rows), 64 a top-k row's binned finish needed a sort;
  *       path 6: 1 << 16 its appended entries overflowed, 1 << 17 the
@@ -292,7 +294,8 @@ const char *sampler_status_string(int status);
  *       [9] the finish, [11] the sampled first part, [13] the rest of the
  *       stream, [14] and [15] the padding and the sort when the finish
  *       sorts; top-p-only [8] loads and histogram, [9] first exchange,
- *       [10] its analysis and the second publication, [11] second exchange,
+ *       [10] its analysis and the second publication, [11] second exchange
+ *       (bf16 rows: nothing, their fine histograms went with the first),
  *       [12] gather and arrival, [13] the last segment's finish, [14] its
  *       loads, [15] its boundary select; other words 0.  Exception: with
  *       renorm_out, [10] of a top-k or greedy row holds the number of kept

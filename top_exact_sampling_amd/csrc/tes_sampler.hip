@@ -39,7 +39,9 @@
 //     counter; readers acquire; every wait is bounded): the summed 1/8-octave
 //     histogram names the coarse bin of the top-p boundary and the coarse bins
 //     the draw can fall in, and the fine bins of just those coarse bins then
-//     name the fine boundary bin and the fine draw bins.  Every segment
+//     name the fine boundary bin and the fine draw bins (bf16 rows publish
+//     their whole fine histograms with the first exchange and skip the
+//     second).  Every segment
 //     gathers the entries of those few fine bins (from its registers, or a
 //     second read of its part for logit rows) and the last segment to arrive
 //     finishes with binned selects.  This is the exact-integer analogue of the pivot and
@@ -89,7 +91,7 @@ constexpr u32 kSampleDepth = 4;        // leading steps of a top-k stream that s
 constexpr u32 kChunk = 1024;           // rows per launch
 constexpr u32 kSlabMaxK = 1024;        // largest k served by the streaming top-k path
 static_assert(kSlabMaxK < 65536, "top-k row k is kept as u16");
-constexpr size_t kWsBudget = 256u << 20;  // workspace bytes per sampler (rows per launch follow)
+constexpr size_t kWsBudget = 512u << 20;  // workspace bytes per sampler (rows per launch follow)
 constexpr int kBins = 2048;            // 11-bit radix digits
 constexpr u32 kInfKey = 0x7F800000u;
 constexpr u32 kOneKey = 0x3F800000u;   // 1.0f: masses saturate at 2^32 from here
@@ -122,7 +124,7 @@ constexpr int kStatWords = 16;  // per-row debug statistics (TES_FLAG_STATS)
 // ---------------------------------------------------------------------------
 struct RowState {  // zero between calls
     u32 arrive_a;  // top-p-only: first exchange
-    u32 arrive_b;  // top-p-only: second exchange
+    u32 arrive_b;  // top-p-only: second exchange (fp32 rows)
     u32 ticket;    // last-arriver ticket
     u32 flags;     // kFlagFail
     u32 vticket;   // speculative verification: last-arriver ticket of a request's chunks
@@ -207,6 +209,15 @@ __device__ __forceinline__ PubF* pub_f(const Params& p, u32 r, u32 seg) {
 __device__ __forceinline__ u64* gather_area(const Params& p, u32 r, u32 seg) {
     return reinterpret_cast<u64*>(ws_row(p, r) + (size_t)p.s_ws * (sizeof(PubC) + sizeof(PubF))) +
            (size_t)seg * kGSeg;
+}
+// bf16 rows publish a segment's whole fine histogram with the first exchange,
+// so that no second exchange is needed.  These areas follow the last row's
+// exchange area (s_ws per row), which keeps the other rows' layout as it is.
+struct PubFF {
+    u64 fine[kFineBins];
+};
+__device__ __forceinline__ PubFF* pub_ff(const Params& p, u32 r, u32 seg) {
+    return reinterpret_cast<PubFF*>(ws_row(p, p.chunk)) + (size_t)r * p.s_ws + seg;
 }
 // A top-k or greedy row streamed by S <= kMaxSplit workgroups, one part each:
 // each publishes its part's result in the row's exchange area, and the last
@@ -2873,13 +2884,13 @@ __device__ __forceinline__ void coarse_plan_wave(Smem& s, u64 T, u64 u) {
     }
 }
 
-// One wave, after the second exchange: the fine bin holding T (in the first
-// listed coarse bin) with the mass above it, then the fine bins holding the
-// draw positions t_lo + 1 and t_hi + 1 (t_hi from the boundary fine bin's
-// largest mass).  Each row of 16 lanes scans the fine masses of one listed
-// coarse bin, highest fine bin first.  Results: s.loc_bin[0..2] = fbT, fine
-// bin of t_lo + 1, of t_hi + 1 (-1 if not found), s.loc_above[0] = mass above
-// fbT.
+// One wave, once the listed fine masses are summed: the fine bin holding T
+// (in the first listed coarse bin) with the mass above it, then the fine bins
+// holding the draw positions t_lo + 1 and t_hi + 1 (t_hi from the boundary
+// fine bin's largest mass).  Each row of 16 lanes scans the fine masses of one
+// listed coarse bin, highest fine bin first.  Results: s.loc_bin[0..2] = fbT,
+// fine bin of t_lo + 1, of t_hi + 1 (-1 if not found), s.loc_above[0] = mass
+// above fbT.
 __device__ __forceinline__ void fine_plan_wave(Smem& s, int nlist, u64 T, u64 u) {
     const u32 lane = lane_id();
     const int f = 15 - (int)(lane & 15u);  // fine bin within the coarse bin
@@ -3041,6 +3052,15 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         st_dev(&pc->ninf, ninf);
         st_dev(&pc->mf, mf);
     }
+    // bf16 rows: the whole fine histogram goes out with the first exchange.
+    // (A bf16 row's segments are per-entry bound and end late, so the second
+    // exchange's wait costs them more than the stores; for fp32 rows the
+    // stores cost the other rows' streams more than the wait: measured.)
+    constexpr bool kFused = VEC == 8;
+    if constexpr (kFused) {
+        PubFF* pff = pub_ff(p, r, seg);
+        for (int i = threadIdx.x; i < kFineBins; i += kBlock) st_dev(&pff->fine[i], shfine(s)[i]);
+    }
     const bool ok = arrive_wait(s, &rs->arrive_a, nseg);
     tp = stat_phase(p, r, 9, tp);
 
@@ -3099,11 +3119,13 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             stat_why(p, r, 2u | (u32)min(cnt, 255) << 8);
         } else {
             nlist = cnt;
-            // Second exchange: this segment's fine bins of the listed coarse bins.
-            PubF* pf = pub_f(p, r, seg);
-            for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
-                const int fb = s.flist[i / 16] * 16 + (i % 16);
-                st_dev(&pf->fine[i / 16][i % 16], fb < kFineBins ? shfine(s)[fb] : (u64)0);
+            if constexpr (!kFused) {
+                // Second exchange: this segment's fine bins of the listed coarse bins.
+                PubF* pf = pub_f(p, r, seg);
+                for (int i = threadIdx.x; i < nlist * 16; i += kBlock) {
+                    const int fb = s.flist[i / 16] * 16 + (i % 16);
+                    st_dev(&pf->fine[i / 16][i % 16], fb < kFineBins ? shfine(s)[fb] : (u64)0);
+                }
             }
         }
     }
@@ -3111,7 +3133,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     if (!decidable && threadIdx.x == 0)
         or_dev(&rs->flags, (u32)kFlagFail);
     tp = stat_phase(p, r, 10, tp);
-    arrive_only(s, &rs->arrive_b);
+    if constexpr (!kFused) arrive_only(s, &rs->arrive_b);
     // While the other segments' fine masses arrive, collect this segment's
     // entries of the listed coarse bins (a superset of the fine bins the
     // gather will want) into per-wave LDS regions; the fine publication above
@@ -3119,7 +3141,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     constexpr u32 kSpecReg = kSlabCap / kWaves;  // entries per wave region
     const u32 wave = uni(wave_id());
     u32 sfill = 0;
-    const bool spec = nlist > 0 && !tiny;
+    const bool spec = !kFused && nlist > 0 && !tiny;
     if (spec) {
         const int cb = s.flist[0];
         const int chi = s.flist[nlist > 1 ? 1 : 0], clo = s.flist[nlist - 1];
@@ -3146,16 +3168,19 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
         seg_each(collect);
         if (lane_id() == 0) s.gn[32 + wave] = sfill;  // read after the barriers below
     }
-    const bool ok2 = wait_arrivals(s, &rs->arrive_b, nseg);
-    if (!ok2) stat_why(p, r, 4u);
-    if (threadIdx.x == 0) {
-        if (!ok2)
-            or_dev(&rs->flags, (u32)kFlagFail);
-        s.misc[4] = (!ok2 || (ld_dev(&rs->flags) & kFlagFail)) ? 1u : 0u;
+    bool failed = !ok || !decidable;
+    if constexpr (!kFused) {
+        const bool ok2 = wait_arrivals(s, &rs->arrive_b, nseg);
+        if (!ok2) stat_why(p, r, 4u);
+        if (threadIdx.x == 0) {
+            if (!ok2)
+                or_dev(&rs->flags, (u32)kFlagFail);
+            s.misc[4] = (!ok2 || (ld_dev(&rs->flags) & kFlagFail)) ? 1u : 0u;
+        }
+        __syncthreads();
+        failed = uni(s.misc[4]) != 0;
+        __syncthreads();
     }
-    __syncthreads();
-    const bool failed = uni(s.misc[4]) != 0;
-    __syncthreads();
     tp = stat_phase(p, r, 11, tp);
 
     // Gather, from registers, the entries the last segment needs.
@@ -3165,8 +3190,28 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     u64* garea = gather_area(p, r, seg);
     if (!failed && kind == kNormal) {
         static_assert(sizeof(PubF) == 8 * 16 * kDMax, "PubF is fine[kDMax][16]");
-        sum_words(reinterpret_cast<const u64*>(pub_f(p, r, 0)), sizeof(PubF) / 8, nseg,
-                  (u32)nlist * 16, [&](u32 i, u64 v) { s.finem[i] = v; });
+        if constexpr (kFused) {
+            // The listed coarse bins' fine masses from the segments' whole
+            // histograms (acquired with the first exchange).
+            for (u32 i = threadIdx.x; i < (u32)nlist * 16; i += kBlock) {
+                const int fb = s.flist[i / 16] * 16 + (int)(i % 16);
+                u64 v = 0;
+                if (fb < kFineBins) {
+                    for (u32 q0 = 0; q0 < nseg; q0 += 4) {
+                        u64 w[4];
+#pragma unroll
+                        for (u32 j = 0; j < 4; ++j)
+                            w[j] = q0 + j < nseg ? ld_g(&pub_ff(p, r, q0 + j)->fine[fb]) : 0ull;
+#pragma unroll
+                        for (u32 j = 0; j < 4; ++j) v += w[j];
+                    }
+                }
+                s.finem[i] = v;
+            }
+        } else {
+            sum_words(reinterpret_cast<const u64*>(pub_f(p, r, 0)), sizeof(PubF) / 8, nseg,
+                      (u32)nlist * 16, [&](u32 i, u64 v) { s.finem[i] = v; });
+        }
         __syncthreads();
         if (wave_id() == 0) fine_plan_wave(s, nlist, T, u);
         __syncthreads();
@@ -4951,7 +4996,9 @@ extern "C" int sampler_create(tes_sampler** out, int device, int max_batch, int 
     rb = (rb + 255) & ~(size_t)255;
     s->rowbytes = (u32)rb;
     s->chunk = (u32)max_batch < kChunk ? (u32)max_batch : kChunk;
-    const size_t per_row = sizeof(RowState) + sizeof(Decision) + sizeof(XMax) + rb;
+    // (and the fine histograms of a bf16 top-p-only row's segments)
+    const size_t per_row =
+        sizeof(RowState) + sizeof(Decision) + sizeof(XMax) + rb + (size_t)s->s_ws * sizeof(PubFF);
     const size_t budget_rows = kWsBudget / per_row;
     if (budget_rows < s->chunk) s->chunk = budget_rows < 1 ? 1u : (u32)budget_rows;
     s->ws_bytes = (size_t)s->chunk * per_row;
