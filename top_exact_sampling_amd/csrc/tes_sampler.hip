@@ -366,6 +366,27 @@ __device__ __forceinline__ u64 key_mass(u32 key) {
     return (u64)(u32)(__uint_as_float(key) * 4294967296.0f);
 }
 
+// Adds the raw bits b of an entry to an exact fine mass histogram, branch
+// free: the bin (b >> 16) - base is clamped to [dslot, kFineBins - 1] by one
+// three-way median, sending keys below 2^-32 to the lane's discard slot
+// dslot (< 0: a word of its own, so that rows of mostly zeros do not send
+// every lane's atomic to one address) and keys >= 1.0, +inf, NaN and
+// negative bits to the top bin; the mass
+// floor(x * 2^32) comes from the hardware conversion, which saturates: zero
+// for NaN and negatives, exact below 1.0, 2^32 - 1 (kTopUnit) from 1.0 up.
+// The top bin thus ends holding kTopUnit times its count, whose mass is
+// count * 2^32.
+constexpr u64 kTopUnit = 0xFFFFFFFFull;
+__device__ __forceinline__ void hist_add(u64* fine, u32 b, int dslot) {
+    int bin;
+    asm("v_med3_i32 %0, %1, %2, %3"
+        : "=v"(bin)
+        : "v"((int)(b >> kFineShift) - (int)kFineBase), "v"(dslot), "s"(kFineBins - 1));
+    u32 q;
+    asm("v_cvt_u32_f32 %0, %1" : "=v"(q) : "v"(__uint_as_float(b) * 4294967296.0f));
+    atomicAdd((unsigned long long*)&fine[bin], (unsigned long long)q);
+}
+
 // Fine mass bin of a key >= kMinMassKey; bins ascend with the key.
 __device__ __forceinline__ u32 fine_bin(u32 key) {
     return key >= kOneKey ? (u32)(kFineBins - 1) : (key >> kFineShift) - kFineBase;
@@ -2982,17 +3003,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             }
         }
     };
-    // Branch-free binning of the raw bits: the bin index (key >> 16) - base
-    // clamped to [-1 - lane, kFineBins - 1] sends keys below 2^-32 to the
-    // lane's discard slot and keys >= 1.0, +inf, NaN and negative bits to the
-    // top bin; the
-    // mass floor(x * 2^32) clamped to [0, 2^32 - 256] is zero for NaN and
-    // negatives, exact below 1.0, and 2^32 - 256 from 1.0 up, so the top bin
-    // ends holding (2^32 - 256) times its count, whose mass is count * 2^32.
-    // The segment's mass is the sum of the histogram, taken afterwards; +inf
-    // entries (and NaN bits) show up as signed maxima >= +inf and are counted
-    // only by waves that hold one.
-    constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256, the largest float below 2^32
+    // Branch-free binning of the raw bits (hist_add).  The segment's mass is
+    // the sum of the histogram, taken afterwards; +inf entries (and NaN bits)
+    // show up as signed maxima >= +inf and are counted only by waves that
+    // hold one.
     u64 ninf = 0;
     // Min-p on logit rows: the largest mass is that of the top weight 1
     // (2^32), so the floor and its key are known up front; the segment adds
@@ -3010,9 +3024,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             for (int e = 0; e < VEC; ++e) {
                 const u32 b = __float_as_uint(VecT<VEC>::get(w, e));
                 mx = max(mx, (int)b);
-                const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, dslot), kFineBins - 1);
-                const float q = fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
-                atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)(u32)q);
+                hist_add(shfine(s), b, dslot);
                 if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
             }
             if (__ballot(mx >= (int)kInfKey)) {
@@ -3029,7 +3041,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
     __syncthreads();
     if (threadIdx.x == 0) {
         u64& top = shfine(s)[kFineBins - 1];
-        top = (top / (u64)kTopMass) << 32;
+        top = (top / kTopUnit) << 32;
     }
     __syncthreads();
     u64 M = 0;
@@ -3582,6 +3594,11 @@ __device__ __forceinline__ u32 fkey1(int f) {
 struct KeyWin {
     u32 k0, w0, k1, w1;
     __device__ bool has(u32 b) const { return (b - k0 < w0) | (b - k1 < w1); }
+    // The wave's lanes whose b is inside (each compare's lane mask is its
+    // ballot: no per-lane value is built).
+    __device__ u64 ballot(u32 b) const {
+        return __builtin_amdgcn_ballot_w64(b - k0 < w0) | __builtin_amdgcn_ballot_w64(b - k1 < w1);
+    }
     __device__ bool covers(int f) const {
         const u32 a = fkey0(f), e = fkey1(f) - 1;
         return (a - k0 < w0 && e - k0 < w0) || (a - k1 < w1 && e - k1 < w1);
@@ -3674,18 +3691,10 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     u64 tp = p.stats ? wall_clock64() : 0;
     if (threadIdx.x == 0) s.npass = 0;
 
-    // Fine binning of the segments, branch free: bin (key >> 16) - base
-    // clamped to [-1 - lane, kFineBins - 1] (below 0: the lane's discard
-    // slot) and mass floor(x * 2^32) clamped to [0, 2^32 - 256]; the top
-    // bin's sum is then turned into count * 2^32.
-    constexpr float kTopMass = 4294967040.0f;  // 2^32 - 256
+    // Fine binning of the row, branch free (hist_add, with this lane's
+    // discard slot); the top bin is turned into count * 2^32 after the pass.
     const int dslot = -1 - (int)lane_id();
-    auto bin_add = [&](u32 b) -> u32 {
-        const int bin = min(max((int)(b >> kFineShift) - (int)kFineBase, dslot), kFineBins - 1);
-        const u32 q = (u32)fminf(fmaxf(__uint_as_float(b) * 4294967296.0f, 0.0f), kTopMass);
-        atomicAdd((unsigned long long*)&shfine(s)[bin], (unsigned long long)q);
-        return q;
-    };
+    auto bin_add = [&](u32 b) { hist_add(shfine(s), b, dslot); };
 
     auto wb = [&](int b) { return shfine(s)[b]; };
 
@@ -3716,9 +3725,23 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     for (int i = (int)threadIdx.x - 1; i < kFineBins; i += kBlock) shfine(s)[i] = 0;
     __syncthreads();
 
-    // Appends this lane's entries c[e] with bit e of mask set to the wave's
-    // region (slots in lane order from a prefix sum over the lanes' counts).
-    auto append = [&](u32 mask, const u64 (&c)[VEC]) {
+    // Appends one entry position of a step: the lanes whose take is set (bm,
+    // the wave's ballot of take) store their entry's composite at the wave's
+    // count plus their rank among those lanes.  The ballots of a step's
+    // window tests are its masks: nothing else is built per lane.
+    auto append1 = [&](u64 bm, bool take, u32 b, u32 idx) {
+        if (bm == 0) return;
+        const u32 pos = wcnt + mbcnt64(bm);
+        if (take && pos < wcap) wreg[pos] = composite(b, idx);
+        wcnt += (u32)__popcll(bm);
+    };
+    // bf16 rows: appends this lane's entries c[e] with bit e of mask set, in
+    // lane order from a prefix sum over the lanes' counts (for eight entries
+    // a vector, per-entry ballots measured slower: 195 -> 201 us on the
+    // speculative-verify batch).  One condition per store and a branch-free
+    // position: nesting the position update under the condition measured 2x
+    // slower.
+    auto append_lanes = [&](u32 mask, const u64 (&c)[VEC]) {
         const u32 cnt = (u32)__popc(mask);
         u32 pre = 0, tot = 0;
 #pragma unroll
@@ -3728,9 +3751,6 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
             tot += (u32)__popcll(bb) << b;
         }
         u32 pos = wcnt + pre;
-        // (One condition per store and a branch-free position: nesting the
-        // position update under the condition measured 2x slower for the
-        // eight entries of a bf16 vector.)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const bool take = (mask >> e) & 1u;
@@ -3738,6 +3758,37 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
             pos += take ? 1u : 0u;
         }
         wcnt += tot;
+    };
+    // Appends the step's entries taken by in (inb: the wave's ballot of in).
+    auto append_step = [&](const VT& x, u32 iv, bool valid, auto in, auto inb) {
+        if constexpr (VEC == 8) {
+            u32 mask = 0;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                mask |= (valid && in(__float_as_uint(VecT<VEC>::get(x, e)))) ? 1u << e : 0u;
+            if (__ballot(mask != 0) == 0) return;
+            u64 c[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                c[e] = composite(__float_as_uint(VecT<VEC>::get(x, e)), iv * VEC + e);
+            append_lanes(mask, c);
+        } else {
+            const u64 vm = __builtin_amdgcn_ballot_w64(valid);
+            bool tk[VEC];
+            u64 bm[VEC];
+            u64 any = 0;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
+                tk[e] = valid & in(b);
+                bm[e] = inb(b) & vm;
+                any |= bm[e];
+            }
+            if (any == 0) return;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                append1(bm[e], tk[e], __float_as_uint(VecT<VEC>::get(x, e)), iv * VEC + e);
+        }
     };
     // Keeps, in place, this wave's appended entries inside win (one wave:
     // each chunk of 64 * 8 slots is loaded before any of its kept entries is
@@ -3897,10 +3948,6 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     // first one again (their entries of the predicted bins only).
     u32 jend = nj;
     stream_rounds<VEC, LG>(row, p.nvec, S8, jend, [&](const VT& x, u32 iv, bool valid, bool first) {
-        u32 mask = 0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            mask |= (valid && win.has(__float_as_uint(VecT<VEC>::get(x, e)))) ? 1u << e : 0u;
         if (first) {
             // Branch free: a lane past the row adds nothing to the discard slot.
             int mx = kIntMin;
@@ -3916,11 +3963,10 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
                 for (int e = 0; e < VEC; ++e) ninf += __float_as_uint(VecT<VEC>::get(x, e)) == kInfKey;
             }
         }
-        if (__ballot(mask != 0) == 0) return;
-        u64 c[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) c[e] = composite(__float_as_uint(VecT<VEC>::get(x, e)), iv * VEC + e);
-        append(mask, c);
+        // (The window tests follow the histogram: lane masks kept across its
+        // branches would be copied through vector registers.)
+        append_step(x, iv, valid, [&](u32 b) { return win.has(b); },
+                    [&](u32 b) { return win.ballot(b); });
     }, [&](u32 j) {
         if (j == next_upd) {
             const u64 t0 = p.stats ? wall_clock64() : 0;
@@ -3944,7 +3990,7 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     const bool fits = publish();
     if (threadIdx.x == 0) {
         u64& top = shfine(s)[kFineBins - 1];
-        top = (top / (u64)kTopMass) << 32;
+        top = (top / kTopUnit) << 32;
     }
     __syncthreads();
     u64 M = 0;
@@ -3961,19 +4007,8 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     // its entries (the counts are in s.gn).
     auto take = [&](auto pred) {
         return [&, pred](const VT& x, u32 iv, bool valid) {
-            bool any = false;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) any = any || pred(__float_as_uint(VecT<VEC>::get(x, e)));
-            if (__ballot(valid && any) == 0) return;
-            u32 mask = 0;
-            u64 c[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const u32 b = __float_as_uint(VecT<VEC>::get(x, e));
-                mask |= (valid && pred(b)) ? 1u << e : 0u;
-                c[e] = composite(b, iv * VEC + e);
-            }
-            append(mask, c);
+            append_step(x, iv, valid, pred,
+                        [&](u32 b) { return __builtin_amdgcn_ballot_w64(pred(b)); });
         };
     };
     auto pass = [&](auto pred) -> bool {
