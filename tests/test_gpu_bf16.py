@@ -114,6 +114,43 @@ def test_split_rows(sampler, orc):
     log("[gpu]   parts per row %s" % np.unique(st[:, 2]).tolist())
 
 
+def test_exchange_timeout_fallback(orc, torch_cuda):
+    # bf16 top-p-only segments publish their whole fine histograms with the
+    # first exchange and have no second one.  With TES_FLAG_NO_WAIT a wait
+    # that is not already satisfied gives up at once: such a segment flags
+    # the row and the last segment decides it by whole-row passes (path 2).
+    # Tokens, kept sets and renorm_out must equal the oracle's whichever way
+    # each row goes, also on a second identical call (from the reset row
+    # state).
+    s = tes.Sampler(0, 1024, 1 << 18, tes.TES_FLAG_NO_WAIT | tes.TES_FLAG_STATS)
+    try:
+        w3 = workloads.make(3)
+        rng = np.random.default_rng(78)
+        full3 = np.flatnonzero(w3.top_k >= w3.V)
+        rows3 = np.sort(np.concatenate([full3, rng.choice(np.flatnonzero(w3.top_k < w3.V), 16,
+                                                          replace=False)]))
+        adv, aks, aps, _ = _adversarial_batch(262144, np.random.default_rng(262145))
+        cases = [
+            ("hetero subset", np.ascontiguousarray(w3.probs[rows3]), w3.top_k[rows3],
+             w3.top_p[rows3], w3.seed, w3.offset),
+            ("adversarial V=262144", adv, aks, aps, 9, 3),
+        ]
+        for label, probs, ks, ps, seed, off in cases:
+            multi = np.asarray(ks) >= probs.shape[1]
+            for call in (1, 2):
+                check(s, orc, probs, ks, ps, seed, off,
+                      "timeout fallback %s call %d" % (label, call))
+                st = s.stats(len(ks))
+                assert np.all(st[multi, 2] >= 2), "top-p-only rows were not segmented"
+                timed_out = (st[multi, 7] & 1) != 0
+                assert not np.any(st[multi, 7] & 4), "bf16 rows have no second exchange"
+                assert np.all(st[multi, 0][timed_out] == 2), "paths %s" % st[multi, 0]
+                assert timed_out.sum() >= multi.sum() // 2, "only %d of %d rows timed out" % (
+                    timed_out.sum(), multi.sum())
+    finally:
+        s.close()
+
+
 @pytest.mark.parametrize("trial", range(4))
 def test_random_shapes(sampler, orc, trial):
     rng = np.random.default_rng(2000 + trial)
