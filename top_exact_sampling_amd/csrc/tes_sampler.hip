@@ -4057,22 +4057,68 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
         // Min-p: the kept set ends where the inclusive mass reaches
         // min(T, the mass at or above the floor).
         if (minp) T = mf < T ? mf : T;
-        // (Three block-wide searches.  One read of the bins and one scan
-        // serving all three measured 2.3 us faster for fp32 rows but, through
-        // register allocation, made the bf16 rows' pass loop twice as slow.)
-        const Digit gT = find_desc(s, kFineBins, T, wb, wb);
-        const int fbT = (int)gT.d;
-        const u64 aboveT = gT.above;
-        const u64 mT = uni(shfine(s)[fbT]);
-        const u64 t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, aboveT + mT);
-        const Digit g1 = find_desc(s, kFineBins, t_lo + 1, wb, wb);
-        const Digit g2 = find_desc(s, kFineBins, t_hi + 1, wb, wb);
-        const int bhi = (int)g1.d, blo = (int)g2.d;  // the draw's fine bins, bhi >= blo >= fbT
+        // The boundary's bin (by T), then the bins of draw positions t_lo + 1
+        // and t_hi + 1, which depend on it.
+        int fbT, bhi, blo;  // the draw's fine bins: bhi >= blo >= fbT
+        u64 aboveT, mT, t_lo, t_hi, above_hi;
+        if constexpr (VEC == 8) {
+            // (bf16 rows: three block-wide searches.  The one scan below made
+            // their pass loop twice as slow through register allocation.)
+            const Digit gT = find_desc(s, kFineBins, T, wb, wb);
+            fbT = (int)gT.d;
+            aboveT = gT.above;
+            mT = uni(shfine(s)[fbT]);
+            t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, aboveT + mT);
+            const Digit g1 = find_desc(s, kFineBins, t_lo + 1, wb, wb);
+            const Digit g2 = find_desc(s, kFineBins, t_hi + 1, wb, wb);
+            bhi = (int)g1.d, blo = (int)g2.d;
+            above_hi = g1.above;
+        } else {
+            // One exclusive scan of this thread's bins (descending) serves the
+            // three searches.
+            const int top = kFineBins - 1 - (int)threadIdx.x * kPer;
+            u64 local = 0;
+#pragma unroll
+            for (int jj = 0; jj < kPer; ++jj)
+                if (top - jj >= 0) local += shfine(s)[top - jj];
+            if (threadIdx.x == 0) {
+                s.bc[0] = 0, s.bc[1] = 0;
+                s.loc_bin[0] = 0, s.loc_bin[1] = 0;
+                s.loc_above[0] = 0;
+            }
+            const u64 ex = block_excl_scan(s, local);  // (its barriers order the above)
+            // The bin where the descending cumulative mass reaches W, and the
+            // mass above it: put(b, above) by the one thread holding it.
+            auto search = [&](u64 W, auto put) {
+                u64 acc = ex;
+#pragma unroll
+                for (int jj = 0; jj < kPer; ++jj) {
+                    const int b = top - jj;
+                    if (b >= 0) {
+                        const u64 w = shfine(s)[b];
+                        if (acc < W && W <= acc + w) put(b, acc);
+                        acc += w;
+                    }
+                }
+            };
+            search(T, [&](int b, u64 a) { s.bc[0] = (u64)b, s.bc[1] = a; });
+            __syncthreads();
+            fbT = (int)uni((u32)s.bc[0]);
+            aboveT = uni(s.bc[1]);
+            mT = uni(shfine(s)[fbT]);
+            t_lo = __umul64hi(u, T), t_hi = __umul64hi(u, aboveT + mT);
+            search(t_lo + 1, [&](int b, u64 a) { s.loc_bin[0] = b, s.loc_above[0] = a; });
+            search(t_hi + 1, [&](int b, u64) { s.loc_bin[1] = b; });
+            __syncthreads();
+            bhi = (int)uni((u32)s.loc_bin[0]), blo = (int)uni((u32)s.loc_bin[1]);
+            above_hi = uni(s.loc_above[0]);
+            __syncthreads();
+        }
         // The non-empty bins of [blo, bhi] with their masses and the mass
         // above each, highest first (one wave, 64 bins per step).
         if (wave_id() == 0) {
             const u32 lane = lane_id();
-            u64 base = g1.above;
+            u64 base = above_hi;
             u32 q = 0;
             for (int b0 = bhi; b0 >= blo; b0 -= 64) {
                 const int b = b0 - (int)lane;
