@@ -300,7 +300,9 @@ const char *sampler_status_string(int status);
  *       loads, [15] its boundary select; other words 0.  Exception: with
  *       renorm_out, [10] of a top-k or greedy row holds the number of kept
  *       entries it recorded (renorm_out's row is then written without
- *       reading the row again).
+ *       reading the row again); with the slab export, the number of positive
+ *       support entries it recorded (the slab is then sorted from them when
+ *       they are the whole support).
  * The wall clock is the device's constant 100 MHz counter.  Synchronises the
  * device.  `host_out` holds 16 * B uint32. */
 int sampler_get_stats(tes_sampler *s, uint32_t *host_out, int B);

@@ -608,6 +608,17 @@ def test_slab_export(sampler, orc, cfg):
     assert_slab_parity(orc, w.probs, w.top_k, w.top_p, w.seed, w.offset, 1024, out, w.name)
     st = sampler.stats(w.B)
     assert np.array_equal(out[5], st[:, 0]), "route differs from the recorded paths"
+    # With the slab export, top-k and greedy rows record their support's
+    # positive entries (stats word 10), min(k_eff, positive entries) of them;
+    # rows whose list holds the whole support are exported from it.
+    listed = np.isin(st[:, 0], [0, 4, 5])
+    k_eff = np.where((w.top_k <= 0) | (w.top_k >= w.V), w.V, w.top_k)
+    expect = np.minimum(k_eff, np.count_nonzero(w.probs > 0, axis=1))
+    bad = np.flatnonzero(listed & (st[:, 10] != expect))
+    assert bad.size == 0, "support lists: rows %s lengths %s expected %s" % (
+        bad[:8], st[bad[:8], 10], expect[bad[:8]])
+    log("[gpu]   %d rows exported from their support lists" % int(
+        (listed & (st[:, 10] == k_eff)).sum()))
 
 
 @pytest.mark.parametrize("V", [151936, 20000, 1000])

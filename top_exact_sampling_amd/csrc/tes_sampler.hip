@@ -55,7 +55,9 @@
 //     resolved by one workgroup with exact multi-pass radix selects over the
 //     whole row.
 //   * renorm_out is written by a second kernel from the per-row decision
-//     (and, for top-k and greedy rows, their recorded kept entries).
+//     (and, for top-k and greedy rows, their recorded kept entries); the
+//     slab export sorts each row's support (for top-k and greedy rows, from
+//     their recorded support entries).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -147,7 +149,7 @@ struct Decision {  // what renorm_out and the slab export need
     u64 c_keep;  // kept entries have composite >= c_keep
     u64 M_p;     // kept mass (normal rows)
     u64 c_k;     // the support is the entries with composite >= c_k (k_eff < V)
-    u32 nlist;   // with renorm_out: entries in the row's kept list, or kNoList
+    u32 nlist;   // with a row list: its entries, or kNoList
     u32 pad;
 };
 
@@ -2068,30 +2070,35 @@ __device__ __noinline__ Outcome resolve_row(Smem& s, const float* row, u32 nvec,
 // ---------------------------------------------------------------------------
 // Row completion
 // ---------------------------------------------------------------------------
-// Kept lists, recorded only when renorm_out is requested: a top-k or greedy
-// row, whose kept entries are all at hand when it finishes, writes their
-// composites (in no particular order) to the start of its exchange area and
-// their number to its Decision, so that the renorm kernel writes the row
-// without reading it again.  A row without mass keeps nothing (an empty
-// list); other rows (top-p-only rows) record kNoList and are re-read.
+// Row lists, recorded only when renorm_out or the slab export is requested:
+// a top-k or greedy row, whose support (the entries with composite >= c_k)
+// is at hand when it finishes, writes the composites of its kept entries
+// (>= c_keep), or, for the slab export, of its positive support entries, in
+// no particular order, to the start of its exchange area and their number to
+// its Decision.  The renorm kernel then writes the row's kept entries (the
+// list's entries >= c_keep) without reading the row again, and the slab
+// export sorts a list that holds the whole support instead of re-reading the
+// row.  A row without mass records an empty list; other rows (top-p-only
+// rows) record kNoList and are re-read.
 constexpr u32 kNoList = ~0u;
-// Launch flag (beside the sampler's TES_FLAG_* bits, which never use it):
-// renorm_out was requested.  (A flag rather than another parameter word: the
-// parameters sit in LDS ahead of the work regions, whose placement the
-// streams' bank conflicts are sensitive to.)
-constexpr u32 kFlagKeepList = 0x80000000u;
-__device__ __forceinline__ u64* kept_list(const Params& p, u32 r) {
+// Launch flags (beside the sampler's TES_FLAG_* bits, which never use them):
+// record row lists; make them support lists.  (Flags rather than another
+// parameter word: the parameters sit in LDS ahead of the work regions, whose
+// placement the streams' bank conflicts are sensitive to.)
+constexpr u32 kFlagList = 0x80000000u;
+constexpr u32 kFlagSupport = 0x40000000u;
+__device__ __forceinline__ u64* row_list(const Params& p, u32 r) {
     return reinterpret_cast<u64*>(ws_row(p, r));
 }
-// Writes the entries c[j] >= c_keep held by the workgroup's threads to row
-// r's kept list and returns their number.  Entries below c_keep (zero
-// padding included; c_keep > 0) are skipped.  All threads call it; the
-// exchange area must no longer be read by anyone.
+// Writes the entries c[j] >= c_min held by the workgroup's threads to row r's
+// list and returns their number (c_min: c_keep, or c_k for a support list).
+// Entries below c_min (zero padding included; c_min > 0) are skipped.  All
+// threads call it; the exchange area must no longer be read by anyone.
 template <int J>
-__device__ u32 emit_kept(Smem& s, const Params& p, u32 r, const u64 (&c)[J], u64 c_keep) {
+__device__ u32 emit_list(Smem& s, const Params& p, u32 r, const u64 (&c)[J], u64 c_min) {
     u32 cnt = 0;
 #pragma unroll
-    for (int j = 0; j < J; ++j) cnt += c[j] >= c_keep ? 1u : 0u;
+    for (int j = 0; j < J; ++j) cnt += c[j] >= c_min ? 1u : 0u;
     const u64 x = wave_incl_scan((u64)cnt);
     if (lane_id() == 63) s.wpart[wave_id()] = x;
     __syncthreads();
@@ -2104,11 +2111,11 @@ __device__ u32 emit_kept(Smem& s, const Params& p, u32 r, const u64 (&c)[J], u64
         tot += t;
     }
     __syncthreads();
-    TES_GLOBAL u64* list = gp(kept_list(p, r));
+    TES_GLOBAL u64* list = gp(row_list(p, r));
     u32 pos = (u32)(pre + x) - cnt;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const bool take = c[j] >= c_keep;
+        const bool take = c[j] >= c_min;
         if (take) list[pos] = c[j];
         pos += take ? 1u : 0u;
     }
@@ -2283,8 +2290,8 @@ __device__ __attribute__((always_inline)) void do_greedy(Smem& s, u32 r, u32 h, 
     o.M_p = key_mass(key);
     o.kind = key == kInfKey ? kInfRow : (o.M_p == 0 ? kZeroRow : kNormal);
     // The kept entry is the token.
-    if ((p.flags & kFlagKeepList) && threadIdx.x == 0) *gp(kept_list(p, r)) = cbest;
-    finish_row(s, p, r, o, kPathGreedy, 0, (p.flags & kFlagKeepList) ? 1u : kNoList);
+    if ((p.flags & kFlagList) && threadIdx.x == 0) *gp(row_list(p, r)) = cbest;
+    finish_row(s, p, r, o, kPathGreedy, 0, (p.flags & kFlagList) ? 1u : kNoList);
 }
 
 // ---------------------------------------------------------------------------
@@ -2756,7 +2763,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
             stat_phase(p, r, 9, tp);
             if (c_k != ~0ull) ob.c_k = c_k;
             u32 nl = kNoList;
-            if ((p.flags & kFlagKeepList) && ob.kind != kZeroRow) {
+            if ((p.flags & kFlagList) && ob.kind != kZeroRow) {
                 // The binned finish left the n entries packed at the buffer's start.
                 constexpr int J = kSlabCap / kBlock;
                 u64 c[J];
@@ -2765,7 +2772,7 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
                     const u32 i = threadIdx.x + (u32)j * kBlock;
                     c[j] = i < n ? sbuf(s)[i] : 0ull;
                 }
-                nl = emit_kept<J>(s, p, r, c, ob.c_keep);
+                nl = emit_list<J>(s, p, r, c, (p.flags & kFlagSupport) ? ob.c_k : ob.c_keep);
             }
             finish_row(s, p, r, ob, path, gathered, nl);
             return;
@@ -2788,7 +2795,9 @@ __device__ __forceinline__ void slab_finish(Smem& s, u32 r, u32 n, u32 k, u32 tk
         sort_desc<E>(s, v);
         ts = stat_phase(p, r, 15, ts);
         o = resolve_sorted<E, MINP>(s, v, k, P, u, theta);
-        if ((p.flags & kFlagKeepList) && o.kind != kZeroRow) nl = emit_kept<E>(s, p, r, v, o.c_keep);
+        if ((p.flags & kFlagList) && o.kind != kZeroRow)
+            nl = emit_list<E>(s, p, r, v,
+                              (p.flags & kFlagSupport) ? (c_k != ~0ull ? c_k : o.c_k) : o.c_keep);
     };
     if (pad == kBlock) {
         u64 v[1];
@@ -4384,11 +4393,12 @@ __global__ __launch_bounds__(kBlock, kWavesPerSimd) void tes_main_kernel(Params 
 
 // renorm_out[r][i] = q_i / M_p for kept entries (1/m for kept +inf), else 0
 // (q from the weights for logit rows).  Each workgroup writes one contiguous
-// range of at most kRenormSpan entries of a row.  A row with a kept list is
-// written without being read: the list's entries in the range are stored by
-// the threads that read them from the list and marked in an LDS bitmap, then
-// the range's other entries are stored as zeros (each entry has one writer).
-// Rows without a list are read, and each entry tested against c_keep.
+// range of at most kRenormSpan entries of a row.  A row with a list is
+// written without being read: the list's kept entries (>= c_keep) in the
+// range are stored by the threads that read them from the list and marked in
+// an LDS bitmap, then the range's other entries are stored as zeros (each
+// entry has one writer).  Rows without a list are read, and each entry
+// tested against c_keep.
 constexpr u32 kRenormSpan = 32768;
 template <int VEC, bool LG>
 __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decision* __restrict__ dec,
@@ -4420,11 +4430,11 @@ __global__ __launch_bounds__(256) void tes_renorm_kernel(Params p, const Decisio
         const u32 e0 = v0 * VEC, e1 = v1 * VEC;
         for (u32 i = threadIdx.x; i < kRenormSpan / 32; i += 256) marks[i] = 0;
         __syncthreads();
-        const u64* list = kept_list(p, r);
+        const u64* list = row_list(p, r);
         for (u32 i = threadIdx.x; i < d.nlist; i += 256) {
             const u64 c = ld_g(&list[i]);
             const u32 idx = comp_index(c);
-            if (idx >= e0 && idx < e1) {
+            if (c >= d.c_keep && idx >= e0 && idx < e1) {
                 atomicOr(&marks[(idx - e0) >> 5], 1u << ((idx - e0) & 31));
                 orow[idx] = value(comp_key(c));
             }
@@ -4857,16 +4867,18 @@ __global__ __launch_bounds__(256) void tes_rowmax_kernel(Params p) {
 // cake_sampling page emits its slab) with the renormalised weight of each
 // entry (the renorm_out value at that index), for supports of at most `cap`
 // entries; other rows get length -1.  The support is every entry whose
-// composite is at least the row's boundary c_k (the whole row when k_eff = V),
-// collected in one pass over the row and sorted by a bitonic network in LDS.
+// composite is at least the row's boundary c_k (the whole row when k_eff = V):
+// a row whose support list holds it all loads the list, others collect it in
+// one pass over the row; it is then sorted by a bitonic network in LDS.
 constexpr int kSlabThreads = 512;
 constexpr u32 kSlabExportMax = 1024;
 
 template <int VEC>
 __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
     const float* __restrict__ probs, u32 V, u32 nvec, const int32_t* __restrict__ top_k,
-    const Decision* __restrict__ dec, u32 cap, int32_t* __restrict__ slab_index,
-    float* __restrict__ slab_renorm, int32_t* __restrict__ slab_len, u32* __restrict__ route) {
+    const Decision* __restrict__ dec, const unsigned char* __restrict__ lists, u32 list_stride,
+    u32 cap, int32_t* __restrict__ slab_index, float* __restrict__ slab_renorm,
+    int32_t* __restrict__ slab_len, u32* __restrict__ route) {
     typedef typename VecT<VEC>::T VT;
     __shared__ u64 buf[kSlabExportMax];
     __shared__ u32 cnt;
@@ -4896,6 +4908,14 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
             buf[0] = lo;
             cnt = 1;
         }
+    } else if (d.nlist == k_eff) {
+        // The row's support list holds its whole support: k_eff entries, all
+        // >= c_k.  (A support list is shorter when zeros complete the
+        // support, and empty for a row without mass.)
+        const u64* __restrict__ list =
+            reinterpret_cast<const u64*>(lists + (size_t)r * list_stride);
+        for (u32 i = threadIdx.x; i < d.nlist; i += kSlabThreads) buf[i] = ld_g(&list[i]);
+        if (threadIdx.x == 0) cnt = d.nlist;
     } else {
         // Eight loads per thread in flight: a single workgroup streams the row.
         const VT* __restrict__ rv = reinterpret_cast<const VT*>(row_ptr<VEC>(probs, r, V));
@@ -5162,9 +5182,12 @@ int launch_chunk(tes_sampler* s, const Params& p, hipStream_t st, u32 grid, u32 
     }
     if (slab && !LG) {
         const size_t o = c0 * slab->cap;
+        const unsigned char* lists =
+            s->ws + (size_t)s->chunk * (sizeof(RowState) + sizeof(Decision) + sizeof(XMax));
         hipLaunchKernelGGL(tes_slab_kernel<VEC>, dim3(rows), dim3(kSlabThreads), 0, st, p.probs,
-                           V, nvec, p.top_k, dec, slab->cap, slab->index + o, slab->renorm + o,
-                           slab->len + c0, slab->route ? slab->route + c0 : nullptr);
+                           V, nvec, p.top_k, dec, lists, s->rowbytes, slab->cap, slab->index + o,
+                           slab->renorm + o, slab->len + c0,
+                           slab->route ? slab->route + c0 : nullptr);
         if (hipGetLastError() != hipSuccess) return TES_ERR_LAUNCH;
     }
     return TES_OK;
@@ -5229,7 +5252,8 @@ int sample_impl(tes_sampler* s, const void* probs, bool bf16, int B, int V, cons
         p.rowbytes = s->rowbytes;
         p.chunk = s->chunk;
         p.flags = s->flags;
-        if (renorm_out) p.flags |= kFlagKeepList;
+        if (renorm_out || slab) p.flags |= kFlagList;
+        if (slab) p.flags |= kFlagSupport;
         // Top-k and greedy rows may be split into up to kMaxSplit parts of at
         // least kMinPartVec vectors (the kernel splits only when every part
         // is resident at once).
