@@ -1220,11 +1220,12 @@ __device__ __forceinline__ u32 gather_seg(Smem& s, Each each, Pred pred, u64* ou
     return total;
 }
 
-// Bitonic sort, descending, of sbuf(s)[0, kBlock * E) (E = 1, 2 or 4).  Thread t
-// holds positions [t * E, t * E + E) in registers: pairs within a thread are
-// exchanged directly, pairs within a wave through lane shuffles, and pairs
-// across waves through LDS, alternating between the two halves of the region
-// so that each such stage needs one barrier.
+// Bitonic sort, descending, of buf[0, kBlock * E) (E = 1, 2 or 4; buf holds
+// 2 kBlock E words of LDS) by kBlock threads.  Thread t holds positions
+// [t * E, t * E + E) in registers: pairs within a thread are exchanged
+// directly, pairs within a wave through lane shuffles, and pairs across waves
+// through LDS, alternating between the two halves of buf so that each such
+// stage needs one barrier.
 template <int E, int S>
 __device__ __forceinline__ void cas_local(u64 (&v)[E], u32 base, u32 size) {
 #pragma unroll
@@ -1240,12 +1241,11 @@ __device__ __forceinline__ void cas_local(u64 (&v)[E], u32 base, u32 size) {
 }
 
 template <int E>
-__device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
+__device__ __forceinline__ void sort_desc_buf(u64* buf, u64 (&v)[E]) {
     constexpr u32 N = kBlock * E;
-    static_assert(2 * N <= kSlabCap, "sort needs two LDS halves");
     const u32 base = threadIdx.x * E;
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = sbuf(s)[base + j];
+    for (int j = 0; j < E; ++j) v[j] = buf[base + j];
     u32 half = 0;
     // Fully unrolled: every stage's kind (in-thread, lane shuffle, LDS) and
     // partner offsets are compile-time constants, and the shuffles of one
@@ -1270,7 +1270,7 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
                     v[j] = keep_max ? (o > v[j] ? o : v[j]) : (o < v[j] ? o : v[j]);
                 }
             } else {
-                u64* bx = sbuf(s) + half;
+                u64* bx = buf + half;
                 half ^= N;
 #pragma unroll
                 for (int j = 0; j < E; ++j) bx[base + j] = v[j];
@@ -1286,6 +1286,11 @@ __device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
         }
     }
     __syncthreads();
+}
+template <int E>
+__device__ __forceinline__ void sort_desc(Smem& s, u64 (&v)[E]) {
+    static_assert(2 * kBlock * E <= kSlabCap, "sort needs two LDS halves");
+    sort_desc_buf<E>(sbuf(s), v);
 }
 
 // Finish a row from its support sorted descending: positions [0, kk) of the
@@ -4880,7 +4885,8 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
     u32 cap, int32_t* __restrict__ slab_index, float* __restrict__ slab_renorm,
     int32_t* __restrict__ slab_len, u32* __restrict__ route) {
     typedef typename VecT<VEC>::T VT;
-    __shared__ u64 buf[kSlabExportMax];
+    static_assert(kSlabThreads == kBlock && kSlabExportMax == 2 * kBlock, "the register sort's shape");
+    __shared__ u64 buf[2 * kSlabExportMax];  // the support, then the sort's two halves
     __shared__ u32 cnt;
     const u32 r = blockIdx.x;
     const Decision d = dec[r];
@@ -4944,40 +4950,39 @@ __global__ __launch_bounds__(kSlabThreads) void tes_slab_kernel(
     }
     __syncthreads();
     const u32 n = cnt < k_eff ? cnt : k_eff;  // exactly k_eff for a consistent boundary
-    u32 n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (u32 i = n + threadIdx.x; i < n2; i += kSlabThreads) buf[i] = 0;
+    // Descending sort of buf[0, n) padded with zeros (composites are unique;
+    // zeros sort last), held in registers: kBlock or 2 kBlock positions.
+    const u32 N = n <= kBlock ? kBlock : 2 * kBlock;
+    for (u32 i = n + threadIdx.x; i < N; i += kSlabThreads) buf[i] = 0;
     __syncthreads();
-    // Bitonic sort of buf[0, n2), descending (composites are unique; zeros pad).
-    for (u32 size = 2; size <= n2; size <<= 1) {
-        for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
-            for (u32 t = threadIdx.x; t < n2 / 2; t += kSlabThreads) {
-                const u32 i = 2 * t - (t & (stride - 1));  // lower element of the pair
-                const u32 j = i + stride;
-                const u64 a = buf[i], b = buf[j];
-                const bool desc = (i & size) == 0;
-                if (desc ? a < b : a > b) {
-                    buf[i] = b;
-                    buf[j] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
     const double inv = d.kind == kNormal ? 1.0 / (double)d.M_p : 0.0;
     const float w_inf = d.kind == kInfRow ? (float)(1.0 / (double)d.m) : 0.0f;
-    for (u32 j = threadIdx.x; j < cap; j += kSlabThreads) {
-        if (j < n) {
-            const u64 c = buf[j];
-            const u32 key = comp_key(c);
-            const bool kept = d.kind != kZeroRow && c >= d.c_keep;
-            oi[j] = (int32_t)comp_index(c);
-            ow[j] = !kept ? 0.0f
-                          : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
-        } else {
-            oi[j] = -1;
-            ow[j] = 0.0f;
+    auto put = [&](u32 j, u64 c) {
+        const u32 key = comp_key(c);
+        const bool kept = d.kind != kZeroRow && c >= d.c_keep;
+        oi[j] = (int32_t)comp_index(c);
+        ow[j] = !kept ? 0.0f : (d.kind == kInfRow ? w_inf : (float)((double)key_mass(key) * inv));
+    };
+    auto write = [&](const auto& v) {
+        constexpr u32 E = sizeof(v) / sizeof(u64);
+#pragma unroll
+        for (u32 e = 0; e < E; ++e) {
+            const u32 j = threadIdx.x * E + e;
+            if (j < n) put(j, v[e]);
         }
+    };
+    if (N == kBlock) {
+        u64 v[1];
+        sort_desc_buf<1>(buf, v);
+        write(v);
+    } else {
+        u64 v[2];
+        sort_desc_buf<2>(buf, v);
+        write(v);
+    }
+    for (u32 j = n + threadIdx.x; j < cap; j += kSlabThreads) {
+        oi[j] = -1;
+        ow[j] = 0.0f;
     }
 }
 
