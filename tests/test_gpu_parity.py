@@ -711,9 +711,8 @@ def test_wide_draw_ranges_stay_on_the_fast_path(sampler, orc):
 
 def test_exchange_timeout_fallback(orc, torch_cuda):
     # Top-p-only rows cut into several segments exchange their histograms
-    # through bounded waits.  With TES_FLAG_NO_WAIT every wait that is not
-    # already satisfied gives up at once, so each such row takes the timeout
-    # path (failure flag, the last segment decides the row by whole-row
+    # through bounded waits.  With TES_FLAG_NO_WAIT every wait reports a
+    # timeout without polling, so each such row takes the timeout path (failure flag, the last segment decides the row by whole-row
     # passes, the row state is reset).  Tokens, kept sets and renorm_out must
     # still equal the oracle's, and a second identical call (which starts
     # from the reset row state) must agree too.
