@@ -206,6 +206,10 @@ def main():
                     help="also run one device copy of this size (counter calibration)")
     ap.add_argument("--renorm", action="store_true",
                     help="also write renorm_out (dense [B][V] fp32) in every timed call")
+    ap.add_argument("--slab", type=int, default=0, metavar="CAP",
+                    help="--mode probs: call topk_topp_sample_slab instead, exporting each "
+                         "row's sorted support (rows with k_eff <= CAP, 1..1024) in every "
+                         "timed call")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed repetitions of --steps calls; the first is the timed region of "
                          "the line, the median over all is reported beside it")
@@ -230,6 +234,8 @@ def main():
     bf16 = args.input_dtype == "bf16"
     if bf16 and args.mode != "probs":
         raise SystemExit("--input-dtype bf16 applies to --mode probs only")
+    if args.slab and (args.mode != "probs" or bf16 or not 1 <= args.slab <= 1024):
+        raise SystemExit("--slab CAP (1..1024) applies to --mode probs with fp32 rows only")
     if args.mode == "spec":
         sw = workloads.make_spec(args.workload)
         w = workloads.make(args.workload)  # the target rows (same inputs)
@@ -267,7 +273,26 @@ def main():
 
     # Call i draws with Philox offset w.offset + i, as a decode loop advances
     # it, so that draw-dependent paths are sampled rather than one fixed draw.
-    if args.mode == "probs":
+    if args.mode == "probs" and args.slab:
+        s_idx = torch.empty((B, args.slab), dtype=torch.int32, device=dev)
+        s_ren = torch.empty((B, args.slab), dtype=torch.float32, device=dev)
+        s_len = torch.empty(B, dtype=torch.int32, device=dev)
+        s_route = torch.empty(B, dtype=torch.int32, device=dev)
+
+        def step(i, st=None):
+            rc = tes.topk_topp_sample_slab(
+                sampler.handle, probs[i % args.copies].data_ptr(), B, V, top_k.data_ptr(),
+                top_p.data_ptr(), w.seed, w.offset + i, out.data_ptr(),
+                ren.data_ptr() if ren is not None else None, s_idx.data_ptr(), s_ren.data_ptr(),
+                args.slab, s_len.data_ptr(), s_route.data_ptr(),
+                (stream if st is None else st).cuda_stream)
+            if rc != 0:
+                raise RuntimeError("topk_topp_sample_slab failed: %d" % rc)
+
+        def oracle_call(lo, hi, nt, off):
+            return orc.sample(w.probs[lo:hi], w.top_k[lo:hi], w.top_p[lo:hi], w.seed,
+                              w.offset + off, n_threads=nt)[0]
+    elif args.mode == "probs":
         def step(i, st=None):
             sampler.sample(probs[i % args.copies], top_k, top_p, w.seed, w.offset + i,
                            out_tokens=out, renorm_out=ren, stream=stream if st is None else st)
@@ -337,8 +362,8 @@ def main():
 
     # Timed region: exactly `steps` calls, back to back on the launch stream,
     # bracketed by one pair of HIP events on that stream (each call is one
-    # sampler launch, or two with renorm_out, so the events give the call's
-    # average duration).  Further repetitions of the same loop follow; their
+    # sampler launch, plus one each for renorm_out and the slab export, so
+    # the events give the call's average duration).  Further repetitions of the same loop follow; their
     # median is reported beside the first.
     def timed_loop(first):
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -366,6 +391,8 @@ def main():
     # rejections are counted on the call checked below.
     per_row = {"probs": 12, "logits": 20, "spec": 12}[args.mode]
     alg_bytes = B * V * esize + per_row * B + (B * V * 4 if args.renorm else 0)
+    # The slab export writes an index and a weight per slot, a length and a route per row.
+    alg_bytes += B * (args.slab * 8 + 8) if args.slab else 0
     parity = None
     step(0)
     torch.cuda.synchronize()
@@ -385,7 +412,7 @@ def main():
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
     traffic = traffic_from_profile() if (args.workload == 3 and not bf16 and not args.renorm
-                                         and args.mode == "probs") else None
+                                         and args.mode == "probs" and not args.slab) else None
     line = {
         "metric": METRIC,
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -414,6 +441,7 @@ def main():
             args.mode != "logits" else "fp32 logits of the same recipe, before the softmax",
             "input_dtype": args.input_dtype,
             "renorm_out": "dense [B][V] fp32" if args.renorm else None,
+            "slab_export_cap": args.slab or None,
             "arithmetic": "u32 keys, u64 fixed-point masses, u128 products (integer decisions)",
             "input_sha256": workloads.sha256_of(w) if args.mode != "spec" else
             workloads.sha256_of(w) + "+draft",
