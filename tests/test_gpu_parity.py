@@ -208,6 +208,50 @@ def test_adversarial_rows(sampler, variant_samplers, orc, V):
         assert_parity(orc, probs, ks, ps, 9, 3, gtok, gren, "adversarial V=%d %s" % (V, label))
 
 
+@pytest.mark.parametrize("V", [151936, 20000])
+def test_entries_at_and_above_one(sampler, variant_samplers, orc, V):
+    # The mass histograms take floor(x * 2^32) from a saturating conversion:
+    # every entry from 1.0 up weighs 2^32 - 1 in the top bin, whose count
+    # (its sum over 2^32 - 1) becomes count * 2^32, and NaN or negative bits
+    # weigh nothing.  Rows with entries of exactly 1.0, finite entries above
+    # it, and NaN / negatives beside them, on the segment path, the
+    # one-workgroup path and the top-k paths.
+    rng = np.random.default_rng(V + 1)
+    rows, ks, ps = [], [], []
+
+    def add(x, p):
+        for k in (V, 1000, 1):
+            rows.append(np.asarray(x, np.float32))
+            ks.append(k)
+            ps.append(p)
+
+    base = (rng.random(V) * 1e-4).astype(np.float32)
+    one_hot = np.zeros(V, np.float32)
+    one_hot[rng.integers(V)] = 1.0
+    add(one_hot, 0.9)
+    x = base.copy()
+    x[rng.choice(V, 2, replace=False)] = 1.0
+    add(x, 0.5)
+    x = base.copy()
+    x[rng.choice(V, 3, replace=False)] = [1.5, 3e38, 1.0]
+    add(x, 0.95)
+    x = base.copy()
+    i = rng.choice(V, 40, replace=False)
+    x[i[:20]] = rng.uniform(1.0, 4.0, 20).astype(np.float32)
+    x[i[20:30]] = np.nan
+    x[i[30:]] = -rng.random(10).astype(np.float32)
+    add(x, 1.0)
+    x = np.full(V, np.float32(1e-40), np.float32)
+    x[rng.integers(V)] = 1.0
+    add(x, 0.9)
+    probs, ks, ps = np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32)
+    for label, s in (("default", sampler), ("small_segments", variant_samplers["small_segments"]),
+                     ("row_topp", variant_samplers["row_topp"])):
+        log("[gpu] entries at and above 1.0, V=%d sampler=%s" % (V, label))
+        gtok, gren = run_gpu(s, probs, ks, ps, 21, 5, renorm=True)
+        assert_parity(orc, probs, ks, ps, 21, 5, gtok, gren, "above one V=%d %s" % (V, label))
+
+
 @pytest.mark.parametrize("V", [1, 2, 3, 7, 999, 1000, 1024, 1025, 4097, 8191, 8192, 8193, 40000])
 def test_ragged_vocab_sizes(sampler, variant_samplers, orc, V):
     rng = np.random.default_rng(V + 17)
