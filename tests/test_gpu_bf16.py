@@ -13,7 +13,8 @@ import pytest
 import top_exact_sampling_amd as tes
 import workloads
 from tests.gpu_util import assert_parity, log, to_dev
-from tests.test_gpu_parity import _adversarial_batch, _restream_batch, _split_batch
+from tests.test_gpu_parity import (_above_one_batch, _adversarial_batch, _restream_batch,
+                                   _split_batch)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +94,16 @@ def test_adversarial_rows(sampler, variants, orc, V):
     probs, ks, ps, names = _adversarial_batch(V, rng)
     for label, s in (("default", sampler),) + tuple(variants.items()):
         check(s, orc, probs, ks, ps, 9, 3, "adversarial V=%d %s" % (V, label))
+
+
+@pytest.mark.parametrize("V", [151936, 20000])
+def test_entries_at_and_above_one(sampler, variants, orc, V):
+    # bf16 entries of 1.0 and above (1.5, 3e38 round to bf16 values above
+    # 1.0), NaN and negatives: the saturating mass conversion on 8-entry
+    # vectors, on the segment path and the one-workgroup path.
+    probs, ks, ps = _above_one_batch(V, np.random.default_rng(V + 2))
+    for label, s in (("default", sampler), ("row_topp", variants["row_topp"])):
+        check(s, orc, probs, ks, ps, 21, 5, "above one V=%d %s" % (V, label))
 
 
 @pytest.mark.parametrize("V", [151936, 128256, 20000])

@@ -208,15 +208,10 @@ def test_adversarial_rows(sampler, variant_samplers, orc, V):
         assert_parity(orc, probs, ks, ps, 9, 3, gtok, gren, "adversarial V=%d %s" % (V, label))
 
 
-@pytest.mark.parametrize("V", [151936, 20000])
-def test_entries_at_and_above_one(sampler, variant_samplers, orc, V):
-    # The mass histograms take floor(x * 2^32) from a saturating conversion:
-    # every entry from 1.0 up weighs 2^32 - 1 in the top bin, whose count
-    # (its sum over 2^32 - 1) becomes count * 2^32, and NaN or negative bits
-    # weigh nothing.  Rows with entries of exactly 1.0, finite entries above
-    # it, and NaN / negatives beside them, on the segment path, the
-    # one-workgroup path and the top-k paths.
-    rng = np.random.default_rng(V + 1)
+def _above_one_batch(V, rng):
+    """Rows with entries of exactly 1.0, finite entries above it, and NaN /
+    negatives beside them; each as a top-p-only row, a k=1000 row and a
+    greedy row."""
     rows, ks, ps = [], [], []
 
     def add(x, p):
@@ -244,7 +239,17 @@ def test_entries_at_and_above_one(sampler, variant_samplers, orc, V):
     x = np.full(V, np.float32(1e-40), np.float32)
     x[rng.integers(V)] = 1.0
     add(x, 0.9)
-    probs, ks, ps = np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32)
+    return np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32)
+
+
+@pytest.mark.parametrize("V", [151936, 20000])
+def test_entries_at_and_above_one(sampler, variant_samplers, orc, V):
+    # The mass histograms take floor(x * 2^32) from a saturating conversion:
+    # every entry from 1.0 up weighs 2^32 - 1 in the top bin, whose count
+    # (its sum over 2^32 - 1) becomes count * 2^32, and NaN or negative bits
+    # weigh nothing.  The rows of _above_one_batch on the segment path, the
+    # one-workgroup path and the top-k paths.
+    probs, ks, ps = _above_one_batch(V, np.random.default_rng(V + 1))
     for label, s in (("default", sampler), ("small_segments", variant_samplers["small_segments"]),
                      ("row_topp", variant_samplers["row_topp"])):
         log("[gpu] entries at and above 1.0, V=%d sampler=%s" % (V, label))
