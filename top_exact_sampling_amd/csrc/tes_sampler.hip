@@ -379,7 +379,7 @@ __device__ __forceinline__ u64 key_mass(u32 key) {
 // The top bin thus ends holding kTopUnit times its count, whose mass is
 // count * 2^32.
 constexpr u64 kTopUnit = 0xFFFFFFFFull;
-__device__ __forceinline__ void hist_add(u64* fine, u32 b, int dslot) {
+__device__ __forceinline__ void fine_hist_add(u64* fine, u32 b, int dslot) {
     int bin;
     asm("v_med3_i32 %0, %1, %2, %3"
         : "=v"(bin)
@@ -3017,10 +3017,10 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             }
         }
     };
-    // Branch-free binning of the raw bits (hist_add).  The segment's mass is
-    // the sum of the histogram, taken afterwards; +inf entries (and NaN bits)
-    // show up as signed maxima >= +inf and are counted only by waves that
-    // hold one.
+    // Branch-free binning of the raw bits (fine_hist_add).  The segment's
+    // mass is the sum of the histogram, taken afterwards; +inf entries (and
+    // NaN bits) show up as signed maxima >= +inf and are counted only by
+    // waves that hold one.
     u64 ninf = 0;
     // Min-p on logit rows: the largest mass is that of the top weight 1
     // (2^32), so the floor and its key are known up front; the segment adds
@@ -3038,7 +3038,7 @@ __device__ __attribute__((always_inline)) void do_full(Smem& s, u32 r, u32 seg, 
             for (int e = 0; e < VEC; ++e) {
                 const u32 b = __float_as_uint(VecT<VEC>::get(w, e));
                 mx = max(mx, (int)b);
-                hist_add(shfine(s), b, dslot);
+                fine_hist_add(shfine(s), b, dslot);
                 if (minp) mf += (b >= kf && b <= kInfKey) ? key_mass(b) : 0ull;
             }
             if (__ballot(mx >= (int)kInfKey)) {
@@ -3705,10 +3705,10 @@ __device__ __attribute__((always_inline)) void do_rowtopp(Smem& s, u32 r) {
     u64 tp = p.stats ? wall_clock64() : 0;
     if (threadIdx.x == 0) s.npass = 0;
 
-    // Fine binning of the row, branch free (hist_add, with this lane's
+    // Fine binning of the row, branch free (fine_hist_add, with this lane's
     // discard slot); the top bin is turned into count * 2^32 after the pass.
     const int dslot = -1 - (int)lane_id();
-    auto bin_add = [&](u32 b) { hist_add(shfine(s), b, dslot); };
+    auto bin_add = [&](u32 b) { fine_hist_add(shfine(s), b, dslot); };
 
     auto wb = [&](int b) { return shfine(s)[b]; };
 
