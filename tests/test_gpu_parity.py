@@ -242,6 +242,31 @@ def _above_one_batch(V, rng):
     return np.stack(rows), np.array(ks, np.int32), np.array(ps, np.float32)
 
 
+def test_row_path_over_many_draws(sampler, orc, torch_cuda):
+    # The one-workgroup top-p path predicts the boundary's and the draw's
+    # bins from a prefix of the row; a row whose bins fall outside the
+    # predicted window takes another (exact) pass.  Over twelve draws of the
+    # speculative-verify batch some rows do: tokens must match the oracle
+    # on every draw, and the extra-pass rows must occur.
+    w = wl(5)
+    x = torch_cuda.from_numpy(w.probs).cuda()
+    k = torch_cuda.from_numpy(w.top_k).cuda()
+    p = torch_cuda.from_numpy(w.top_p).cuda()
+    extra = 0
+    for off in range(12):
+        log("[gpu] row path draw %d" % off)
+        g = sampler.sample(x, k, p, w.seed, off)
+        torch_cuda.cuda.synchronize()
+        otok = orc.sample(w.probs, w.top_k, w.top_p, w.seed, off)[0]
+        bad = np.flatnonzero(g.cpu().numpy() != otok)
+        assert bad.size == 0, "draw %d: rows %s differ" % (off, bad[:8])
+        st = sampler.stats(w.B)
+        assert np.all(st[:, 0] == 6), "paths %s" % np.bincount(st[:, 0]).tolist()
+        extra += int(((st[:, 3] > 1) | ((st[:, 7] >> 16) != 0)).sum())
+    log("[gpu]   rows with an extra pass over 12 draws: %d" % extra)
+    assert extra > 0, "no row took the extra pass: the test no longer reaches it"
+
+
 @pytest.mark.parametrize("V", [151936, 20000])
 def test_entries_at_and_above_one(sampler, variant_samplers, orc, V):
     # The mass histograms take floor(x * 2^32) from a saturating conversion:
